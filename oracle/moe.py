@@ -1,0 +1,312 @@
+"""CPU oracle for one GPU's share of a Mixture-of-Experts layer.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline
+leg may import or call this module; the library's product path never does, and this module
+imports nothing from it.  It is plain numpy in float64, written from the pages' description
+of the layer, slow on purpose and meant to be checked by eye.
+
+Pages cited (title, then the section a step follows):
+  [EP-serving]  aiunderstanding.org, "Expert parallelism for MoE serving" (Russian, Wolof and
+                Indonesian versions of one article).
+  [EP-checks]   airouter.kz blog, "Expert parallelism in MoE needs measurements before
+                launch" ("Экспертный параллелизм MoE требует замеров до запуска").
+Steps the pages leave open are marked READING; they follow the layer's specification
+(softmax top-k with lowest-index tie-break and renormalised gates, a SwiGLU expert FFN,
+capacity-factor truncation with dropped-token accounting) in its plainest form.
+
+Parity unpinned: the nearest-rank reading of expert_p50 / expert_p95 in expert_stats()
+(the page's printed example matches no standard percentile rule, so nothing pins it).
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Optional
+
+import numpy as np
+
+
+# ------------------------------------------------------------------------------------------
+# S1  router logits
+# ------------------------------------------------------------------------------------------
+def router_logits(x: np.ndarray, w_router: np.ndarray,
+                  b_router: Optional[np.ndarray] = None) -> np.ndarray:
+    """L[t, e] = sum_i x[t, i] * w_router[e, i] + b_router[e], accumulated in float64 and
+    stored as float32.
+
+    [EP-serving] "Deep dive": a router scores the experts for each token.  READING: the
+    score is a linear map of the token (weights [E, d], nn.Linear layout) plus an optional
+    per-expert bias, and the logits are kept in fp32, the precision both sides route from.
+    """
+    L = np.asarray(x, dtype=np.float64) @ np.asarray(w_router, dtype=np.float64).T
+    if b_router is not None:
+        L = L + np.asarray(b_router, dtype=np.float64)[None, :]
+    return L.astype(np.float32)
+
+
+# ------------------------------------------------------------------------------------------
+# S2  top-k selection and gates
+# ------------------------------------------------------------------------------------------
+def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
+    """idx[t, j] = the (j+1)-th best expert of token t.
+
+    [EP-serving] "Deep dive": the router picks the top-k experts (often 1 or 2) per token.
+    READING: "best" is the order (logit descending, expert index ascending), so equal logits
+    go to the lower index; -0.0 and +0.0 are equal.  Softmax is strictly increasing, so this
+    is the top-k of the softmax probabilities as well.  A stable sort of the negated logits
+    is exactly that order.
+    """
+    L = np.asarray(logits, dtype=np.float32)
+    assert np.all(np.isfinite(L)), "non-finite logits are outside the oracle's contract"
+    T, E = L.shape
+    assert 1 <= k <= E
+    canon = L + np.float32(0.0)  # -0.0 + 0.0 == +0.0
+    order = np.argsort(-canon, axis=1, kind="stable")
+    return order[:, :k].astype(np.int32)
+
+
+def gate_weights(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """w[t, j] = exp(L[t, idx[t, j]] - m) / sum_i exp(L[t, idx[t, i]] - m), m = best logit.
+
+    READING (the layer's specification): softmax over all experts, restricted to the
+    selected ones and renormalised to sum 1.  The full-softmax denominator cancels, so only
+    the selected logits are needed.
+    """
+    L = np.asarray(logits, dtype=np.float64)
+    sel = np.take_along_axis(L, np.asarray(idx, dtype=np.int64), axis=1)
+    m = sel.max(axis=1, keepdims=True)
+    p = np.exp(sel - m)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+# ------------------------------------------------------------------------------------------
+# S4  capacity
+# ------------------------------------------------------------------------------------------
+def capacity(T: int, k: int, E: int, cf: Optional[float]) -> int:
+    """Per-expert capacity C; 0 means no limit.
+
+    [EP-checks] "Capacity factor changes quality, memory and tail latency": capacity is the
+    mean number of tokens per expert times the capacity factor, rounding left to the engine;
+    a disabled limit means effectively unlimited capacity.  [EP-checks] "Mean expert load
+    proves almost nothing" gives the mean as sum_e n_e / E = T*k / E.
+    READING: C = ceil(((cf * T) * k) / E) evaluated in IEEE double; cf None or <= 0 is
+    'no limit'.
+    """
+    if cf is None or not (cf > 0):
+        return 0
+    return int(math.ceil(((float(cf) * T) * k) / E))
+
+
+def effective_capacity(T: int, C: int) -> int:
+    """No expert can receive more than T rows, so 'no limit' and C > T both mean C = T."""
+    return T if (C <= 0 or C > T) else C
+
+
+# ------------------------------------------------------------------------------------------
+# S3-S5  dispatch: counts, capacity truncation, offsets, permutation
+# ------------------------------------------------------------------------------------------
+def dispatch(idx: np.ndarray, E: int, C: int) -> dict:
+    """Routing tables for the single-GPU stand-in of the dispatch all-to-all.
+
+    [EP-serving] "Technical details": tokens are sent to their experts, experts get
+    capacity-limited buffers and overflow tokens are dropped.  [EP-checks] "Capacity factor
+    changes quality, memory and tail latency": in capacity mode overflow is dropped before
+    the exchange, so every keep/drop decision here is made before any row moves.
+    READING (drop priority, not on the pages): first come, first kept, in token order.  The
+    assignment (t, j) -> e has position pos = number of earlier assignments to e in the
+    token-major list (t, j); it is kept iff pos < C.  Kept rows of an expert are stored
+    contiguously in token order; experts follow each other in index order.
+
+    Returns routed_counts n_e, tokens_per_expert c_e = min(n_e, C), expert_offsets [E+1],
+    pos, dest_row [T, k] (-1 when dropped), src_token / src_slot [T*k] (-1 past N),
+    drops (total, per slot, tokens with every slot dropped).
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    Ceff = effective_capacity(T, C)
+    flat = idx.reshape(-1)
+    pos = np.empty(T * k, dtype=np.int64)
+    seen = [0] * E
+    for f in range(T * k):  # token-major walk: f = t * k + j
+        e = int(flat[f])
+        pos[f] = seen[e]
+        seen[e] += 1
+    routed = np.array(seen, dtype=np.int64)
+    kept_counts = np.minimum(routed, Ceff)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept_counts)
+    kept = pos < Ceff
+    dest = np.where(kept, offsets[flat] + pos, -1)
+    N = int(offsets[E])
+    src_token = np.full(T * k, -1, dtype=np.int64)
+    src_slot = np.full(T * k, -1, dtype=np.int64)
+    fk = np.nonzero(kept)[0]
+    src_token[dest[fk]] = fk // k
+    src_slot[dest[fk]] = fk % k
+    dropped = ~kept.reshape(T, k)
+    return {
+        "routed_counts": routed,
+        "tokens_per_expert": kept_counts,
+        "expert_offsets": offsets,
+        "capacity": Ceff,
+        "pos": pos.reshape(T, k),
+        "dest_row": dest.reshape(T, k),
+        "src_token": src_token,
+        "src_slot": src_slot,
+        "n_kept": N,
+        "drops_total": int(dropped.sum()),
+        "drops_per_slot": dropped.sum(axis=0).astype(np.int64),
+        "fully_dropped_tokens": int(dropped.all(axis=1).sum()),
+    }
+
+
+def permute(x: np.ndarray, src_token: np.ndarray, n_kept: int) -> np.ndarray:
+    """X_perm[r] = x[src_token[r]] for the n_kept kept rows (the pack step of [EP-checks]
+    "All-to-all must be profiled separately from compute")."""
+    return np.asarray(x)[np.asarray(src_token[:n_kept], dtype=np.int64)]
+
+
+# ------------------------------------------------------------------------------------------
+# S6-S7  expert FFN
+# ------------------------------------------------------------------------------------------
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn(rows: np.ndarray, w_gate_e: np.ndarray, w_up_e: np.ndarray,
+               w_down_e: np.ndarray) -> np.ndarray:
+    """One expert on a block of rows: silu(r Wg^T) * (r Wu^T), then times Wd^T, in float64.
+
+    [EP-serving] "Deep dive": each expert is a small feed-forward network.  READING (the
+    layer's specification): the SwiGLU form, weights in nn.Linear layout
+    (Wg, Wu: [F, d]; Wd: [d, F]).
+    """
+    r = np.asarray(rows, dtype=np.float64)
+    g = r @ np.asarray(w_gate_e, dtype=np.float64).T
+    u = r @ np.asarray(w_up_e, dtype=np.float64).T
+    h = silu(g) * u
+    return h @ np.asarray(w_down_e, dtype=np.float64).T
+
+
+def expert_ffn(x_perm: np.ndarray, expert_offsets: np.ndarray, w_gate, w_up, w_down
+               ) -> np.ndarray:
+    """Y[r] = FFN_e(X_perm[r]) for each expert's segment [off_e, off_{e+1})."""
+    off = np.asarray(expert_offsets, dtype=np.int64)
+    E = off.shape[0] - 1
+    N = int(off[E])
+    d = np.asarray(x_perm).shape[1]
+    Y = np.zeros((N, d), dtype=np.float64)
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            Y[a:b] = swiglu_ffn(x_perm[a:b], w_gate[e], w_up[e], w_down[e])
+    return Y
+
+
+# ------------------------------------------------------------------------------------------
+# S8  combine
+# ------------------------------------------------------------------------------------------
+def combine(y_perm: np.ndarray, dest_row: np.ndarray, gates: np.ndarray) -> np.ndarray:
+    """out[t] = sum over slots j with dest_row[t, j] >= 0 of gates[t, j] * Y[dest_row[t, j]].
+
+    [EP-serving] "Technical details": the combine step brings the expert outputs back to
+    their tokens.  READING: the gates of dropped assignments are not renormalised, and a
+    token with every slot dropped gets a zero row.
+    """
+    dest = np.asarray(dest_row, dtype=np.int64)
+    w = np.asarray(gates, dtype=np.float64)
+    T, k = dest.shape
+    Y = np.asarray(y_perm, dtype=np.float64)
+    out = np.zeros((T, Y.shape[1]), dtype=np.float64)
+    for j in range(k):
+        m = dest[:, j] >= 0
+        out[m] += w[m, j][:, None] * Y[dest[m, j]]
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# S9  per-layer expert statistics
+# ------------------------------------------------------------------------------------------
+def expert_stats(routed_counts: np.ndarray, T: int, k: int,
+                 tokens_per_expert: Optional[np.ndarray] = None,
+                 dropped: int = 0) -> dict:
+    """The per-layer record of [EP-checks] "Mean expert load proves almost nothing".
+
+    n_e = assignments to expert e after top-k, mean mu = sum_e n_e / E, expert_max and
+    expert_max_to_mean = max / mu.  READING: the statistics are over routed counts (before
+    capacity truncation); p50 / p95 use the nearest rank, s[ceil(q * E) - 1] of the sorted
+    counts (parity unpinned).
+    """
+    n = np.asarray(routed_counts, dtype=np.int64)
+    E = n.shape[0]
+    mu = n.sum() / E
+    s = np.sort(n)
+
+    def nearest_rank(q):
+        return int(s[max(0, math.ceil(q * E) - 1)])
+
+    rec = {
+        "active_tokens": int(T),
+        "top_k": int(k),
+        "routed_per_expert": n.tolist(),
+        "expert_p50": nearest_rank(0.50),
+        "expert_p95": nearest_rank(0.95),
+        "expert_max": int(s[-1]),
+        "expert_mean": float(mu),
+        "expert_max_to_mean": float(s[-1] / mu) if mu > 0 else float("nan"),
+        "dropped_tokens": int(dropped),
+    }
+    if tokens_per_expert is not None:
+        rec["tokens_per_expert"] = np.asarray(tokens_per_expert, dtype=np.int64).tolist()
+    return rec
+
+
+# ------------------------------------------------------------------------------------------
+# the whole layer
+# ------------------------------------------------------------------------------------------
+def moe_layer(x, w_router, b_router, w_gate, w_up, w_down, k: int, C: int,
+              logits: Optional[np.ndarray] = None) -> dict:
+    """Router -> dispatch -> expert FFN -> combine on one GPU's share (expert parallel size
+    1: every expert is local and no all-to-all runs, the control run of [EP-checks]
+    "All-to-all must be profiled separately from compute").
+
+    If `logits` is given the oracle routes from it instead of computing S1.
+    """
+    if logits is None:
+        logits = router_logits(x, w_router, b_router)
+    E = logits.shape[1]
+    idx = select_topk(logits, k)
+    gates = gate_weights(logits, idx)
+    tab = dispatch(idx, E, C)
+    xp = permute(x, tab["src_token"], tab["n_kept"])
+    Y = expert_ffn(xp, tab["expert_offsets"], w_gate, w_up, w_down)
+    out = combine(Y, tab["dest_row"], gates)
+    res = dict(tab)
+    res.update(logits=logits, topk_idx=idx, topk_w=gates, x_perm=xp, y_perm=Y, out=out)
+    return res
+
+
+def token_outputs(x_rows: np.ndarray, idx_rows: np.ndarray, kept_rows: np.ndarray,
+                  gates_rows: np.ndarray,
+                  expert_weights: Callable[[int], tuple]) -> np.ndarray:
+    """out for a sample of tokens, one token at a time, for layers too large to hold.
+
+    Row-wise identity of the layer: Y[dest[t, j]] = FFN_{idx[t, j]}(x[t]), so out[t] needs
+    only token t, its routing row and the weights of its kept experts.
+    expert_weights(e) returns (Wg_e, Wu_e, Wd_e).
+    """
+    xs = np.asarray(x_rows, dtype=np.float64)
+    n, k = np.asarray(idx_rows).shape
+    y = {}
+    need = sorted({int(e) for e, kp in zip(np.ravel(idx_rows), np.ravel(kept_rows)) if kp})
+    for e in need:  # one expert's weights at a time
+        wg, wu, wd = expert_weights(e)
+        for t in range(n):
+            for j in range(k):
+                if kept_rows[t, j] and int(idx_rows[t, j]) == e:
+                    y[(t, j)] = swiglu_ffn(xs[t:t + 1], wg, wu, wd)[0]
+    out = np.zeros_like(xs)
+    for t in range(n):
+        for j in range(k):  # slot order, as in combine()
+            if kept_rows[t, j]:
+                out[t] += float(gates_rows[t, j]) * y[(t, j)]
+    return out
