@@ -1,0 +1,210 @@
+/*
+ * moe.h -- C ABI of one GPU's share of a Mixture-of-Experts layer on MI355X (gfx950).
+ *
+ * The layer: a router (logits GEMM, softmax top-k, renormalised gates), dispatch into
+ * expert-contiguous buffers with capacity truncation, a grouped SwiGLU expert FFN, and a
+ * gate-weighted combine back to token order.  Every call below only enqueues HIP kernels on
+ * the given stream and returns; none synchronises, allocates or frees.
+ *
+ * Pages cited:
+ *   [EP-serving] aiunderstanding.org, "Expert parallelism for MoE serving" (ru / wo / id).
+ *   [EP-checks]  airouter.kz blog, "Expert parallelism in MoE needs measurements before
+ *                launch" ("Экспертный параллелизм MoE требует замеров до запуска").
+ *
+ * Conventions shared by every entry point
+ *   - Shapes: T tokens, d model width, E experts, k experts per token, F expert FFN width,
+ *     capacity C (see moe_shape.capacity).
+ *   - Layouts: row-major.  Weights use the nn.Linear convention [out_features, in_features]
+ *     stacked over experts: w_router [E, d], w_gate and w_up [E, F, d], w_down [E, d, F],
+ *     so every GEMM operand is contiguous along its reduction axis.
+ *   - Types: MOE_BF16 means bf16 activations and weights, fp32 logits, gates and
+ *     accumulation, bf16 hidden/expert/layer outputs.  MOE_F32 means fp32 throughout.
+ *     Index tables are int32.
+ *   - Pointers are device pointers on the current HIP device unless marked "host".  Tensor
+ *     pointers (x, weights, x_perm, y_perm, out) must be 16-byte aligned.
+ *   - The caller owns every buffer; the library keeps no state between calls, so calls
+ *     with distinct workspaces and outputs may run concurrently on different streams.
+ *   - Errors: arguments are validated before anything is enqueued and a negative
+ *     moe_status is returned on failure (nothing is launched).  A failed launch returns
+ *     MOE_ERR_HIP.  T = 0 is valid.
+ *   - Limits: 1 <= E <= 1024, 1 <= k <= min(E, 64), d and F multiples of 128,
+ *     T * k < 2^31.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad shape value, k > E, ... */
+  MOE_ERR_UNSUPPORTED = -2, /* outside the limits above or unknown dtype */
+  MOE_ERR_ALIGNMENT = -3,   /* a tensor pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = -4,   /* workspace null or smaller than moe_workspace_size() */
+  MOE_ERR_HIP = -5          /* a kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef struct {
+  int64_t T;        /* tokens (rows of x) */
+  int64_t d;        /* model width */
+  int64_t E;        /* experts */
+  int64_t k;        /* experts per token */
+  int64_t F;        /* expert FFN width */
+  int64_t capacity; /* per-expert capacity C; <= 0 means no limit (C = T) */
+  int32_t dtype;    /* moe_dtype */
+  int32_t reserved; /* must be 0 */
+} moe_shape;
+
+/* Drop counters written by moe_dispatch / moe_layer: drops[0] = dropped assignments,
+ * drops[1 + j] = dropped assignments of slot j (j < k), drops[1 + k] = tokens whose k
+ * assignments were all dropped.  Length k + 2. */
+
+/* Regions of the workspace, for callers that want to read intermediate tables of
+ * moe_layer (see moe_workspace_layout). */
+typedef enum {
+  MOE_WS_LOGITS = 0,  /* float [T, E] */
+  MOE_WS_TOPK_IDX,    /* int32 [T, k] */
+  MOE_WS_TOPK_W,      /* float [T, k] */
+  MOE_WS_ROUTED,      /* int32 [E]   routed counts n_e */
+  MOE_WS_KEPT,        /* int32 [E]   kept counts c_e */
+  MOE_WS_OFFSETS,     /* int32 [E+1] */
+  MOE_WS_SRC_TOKEN,   /* int32 [R]   R = moe_max_rows() */
+  MOE_WS_DEST_ROW,    /* int32 [T, k] */
+  MOE_WS_DROPS,       /* int32 [k+2] */
+  MOE_WS_STATUS,      /* int32 [1] */
+  MOE_WS_TILE_HIST,   /* internal */
+  MOE_WS_TILE_BASE,   /* internal */
+  MOE_WS_SCHED,       /* internal */
+  MOE_WS_X_PERM,      /* [R, d] */
+  MOE_WS_H,           /* [R, F] */
+  MOE_WS_Y_PERM,      /* [R, d] */
+  MOE_WS_COUNT
+} moe_ws_region;
+
+/* Per-expert capacity from a capacity factor ([EP-checks], "Capacity factor changes
+ * quality, memory and tail latency": mean tokens per expert times the factor; the mean is
+ * T*k/E by the section "Mean expert load proves almost nothing").  Returns
+ * ceil(((cf * T) * k) / E) evaluated in IEEE double; 0 (no limit) when cf <= 0; -1 when T < 0,
+ * k < 1 or E < 1 or cf is not finite.  Host function. */
+int64_t moe_capacity(int64_t T, int64_t k, int64_t E, double cf);
+
+/* Upper bound R on kept rows: min(T*k, E*C) with C = T when unlimited.  x_perm, y_perm
+ * and src_token hold R rows.  Returns -1 for an invalid shape.  Host function. */
+int64_t moe_max_rows(const moe_shape* shape);
+
+/* Bytes of device workspace that any call below needs for this shape (the same size
+ * serves all of them); 0 for an invalid shape.  Host function. */
+size_t moe_workspace_size(const moe_shape* shape);
+
+/* Byte offsets (host array of MOE_WS_COUNT) of each region in the workspace; a region of
+ * size 0 still gets an offset.  Returns a moe_status.  Host function. */
+int moe_workspace_layout(const moe_shape* shape, int64_t* offsets);
+
+/* Human-readable name of a moe_status value (static string).  Host function. */
+const char* moe_status_string(int status);
+
+/*
+ * moe_route -- S1 router logits and S2 top-k gating.
+ * [EP-serving] "Deep dive": a router picks the top-k experts (often 1 or 2) of each token.
+ * Layer specification: logits L = x w_router^T + b_router (fp32); the k largest logits
+ * per token under (value descending, expert index ascending), -0.0 equal to +0.0; gates
+ * w_j = exp(L_j - L_max) / sum over the k selected exp(L_i - L_max) (softmax restricted to
+ * the selection and renormalised).
+ *   x          [T, d] dtype          (unused when logits_given)
+ *   w_router   [E, d] dtype          (unused when logits_given)
+ *   b_router   [E] float, nullable
+ *   logits     [T, E] float: output, or input when logits_given != 0
+ *   topk_idx   [T, k] int32 out, slot 0 = best expert
+ *   topk_w     [T, k] float out
+ *   status     [1] int32 out, nullable: number of tokens with a non-finite logit (their
+ *              selection and gates are then unspecified)
+ */
+int moe_route(const moe_shape* shape, const void* x, const void* w_router,
+              const float* b_router, float* logits, int logits_given, int32_t* topk_idx,
+              float* topk_w, int32_t* status, hipStream_t stream);
+
+/*
+ * moe_dispatch -- S3-S5: the single-GPU stand-in of the dispatch all-to-all.
+ * [EP-serving] "Technical details" (tokens go to the experts they chose; experts have
+ * capacity-limited buffers; overflow is dropped) and [EP-checks] "Capacity factor changes
+ * quality, memory and tail latency" (overflow is dropped before the exchange).
+ * Drop priority: first come, first kept in token order.  The assignment (t, j) -> e is
+ * kept iff fewer than C earlier assignments (token-major order) went to e.  Kept rows of
+ * expert e fill rows [expert_offsets[e], expert_offsets[e+1]) of x_perm in token order.
+ * Entries of topk_idx outside [0, E) are dropped.
+ *   topk_idx          [T, k] int32 in
+ *   x                 [T, d] dtype in
+ *   workspace         moe_workspace_size() bytes; workspace_bytes its size
+ *   routed_counts     [E] int32 out: n_e, assignments routed to e
+ *   tokens_per_expert [E] int32 out: c_e = min(n_e, C)
+ *   expert_offsets    [E+1] int32 out: exclusive scan of c_e
+ *   src_token         [R] int32 out: token of each kept row, -1 for rows >= N = sum c_e
+ *   dest_row          [T, k] int32 out: row of each assignment in x_perm, -1 if dropped
+ *   drops             [k+2] int32 out (see above)
+ *   x_perm            [R, d] dtype out: x_perm[r] = x[src_token[r]] for r < N
+ */
+int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const void* x,
+                 void* workspace, size_t workspace_bytes, int32_t* routed_counts,
+                 int32_t* tokens_per_expert, int32_t* expert_offsets, int32_t* src_token,
+                 int32_t* dest_row, int32_t* drops, void* x_perm, hipStream_t stream);
+
+/*
+ * moe_expert_ffn -- S6-S7: grouped SwiGLU FFN over the expert-contiguous rows.
+ * [EP-serving] "Deep dive" (each expert is a small feed-forward network) and "Technical
+ * details" (expert buffers keep the GEMM shapes regular); layer specification: for rows r
+ * of expert e, h = silu(x_perm[r] w_gate[e]^T) * (x_perm[r] w_up[e]^T), rounded to dtype,
+ * and y_perm[r] = h w_down[e]^T.  Row counts per expert are read on the device from
+ * expert_offsets; rows >= expert_offsets[E] are not written.
+ *   x_perm          [R, d] dtype in
+ *   expert_offsets  [E+1] int32 in (non-decreasing, expert_offsets[E] <= R)
+ *   w_gate, w_up    [E, F, d] dtype; w_down [E, d, F] dtype
+ *   workspace       holds h [R, F] and the tile schedule
+ *   y_perm          [R, d] dtype out
+ */
+int moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int32_t* expert_offsets,
+                   const void* w_gate, const void* w_up, const void* w_down, void* workspace,
+                   size_t workspace_bytes, void* y_perm, hipStream_t stream);
+
+/*
+ * moe_combine -- S8: gate-weighted sum back to token order, without atomics.
+ * [EP-serving] "Technical details" (the combine step returns expert outputs to their
+ * tokens); layer specification: out[t] = sum over slots j = 0..k-1 in order, skipping
+ * dropped ones (dest_row < 0), of topk_w[t, j] * y_perm[dest_row[t, j]], accumulated in
+ * fp32.  Gates of dropped assignments are not renormalised; a token with every slot dropped
+ * gets a zero row.
+ *   y_perm [R, d] dtype in; dest_row [T, k] int32 in; topk_w [T, k] float in
+ *   out    [T, d] dtype out
+ */
+int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* dest_row,
+                const float* topk_w, void* out, hipStream_t stream);
+
+/*
+ * moe_layer -- the whole layer: moe_route, moe_dispatch, moe_expert_ffn, moe_combine on one
+ * stream, with every intermediate in the workspace (regions in moe_ws_region).  This is
+ * the expert-parallel-size-1 configuration of [EP-checks] "All-to-all must be profiled
+ * separately from compute": every expert is local and no all-to-all runs.
+ *   out               [T, d] dtype out
+ *   routed_counts, tokens_per_expert [E] int32 out, nullable (then kept in the workspace)
+ *   drops             [k+2] int32 out, nullable
+ *   status            [1] int32 out, nullable (non-finite logit count, as in moe_route)
+ */
+int moe_layer(const moe_shape* shape, const void* x, const void* w_router,
+              const float* b_router, const void* w_gate, const void* w_up, const void* w_down,
+              void* workspace, size_t workspace_bytes, void* out, int32_t* routed_counts,
+              int32_t* tokens_per_expert, int32_t* drops, int32_t* status,
+              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

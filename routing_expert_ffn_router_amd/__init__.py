@@ -1,0 +1,228 @@
+"""One GPU's share of a Mixture-of-Experts layer on MI355X (gfx950).
+
+A thin ctypes binding of libmoe.so, whose C ABI is declared in include/moe.h.  The functions
+here only marshal arguments (device pointers of torch tensors, the current HIP stream);
+every step of the layer runs in the library's HIP kernels.  PyTorch provides device memory
+and streams.  If libmoe.so is missing, loading fails with an error: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe.h")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_ALIGNMENT = -3
+MOE_ERR_WORKSPACE = -4
+MOE_ERR_HIP = -5
+
+MOE_F32 = 0
+MOE_BF16 = 1
+
+WS_REGIONS = ["logits", "topk_idx", "topk_w", "routed", "kept", "offsets", "src_token",
+              "dest_row", "drops", "status", "tile_hist", "tile_base", "sched", "x_perm", "h",
+              "y_perm"]
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("F", ctypes.c_int64), ("capacity", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"MoeShape(T={self.T}, d={self.d}, E={self.E}, k={self.k}, F={self.F}, "
+                f"capacity={self.capacity}, dtype={'bf16' if self.dtype == 1 else 'f32'})")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+_lib = None
+_P = ctypes.c_void_p
+_S = ctypes.POINTER(MoeShape)
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoe.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    i64, i32, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "moe_capacity": (i64, [i64, i64, i64, ctypes.c_double]),
+        "moe_max_rows": (i64, [_S]),
+        "moe_workspace_size": (sz, [_S]),
+        "moe_workspace_layout": (i32, [_S, ctypes.POINTER(i64)]),
+        "moe_status_string": (ctypes.c_char_p, [i32]),
+        "moe_route": (i32, [_S, _P, _P, _P, _P, i32, _P, _P, _P, _P]),
+        "moe_dispatch": (i32, [_S, _P, _P, _P, sz, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "moe_expert_ffn": (i32, [_S, _P, _P, _P, _P, _P, _P, sz, _P, _P]),
+        "moe_combine": (i32, [_S, _P, _P, _P, _P, _P]),
+        "moe_layer": (i32, [_S, _P, _P, _P, _P, _P, _P, _P, sz, _P, _P, _P, _P, _P, _P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER_PATH) -> list:
+    """Names of the functions include/moe.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return load_library().moe_status_string(status).decode()
+
+
+def shape(T: int, d: int, E: int, k: int, F: int, capacity: int = 0,
+          dtype: int = MOE_BF16) -> MoeShape:
+    return MoeShape(T, d, E, k, F, capacity, dtype, 0)
+
+
+def capacity(T: int, k: int, E: int, cf: Optional[float]) -> int:
+    """Per-expert capacity of a capacity factor (0 = no limit); see moe_capacity."""
+    return int(load_library().moe_capacity(T, k, E, 0.0 if cf is None else float(cf)))
+
+
+def max_rows(s: MoeShape) -> int:
+    return int(load_library().moe_max_rows(ctypes.byref(s)))
+
+
+def workspace_size(s: MoeShape) -> int:
+    return int(load_library().moe_workspace_size(ctypes.byref(s)))
+
+
+def workspace_layout(s: MoeShape) -> dict:
+    offs = (ctypes.c_int64 * len(WS_REGIONS))()
+    rc = load_library().moe_workspace_layout(ctypes.byref(s), offs)
+    if rc != MOE_OK:
+        raise MoeError("moe_workspace_layout", rc)
+    return {n: int(o) for n, o in zip(WS_REGIONS, offs)}
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check(fn: str, rc: int):
+    if rc != MOE_OK:
+        raise MoeError(fn, rc)
+
+
+def route(s: MoeShape, x, w_router, b_router, logits, topk_idx, topk_w, status=None,
+          logits_given: bool = False, stream=None) -> None:
+    _check("moe_route", load_library().moe_route(
+        ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(b_router), _ptr(logits),
+        int(bool(logits_given)), _ptr(topk_idx), _ptr(topk_w), _ptr(status), _stream(stream)))
+
+
+def dispatch(s: MoeShape, topk_idx, x, workspace, routed_counts, tokens_per_expert,
+             expert_offsets, src_token, dest_row, drops, x_perm, stream=None) -> None:
+    _check("moe_dispatch", load_library().moe_dispatch(
+        ctypes.byref(s), _ptr(topk_idx), _ptr(x), _ptr(workspace), _nbytes(workspace),
+        _ptr(routed_counts), _ptr(tokens_per_expert), _ptr(expert_offsets), _ptr(src_token),
+        _ptr(dest_row), _ptr(drops), _ptr(x_perm), _stream(stream)))
+
+
+def expert_ffn(s: MoeShape, x_perm, expert_offsets, w_gate, w_up, w_down, workspace, y_perm,
+               stream=None) -> None:
+    _check("moe_expert_ffn", load_library().moe_expert_ffn(
+        ctypes.byref(s), _ptr(x_perm), _ptr(expert_offsets), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(workspace), _nbytes(workspace), _ptr(y_perm), _stream(stream)))
+
+
+def combine(s: MoeShape, y_perm, dest_row, topk_w, out, stream=None) -> None:
+    _check("moe_combine", load_library().moe_combine(
+        ctypes.byref(s), _ptr(y_perm), _ptr(dest_row), _ptr(topk_w), _ptr(out),
+        _stream(stream)))
+
+
+def layer(s: MoeShape, x, w_router, b_router, w_gate, w_up, w_down, workspace, out,
+          routed_counts=None, tokens_per_expert=None, drops=None, status=None,
+          stream=None) -> None:
+    _check("moe_layer", load_library().moe_layer(
+        ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(b_router), _ptr(w_gate), _ptr(w_up),
+        _ptr(w_down), _ptr(workspace), _nbytes(workspace), _ptr(out), _ptr(routed_counts),
+        _ptr(tokens_per_expert), _ptr(drops), _ptr(status), _stream(stream)))
+
+
+def workspace_view(workspace, s: MoeShape, region: str):
+    """A typed view of one workspace region (for reading moe_layer's intermediate tables)."""
+    import torch
+
+    lay = workspace_layout(s)
+    off = lay[region]
+    T, E, k, d, F = s.T, s.E, s.k, s.d, s.F
+    R = max_rows(s)
+    act = torch.bfloat16 if s.dtype == MOE_BF16 else torch.float32
+    spec = {
+        "logits": (torch.float32, (T, E)), "topk_idx": (torch.int32, (T, k)),
+        "topk_w": (torch.float32, (T, k)), "routed": (torch.int32, (E,)),
+        "kept": (torch.int32, (E,)), "offsets": (torch.int32, (E + 1,)),
+        "src_token": (torch.int32, (R,)), "dest_row": (torch.int32, (T, k)),
+        "drops": (torch.int32, (k + 2,)), "status": (torch.int32, (1,)),
+        "x_perm": (act, (R, d)), "h": (act, (R, F)), "y_perm": (act, (R, d)),
+    }
+    dt, shp = spec[region]
+    n = 1
+    for v in shp:
+        n *= v
+    esz = torch.tensor([], dtype=dt).element_size()
+    return workspace[off:off + n * esz].view(dt).view(shp)
+
+
+class MoELayer:
+    """Convenience owner of the workspace and outputs of moe_layer for one shape."""
+
+    def __init__(self, s: MoeShape, device="cuda"):
+        import torch
+
+        self.shape = s
+        self.workspace = torch.empty(workspace_size(s), dtype=torch.uint8, device=device)
+        act = torch.bfloat16 if s.dtype == MOE_BF16 else torch.float32
+        self.out = torch.empty((s.T, s.d), dtype=act, device=device)
+        self.routed_counts = torch.empty(s.E, dtype=torch.int32, device=device)
+        self.tokens_per_expert = torch.empty(s.E, dtype=torch.int32, device=device)
+        self.drops = torch.empty(s.k + 2, dtype=torch.int32, device=device)
+        self.status = torch.empty(1, dtype=torch.int32, device=device)
+
+    def __call__(self, x, w_router, b_router, w_gate, w_up, w_down, stream=None):
+        layer(self.shape, x, w_router, b_router, w_gate, w_up, w_down, self.workspace,
+              self.out, self.routed_counts, self.tokens_per_expert, self.drops, self.status,
+              stream)
+        return self.out
+
+    def view(self, region: str):
+        return workspace_view(self.workspace, self.shape, region)

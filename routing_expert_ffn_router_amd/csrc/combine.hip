@@ -1,0 +1,59 @@
+// S8: gate-weighted combine back to token order.
+//
+// [EP-serving] aiunderstanding.org, "Expert parallelism for MoE serving", section
+// "Technical details": the combine step brings expert outputs back to their tokens.  On one
+// GPU it is a gather: every token reads its k expert rows through dest_row (the inverse of
+// the dispatch permutation), so no two threads write the same output and no atomics are
+// needed.  Slots are summed in order 0..k-1 in fp32, which makes the result deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+template <class T>
+__global__ void __launch_bounds__(256)
+combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ dest,
+               const float* __restrict__ w, T* __restrict__ out, int64_t T_, int d, int k) {
+  constexpr int P = Elt<T>::kPerChunk;
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= T_) return;
+  const int nchunks = d / P;
+  const int32_t* dt = dest + t * k;
+  const float* wt = w + t * k;
+  for (int c = lane; c < nchunks; c += kWave) {
+    float acc[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) acc[i] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int r = dt[j];
+      if (r < 0) continue;
+      const float g = wt[j];
+      const u32x4 v = ld16(y + (int64_t)r * d + (int64_t)c * P);
+      const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+      for (int i = 0; i < P; ++i) acc[i] = fmaf(g, Elt<T>::to_f32(e[i]), acc[i]);
+    }
+    u32x4 o;
+    T* oe = reinterpret_cast<T*>(&o);
+#pragma unroll
+    for (int i = 0; i < P; ++i) oe[i] = Elt<T>::from_f32(acc[i]);
+    st16(out + t * d + (int64_t)c * P, o);
+  }
+}
+
+hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* dest_row,
+                          const float* topk_w, void* out, int64_t T, int64_t d, int64_t k,
+                          hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((T + 3) / 4);
+  if (dtype == 1)
+    combine_kernel<bf16><<<blocks, 256, 0, s>>>((const bf16*)y_perm, dest_row, topk_w,
+                                                (bf16*)out, T, (int)d, (int)k);
+  else
+    combine_kernel<float><<<blocks, 256, 0, s>>>((const float*)y_perm, dest_row, topk_w,
+                                                 (float*)out, T, (int)d, (int)k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,188 @@
+// S3-S5: the single-GPU stand-in of the dispatch all-to-all.
+//
+// [EP-serving] aiunderstanding.org, "Expert parallelism for MoE serving", section
+// "Technical details": tokens go to the experts they chose, experts have capacity-limited
+// buffers and overflow is dropped.  [EP-checks] airouter.kz, "Expert parallelism in MoE
+// needs measurements before launch", section "Capacity factor changes quality, memory and
+// tail latency": the overflow is dropped before the exchange, so every keep/drop decision
+// below is final before a single row moves.
+//
+// Drop priority is first come, first kept in token order: the flat assignment list
+// f = t * k + j is stably counting-sorted by expert, and an assignment is kept iff its
+// position among its expert's assignments is below the capacity C.
+//
+//   K3 tile_hist   per tile of flat assignments, an LDS histogram over experts
+//   K4 scan        per expert, the exclusive scan over tiles, then counts, capacity,
+//                  offsets (exclusive scan over experts) and zeroed drop counters
+//   K5 rank        per assignment, its position = tile base + earlier waves of the tile
+//                  + rank inside the wave (wave ballots on the expert id bits); keep/drop,
+//                  dest_row, src_token and drop counters
+//   K5b gather     x_perm[r] = x[src_token[r]] with 16-byte vector copies
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__global__ void __launch_bounds__(kTileMax)
+tile_hist_kernel(const int32_t* __restrict__ idx, int64_t total, int te, int E,
+                 int32_t* __restrict__ hist) {
+  extern __shared__ int32_t s_cnt[];  // [E]
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_cnt[e] = 0;
+  __syncthreads();
+  const int64_t f = (int64_t)blockIdx.x * te + threadIdx.x;
+  if ((int)threadIdx.x < te && f < total) {
+    const int e = idx[f];
+    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(int64_t)blockIdx.x * E + e] = s_cnt[e];
+}
+
+__global__ void __launch_bounds__(1024)
+scan_kernel(const int32_t* __restrict__ hist, int ntiles, int E, int C, int k,
+            int32_t* __restrict__ tile_base, int32_t* __restrict__ routed,
+            int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
+            int32_t* __restrict__ drops) {
+  __shared__ int smem[17];
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E) {
+    int run = 0;
+    for (int t = 0; t < ntiles; ++t) {
+      const int64_t i = (int64_t)t * E + e;
+      const int h = hist[i];
+      tile_base[i] = run;
+      run += h;
+    }
+    routed[e] = run;
+    c = run < C ? run : C;
+    kept[e] = c;
+  }
+  int total;
+  const int ex = block_exclusive_scan(c, smem, &total);
+  if (e < E) offsets[e] = ex;
+  if (threadIdx.x == 0) offsets[E] = total;
+  for (int i = threadIdx.x; i < k + 2; i += blockDim.x) drops[i] = 0;
+}
+
+__global__ void __launch_bounds__(kTileMax)
+rank_kernel(const int32_t* __restrict__ idx, int64_t total, int te, int k, int E, int C,
+            int nbits, const int32_t* __restrict__ tile_base,
+            const int32_t* __restrict__ offsets, int32_t* __restrict__ dest_row,
+            int32_t* __restrict__ src_token, int32_t* __restrict__ drops) {
+  extern __shared__ int32_t sm[];
+  constexpr int kWaves = kTileMax / kWave;
+  int32_t* s_cnt = sm;                          // [kWaves][E] per-wave expert counts
+  int32_t* s_tokdrop = sm + kWaves * E;         // [kTileMax] dropped slots per token
+  int32_t* s_drop = s_tokdrop + kTileMax;       // [k + 2] block drop counters
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  for (int i = tid; i < kWaves * E; i += blockDim.x) s_cnt[i] = 0;
+  s_tokdrop[tid] = 0;
+  for (int i = tid; i < k + 2; i += blockDim.x) s_drop[i] = 0;
+  __syncthreads();
+
+  const int64_t f = (int64_t)blockIdx.x * te + tid;
+  const bool active = tid < te && f < total;
+  const int e = active ? idx[f] : -1;
+  const bool valid = active && e >= 0 && e < E;
+
+  // lanes of this wave holding the same expert: intersect the ballots of every id bit
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t m = __ballot(bit);
+    same &= bit ? m : ~m;
+  }
+  const int rank = __popcll(same & ((1ull << lane) - 1ull));
+  if (valid && rank == 0) s_cnt[wave * E + e] = __popcll(same);
+  __syncthreads();
+
+  bool dropped = active;
+  if (valid) {
+    int pos = tile_base[(int64_t)blockIdx.x * E + e] + rank;
+    for (int w = 0; w < wave; ++w) pos += s_cnt[w * E + e];
+    const bool keep = pos < C;
+    dropped = !keep;
+    const int r = keep ? offsets[e] + pos : -1;
+    dest_row[f] = r;
+    if (keep) src_token[r] = (int)(f / k);
+  } else if (active) {
+    dest_row[f] = -1;
+  }
+  if (dropped) {
+    atomicAdd(&s_drop[0], 1);
+    atomicAdd(&s_drop[1 + (int)(f % k)], 1);
+    atomicAdd(&s_tokdrop[tid / k], 1);
+  }
+  __syncthreads();
+  // the tile starts at a multiple of k, so token-local index is tid / k
+  if (active && (tid % k) == 0 && s_tokdrop[tid / k] == k) atomicAdd(&s_drop[k + 1], 1);
+  __syncthreads();
+  for (int i = tid; i < k + 2; i += blockDim.x)
+    if (s_drop[i]) atomicAdd(&drops[i], s_drop[i]);
+}
+
+// One wave per row, four rows per block, grid-stride over the R row slots.  Rows past
+// N = offsets[E] only get src_token = -1.
+__global__ void __launch_bounds__(256)
+gather_rows_kernel(const char* __restrict__ x, int32_t* __restrict__ src_token,
+                   const int32_t* __restrict__ offsets, int E, int64_t R, int64_t row_bytes,
+                   char* __restrict__ x_perm) {
+  const int64_t N = offsets[E];
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int64_t nchunks = row_bytes / 16;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < R; r += (int64_t)gridDim.x * 4) {
+    if (r >= N) {
+      if (lane == 0) src_token[r] = -1;
+      continue;
+    }
+    const int64_t t = src_token[r];
+    const char* src = x + t * row_bytes;
+    char* dst = x_perm + r * row_bytes;
+    int64_t c = lane;
+    for (; c + 3 * kWave < nchunks; c += 4 * kWave) {
+      const u32x4 v0 = ld16(src + (c + 0 * kWave) * 16), v1 = ld16(src + (c + 1 * kWave) * 16);
+      const u32x4 v2 = ld16(src + (c + 2 * kWave) * 16), v3 = ld16(src + (c + 3 * kWave) * 16);
+      st16(dst + (c + 0 * kWave) * 16, v0);
+      st16(dst + (c + 1 * kWave) * 16, v1);
+      st16(dst + (c + 2 * kWave) * 16, v2);
+      st16(dst + (c + 3 * kWave) * 16, v3);
+    }
+    for (; c < nchunks; c += kWave) st16(dst + c * 16, ld16(src + c * 16));
+  }
+}
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+  const int64_t total = a.T * a.k;
+  const int te = (int)dispatch_tile_entries(a.k);
+  const int ntiles = (int)dispatch_ntiles(a.T, a.k);
+  int nbits = 0;
+  while ((1ll << nbits) < a.E) ++nbits;
+  hipError_t err;
+  if (ntiles > 0) {
+    tile_hist_kernel<<<ntiles, kTileMax, a.E * sizeof(int32_t), s>>>(a.topk_idx, total, te,
+                                                                     (int)a.E, a.tile_hist);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  scan_kernel<<<1, 1024, 0, s>>>(a.tile_hist, ntiles, (int)a.E, (int)a.C, (int)a.k,
+                                 a.tile_base, a.routed, a.kept, a.offsets, a.drops);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (ntiles > 0) {
+    const size_t lds = ((kTileMax / kWave) * a.E + kTileMax + a.k + 2) * sizeof(int32_t);
+    rank_kernel<<<ntiles, kTileMax, lds, s>>>(a.topk_idx, total, te, (int)a.k, (int)a.E,
+                                              (int)a.C, nbits, a.tile_base, a.offsets,
+                                              a.dest_row, a.src_token, a.drops);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (a.R > 0) {
+    int64_t blocks = (a.R + 3) / 4;
+    if (blocks > 4096) blocks = 4096;
+    gather_rows_kernel<<<(unsigned)blocks, 256, 0, s>>>(
+        (const char*)a.x, a.src_token, a.offsets, (int)a.E, a.R, a.d * a.elt_bytes,
+        (char*)a.x_perm);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace moe

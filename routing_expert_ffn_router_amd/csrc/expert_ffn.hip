@@ -1,0 +1,289 @@
+// S6-S7: grouped SwiGLU expert FFN over the expert-contiguous rows of x_perm.
+//
+// [EP-serving] aiunderstanding.org, "Expert parallelism for MoE serving", sections "Deep
+// dive" (each expert is a small feed-forward network) and "Technical details" (expert
+// buffers keep the expert GEMMs regular); [EP-checks] airouter.kz, "Expert parallelism in
+// MoE needs measurements before launch", section "All-to-all must be profiled separately
+// from compute" (grouped GEMMs for the expert compute).  Layer specification:
+//     h = silu(X Wg[e]^T) * (X Wu[e]^T)  (rounded to the storage type),  Y = h Wd[e]^T.
+//
+// One kernel template serves both GEMMs: C[rows of expert e, n] = A[rows] . B_e[n]^T with
+// A and B both contiguous along the reduction axis (nn.Linear layout).
+//   - Variable M per expert: the m-tiles of all experts are numbered consecutively; a
+//     schedule kernel writes tile_prefix[e] = sum_{e' < e} ceil(c_e' / BM) on the device,
+//     and each block finds its expert by binary search, so the host never waits for the
+//     routing.  The grid is sized from an upper bound and surplus blocks exit at once.
+//   - Block tile BM x BN_W weight rows, K in 128-byte steps staged through LDS (two stages,
+//     global loads of step k+1 in flight while step k is multiplied).  LDS rows are 128
+//     bytes with the 16-byte chunks XOR-swizzled by (row & 7), so the MFMA fragment reads
+//     (16 rows x one chunk column) hit distinct banks.
+//   - SwiGLU: the B tile of a wave holds NT/2 tiles of gate rows followed by the NT/2 tiles
+//     of up rows for the same output columns, so gate and up accumulators of one output
+//     element sit in the same lane and the epilogue computes silu(g) * u in registers.
+//   - Block order: blocks are dealt round-robin to the 8 XCDs; the logical tile index is
+//     remapped so each XCD walks a contiguous range in which neighbouring tiles share the
+//     A rows (same m-tile) and the B rows (same n-group), keeping both in that XCD's L2.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__device__ inline float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+template <int WAVES_M, int WAVES_N, int MT, int NT, bool SWIGLU>
+struct GemmShape {
+  static constexpr int kThreads = WAVES_M * WAVES_N * kWave;
+  static constexpr int BM = WAVES_M * MT * 16;
+  static constexpr int kWaveRows = NT * 16;             // weight rows per wave
+  static constexpr int BNW = WAVES_N * kWaveRows;       // weight rows per block
+  static constexpr int BN = SWIGLU ? BNW / 2 : BNW;     // output columns per block
+  // 16-byte chunks per thread and stage (A: the last round may leave threads idle)
+  static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;
+  static constexpr bool kAPartial = BM * 8 % kThreads != 0;
+  static constexpr int kBChunks = BNW * 8 / kThreads;
+  static constexpr int kStageBytes = (BM + BNW) * 128;
+  static_assert(BNW * 8 % kThreads == 0, "tile / thread mismatch");
+  static_assert(!SWIGLU || NT % 2 == 0, "SwiGLU needs gate and up halves");
+};
+
+// tile_prefix for two row-tile heights at once (GEMM1 and GEMM2 may differ).
+__global__ void __launch_bounds__(1024)
+tile_schedule_kernel(const int32_t* __restrict__ offsets, int E, int bm1, int bm2,
+                     int32_t* __restrict__ pre1, int32_t* __restrict__ pre2) {
+  __shared__ int smem[17];
+  const int e = threadIdx.x;
+  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+  int tot1, tot2;
+  const int x1 = block_exclusive_scan((c + bm1 - 1) / bm1, smem, &tot1);
+  const int x2 = block_exclusive_scan((c + bm2 - 1) / bm2, smem, &tot2);
+  if (e < E) {
+    pre1[e] = x1;
+    pre2[e] = x2;
+  }
+  if (threadIdx.x == 0) {
+    pre1[E] = tot1;
+    pre2[E] = tot2;
+  }
+}
+
+template <class T, int WAVES_M, int WAVES_N, int MT, int NT, bool SWIGLU>
+__global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
+grouped_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
+                    const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C,
+                    int K, int N_out, const int32_t* __restrict__ offsets,
+                    const int32_t* __restrict__ tile_prefix, int E, int m_tiles_max,
+                    int n_tiles, int group_n, int grid_logical) {
+  using S = GemmShape<WAVES_M, WAVES_N, MT, NT, SWIGLU>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  // ---- block -> (expert, m-tile, n-tile) ------------------------------------------------
+  const int bid = blockIdx.x;
+  const int per_xcd = gridDim.x >> 3;
+  const int logical = (bid & 7) * per_xcd + (bid >> 3);
+  if (logical >= grid_logical) return;
+  const int per_group = m_tiles_max * group_n;
+  const int grp = logical / per_group, rem = logical - grp * per_group;
+  const int mt = rem / group_n, nt = grp * group_n + (rem - (rem / group_n) * group_n);
+  if (nt >= n_tiles) return;
+  if (mt >= tile_prefix[E]) return;
+  int lo = 0, hi = E - 1;  // largest e with tile_prefix[e] <= mt
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int m_begin = offsets[e] + (mt - tile_prefix[e]) * S::BM;
+  const int m_end = offsets[e + 1];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int64_t row_bytes = (int64_t)K * sizeof(T);
+
+  // ---- per-thread global source rows (fixed over k) ---------------------------------------
+  const char* a_src[S::kAChunks];
+  int a_lds[S::kAChunks];
+#pragma unroll
+  for (int i = 0; i < S::kAChunks; ++i) {
+    const int c0 = tid + i * S::kThreads;
+    const int c = (S::kAPartial && c0 >= S::BM * 8) ? c0 % (S::BM * 8) : c0;  // duplicate load
+    const int r = c >> 3, ch = c & 7;
+    const int gr = min(m_begin + r, m_end - 1);  // rows past the expert: computed, not stored
+    a_src[i] = reinterpret_cast<const char*>(A) + (int64_t)gr * row_bytes + ch * 16;
+    a_lds[i] = r * 128 + ((ch ^ (r & 7)) << 4);
+  }
+  const char* b_src[S::kBChunks];
+  int b_lds[S::kBChunks];
+  const T* B0e = B0 + (int64_t)e * b_expert_stride;
+  const T* B1e = SWIGLU ? B1 + (int64_t)e * b_expert_stride : nullptr;
+#pragma unroll
+  for (int i = 0; i < S::kBChunks; ++i) {
+    const int c = tid + i * S::kThreads, r = c >> 3, ch = c & 7;
+    const T* rowp;
+    if (SWIGLU) {
+      const int w = r / S::kWaveRows, within = r % S::kWaveRows, half = S::kWaveRows / 2;
+      // columns past N_out (last n-tile) are clamped: computed, never stored
+      const int col = min(nt * S::BN + w * half + (within % half), N_out - 1);
+      rowp = (within < half ? B0e : B1e) + (int64_t)col * K;
+    } else {
+      rowp = B0e + (int64_t)min(nt * S::BN + r, N_out - 1) * K;
+    }
+    b_src[i] = reinterpret_cast<const char*>(rowp) + ch * 16;
+    b_lds[i] = S::BM * 128 + r * 128 + ((ch ^ (r & 7)) << 4);
+  }
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 ra[S::kAChunks], rb[S::kBChunks];
+  auto load_global = [&](int kt) {
+    const int64_t off = (int64_t)kt * 128;
+#pragma unroll
+    for (int i = 0; i < S::kAChunks; ++i) ra[i] = ld16(a_src[i] + off);
+#pragma unroll
+    for (int i = 0; i < S::kBChunks; ++i) rb[i] = ld16(b_src[i] + off);
+  };
+  auto store_lds = [&](int stage) {
+    char* base = smem + stage * S::kStageBytes;
+#pragma unroll
+    for (int i = 0; i < S::kAChunks; ++i) st16(base + a_lds[i], ra[i]);
+#pragma unroll
+    for (int i = 0; i < S::kBChunks; ++i) st16(base + b_lds[i], rb[i]);
+  };
+
+  // fragment addresses: row (lane & 15) of each 16-row tile, chunk (ks * 4 + lane / 16)
+  // swizzled by (row & 7) == (lane & 7)
+  const int frag_row = lane & 15, frag_grp = lane >> 4, swz = lane & 7;
+  const int a_frag = (wm * MT * 16 + frag_row) * 128;
+  const int b_frag = S::BM * 128 + (wn * NT * 16 + frag_row) * 128;
+
+  auto compute = [&](int stage) {
+    const char* base = smem + stage * S::kStageBytes;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int chunk_off = ((ks * 4 + frag_grp) ^ swz) << 4;
+      u32x4 fa[MT], fb[NT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) fa[i] = ld16(base + a_frag + i * 16 * 128 + chunk_off);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) fb[j] = ld16(base + b_frag + j * 16 * 128 + chunk_off);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) mma_chunk(acc[i][j], fa[i], fb[j], T());
+    }
+  };
+
+  const int KT = (int)(row_bytes / 128);
+  load_global(0);
+  store_lds(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const bool more = kt + 1 < KT;
+    if (more) load_global(kt + 1);
+    compute(kt & 1);
+    if (more) store_lds((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----------------------------------------------------------------------------
+  constexpr int NOUT = SWIGLU ? NT / 2 : NT;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m_begin + wm * MT * 16 + i * 16 + frag_grp * 4 + r;
+      if (row >= m_end) continue;
+      const int col0 = nt * S::BN + wn * NOUT * 16 + frag_row;
+      T* crow = C + (int64_t)row * N_out + col0;
+#pragma unroll
+      for (int j = 0; j < NOUT; ++j) {
+        if (col0 + j * 16 >= N_out) continue;
+        float v;
+        if (SWIGLU)
+          v = silu_f32(acc[i][j][r]) * acc[i][j + NOUT][r];
+        else
+          v = acc[i][j][r];
+        crow[j * 16] = Elt<T>::from_f32(v);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// launch configurations
+// ---------------------------------------------------------------------------------------
+namespace {
+
+template <class T, int WM, int WN, int MT, int NT, bool SW>
+hipError_t launch_gemm(const T* A, const T* B0, const T* B1, int64_t b_stride, T* C, int K,
+                       int N_out, const int32_t* offsets, const int32_t* prefix, int64_t E,
+                       int64_t R, int64_t Ceff, hipStream_t s) {
+  using S = GemmShape<WM, WN, MT, NT, SW>;
+  int64_t m_max = (R + E * (S::BM - 1)) / S::BM;
+  const int64_t m_cap = E * ((Ceff + S::BM - 1) / S::BM);
+  if (m_cap < m_max) m_max = m_cap;
+  if (m_max <= 0) return hipSuccess;
+  const int n_tiles = (N_out + S::BN - 1) / S::BN;
+  const int group_n = n_tiles < 8 ? n_tiles : 8;
+  const int n_groups = (n_tiles + group_n - 1) / group_n;
+  const int64_t logical = m_max * group_n * n_groups;
+  const int64_t grid = (logical + 7) / 8 * 8;
+  const size_t lds = 2 * S::kStageBytes;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_kernel<T, WM, WN, MT, NT, SW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  grouped_gemm_kernel<T, WM, WN, MT, NT, SW><<<(unsigned)grid, S::kThreads, lds, s>>>(
+      A, B0, B1, b_stride, C, K, N_out, offsets, prefix, (int)E, (int)m_max, n_tiles,
+      group_n, (int)logical);
+  return hipGetLastError();
+}
+
+// Row-tile heights: prefill-sized experts use 128-row tiles, decode-sized ones 16.
+constexpr int kBigBM = 128, kSmallBM = 16;
+
+template <class T>
+hipError_t run_ffn(const FfnArgs& a, hipStream_t s) {
+  const bool small = a.T * a.k <= 32 * a.E;  // mean rows per expert <= 32
+  const int bm = small ? kSmallBM : kBigBM;
+  int32_t* pre1 = a.sched;
+  int32_t* pre2 = a.sched + (a.E + 1);
+  tile_schedule_kernel<<<1, 1024, 0, s>>>(a.offsets, (int)a.E, bm, bm, pre1, pre2);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const T* xp = (const T*)a.x_perm;
+  T* h = (T*)a.h;
+  T* y = (T*)a.y_perm;
+  const int64_t gu_stride = a.F * a.d, dn_stride = a.d * a.F;
+  if (small) {
+    err = launch_gemm<T, 1, 4, 1, 8, true>(xp, (const T*)a.w_gate, (const T*)a.w_up,
+                                           gu_stride, h, (int)a.d, (int)a.F, a.offsets, pre1,
+                                           a.E, a.R, a.C, s);
+    if (err != hipSuccess) return err;
+    err = launch_gemm<T, 1, 4, 1, 8, false>(h, (const T*)a.w_down, nullptr, dn_stride, y,
+                                            (int)a.F, (int)a.d, a.offsets, pre2, a.E, a.R,
+                                            a.C, s);
+  } else {
+    err = launch_gemm<T, 2, 2, 4, 8, true>(xp, (const T*)a.w_gate, (const T*)a.w_up,
+                                           gu_stride, h, (int)a.d, (int)a.F, a.offsets, pre1,
+                                           a.E, a.R, a.C, s);
+    if (err != hipSuccess) return err;
+    err = launch_gemm<T, 2, 2, 4, 8, false>(h, (const T*)a.w_down, nullptr, dn_stride, y,
+                                            (int)a.F, (int)a.d, a.offsets, pre2, a.E, a.R,
+                                            a.C, s);
+  }
+  return err;
+}
+
+}  // namespace
+
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
+  if (a.R <= 0) return hipSuccess;
+  return a.dtype == 1 ? run_ffn<bf16>(a, s) : run_ffn<float>(a, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,68 @@
+// Internal launchers of the MoE kernels.  Each enqueues on stream `s` and returns the
+// launch status; argument checking happens in the C ABI layer (moe_abi.cpp) before these
+// are called.  dtype: 0 = fp32, 1 = bf16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Flat assignments handled by one dispatch tile: a multiple of k, at most kTileMax, so the
+// k slots of a token never straddle two tiles.
+constexpr int kTileMax = 512;
+inline int64_t dispatch_tile_entries(int64_t k) { return (kTileMax / k) * k; }
+inline int64_t dispatch_ntiles(int64_t T, int64_t k) {
+  const int64_t te = dispatch_tile_entries(k);
+  return (T * k + te - 1) / te;
+}
+
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
+
+// S1
+hipError_t launch_router_logits(int dtype, const void* x, const void* w, const float* b,
+                                float* logits, int64_t T, int64_t d, int64_t E,
+                                hipStream_t s);
+// S2
+hipError_t launch_topk(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* idx,
+                       float* w, int32_t* status, hipStream_t s);
+
+// S3-S5.  C is the effective capacity (1 <= C <= T when T > 0); R the row bound.
+struct DispatchArgs {
+  const int32_t* topk_idx;
+  const void* x;
+  int64_t T, d, E, k, C, R;
+  int elt_bytes;
+  int32_t* tile_hist;  // [ntiles, E]
+  int32_t* tile_base;  // [ntiles, E]
+  int32_t* routed;     // [E]
+  int32_t* kept;       // [E]
+  int32_t* offsets;    // [E+1]
+  int32_t* src_token;  // [R]
+  int32_t* dest_row;   // [T*k]
+  int32_t* drops;      // [k+2]
+  void* x_perm;        // [R, d]
+};
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+
+// S6-S7
+struct FfnArgs {
+  int dtype;
+  const void* x_perm;
+  const int32_t* offsets;  // [E+1]
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  int64_t T, d, E, k, F, C, R;
+  void* h;               // [R, F]
+  int32_t* sched;        // 2 * (E + 1) ints
+  void* y_perm;          // [R, d]
+};
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s);
+
+// S8
+hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* dest_row,
+                          const float* topk_w, void* out, int64_t T, int64_t d, int64_t k,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,278 @@
+// C ABI of the MoE layer: argument validation, workspace layout and the call sequence of
+// each entry point.  Every check happens before anything is enqueued; kernels only see
+// arguments that passed them.  See include/moe.h for the contract of each function.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kMaxE = 1024;
+constexpr int64_t kMaxK = 64;
+
+int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int elt_bytes(int32_t dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+int64_t eff_capacity(const moe_shape* s) {
+  return (s->capacity <= 0 || s->capacity > s->T) ? s->T : s->capacity;
+}
+
+int check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->F <= 0 || s->reserved != 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s->k > s->E) return MOE_ERR_INVALID_ARG;
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->E > kMaxE || s->k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (s->d % 128 != 0 || s->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (s->T * s->k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (s->d > ((int64_t)1 << 20) || s->F > ((int64_t)1 << 20)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t max_rows(const moe_shape* s) {
+  const int64_t a = s->T * s->k, b = s->E * eff_capacity(s);
+  return a < b ? a : b;
+}
+
+struct Layout {
+  int64_t off[MOE_WS_COUNT];
+  int64_t size[MOE_WS_COUNT];
+  int64_t total;
+};
+
+Layout make_layout(const moe_shape* s) {
+  Layout L;
+  const int64_t T = s->T, E = s->E, k = s->k, R = max_rows(s), b = elt_bytes(s->dtype);
+  const int64_t ntiles = moe::dispatch_ntiles(T, k);
+  L.size[MOE_WS_LOGITS] = T * E * 4;
+  L.size[MOE_WS_TOPK_IDX] = T * k * 4;
+  L.size[MOE_WS_TOPK_W] = T * k * 4;
+  L.size[MOE_WS_ROUTED] = E * 4;
+  L.size[MOE_WS_KEPT] = E * 4;
+  L.size[MOE_WS_OFFSETS] = (E + 1) * 4;
+  L.size[MOE_WS_SRC_TOKEN] = R * 4;
+  L.size[MOE_WS_DEST_ROW] = T * k * 4;
+  L.size[MOE_WS_DROPS] = (k + 2) * 4;
+  L.size[MOE_WS_STATUS] = 4;
+  L.size[MOE_WS_TILE_HIST] = ntiles * E * 4;
+  L.size[MOE_WS_TILE_BASE] = ntiles * E * 4;
+  L.size[MOE_WS_SCHED] = 2 * (E + 1) * 4;
+  L.size[MOE_WS_X_PERM] = R * s->d * b;
+  L.size[MOE_WS_H] = R * s->F * b;
+  L.size[MOE_WS_Y_PERM] = R * s->d * b;
+  int64_t o = 0;
+  for (int i = 0; i < MOE_WS_COUNT; ++i) {
+    L.off[i] = o;
+    o += align_up(L.size[i]);
+  }
+  L.total = o;
+  return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <class P>
+P* region(void* ws, const Layout& L, int r) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + L.off[r]);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int check_workspace(const moe_shape* s, const void* ws, size_t bytes, Layout* L) {
+  *L = make_layout(s);
+  if (!ws || (int64_t)bytes < L->total) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+int route_impl(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+               float* logits, int logits_given, int32_t* idx, float* gates, int32_t* status,
+               hipStream_t st) {
+  hipError_t e;
+  if (status && (e = moe::launch_zero_i32(status, 1, st)) != hipSuccess) return MOE_ERR_HIP;
+  if (s->T == 0) return MOE_OK;
+  if (!logits_given) {
+    e = moe::launch_router_logits(s->dtype, x, w_router, b_router, logits, s->T, s->d, s->E,
+                                  st);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return hip_status(moe::launch_topk(logits, s->T, s->E, s->k, idx, gates, status, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_capacity(int64_t T, int64_t k, int64_t E, double cf) {
+  if (T < 0 || k < 1 || E < 1 || !isfinite(cf)) return -1;
+  if (!(cf > 0)) return 0;
+  return (int64_t)ceil(((cf * (double)T) * (double)k) / (double)E);
+}
+
+int64_t moe_max_rows(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return -1;
+  return max_rows(s);
+}
+
+size_t moe_workspace_size(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return (size_t)make_layout(s).total;
+}
+
+int moe_workspace_layout(const moe_shape* s, int64_t* offsets) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!offsets) return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(s);
+  for (int i = 0; i < MOE_WS_COUNT; ++i) offsets[i] = L.off[i];
+  return MOE_OK;
+}
+
+const char* moe_status_string(int st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_route(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+              float* logits, int logits_given, int32_t* topk_idx, float* topk_w,
+              int32_t* status, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (s->T > 0 && (!logits || !topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if (!logits_given && s->T > 0) {
+    if (!x || !w_router) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_ALIGNMENT;
+  }
+  return route_impl(s, x, w_router, b_router, logits, logits_given, topk_idx, topk_w, status,
+                    st);
+}
+
+int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, void* ws,
+                 size_t ws_bytes, int32_t* routed_counts, int32_t* tokens_per_expert,
+                 int32_t* expert_offsets, int32_t* src_token, int32_t* dest_row, int32_t* drops,
+                 void* x_perm, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!routed_counts || !tokens_per_expert || !expert_offsets || !drops)
+    return MOE_ERR_INVALID_ARG;
+  if (s->T > 0 && (!topk_idx || !x || !src_token || !dest_row || !x_perm))
+    return MOE_ERR_INVALID_ARG;
+  if (s->T > 0 && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_ALIGNMENT;
+  Layout L;
+  if ((rc = check_workspace(s, ws, ws_bytes, &L)) != MOE_OK) return rc;
+  moe::DispatchArgs a;
+  a.topk_idx = topk_idx;
+  a.x = x;
+  a.T = s->T;
+  a.d = s->d;
+  a.E = s->E;
+  a.k = s->k;
+  a.C = eff_capacity(s);
+  a.R = max_rows(s);
+  a.elt_bytes = elt_bytes(s->dtype);
+  a.tile_hist = region<int32_t>(ws, L, MOE_WS_TILE_HIST);
+  a.tile_base = region<int32_t>(ws, L, MOE_WS_TILE_BASE);
+  a.routed = routed_counts;
+  a.kept = tokens_per_expert;
+  a.offsets = expert_offsets;
+  a.src_token = src_token;
+  a.dest_row = dest_row;
+  a.drops = drops;
+  a.x_perm = x_perm;
+  return hip_status(moe::launch_dispatch(a, st));
+}
+
+int moe_expert_ffn(const moe_shape* s, const void* x_perm, const int32_t* expert_offsets,
+                   const void* w_gate, const void* w_up, const void* w_down, void* ws,
+                   size_t ws_bytes, void* y_perm, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (s->T == 0) return MOE_OK;
+  if (!x_perm || !expert_offsets || !w_gate || !w_up || !w_down || !y_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(y_perm))
+    return MOE_ERR_ALIGNMENT;
+  Layout L;
+  if ((rc = check_workspace(s, ws, ws_bytes, &L)) != MOE_OK) return rc;
+  moe::FfnArgs a;
+  a.dtype = s->dtype;
+  a.x_perm = x_perm;
+  a.offsets = expert_offsets;
+  a.w_gate = w_gate;
+  a.w_up = w_up;
+  a.w_down = w_down;
+  a.T = s->T;
+  a.d = s->d;
+  a.E = s->E;
+  a.k = s->k;
+  a.F = s->F;
+  a.C = eff_capacity(s);
+  a.R = max_rows(s);
+  a.h = region<void>(ws, L, MOE_WS_H);
+  a.sched = region<int32_t>(ws, L, MOE_WS_SCHED);
+  a.y_perm = y_perm;
+  return hip_status(moe::launch_expert_ffn(a, st));
+}
+
+int moe_combine(const moe_shape* s, const void* y_perm, const int32_t* dest_row,
+                const float* topk_w, void* out, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (s->T == 0) return MOE_OK;
+  if (!y_perm || !dest_row || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_perm) || !aligned16(out)) return MOE_ERR_ALIGNMENT;
+  return hip_status(
+      moe::launch_combine(s->dtype, y_perm, dest_row, topk_w, out, s->T, s->d, s->k, st));
+}
+
+int moe_layer(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+              const void* w_gate, const void* w_up, const void* w_down, void* ws,
+              size_t ws_bytes, void* out, int32_t* routed_counts, int32_t* tokens_per_expert,
+              int32_t* drops, int32_t* status, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!w_router || !w_gate || !w_up || !w_down) return MOE_ERR_INVALID_ARG;
+  if (s->T > 0 && (!x || !out)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(out))
+    return MOE_ERR_ALIGNMENT;
+  Layout L;
+  if ((rc = check_workspace(s, ws, ws_bytes, &L)) != MOE_OK) return rc;
+  float* logits = region<float>(ws, L, MOE_WS_LOGITS);
+  int32_t* idx = region<int32_t>(ws, L, MOE_WS_TOPK_IDX);
+  float* gates = region<float>(ws, L, MOE_WS_TOPK_W);
+  int32_t* routed = routed_counts ? routed_counts : region<int32_t>(ws, L, MOE_WS_ROUTED);
+  int32_t* kept = tokens_per_expert ? tokens_per_expert : region<int32_t>(ws, L, MOE_WS_KEPT);
+  int32_t* offsets = region<int32_t>(ws, L, MOE_WS_OFFSETS);
+  int32_t* src = region<int32_t>(ws, L, MOE_WS_SRC_TOKEN);
+  int32_t* dest = region<int32_t>(ws, L, MOE_WS_DEST_ROW);
+  int32_t* dr = drops ? drops : region<int32_t>(ws, L, MOE_WS_DROPS);
+  int32_t* stt = status ? status : region<int32_t>(ws, L, MOE_WS_STATUS);
+  void* x_perm = region<void>(ws, L, MOE_WS_X_PERM);
+  void* y_perm = region<void>(ws, L, MOE_WS_Y_PERM);
+
+  rc = route_impl(s, x, w_router, b_router, logits, 0, idx, gates, stt, st);
+  if (rc != MOE_OK) return rc;
+  rc = moe_dispatch(s, idx, x, ws, ws_bytes, routed, kept, offsets, src, dest, dr, x_perm, st);
+  if (rc != MOE_OK) return rc;
+  rc = moe_expert_ffn(s, x_perm, offsets, w_gate, w_up, w_down, ws, ws_bytes, y_perm, st);
+  if (rc != MOE_OK) return rc;
+  return moe_combine(s, y_perm, dest, gates, out, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,210 @@
+// S1 router logits and S2 top-k gating.
+//
+// [EP-serving] aiunderstanding.org, "Expert parallelism for MoE serving", section "Deep
+// dive": a router chooses the top-k experts of every token.  The layer specification fixes
+// the rest: fp32 logits, softmax top-k with ties to the lower expert index, and gates
+// renormalised over the selection.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------------------
+// small utility: zero an int32 buffer (used instead of a memset node so that the sequence
+// stays capturable in a HIP graph)
+// ---------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) zero_i32_kernel(int32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  zero_i32_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// S1: L[t, e] = sum_i x[t, i] w[e, i] + b[e]
+//
+// The router GEMM is skinny (E = 8 or 256 columns) and, for E = 8, bound by reading x
+// once from HBM.  Each wave computes a 16-token x (16 * NT)-expert tile with MFMA straight
+// from global memory (no LDS): per 128-byte k-step a lane loads 32 contiguous bytes of its
+// token row and of each expert row.  Both operands use the same k-chunk assignment
+// (lane group g takes chunks 2g and 2g+1), so the products pair up correctly.
+// Block: 4 waves over 64 tokens; grid.y over groups of 16 * NT experts.
+// ---------------------------------------------------------------------------------------
+template <class T, int NT>
+__global__ void __launch_bounds__(256)
+router_logits_kernel(const T* __restrict__ x, const T* __restrict__ w,
+                     const float* __restrict__ bias, float* __restrict__ logits, int T_,
+                     int d, int E) {
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int t0 = blockIdx.x * 64 + wave * 16;
+  if (t0 >= T_) return;
+  const int e0 = blockIdx.y * NT * 16;
+  const int r = lane & 15, g = lane >> 4;
+  const int t = min(t0 + r, T_ - 1);  // clamped rows are computed but never stored
+  const char* xa = reinterpret_cast<const char*>(x + (int64_t)t * d) + g * 32;
+  const char* wb[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int e = min(e0 + n * 16 + r, E - 1);
+    wb[n] = reinterpret_cast<const char*>(w + (int64_t)e * d) + g * 32;
+  }
+  f32x4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int row_bytes = d * (int)sizeof(T);
+  for (int kb = 0; kb < row_bytes; kb += 128) {
+    const u32x4 a0 = ld16(xa + kb), a1 = ld16(xa + kb + 16);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const u32x4 b0 = ld16(wb[n] + kb), b1 = ld16(wb[n] + kb + 16);
+      mma_chunk(acc[n], a0, b0, T());
+      mma_chunk(acc[n], a1, b1, T());
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int e = e0 + n * 16 + r;
+    if (e >= E) continue;
+    const float be = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = t0 + 4 * g + i;
+      if (tt < T_) logits[(int64_t)tt * E + e] = acc[n][i] + be;
+    }
+  }
+}
+
+hipError_t launch_router_logits(int dtype, const void* x, const void* w, const float* b,
+                                float* logits, int64_t T, int64_t d, int64_t E,
+                                hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const unsigned gx = (unsigned)((T + 63) / 64);
+  if (E <= 16) {
+    dim3 grid(gx, 1);
+    if (dtype == 1)
+      router_logits_kernel<bf16, 1><<<grid, 256, 0, s>>>((const bf16*)x, (const bf16*)w, b,
+                                                         logits, (int)T, (int)d, (int)E);
+    else
+      router_logits_kernel<float, 1><<<grid, 256, 0, s>>>((const float*)x, (const float*)w, b,
+                                                          logits, (int)T, (int)d, (int)E);
+  } else {
+    dim3 grid(gx, (unsigned)((E + 63) / 64));
+    if (dtype == 1)
+      router_logits_kernel<bf16, 4><<<grid, 256, 0, s>>>((const bf16*)x, (const bf16*)w, b,
+                                                         logits, (int)T, (int)d, (int)E);
+    else
+      router_logits_kernel<float, 4><<<grid, 256, 0, s>>>((const float*)x, (const float*)w, b,
+                                                          logits, (int)T, (int)d, (int)E);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// S2: top-k under (value descending, index ascending) and renormalised gates.
+//
+// A group of G lanes (G = power of two >= min(E, 64)) handles one token; lane s of the
+// group holds experts s, s + G, s + 2G, ... as 64-bit keys
+//     key = ordered(value) << 32 | (0xFFFFFFFF - e),
+// where ordered() maps fp32 to an unsigned integer of the same order (after turning -0.0
+// into +0.0).  Larger key = better expert; equal values compare by the low word, which
+// prefers the lower index.  k rounds of a group max-reduction pick the experts in order.
+// Non-finite logits are counted into *status (one per token) and get key 0.
+// ---------------------------------------------------------------------------------------
+__device__ inline uint32_t ordered_f32(float v) {
+  if (v == 0.0f) v = 0.0f;  // -0.0 == +0.0
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int V>
+__global__ void __launch_bounds__(256)
+topk_kernel(const float* __restrict__ logits, int T_, int E, int k, int G,
+            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+            int32_t* __restrict__ status) {
+  const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int tok = gtid / G, sub = gtid % G;
+  const bool active = tok < T_;
+  const float* row = logits + (int64_t)(active ? tok : 0) * E;
+
+  uint64_t key[V];
+  int bad = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int e = sub + v * G;
+    key[v] = 0;
+    if (active && e < E) {
+      const float val = row[e];
+      if (__builtin_isfinite(val))
+        key[v] = ((uint64_t)ordered_f32(val) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+      else
+        bad = 1;
+    }
+  }
+  // group OR of the non-finite flag
+  for (int m = G >> 1; m > 0; m >>= 1) bad |= __shfl_xor(bad, m, kWave);
+  if (active && sub == 0 && bad && status) atomicAdd(status, 1);
+
+  // Slot 0 holds the largest logit m, so the renormalised gates are exp(L_j - m) / sum.
+  // The owner lane writes the indices first and re-reads the selected logits afterwards.
+  float m = 0.f, sum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) best = key[v] > best ? key[v] : best;
+    for (int msk = G >> 1; msk > 0; msk >>= 1) {
+      const uint64_t o = shfl_xor_u64(best, msk);
+      best = o > best ? o : best;
+    }
+    // the unique owner retires the winning key
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (key[v] == best) key[v] = 0;
+    if (sub == 0 && active) {
+      const int e = best ? (int)(0xFFFFFFFFu - (uint32_t)best) : 0;
+      topk_idx[(int64_t)tok * k + j] = e;
+      const float val = row[e];
+      if (j == 0) m = val;
+      sum += expf(val - m);
+    }
+  }
+  if (sub == 0 && active) {
+    const float inv = 1.0f / sum;
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[(int64_t)tok * k + j];
+      topk_w[(int64_t)tok * k + j] = expf(row[e] - m) * inv;
+    }
+  }
+}
+
+hipError_t launch_topk(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* idx,
+                       float* w, int32_t* status, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  int G = 1;
+  while (G < E && G < 64) G <<= 1;
+  const int V = (int)((E + G - 1) / G);
+  const int64_t threads = T * G;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+#define MOE_TOPK(VV)                                                                        \
+  topk_kernel<VV><<<blocks, 256, 0, s>>>(logits, (int)T, (int)E, (int)k, G, idx, w, status)
+  if (V <= 1)
+    MOE_TOPK(1);
+  else if (V <= 2)
+    MOE_TOPK(2);
+  else if (V <= 4)
+    MOE_TOPK(4);
+  else if (V <= 8)
+    MOE_TOPK(8);
+  else
+    MOE_TOPK(16);
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,160 @@
+"""The C-ABI library on the host: it loads, exports every declared entry point, and its host
+logic (capacity, row bound, workspace layout, argument validation) behaves as documented.
+Nothing here launches a kernel: every call below is rejected before the first HIP call."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import routing_expert_ffn_router_amd as moe
+
+lib = moe.load_library()
+
+
+def test_exports_every_declared_function():
+    names = moe.header_functions()
+    assert {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_cites_the_pages():
+    text = " ".join(open(moe.HEADER_PATH).read().replace("*", " ").split())
+    for section in ("Deep dive", "Technical details", "Capacity factor changes quality",
+                    "All-to-all must be profiled separately from compute"):
+        assert section in text
+
+
+@pytest.mark.parametrize("T", [0, 1, 7, 64, 100, 2048, 4096, 8192, 25, 80, 333])
+@pytest.mark.parametrize("k,E", [(1, 4), (2, 8), (8, 256), (3, 5), (8, 4)])
+@pytest.mark.parametrize("cf", [0.5, 1.0, 1.1, 1.25, 2.0, 3.3, None])
+def test_capacity_matches_oracle(T, k, E, cf):
+    if k > E:
+        return
+    assert moe.capacity(T, k, E, cf) == oracle.capacity(T, k, E, cf)
+
+
+def test_capacity_invalid():
+    assert lib.moe_capacity(-1, 2, 8, 1.0) == -1
+    assert lib.moe_capacity(10, 0, 8, 1.0) == -1
+    assert lib.moe_capacity(10, 2, 8, float("nan")) == -1
+    assert lib.moe_capacity(10, 2, 8, -1.0) == 0
+
+
+def test_max_rows_and_workspace():
+    s = moe.shape(4096, 4096, 8, 2, 14336, 1280)
+    assert moe.max_rows(s) == 8192
+    s2 = moe.shape(2048, 6144, 8, 2, 16384, 640)
+    assert moe.max_rows(s2) == 4096
+    s3 = moe.shape(256, 7168, 256, 8, 2048, 0)
+    assert moe.max_rows(s3) == 2048
+    s4 = moe.shape(100, 128, 8, 2, 128, 5)
+    assert moe.max_rows(s4) == 40  # E * C < T * k
+    lay = moe.workspace_layout(s)
+    offs = [lay[n] for n in moe.WS_REGIONS]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    total = moe.workspace_size(s)
+    R, d, F = 8192, 4096, 14336
+    assert total >= lay["y_perm"] + R * d * 2
+    assert lay["h"] - lay["x_perm"] >= R * d * 2
+    assert lay["y_perm"] - lay["h"] >= R * F * 2
+
+
+BAD_SHAPES = [
+    (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(k=9), moe.MOE_ERR_INVALID_ARG),
+    (dict(k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(E=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(d=100), moe.MOE_ERR_UNSUPPORTED),
+    (dict(F=200), moe.MOE_ERR_UNSUPPORTED),
+    (dict(dtype=7), moe.MOE_ERR_UNSUPPORTED),
+    (dict(E=2048, k=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(E=128, k=65), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 30, k=2), moe.MOE_ERR_UNSUPPORTED),
+]
+
+
+def _shape(**kw):
+    base = dict(T=64, d=128, E=8, k=2, F=256, capacity=32, dtype=moe.MOE_F32)
+    base.update(kw)
+    return moe.shape(base["T"], base["d"], base["E"], base["k"], base["F"], base["capacity"],
+                     base["dtype"])
+
+
+FAKE = 1 << 40  # an aligned address that is never dereferenced: calls fail validation first
+
+
+@pytest.mark.parametrize("kw,err", BAD_SHAPES)
+def test_bad_shapes_rejected_everywhere(kw, err):
+    s = ctypes.byref(_shape(**kw))
+    p = FAKE
+    assert lib.moe_workspace_size(s) == 0
+    assert lib.moe_max_rows(s) == -1
+    assert lib.moe_route(s, p, p, None, p, 0, p, p, None, None) == err
+    assert lib.moe_dispatch(s, p, p, p, 1 << 40, p, p, p, p, p, p, p, None) == err
+    assert lib.moe_expert_ffn(s, p, p, p, p, p, p, 1 << 40, p, None) == err
+    assert lib.moe_combine(s, p, p, p, p, None) == err
+    assert lib.moe_layer(s, p, p, None, p, p, p, p, 1 << 40, p, None, None, None, None,
+                         None) == err
+
+
+def test_null_shape():
+    assert lib.moe_route(None, FAKE, FAKE, None, FAKE, 0, FAKE, FAKE, None, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_size(None) == 0
+
+
+def test_null_pointers_rejected():
+    s = ctypes.byref(_shape())
+    p = FAKE
+    E = moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(s, None, p, None, p, 0, p, p, None, None) == E  # x
+    assert lib.moe_route(s, p, p, None, None, 0, p, p, None, None) == E  # logits
+    assert lib.moe_dispatch(s, None, p, p, 1 << 40, p, p, p, p, p, p, p, None) == E
+    assert lib.moe_dispatch(s, p, p, p, 1 << 40, None, p, p, p, p, p, p, None) == E
+    assert lib.moe_expert_ffn(s, p, p, None, p, p, p, 1 << 40, p, None) == E
+    assert lib.moe_combine(s, p, None, p, p, None) == E
+    assert lib.moe_layer(s, p, None, None, p, p, p, p, 1 << 40, p, None, None, None, None,
+                         None) == E
+
+
+def test_misaligned_pointers_rejected():
+    s = ctypes.byref(_shape())
+    p, q = FAKE, FAKE + 8
+    A = moe.MOE_ERR_ALIGNMENT
+    assert lib.moe_route(s, q, p, None, p, 0, p, p, None, None) == A
+    assert lib.moe_dispatch(s, p, p, p, 1 << 40, p, p, p, p, p, p, q, None) == A
+    assert lib.moe_expert_ffn(s, p, p, p, q, p, p, 1 << 40, p, None) == A
+    assert lib.moe_combine(s, q, p, p, p, None) == A
+    assert lib.moe_layer(s, p, p, None, p, p, p, p, 1 << 40, q, None, None, None, None,
+                         None) == A
+    # the workspace must be 256-byte aligned
+    assert lib.moe_dispatch(s, p, p, p + 16, 1 << 40, p, p, p, p, p, p, p, None) == A
+
+
+def test_workspace_checked():
+    sh = _shape()
+    s = ctypes.byref(sh)
+    p = FAKE
+    need = moe.workspace_size(sh)
+    W = moe.MOE_ERR_WORKSPACE
+    assert lib.moe_dispatch(s, p, p, None, need, p, p, p, p, p, p, p, None) == W
+    assert lib.moe_dispatch(s, p, p, p, need - 1, p, p, p, p, p, p, p, None) == W
+    assert lib.moe_expert_ffn(s, p, p, p, p, p, p, need - 256, p, None) == W
+    assert lib.moe_layer(s, p, p, None, p, p, p, p, 16, p, None, None, None, None, None) == W
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, -5, 42):
+        assert isinstance(moe.status_string(st), str)
+    assert moe.status_string(-4).startswith("workspace")
+
+
+def test_library_has_no_oracle_or_torch_dependency():
+    # the product library is self-contained HIP code: no Python, no torch symbols
+    import subprocess
+
+    out = subprocess.run(["ldd", moe.LIB_PATH], capture_output=True, text=True).stdout
+    assert "torch" not in out and "python" not in out.lower()
+    assert "amdhip64" in out

@@ -1,0 +1,369 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on seeded inputs.
+
+Sizes are small enough for the oracle to finish in seconds but span several tiles of every
+kernel and end in ragged tails.  Routing tables and the permutation are compared bit for
+bit; floating-point outputs within the tolerances stated next to each check.
+"""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+import oracle
+import routing_expert_ffn_router_amd as moe
+from _util import (OUT_TOL, device_inputs, host_inputs, log, logits_tol, near_tie_ok, rel_err,
+                   shape_of, to_device, to_host, torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+W = mi.Workload
+# small layers: (name, T, d, E, k, F, cf, dtype, zipf_s)
+SMALL = {
+    "tiny_f32": mi.WORKLOADS["tiny_f32"],
+    "bf16_e8_big_tiles": W("bf16_e8_big_tiles", 1000, 384, 8, 2, 384, 1.25, "bf16"),
+    "bf16_e8_zipf_drops": W("bf16_e8_zipf_drops", 700, 256, 8, 2, 640, 1.25, "bf16", 1.1),
+    "bf16_e16_small_tiles": W("bf16_e16_small_tiles", 64, 384, 16, 2, 640, None, "bf16"),
+    "bf16_e256_k8_drops": W("bf16_e256_k8_drops", 512, 256, 256, 8, 256, 1.0, "bf16", 0.05),
+    "bf16_e256_k8_decode": W("bf16_e256_k8_decode", 37, 512, 256, 8, 384, None, "bf16"),
+    "f32_e4_big_tiles": W("f32_e4_big_tiles", 600, 256, 4, 2, 384, 1.0, "f32"),
+    "bf16_e3_k3": W("bf16_e3_k3", 333, 128, 3, 3, 256, None, "bf16"),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _i32(n, *shape):
+    return torch.empty(shape if shape else (n,), dtype=torch.int32, device="cuda")
+
+
+# ------------------------------------------------------------------------------- S2 routing
+ROUTE_CASES = [(1000, 8, 2, "normal"), (37, 8, 1, "ties"), (513, 256, 8, "normal"),
+               (300, 256, 8, "ties"), (64, 1000, 4, "normal"), (129, 3, 3, "ties"),
+               (50, 1, 1, "normal"), (0, 8, 2, "normal"), (70, 64, 64, "ties"),
+               (200, 1024, 64, "normal")]
+
+
+@pytest.mark.parametrize("T,E,k,kind", ROUTE_CASES)
+def test_route_given_logits(T, E, k, kind):
+    log(f"route T={T} E={E} k={k} {kind}")
+    rng = np.random.default_rng(T * 7919 + E * 31 + k)
+    if kind == "normal":
+        L = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+    else:
+        L = rng.choice(np.array([-1.0, -0.0, 0.0, 0.5, 1.0], np.float32), size=(T, E))
+    s = moe.shape(T, 128, E, k, 128, 0, moe.MOE_F32)
+    logits = to_device(L, torch.float32)
+    idx = _i32(0, T, k)
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    status = _i32(1)
+    moe.route(s, None, None, None, logits, idx, w, status, logits_given=True)
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    if T == 0:
+        return
+    ref_idx = oracle.select_topk(L, k)
+    ref_w = oracle.gate_weights(L, ref_idx)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    assert np.max(np.abs(w.cpu().numpy() - ref_w)) <= 1e-6
+
+
+def test_route_nonfinite_logits_counted():
+    T, E, k = 100, 16, 2
+    rng = np.random.default_rng(5)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    bad_rows = [3, 17, 18, 99]
+    L[3, 5] = np.nan
+    L[17, 0] = np.inf
+    L[18, 15] = -np.inf
+    L[99, 7] = np.nan
+    s = moe.shape(T, 128, E, k, 128, 0, moe.MOE_F32)
+    idx, w, status = _i32(0, T, k), torch.empty((T, k), device="cuda"), _i32(1)
+    moe.route(s, None, None, None, to_device(L, torch.float32), idx, w, status,
+              logits_given=True)
+    torch.cuda.synchronize()
+    assert status.item() == len(bad_rows)
+    good = np.setdiff1d(np.arange(T), bad_rows)
+    ref_idx = oracle.select_topk(L[good], k)
+    assert np.array_equal(idx.cpu().numpy()[good], ref_idx)
+
+
+# ------------------------------------------------------------------------------- S1 logits
+@pytest.mark.parametrize("name", ["tiny_f32", "bf16_e8_zipf_drops", "bf16_e256_k8_drops",
+                                  "f32_e4_big_tiles"])
+def test_router_logits(name):
+    w = SMALL[name]
+    log(f"logits {w}")
+    h = host_inputs(w)
+    dt = torch_dtype(w)
+    s = shape_of(w)
+    L = torch.empty((w.T, w.E), dtype=torch.float32, device="cuda")
+    idx, gw = _i32(0, w.T, w.k), torch.empty((w.T, w.k), device="cuda")
+    b = None if h["b_router"] is None else to_device(h["b_router"], torch.float32)
+    moe.route(s, to_device(h["x"], dt), to_device(h["w_router"], dt), b, L, idx, gw)
+    torch.cuda.synchronize()
+    ref = oracle.router_logits(h["x"], h["w_router"], h["b_router"])
+    err = float(np.max(np.abs(L.cpu().numpy() - ref)))
+    log(f"  max|dL| = {err:.3e}, tol {logits_tol(ref):.3e}")
+    assert err <= logits_tol(ref)
+
+
+# ------------------------------------------------------------------------------- S3-S5
+DISPATCH_CASES = [
+    # T, E, k, C, d, dtype, bias s
+    (1000, 8, 2, 250, 256, "bf16", 0.8),
+    (777, 8, 2, 0, 128, "f32", 0.0),
+    (8192, 256, 8, 256, 128, "bf16", 0.05),
+    (3, 3, 2, 1, 128, "f32", 0.0),
+    (513, 5, 3, 100, 128, "bf16", 0.3),
+    (2000, 1024, 64, 50, 128, "bf16", 0.01),
+    (100, 1, 1, 40, 128, "f32", 0.0),
+    (4096, 8, 2, 1280, 384, "bf16", 0.0),
+    (1, 8, 8, 0, 128, "bf16", 0.0),
+]
+
+
+def _run_dispatch(T, E, k, C, d, dtype, idx_np, x_np):
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    s = moe.shape(T, d, E, k, 128, C, moe.MOE_BF16 if dtype == "bf16" else moe.MOE_F32)
+    R = moe.max_rows(s)
+    ws = torch.empty(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
+    out = dict(routed=_i32(E), kept=_i32(E), offsets=_i32(E + 1), src=_i32(R),
+               dest=_i32(0, T, k), drops=_i32(k + 2),
+               x_perm=torch.full((R, d), 7.0, dtype=dt, device="cuda"))
+    moe.dispatch(s, to_device(idx_np, torch.int32), to_device(x_np, dt), ws, out["routed"],
+                 out["kept"], out["offsets"], out["src"], out["dest"], out["drops"],
+                 out["x_perm"])
+    torch.cuda.synchronize()
+    return s, R, out
+
+
+@pytest.mark.parametrize("T,E,k,C,d,dtype,bias", DISPATCH_CASES)
+def test_dispatch_bit_exact(T, E, k, C, d, dtype, bias):
+    log(f"dispatch T={T} E={E} k={k} C={C} d={d} {dtype}")
+    rng = np.random.default_rng(T + 13 * E + 101 * k)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    L += (-bias * np.log(np.arange(1, E + 1))).astype(np.float32)[None, :]
+    idx = oracle.select_topk(L, k)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    if dtype == "bf16":
+        x = mi.bf16_bits_to_f32(mi.bf16_rne_np(x))
+    s, R, g = _run_dispatch(T, E, k, C, d, dtype, idx, x)
+    ref = oracle.dispatch(idx, E, C)
+    N = ref["n_kept"]
+    assert np.array_equal(g["routed"].cpu().numpy(), ref["routed_counts"])
+    assert np.array_equal(g["kept"].cpu().numpy(), ref["tokens_per_expert"])
+    assert np.array_equal(g["offsets"].cpu().numpy(), ref["expert_offsets"])
+    assert np.array_equal(g["dest"].cpu().numpy(), ref["dest_row"])
+    assert np.array_equal(g["src"].cpu().numpy(), ref["src_token"][:R])
+    drops = g["drops"].cpu().numpy()
+    assert drops[0] == ref["drops_total"]
+    assert np.array_equal(drops[1:k + 1], ref["drops_per_slot"])
+    assert drops[k + 1] == ref["fully_dropped_tokens"]
+    # the permutation is a pure copy: bit-exact
+    xp = to_host(g["x_perm"][:N])
+    assert np.array_equal(xp.view(np.uint32), oracle.permute(x, ref["src_token"], N).view(np.uint32))
+    # conservation
+    assert int(g["kept"].sum()) == T * k - int(drops[0])
+
+
+def test_dispatch_zero_tokens():
+    s, R, g = _run_dispatch(0, 8, 2, 10, 128, "bf16", np.zeros((0, 2), np.int32),
+                            np.zeros((0, 128), np.float32))
+    assert R == 0
+    assert g["routed"].abs().sum().item() == 0 and g["kept"].abs().sum().item() == 0
+    assert g["offsets"].abs().sum().item() == 0 and g["drops"].abs().sum().item() == 0
+
+
+def test_dispatch_invalid_and_duplicate_ids():
+    # Entries outside [0, E) are dropped; a token repeating an expert is still counted in
+    # token-major order (the counting-sort definition).  Invalid ids are checked against the
+    # oracle on a table where they are replaced by an extra expert E, whose rows are then
+    # removed: the other experts' positions do not depend on it.
+    T, E, k, C, d = 300, 6, 3, 40, 128
+    rng = np.random.default_rng(77)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    inval = rng.random((T, k)) < 0.05
+    idx_gpu = np.where(inval, np.where(rng.random((T, k)) < 0.5, -1, E), idx).astype(np.int32)
+    idx_ref = np.where(inval, E, idx)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    s, R, g = _run_dispatch(T, E, k, C, d, "f32", idx_gpu, x)
+    ref = oracle.dispatch(idx_ref, E + 1, C)
+    assert np.array_equal(g["routed"].cpu().numpy(), ref["routed_counts"][:E])
+    assert np.array_equal(g["kept"].cpu().numpy(), ref["tokens_per_expert"][:E])
+    assert np.array_equal(g["offsets"].cpu().numpy(), ref["expert_offsets"][:E + 1])
+    dest_ref = np.where(inval, -1, ref["dest_row"])
+    assert np.array_equal(g["dest"].cpu().numpy(), dest_ref)
+    drops = g["drops"].cpu().numpy()
+    dropped = dest_ref < 0
+    assert drops[0] == dropped.sum()
+    assert np.array_equal(drops[1:k + 1], dropped.sum(0))
+    assert drops[k + 1] == dropped.all(1).sum()
+
+
+# ------------------------------------------------------------------------------- S6-S7
+@pytest.mark.parametrize("name", ["tiny_f32", "bf16_e8_big_tiles", "bf16_e16_small_tiles",
+                                  "bf16_e256_k8_decode", "f32_e4_big_tiles",
+                                  "bf16_e8_zipf_drops", "bf16_e3_k3"])
+def test_expert_ffn(name):
+    w = SMALL[name]
+    log(f"expert_ffn {w}")
+    h = host_inputs(w)
+    dt = torch_dtype(w)
+    s = shape_of(w)
+    C = s.capacity
+    L = oracle.router_logits(h["x"], h["w_router"], h["b_router"])
+    idx = oracle.select_topk(L, w.k)
+    tab = oracle.dispatch(idx, w.E, C)
+    N, R = tab["n_kept"], moe.max_rows(s)
+    xp = np.zeros((R, w.d), np.float32)
+    xp[:N] = oracle.permute(h["x"], tab["src_token"], N)
+    ws = torch.empty(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
+    y = torch.zeros((R, w.d), dtype=dt, device="cuda")
+    moe.expert_ffn(s, to_device(xp, dt), to_device(tab["expert_offsets"].astype(np.int32),
+                                                   torch.int32),
+                   to_device(h["w_gate"], dt), to_device(h["w_up"], dt),
+                   to_device(h["w_down"], dt), ws, y)
+    torch.cuda.synchronize()
+    ref = oracle.expert_ffn(xp[:N], tab["expert_offsets"], h["w_gate"], h["w_up"], h["w_down"])
+    err = rel_err(to_host(y[:N]), ref)
+    log(f"  N={N} rel err {err:.3e}")
+    assert err <= (1e-5 if w.dtype == "f32" else OUT_TOL)
+    assert np.all(np.isfinite(to_host(y[:N])))
+
+
+# ------------------------------------------------------------------------------- S8
+@pytest.mark.parametrize("T,E,k,C,d,dtype", [(500, 8, 2, 110, 256, "bf16"),
+                                             (300, 256, 8, 10, 128, "bf16"),
+                                             (200, 4, 3, 0, 384, "f32")])
+def test_combine(T, E, k, C, d, dtype):
+    rng = np.random.default_rng(T + k)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    idx = oracle.select_topk(L, k)
+    gates = oracle.gate_weights(L, idx).astype(np.float32)
+    tab = oracle.dispatch(idx, E, C)
+    s = moe.shape(T, d, E, k, 128, C, moe.MOE_BF16 if dtype == "bf16" else moe.MOE_F32)
+    R = moe.max_rows(s)
+    Y = rng.standard_normal((R, d)).astype(np.float32)
+    if dtype == "bf16":
+        Y = mi.bf16_bits_to_f32(mi.bf16_rne_np(Y))
+    out = torch.empty((T, d), dtype=dt, device="cuda")
+    moe.combine(s, to_device(Y, dt), to_device(tab["dest_row"].astype(np.int32), torch.int32),
+                to_device(gates, torch.float32), out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(Y, tab["dest_row"], gates)
+    err = rel_err(to_host(out), ref)
+    assert err <= (1e-6 if dtype == "f32" else 8e-3)  # one bf16 rounding of the sum
+    full_drop = np.all(tab["dest_row"] < 0, axis=1)
+    assert np.all(to_host(out)[full_drop] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dispatch_combine_identity_round_trip(dtype):
+    # identity experts (y_perm = x_perm), k = 1, no capacity limit: out == x bit for bit
+    T, E, k, d = 1000, 8, 1, 256
+    rng = np.random.default_rng(11)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    idx = oracle.select_topk(L, k)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    if dtype == "bf16":
+        x = mi.bf16_bits_to_f32(mi.bf16_rne_np(x))
+    s, R, g = _run_dispatch(T, E, k, 0, d, dtype, idx, x)
+    gates = torch.ones((T, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, d), dtype=dt, device="cuda")
+    moe.combine(s, g["x_perm"], g["dest"], gates, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out).view(np.uint32), x.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------- layer
+def _layer_gpu(w, d_in, s):
+    lay = moe.MoELayer(s)
+    out = lay(d_in["x"], d_in["w_router"], d_in["b_router"], d_in["w_gate"], d_in["w_up"],
+              d_in["w_down"])
+    torch.cuda.synchronize()
+    return lay, out
+
+
+def check_layer_against_oracle(w, lay, h):
+    """Compare one moe_layer result with the oracle run on the same seeded inputs."""
+    s = lay.shape
+    L_ref = oracle.router_logits(h["x"], h["w_router"], h["b_router"])
+    L_gpu = lay.view("logits").cpu().numpy()
+    tol = logits_tol(L_ref)
+    assert float(np.max(np.abs(L_gpu - L_ref))) <= tol
+    res = oracle.moe_layer(h["x"], h["w_router"], h["b_router"], h["w_gate"], h["w_up"],
+                           h["w_down"], w.k, s.capacity, logits=L_ref)
+    idx_gpu = lay.view("topk_idx").cpu().numpy()
+    bad, unexplained = near_tie_ok(L_ref, idx_gpu, res["topk_idx"], tol)
+    assert not unexplained, f"selection differs beyond near-ties at tokens {unexplained[:10]}"
+    dest_gpu = lay.view("dest_row").cpu().numpy()
+    out_gpu = to_host(lay.out)
+    if len(bad) == 0:
+        assert np.array_equal(idx_gpu, res["topk_idx"])
+        assert np.array_equal(lay.routed_counts.cpu().numpy(), res["routed_counts"])
+        assert np.array_equal(lay.tokens_per_expert.cpu().numpy(), res["tokens_per_expert"])
+        assert np.array_equal(dest_gpu, res["dest_row"])
+        drops = lay.drops.cpu().numpy()
+        assert drops[0] == res["drops_total"]
+        assert np.array_equal(drops[1:w.k + 1], res["drops_per_slot"])
+        assert drops[w.k + 1] == res["fully_dropped_tokens"]
+        same = np.ones(w.T, bool)
+    else:
+        # near-tie flips shift later positions of the affected experts: compare the tokens
+        # whose routing and keep pattern agree
+        same = np.all(idx_gpu == res["topk_idx"], axis=1) & np.all(
+            (dest_gpu >= 0) == (res["dest_row"] >= 0), axis=1)
+        log(f"  {len(bad)} near-tie tokens; comparing {same.sum()} of {w.T}")
+        assert same.sum() >= 0.9 * w.T
+    err = rel_err(out_gpu[same], res["out"][same])
+    log(f"  out rel err {err:.3e}, drops {int(lay.drops[0])}")
+    assert err <= OUT_TOL
+    return res
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_end_to_end(name):
+    w = SMALL[name]
+    log(f"layer {w}")
+    h = host_inputs(w)
+    s = shape_of(w)
+    lay, _ = _layer_gpu(w, device_inputs(w), s)
+    assert lay.status.item() == 0
+    check_layer_against_oracle(w, lay, h)
+
+
+def test_layer_deterministic():
+    w = SMALL["bf16_e256_k8_drops"]
+    s = shape_of(w)
+    d_in = device_inputs(w)
+    lay, out1 = _layer_gpu(w, d_in, s)
+    first = (out1.clone(), lay.view("dest_row").clone(), lay.view("x_perm").clone())
+    lay2, out2 = _layer_gpu(w, d_in, s)
+    assert torch.equal(first[0], out2)
+    assert torch.equal(first[1], lay2.view("dest_row"))
+    assert torch.equal(first[2], lay2.view("x_perm"))
+
+
+def test_layer_zero_tokens():
+    w = W("zero", 0, 128, 8, 2, 128, 1.0, "bf16")
+    s = shape_of(w, capacity=0)
+    d_in = device_inputs(w)
+    lay, _ = _layer_gpu(w, d_in, s)
+    assert lay.routed_counts.abs().sum().item() == 0
+    assert lay.drops.abs().sum().item() == 0 and lay.status.item() == 0
+
+
+def test_device_generator_matches_host():
+    w = SMALL["bf16_e8_zipf_drops"]
+    for name in ("x", "w_gate", "w_down"):
+        dev = to_host(mi.device_tensor(w, name))
+        assert np.array_equal(dev, mi.host_tensor_f32(w, name))
