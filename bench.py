@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""MoE-layer throughput on one MI355X: tokens/s of route + dispatch + expert GEMMs + combine.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one moe_layer call (router logits, top-k gating, dispatch with capacity
+truncation, grouped SwiGLU expert FFN, combine) over the workload's T tokens, with every
+input already resident in HBM.  W untimed steps, then exactly K timed steps between
+device synchronisations.  Prints one JSON line.
+
+A second pass runs the same layer as its five ABI calls with HIP events between them:
+it yields the per-stage timing record (router / pack / expert compute / unpack, as in
+airouter.kz, "Expert parallelism in MoE needs measurements before launch", section
+"All-to-all must be profiled separately from compute") and the duration of the dominant
+kernel, from which the roofline fraction is computed.  The CPU oracle, timed on a bounded
+sample of the same workload, is reported as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s (route+dispatch+expert GEMM+combine), % MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3  # MI355X fp32 matrix/vector
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+DEFAULT_WORKLOAD = "mixtral_8x7b_prefill"
+CPU_SAMPLE_TOKENS = {"mixtral_8x7b_prefill": 1024, "mixtral_8x22b_zipf": 512,
+                     "dsv3_decode": 64, "dsv3_mixed": 256, "tiny_f32": 64}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=None,
+                   help="tokens in the oracle's timed sample (default per workload)")
+    return p.parse_args()
+
+
+def build_if_missing():
+    import __graft_entry__
+
+    __graft_entry__._ensure_built()
+
+
+def percentile(v, q):
+    s = sorted(v)
+    return s[min(len(s) - 1, max(0, math.ceil(q * len(s)) - 1))]
+
+
+def cpu_baseline(w, ntok: int) -> dict:
+    """The oracle, as it stands, on the first `ntok` tokens of the workload (capacity
+    recomputed for ntok tokens with the same factor), full router and expert weights."""
+    import numpy as np
+    import threadpoolctl
+
+    import moe_inputs as mi
+    import oracle
+
+    x = mi.host_tensor_f32(w, "x", 0, ntok)
+    wr = mi.host_tensor_f32(w, "w_router")
+    b = mi.router_bias(w)
+    wg, wu, wd = (mi.host_tensor_f32(w, n) for n in ("w_gate", "w_up", "w_down"))
+    C = oracle.capacity(ntok, w.k, w.E, w.capacity_factor)
+    t0 = time.perf_counter()
+    res = oracle.moe_layer(x, wr, b, wg, wu, wd, w.k, C)
+    dt = time.perf_counter() - t0
+    assert np.all(np.isfinite(res["out"]))
+    threads = 0
+    for info in threadpoolctl.threadpool_info():
+        threads = max(threads, int(info.get("num_threads", 0)))
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"first {ntok} of {w.T} tokens of {w.name}, all {w.E} experts, "
+                      f"capacity {C} (same factor), float64 numpy oracle",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the MoE layer (expert parallel size 1); "
+              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    build_if_missing()
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import routing_expert_ffn_router_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = mi.WORKLOADS[args.workload]
+    C = moe.capacity(w.T, w.k, w.E, w.capacity_factor)
+    dtype = moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32
+    s = moe.shape(w.T, w.d, w.E, w.k, w.F, C, dtype)
+    b_elt = w.elt_bytes
+    print(f"# workload {w.name}: {s}", file=sys.stderr, flush=True)
+
+    dev = {n: mi.device_tensor(w, n) for n in ("x", "w_router", "w_gate", "w_up", "w_down")}
+    b_np = mi.router_bias(w)
+    bias = None if b_np is None else torch.from_numpy(b_np).cuda()
+    args_l = (dev["x"], dev["w_router"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])
+    lay = moe.MoELayer(s)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        lay(*args_l)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K moe_layer calls ------------------------------------------
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(K):
+        lay(*args_l)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]
+    total_ms = ev[0].elapsed_time(ev[K])
+    ms_per_step = total_ms / K
+    print(f"# timed {K} steps: {ms_per_step:.4f} ms/step (wall {wall * 1e3 / K:.4f})",
+          file=sys.stderr, flush=True)
+
+    # ---- staged pass: the same launches with events between the ABI calls ------------------
+    stage_times = {}
+    for i in range(max(K, 5)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        marks = []
+        for name in lay.stages(*args_l):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            marks.append((name, e))
+        torch.cuda.synchronize()
+        prev = e0
+        for name, e in marks:
+            stage_times.setdefault(name, []).append(prev.elapsed_time(e))
+            prev = e
+    stage_ms = {n: statistics.mean(v) for n, v in stage_times.items()}
+
+    # ---- routing statistics of the last call ------------------------------------------------
+    routed = lay.routed_counts.cpu().numpy().astype(np.int64)
+    kept = lay.tokens_per_expert.cpu().numpy().astype(np.int64)
+    drops = lay.drops.cpu().numpy().astype(np.int64)
+    N = int(kept.sum())
+    E_active = int((kept > 0).sum())
+    srt = np.sort(routed)
+    mu = routed.sum() / w.E
+    stats = {"active_tokens": w.T, "top_k": w.k, "capacity": C,
+             "expert_p50": int(srt[max(0, math.ceil(0.5 * w.E) - 1)]),
+             "expert_p95": int(srt[max(0, math.ceil(0.95 * w.E) - 1)]),
+             "expert_max": int(srt[-1]), "expert_max_to_mean": round(float(srt[-1] / mu), 4),
+             "dropped_tokens": int(drops[0]), "dropped_per_slot": drops[1:w.k + 1].tolist(),
+             "fully_dropped_tokens": int(drops[w.k + 1]), "kept_rows": N,
+             "active_experts": E_active}
+
+    # ---- roofline of the dominant kernel (gate/up grouped GEMM) ------------------------------
+    t_gu = stage_ms["gate_up"] * 1e-3
+    flops_gu = 4.0 * N * w.d * w.F
+    bytes_gu = b_elt * (2.0 * E_active * w.F * w.d + N * w.d + N * w.F)
+    peak_flops = (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS) * 1e12
+    ridge = peak_flops / (PEAK_HBM_GBS * 1e9)
+    if flops_gu / bytes_gu >= ridge:
+        roof = {"bound": "mfma", "achieved": round(flops_gu / t_gu / 1e12, 2),
+                "peak": peak_flops / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(bytes_gu / t_gu / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = "grouped_gemm_kernel (gate/up + SwiGLU), incl. its tile-table launch"
+    roof["kernel_ms"] = round(stage_ms["gate_up"], 4)
+
+    # whole-layer roofline: algorithmic work of the layer against both peaks
+    F_alg = 2.0 * w.T * w.d * w.E + 6.0 * w.d * w.F * N
+    B_alg = b_elt * (2.0 * w.T * w.d + w.E * w.d + 3.0 * w.d * w.F * E_active)
+    t_roof = max(F_alg / peak_flops, B_alg / (PEAK_HBM_GBS * 1e9))
+    layer_frac = t_roof / (ms_per_step * 1e-3)
+
+    result = {
+        "metric": METRIC,
+        "value": round(w.T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Philox inputs, random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F,
+                   "capacity_factor": w.capacity_factor, "capacity": C,
+                   "router_bias_zipf_s": w.zipf_s},
+        "roofline": roof,
+        "layer_roofline_frac": round(layer_frac, 4),
+        "step_ms_p50_p95_p99": [round(percentile(step_ms, q), 4) for q in (0.5, 0.95, 0.99)],
+        "stage_ms": {"router_ms": round(stage_ms["router"], 4),
+                     "pack_ms": round(stage_ms["dispatch"], 4),
+                     "expert_compute_ms": round(stage_ms["gate_up"] + stage_ms["down"], 4),
+                     "gate_up_ms": round(stage_ms["gate_up"], 4),
+                     "down_ms": round(stage_ms["down"], 4),
+                     "unpack_ms": round(stage_ms["combine"], 4)},
+        "expert_stats": stats,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        ntok = args.cpu_tokens or CPU_SAMPLE_TOKENS.get(w.name, 256)
+        print(f"# cpu baseline: oracle on {ntok} tokens", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, ntok)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

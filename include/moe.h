@@ -175,6 +175,27 @@ int moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int32_t* ex
                    size_t workspace_bytes, void* y_perm, hipStream_t stream);
 
 /*
+ * moe_expert_gate_up -- S6 alone: h = silu(x_perm w_gate[e]^T) * (x_perm w_up[e]^T) for
+ * the rows of each expert, rounded to dtype (same sources as moe_expert_ffn).  One grouped
+ * GEMM launch after a one-block tile-table launch.
+ *   h  [R, F] dtype out (rows >= expert_offsets[E] not written)
+ */
+int moe_expert_gate_up(const moe_shape* shape, const void* x_perm,
+                       const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                       void* workspace, size_t workspace_bytes, void* h, hipStream_t stream);
+
+/*
+ * moe_expert_down -- S7 alone: y_perm[r] = h[r] w_down[e]^T for the rows of each expert
+ * (same sources as moe_expert_ffn).  One grouped GEMM launch after a one-block tile-table
+ * launch.
+ *   h      [R, F] dtype in
+ *   y_perm [R, d] dtype out (rows >= expert_offsets[E] not written)
+ */
+int moe_expert_down(const moe_shape* shape, const void* h, const int32_t* expert_offsets,
+                    const void* w_down, void* workspace, size_t workspace_bytes, void* y_perm,
+                    hipStream_t stream);
+
+/*
  * moe_combine -- S8: gate-weighted sum back to token order, without atomics.
  * [EP-serving] "Technical details" (the combine step returns expert outputs to their
  * tokens); layer specification: out[t] = sum over slots j = 0..k-1 in order, skipping

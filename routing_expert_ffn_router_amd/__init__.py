@@ -70,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_route": (i32, [_S, _P, _P, _P, _P, i32, _P, _P, _P, _P]),
         "moe_dispatch": (i32, [_S, _P, _P, _P, sz, _P, _P, _P, _P, _P, _P, _P, _P]),
         "moe_expert_ffn": (i32, [_S, _P, _P, _P, _P, _P, _P, sz, _P, _P]),
+        "moe_expert_gate_up": (i32, [_S, _P, _P, _P, _P, _P, sz, _P, _P]),
+        "moe_expert_down": (i32, [_S, _P, _P, _P, _P, sz, _P, _P]),
         "moe_combine": (i32, [_S, _P, _P, _P, _P, _P]),
         "moe_layer": (i32, [_S, _P, _P, _P, _P, _P, _P, _P, sz, _P, _P, _P, _P, _P, _P]),
     }
@@ -163,6 +165,20 @@ def expert_ffn(s: MoeShape, x_perm, expert_offsets, w_gate, w_up, w_down, worksp
         _ptr(w_down), _ptr(workspace), _nbytes(workspace), _ptr(y_perm), _stream(stream)))
 
 
+def expert_gate_up(s: MoeShape, x_perm, expert_offsets, w_gate, w_up, workspace, h,
+                   stream=None) -> None:
+    _check("moe_expert_gate_up", load_library().moe_expert_gate_up(
+        ctypes.byref(s), _ptr(x_perm), _ptr(expert_offsets), _ptr(w_gate), _ptr(w_up),
+        _ptr(workspace), _nbytes(workspace), _ptr(h), _stream(stream)))
+
+
+def expert_down(s: MoeShape, h, expert_offsets, w_down, workspace, y_perm,
+                stream=None) -> None:
+    _check("moe_expert_down", load_library().moe_expert_down(
+        ctypes.byref(s), _ptr(h), _ptr(expert_offsets), _ptr(w_down), _ptr(workspace),
+        _nbytes(workspace), _ptr(y_perm), _stream(stream)))
+
+
 def combine(s: MoeShape, y_perm, dest_row, topk_w, out, stream=None) -> None:
     _check("moe_combine", load_library().moe_combine(
         ctypes.byref(s), _ptr(y_perm), _ptr(dest_row), _ptr(topk_w), _ptr(out),
@@ -226,3 +242,23 @@ class MoELayer:
 
     def view(self, region: str):
         return workspace_view(self.workspace, self.shape, region)
+
+    def stages(self, x, w_router, b_router, w_gate, w_up, w_down, stream=None):
+        """The same layer as __call__, as the five ABI calls moe_layer makes internally
+        (route, dispatch, gate/up GEMM, down GEMM, combine), yielding after each one so a
+        caller can record events between stages."""
+        s, ws = self.shape, self.workspace
+        v = self.view
+        route(s, x, w_router, b_router, v("logits"), v("topk_idx"), v("topk_w"), self.status,
+              stream=stream)
+        yield "router"
+        dispatch(s, v("topk_idx"), x, ws, self.routed_counts, self.tokens_per_expert,
+                 v("offsets"), v("src_token"), v("dest_row"), self.drops, v("x_perm"),
+                 stream=stream)
+        yield "dispatch"
+        expert_gate_up(s, v("x_perm"), v("offsets"), w_gate, w_up, ws, v("h"), stream=stream)
+        yield "gate_up"
+        expert_down(s, v("h"), v("offsets"), w_down, ws, v("y_perm"), stream=stream)
+        yield "down"
+        combine(s, v("y_perm"), v("dest_row"), v("topk_w"), self.out, stream=stream)
+        yield "combine"

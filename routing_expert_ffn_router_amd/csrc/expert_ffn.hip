@@ -9,10 +9,10 @@
 //
 // One kernel template serves both GEMMs: C[rows of expert e, n] = A[rows] . B_e[n]^T with
 // A and B both contiguous along the reduction axis (nn.Linear layout).
-//   - Variable M per expert: the m-tiles of all experts are numbered consecutively; a
-//     schedule kernel writes tile_prefix[e] = sum_{e' < e} ceil(c_e' / BM) on the device,
-//     and each block finds its expert by binary search, so the host never waits for the
-//     routing.  The grid is sized from an upper bound and surplus blocks exit at once.
+//   - Variable M per expert: the m-tiles of all experts are numbered consecutively and a
+//     one-block kernel writes the table tile -> (expert, first row) on the device from the
+//     expert offsets, so the host never waits for the routing.  The grid is sized from an
+//     upper bound on the tile count and surplus blocks exit at once.
 //   - Block tile BM x BN_W weight rows, K in 128-byte steps staged through LDS (two stages,
 //     global loads of step k+1 in flight while step k is multiplied).  LDS rows are 128
 //     bytes with the 16-byte chunks XOR-swizzled by (row & 7), so the MFMA fragment reads
@@ -46,23 +46,33 @@ struct GemmShape {
   static_assert(!SWIGLU || NT % 2 == 0, "SwiGLU needs gate and up halves");
 };
 
-// tile_prefix for two row-tile heights at once (GEMM1 and GEMM2 may differ).
+// Tile table for one row-tile height BM: table[0] = number of m-tiles over all experts;
+// entry i (i < table[0]) is (expert, first row) at table[1 + 2i], table[2 + 2i].  Experts
+// are numbered in index order and their tiles in row order.
 __global__ void __launch_bounds__(1024)
-tile_schedule_kernel(const int32_t* __restrict__ offsets, int E, int bm1, int bm2,
-                     int32_t* __restrict__ pre1, int32_t* __restrict__ pre2) {
+tile_table_kernel(const int32_t* __restrict__ offsets, int E, int bm, int m_max,
+                  int32_t* __restrict__ table) {
   __shared__ int smem[17];
+  __shared__ int s_pre[1024];
+  __shared__ int s_cnt[1024];
   const int e = threadIdx.x;
   const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-  int tot1, tot2;
-  const int x1 = block_exclusive_scan((c + bm1 - 1) / bm1, smem, &tot1);
-  const int x2 = block_exclusive_scan((c + bm2 - 1) / bm2, smem, &tot2);
+  const int tiles = (c + bm - 1) / bm;
+  int total;
+  const int pre = block_exclusive_scan(tiles, smem, &total);
   if (e < E) {
-    pre1[e] = x1;
-    pre2[e] = x2;
+    s_pre[e] = pre;
+    s_cnt[e] = tiles;
   }
-  if (threadIdx.x == 0) {
-    pre1[E] = tot1;
-    pre2[E] = tot2;
+  if (threadIdx.x == 0) table[0] = total < m_max ? total : m_max;
+  __syncthreads();
+  for (int x = 0; x < E; ++x) {
+    const int n = s_cnt[x], p0 = s_pre[x], row0 = offsets[x];
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      if (p0 + i >= m_max) break;
+      table[1 + 2 * (p0 + i)] = x;
+      table[2 + 2 * (p0 + i)] = row0 + i * bm;
+    }
   }
 }
 
@@ -71,8 +81,8 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
 grouped_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
                     const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C,
                     int K, int N_out, const int32_t* __restrict__ offsets,
-                    const int32_t* __restrict__ tile_prefix, int E, int m_tiles_max,
-                    int n_tiles, int group_n, int grid_logical) {
+                    const int32_t* __restrict__ table, int m_tiles_max, int n_tiles,
+                    int group_n, int grid_logical) {
   using S = GemmShape<WAVES_M, WAVES_N, MT, NT, SWIGLU>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -85,14 +95,9 @@ grouped_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
   const int grp = logical / per_group, rem = logical - grp * per_group;
   const int mt = rem / group_n, nt = grp * group_n + (rem - (rem / group_n) * group_n);
   if (nt >= n_tiles) return;
-  if (mt >= tile_prefix[E]) return;
-  int lo = 0, hi = E - 1;  // largest e with tile_prefix[e] <= mt
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
-  const int m_begin = offsets[e] + (mt - tile_prefix[e]) * S::BM;
+  if (mt >= table[0]) return;
+  const int e = table[1 + 2 * mt];
+  const int m_begin = table[2 + 2 * mt];
   const int m_end = offsets[e + 1];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -215,16 +220,26 @@ grouped_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
 // ---------------------------------------------------------------------------------------
 // launch configurations
 // ---------------------------------------------------------------------------------------
+// Row-tile heights: prefill-sized experts (mean > 32 rows) use 128-row tiles, decode-sized
+// ones 16-row tiles.
+FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R) {
+  FfnPlan p;
+  p.small = T * k <= 32 * E;
+  p.bm = p.small ? 16 : 128;
+  int64_t m_max = (R + E * (p.bm - 1)) / p.bm;
+  const int64_t m_cap = E * ((C + p.bm - 1) / p.bm);
+  p.m_max = m_cap < m_max ? m_cap : m_max;
+  if (p.m_max < 0) p.m_max = 0;
+  return p;
+}
+
 namespace {
 
 template <class T, int WM, int WN, int MT, int NT, bool SW>
 hipError_t launch_gemm(const T* A, const T* B0, const T* B1, int64_t b_stride, T* C, int K,
-                       int N_out, const int32_t* offsets, const int32_t* prefix, int64_t E,
-                       int64_t R, int64_t Ceff, hipStream_t s) {
+                       int N_out, const int32_t* offsets, const int32_t* table, int64_t m_max,
+                       hipStream_t s) {
   using S = GemmShape<WM, WN, MT, NT, SW>;
-  int64_t m_max = (R + E * (S::BM - 1)) / S::BM;
-  const int64_t m_cap = E * ((Ceff + S::BM - 1) / S::BM);
-  if (m_cap < m_max) m_max = m_cap;
   if (m_max <= 0) return hipSuccess;
   const int n_tiles = (N_out + S::BN - 1) / S::BN;
   const int group_n = n_tiles < 8 ? n_tiles : 8;
@@ -238,52 +253,56 @@ hipError_t launch_gemm(const T* A, const T* B0, const T* B1, int64_t b_stride, T
     if (e != hipSuccess) return e;
   }
   grouped_gemm_kernel<T, WM, WN, MT, NT, SW><<<(unsigned)grid, S::kThreads, lds, s>>>(
-      A, B0, B1, b_stride, C, K, N_out, offsets, prefix, (int)E, (int)m_max, n_tiles,
-      group_n, (int)logical);
+      A, B0, B1, b_stride, C, K, N_out, offsets, table, (int)m_max, n_tiles, group_n,
+      (int)logical);
   return hipGetLastError();
 }
 
-// Row-tile heights: prefill-sized experts use 128-row tiles, decode-sized ones 16.
-constexpr int kBigBM = 128, kSmallBM = 16;
+hipError_t launch_table(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
+  if (p.m_max <= 0) return hipSuccess;
+  tile_table_kernel<<<1, 1024, 0, s>>>(a.offsets, (int)a.E, p.bm, (int)p.m_max, a.sched);
+  return hipGetLastError();
+}
 
 template <class T>
-hipError_t run_ffn(const FfnArgs& a, hipStream_t s) {
-  const bool small = a.T * a.k <= 32 * a.E;  // mean rows per expert <= 32
-  const int bm = small ? kSmallBM : kBigBM;
-  int32_t* pre1 = a.sched;
-  int32_t* pre2 = a.sched + (a.E + 1);
-  tile_schedule_kernel<<<1, 1024, 0, s>>>(a.offsets, (int)a.E, bm, bm, pre1, pre2);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+hipError_t run_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   const T* xp = (const T*)a.x_perm;
   T* h = (T*)a.h;
+  const int64_t stride = a.F * a.d;
+  if (p.small)
+    return launch_gemm<T, 1, 4, 1, 8, true>(xp, (const T*)a.w_gate, (const T*)a.w_up, stride,
+                                            h, (int)a.d, (int)a.F, a.offsets, a.sched,
+                                            p.m_max, s);
+  return launch_gemm<T, 2, 2, 4, 8, true>(xp, (const T*)a.w_gate, (const T*)a.w_up, stride, h,
+                                          (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s);
+}
+
+template <class T>
+hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
+  const T* h = (const T*)a.h;
   T* y = (T*)a.y_perm;
-  const int64_t gu_stride = a.F * a.d, dn_stride = a.d * a.F;
-  if (small) {
-    err = launch_gemm<T, 1, 4, 1, 8, true>(xp, (const T*)a.w_gate, (const T*)a.w_up,
-                                           gu_stride, h, (int)a.d, (int)a.F, a.offsets, pre1,
-                                           a.E, a.R, a.C, s);
-    if (err != hipSuccess) return err;
-    err = launch_gemm<T, 1, 4, 1, 8, false>(h, (const T*)a.w_down, nullptr, dn_stride, y,
-                                            (int)a.F, (int)a.d, a.offsets, pre2, a.E, a.R,
-                                            a.C, s);
-  } else {
-    err = launch_gemm<T, 2, 2, 4, 8, true>(xp, (const T*)a.w_gate, (const T*)a.w_up,
-                                           gu_stride, h, (int)a.d, (int)a.F, a.offsets, pre1,
-                                           a.E, a.R, a.C, s);
-    if (err != hipSuccess) return err;
-    err = launch_gemm<T, 2, 2, 4, 8, false>(h, (const T*)a.w_down, nullptr, dn_stride, y,
-                                            (int)a.F, (int)a.d, a.offsets, pre2, a.E, a.R,
-                                            a.C, s);
-  }
-  return err;
+  const int64_t stride = a.d * a.F;
+  if (p.small)
+    return launch_gemm<T, 1, 4, 1, 8, false>(h, (const T*)a.w_down, nullptr, stride, y,
+                                             (int)a.F, (int)a.d, a.offsets, a.sched, p.m_max,
+                                             s);
+  return launch_gemm<T, 2, 2, 4, 8, false>(h, (const T*)a.w_down, nullptr, stride, y,
+                                           (int)a.F, (int)a.d, a.offsets, a.sched, p.m_max, s);
 }
 
 }  // namespace
 
-hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_expert_ffn(const FfnArgs& a, int which, hipStream_t s) {
   if (a.R <= 0) return hipSuccess;
-  return a.dtype == 1 ? run_ffn<bf16>(a, s) : run_ffn<float>(a, s);
+  const FfnPlan p = ffn_plan(a.T, a.E, a.k, a.C, a.R);
+  hipError_t err = launch_table(a, p, s);
+  if (err != hipSuccess) return err;
+  if (which & 1) {
+    err = a.dtype == 1 ? run_gate_up<bf16>(a, p, s) : run_gate_up<float>(a, p, s);
+    if (err != hipSuccess) return err;
+  }
+  if (which & 2) err = a.dtype == 1 ? run_down<bf16>(a, p, s) : run_down<float>(a, p, s);
+  return err;
 }
 
 }  // namespace moe

@@ -45,7 +45,16 @@ struct DispatchArgs {
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 
-// S6-S7
+// S6-S7.  The grouped GEMMs run over a device-side tile table (expert, first row) of
+// row-tile height bm with at most m_max entries.
+struct FfnPlan {
+  bool small;     // decode-sized experts: 16-row tiles
+  int bm;
+  int64_t m_max;  // upper bound on m-tiles over all experts
+};
+FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R);
+inline int64_t ffn_table_ints(const FfnPlan& p) { return 1 + 2 * p.m_max; }
+
 struct FfnArgs {
   int dtype;
   const void* x_perm;
@@ -55,10 +64,12 @@ struct FfnArgs {
   const void* w_down;
   int64_t T, d, E, k, F, C, R;
   void* h;               // [R, F]
-  int32_t* sched;        // 2 * (E + 1) ints
+  int32_t* sched;        // ffn_table_ints() ints
   void* y_perm;          // [R, d]
 };
-hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s);
+// which: 1 = gate/up GEMM (x_perm -> h), 2 = down GEMM (h -> y_perm), 3 = both.  Each
+// call first rebuilds the tile table from `offsets`.
+hipError_t launch_expert_ffn(const FfnArgs& a, int which, hipStream_t s);
 
 // S8
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* dest_row,

@@ -63,7 +63,8 @@ Layout make_layout(const moe_shape* s) {
   L.size[MOE_WS_STATUS] = 4;
   L.size[MOE_WS_TILE_HIST] = ntiles * E * 4;
   L.size[MOE_WS_TILE_BASE] = ntiles * E * 4;
-  L.size[MOE_WS_SCHED] = 2 * (E + 1) * 4;
+  L.size[MOE_WS_SCHED] =
+      moe::ffn_table_ints(moe::ffn_plan(T, E, k, eff_capacity(s), R)) * 4;
   L.size[MOE_WS_X_PERM] = R * s->d * b;
   L.size[MOE_WS_H] = R * s->F * b;
   L.size[MOE_WS_Y_PERM] = R * s->d * b;
@@ -196,16 +197,23 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, voi
   return hip_status(moe::launch_dispatch(a, st));
 }
 
-int moe_expert_ffn(const moe_shape* s, const void* x_perm, const int32_t* expert_offsets,
-                   const void* w_gate, const void* w_up, const void* w_down, void* ws,
-                   size_t ws_bytes, void* y_perm, hipStream_t st) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the three expert-FFN entry points; which = 1 (gate/up), 2 (down), 3 (both).
+int expert_ffn_impl(const moe_shape* s, int which, const void* x_perm, void* h,
+                    const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                    const void* w_down, void* ws, size_t ws_bytes, void* y_perm,
+                    hipStream_t st) {
   int rc = check_shape(s);
   if (rc != MOE_OK) return rc;
   if (s->T == 0) return MOE_OK;
-  if (!x_perm || !expert_offsets || !w_gate || !w_up || !w_down || !y_perm)
-    return MOE_ERR_INVALID_ARG;
+  if (!expert_offsets) return MOE_ERR_INVALID_ARG;
+  if ((which & 1) && (!x_perm || !w_gate || !w_up || !h)) return MOE_ERR_INVALID_ARG;
+  if ((which & 2) && (!w_down || !y_perm || !h)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x_perm) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
-      !aligned16(y_perm))
+      !aligned16(y_perm) || !aligned16(h))
     return MOE_ERR_ALIGNMENT;
   Layout L;
   if ((rc = check_workspace(s, ws, ws_bytes, &L)) != MOE_OK) return rc;
@@ -223,10 +231,40 @@ int moe_expert_ffn(const moe_shape* s, const void* x_perm, const int32_t* expert
   a.F = s->F;
   a.C = eff_capacity(s);
   a.R = max_rows(s);
-  a.h = region<void>(ws, L, MOE_WS_H);
+  a.h = h;
   a.sched = region<int32_t>(ws, L, MOE_WS_SCHED);
   a.y_perm = y_perm;
-  return hip_status(moe::launch_expert_ffn(a, st));
+  return hip_status(moe::launch_expert_ffn(a, which, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_ffn(const moe_shape* s, const void* x_perm, const int32_t* expert_offsets,
+                   const void* w_gate, const void* w_up, const void* w_down, void* ws,
+                   size_t ws_bytes, void* y_perm, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  Layout L;
+  if (s->T > 0 && (rc = check_workspace(s, ws, ws_bytes, &L)) != MOE_OK) return rc;
+  void* h = s->T > 0 ? region<void>(ws, L, MOE_WS_H) : nullptr;
+  return expert_ffn_impl(s, 3, x_perm, h, expert_offsets, w_gate, w_up, w_down, ws, ws_bytes,
+                         y_perm, st);
+}
+
+int moe_expert_gate_up(const moe_shape* s, const void* x_perm, const int32_t* expert_offsets,
+                       const void* w_gate, const void* w_up, void* ws, size_t ws_bytes,
+                       void* h, hipStream_t st) {
+  return expert_ffn_impl(s, 1, x_perm, h, expert_offsets, w_gate, w_up, nullptr, ws, ws_bytes,
+                         nullptr, st);
+}
+
+int moe_expert_down(const moe_shape* s, const void* h, const int32_t* expert_offsets,
+                    const void* w_down, void* ws, size_t ws_bytes, void* y_perm,
+                    hipStream_t st) {
+  return expert_ffn_impl(s, 2, nullptr, const_cast<void*>(h), expert_offsets, nullptr, nullptr,
+                         w_down, ws, ws_bytes, y_perm, st);
 }
 
 int moe_combine(const moe_shape* s, const void* y_perm, const int32_t* dest_row,

@@ -346,11 +346,15 @@ def test_layer_deterministic():
     s = shape_of(w)
     d_in = device_inputs(w)
     lay, out1 = _layer_gpu(w, d_in, s)
-    first = (out1.clone(), lay.view("dest_row").clone(), lay.view("x_perm").clone())
+    N = int(lay.view("offsets")[-1])
+    first = (out1.clone(), lay.view("dest_row").clone(), lay.view("x_perm")[:N].clone(),
+             lay.view("y_perm")[:N].clone())
     lay2, out2 = _layer_gpu(w, d_in, s)
+    assert int(lay2.view("offsets")[-1]) == N
     assert torch.equal(first[0], out2)
     assert torch.equal(first[1], lay2.view("dest_row"))
-    assert torch.equal(first[2], lay2.view("x_perm"))
+    assert torch.equal(first[2], lay2.view("x_perm")[:N])
+    assert torch.equal(first[3], lay2.view("y_perm")[:N])
 
 
 def test_layer_zero_tokens():
