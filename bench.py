@@ -33,7 +33,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3  # MI355X fp32 matrix/vector
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 DEFAULT_WORKLOAD = "mixtral_8x7b_prefill"
-CPU_SAMPLE_TOKENS = {"mixtral_8x7b_prefill": 1024, "mixtral_8x22b_zipf": 512,
+CPU_SAMPLE_TOKENS = {"mixtral_8x7b_prefill": 4096, "mixtral_8x22b_zipf": 512,
                      "dsv3_decode": 64, "dsv3_mixed": 256, "tiny_f32": 64}
 
 

@@ -218,14 +218,217 @@ grouped_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
 }
 
 // ---------------------------------------------------------------------------------------
+// Prefill-sized experts: 256 x 256 block tile, 8 waves, 4-stage LDS pipeline fed by
+// direct global -> LDS loads (global_load_lds_dwordx4).
+//
+// Each stage holds 32 reduction elements (64 bytes) of the block's 256 A rows and 256
+// weight rows: 512 LDS rows of 64 bytes = 32 KB; four stages use 128 KB of the CU's 160 KB.
+// A wave's direct-load instruction writes 64 lanes x 16 bytes = 16 consecutive LDS rows,
+// lane L landing at row L / 4, slot L % 4 of them.  The slot holding k-chunk c of row r is
+// c ^ f(r) with f(r) = ((r >> 1) ^ (r >> 3)) & 1 | (r >> 1) & 2: for 8 consecutive rows
+// read at one chunk position the 16-byte slots cover all 128 bytes of a 32-bank cycle,
+// and for 16 consecutive rows all 256 bytes of a 64-bank cycle, so the MFMA fragment
+// reads are conflict-free either way.  The lane therefore fetches chunk (L % 4) ^ f(r).
+//
+// Pipeline: stages k+1 and k+2 are in flight while stage k is multiplied; at the top of
+// step k a wave waits until its own loads of stage k have landed (vmcnt counts the 4
+// direct loads per wave per stage) and a barrier makes every wave's loads visible; then
+// stage k+3 is issued into the buffer that step k-1 just finished reading.  The stage
+// buffers are distinct __restrict__ pointers of an inlined function so the compiler keeps
+// these explicit waits instead of inserting a full wait before every LDS read.
+//
+// Waves form a 2 (rows) x 4 (weight rows) grid; each owns 128 x 64 of the tile (8 x 4
+// MFMA tiles of 16 x 16).  With SwiGLU a wave's 64 weight rows are 32 gate rows followed
+// by the 32 up rows of the same output columns, so a block produces 256 x 128 of h.
+// ---------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) char lds_char;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+struct PrefillTile {
+  static constexpr int BM = 256, BNW = 256, kWaves = 8, kThreads = 512;
+  static constexpr int WM = 2, WN = 4, MT = 8, NT = 4;
+  static constexpr int kRowBytes = 64;
+  static constexpr int kStageBytes = (BM + BNW) * kRowBytes;
+  static constexpr int kStages = 4;
+  static constexpr int kDmaPerWave = (BM + BNW) / 16 / kWaves;  // 16 LDS rows per load
+};
+
+__device__ inline int swz64(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
+
+template <int N>
+__device__ inline void wait_vm_barrier() {
+  static_assert(N == 0 || N == 4 || N == 8, "vmcnt immediate");
+  if (N == 8)
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else if (N == 4)
+    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <class T, bool SWIGLU>
+__device__ __attribute__((always_inline)) inline void prefill_gemm_body(
+    const T* __restrict__ A, const T* __restrict__ B0, const T* __restrict__ B1,
+    int64_t b_expert_stride, T* __restrict__ C, int K, int N_out,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ table,
+    int m_tiles_max, int n_tiles, int group_n, int grid_logical, lds_char* __restrict__ s0,
+    lds_char* __restrict__ s1, lds_char* __restrict__ s2, lds_char* __restrict__ s3) {
+  using P = PrefillTile;
+  constexpr int BN = SWIGLU ? P::BNW / 2 : P::BNW;
+  const int bid = blockIdx.x;
+  const int per_xcd = gridDim.x >> 3;
+  const int logical = (bid & 7) * per_xcd + (bid >> 3);
+  if (logical >= grid_logical) return;
+  const int per_group = m_tiles_max * group_n;
+  const int grp = logical / per_group, rem = logical - grp * per_group;
+  const int mt = rem / group_n, nt = grp * group_n + (rem - (rem / group_n) * group_n);
+  if (nt >= n_tiles) return;
+  if (mt >= table[0]) return;
+  const int e = table[1 + 2 * mt];
+  const int m_begin = table[2 + 2 * mt];
+  const int m_end = offsets[e + 1];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int wm = wave / P::WN, wn = wave % P::WN;
+  const int64_t row_bytes = (int64_t)K * sizeof(T);
+
+  // per-lane source of each direct load (k offset 0); LDS row of load i of this wave:
+  // (wave * kDmaPerWave + i) * 16 + lane / 4
+  const char* src[P::kDmaPerWave];
+  const T* B0e = B0 + (int64_t)e * b_expert_stride;
+  const T* B1e = SWIGLU ? B1 + (int64_t)e * b_expert_stride : nullptr;
+#pragma unroll
+  for (int i = 0; i < P::kDmaPerWave; ++i) {
+    const int r = (wave * P::kDmaPerWave + i) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz64(r);
+    const char* rowp;
+    if (r < P::BM) {
+      const int gr = min(m_begin + r, m_end - 1);  // rows past the expert: never stored
+      rowp = reinterpret_cast<const char*>(A) + (int64_t)gr * row_bytes;
+    } else {
+      const int br = r - P::BM;
+      if (SWIGLU) {
+        const int w = br / 64, within = br % 64;
+        const int col = min(nt * BN + w * 32 + (within % 32), N_out - 1);
+        rowp = reinterpret_cast<const char*>((within < 32 ? B0e : B1e) + (int64_t)col * K);
+      } else {
+        rowp = reinterpret_cast<const char*>(B0e + (int64_t)min(nt * BN + br, N_out - 1) * K);
+      }
+    }
+    src[i] = rowp + c * 16;
+  }
+  const int dma_lds = wave * P::kDmaPerWave * 1024;
+
+  f32x4 acc[P::MT][P::NT];
+#pragma unroll
+  for (int i = 0; i < P::MT; ++i)
+#pragma unroll
+    for (int j = 0; j < P::NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // a wave whose 128-row band lies past the expert's rows skips its MFMAs
+  const bool band_live = m_begin + wm * P::MT * 16 < m_end;
+  const int frag_row = lane & 15, frag_grp = lane >> 4;
+  const int frag_off = frag_row * P::kRowBytes + ((frag_grp ^ swz64(frag_row)) << 4);
+  const int a_frag = wm * P::MT * 16 * P::kRowBytes + frag_off;
+  const int b_frag = (P::BM + wn * P::NT * 16) * P::kRowBytes + frag_off;
+
+  auto issue = [&](int kt, lds_char* buf) {
+    const int64_t koff = (int64_t)kt * P::kRowBytes;
+#pragma unroll
+    for (int i = 0; i < P::kDmaPerWave; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_void*)(src[i] + koff), buf + dma_lds + i * 1024, 16,
+                                       0, 0);
+  };
+  auto compute = [&](const lds_char* buf) {
+    if (!band_live) return;
+    // all fragment reads first (B, then A in the order the MFMAs consume them), so the
+    // MFMAs wait progressively instead of after each read
+    u32x4 fa[P::MT], fb[P::NT];
+#pragma unroll
+    for (int j = 0; j < P::NT; ++j)
+      fb[j] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          buf + b_frag + j * 16 * P::kRowBytes);
+#pragma unroll
+    for (int i = 0; i < P::MT; ++i)
+      fa[i] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          buf + a_frag + i * 16 * P::kRowBytes);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < P::MT; ++i)
+#pragma unroll
+      for (int j = 0; j < P::NT; ++j) mma_chunk(acc[i][j], fa[i], fb[j], T());
+  };
+  const int KT = (int)(row_bytes / P::kRowBytes);
+  auto step = [&](int kt, const lds_char* cur, lds_char* nxt) {
+    if (kt >= KT) return;
+    if (kt + 2 < KT)
+      wait_vm_barrier<8>();
+    else if (kt + 1 < KT)
+      wait_vm_barrier<4>();
+    else
+      wait_vm_barrier<0>();
+    if (kt + 3 < KT) issue(kt + 3, nxt);
+    compute(cur);
+  };
+
+  issue(0, s0);
+  if (KT > 1) issue(1, s1);
+  if (KT > 2) issue(2, s2);
+  for (int kt = 0; kt < KT; kt += 4) {
+    step(kt + 0, s0, s3);
+    step(kt + 1, s1, s0);
+    step(kt + 2, s2, s1);
+    step(kt + 3, s3, s2);
+  }
+
+  if (!band_live) return;
+  constexpr int NOUT = SWIGLU ? P::NT / 2 : P::NT;
+#pragma unroll
+  for (int i = 0; i < P::MT; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m_begin + wm * P::MT * 16 + i * 16 + frag_grp * 4 + r;
+      if (row >= m_end) continue;
+      const int col0 = nt * BN + wn * NOUT * 16 + frag_row;
+      T* crow = C + (int64_t)row * N_out + col0;
+#pragma unroll
+      for (int j = 0; j < NOUT; ++j) {
+        if (col0 + j * 16 >= N_out) continue;
+        float v;
+        if (SWIGLU)
+          v = silu_f32(acc[i][j][r]) * acc[i][j + NOUT][r];
+        else
+          v = acc[i][j][r];
+        crow[j * 16] = Elt<T>::from_f32(v);
+      }
+    }
+  }
+}
+
+template <class T, bool SWIGLU>
+__global__ void __launch_bounds__(PrefillTile::kThreads)
+prefill_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
+                    const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C, int K,
+                    int N_out, const int32_t* __restrict__ offsets,
+                    const int32_t* __restrict__ table, int m_tiles_max, int n_tiles,
+                    int group_n, int grid_logical) {
+  extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
+  lds_char* base = (lds_char*)smem_dyn;
+  constexpr int S = PrefillTile::kStageBytes;
+  prefill_gemm_body<T, SWIGLU>(A, B0, B1, b_expert_stride, C, K, N_out, offsets, table,
+                               m_tiles_max, n_tiles, group_n, grid_logical, base, base + S,
+                               base + 2 * S, base + 3 * S);
+}
+
+// ---------------------------------------------------------------------------------------
 // launch configurations
 // ---------------------------------------------------------------------------------------
-// Row-tile heights: prefill-sized experts (mean > 32 rows) use 128-row tiles, decode-sized
-// ones 16-row tiles.
+// Row-tile heights: prefill-sized experts (mean > 32 rows) use the 256-row prefill kernel,
+// decode-sized ones 16-row tiles.
 FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R) {
   FfnPlan p;
   p.small = T * k <= 32 * E;
-  p.bm = p.small ? 16 : 128;
+  p.bm = p.small ? 16 : PrefillTile::BM;
   int64_t m_max = (R + E * (p.bm - 1)) / p.bm;
   const int64_t m_cap = E * ((C + p.bm - 1) / p.bm);
   p.m_max = m_cap < m_max ? m_cap : m_max;
@@ -258,6 +461,28 @@ hipError_t launch_gemm(const T* A, const T* B0, const T* B1, int64_t b_stride, T
   return hipGetLastError();
 }
 
+template <class T, bool SW>
+hipError_t launch_prefill(const T* A, const T* B0, const T* B1, int64_t b_stride, T* C, int K,
+                          int N_out, const int32_t* offsets, const int32_t* table,
+                          int64_t m_max, hipStream_t s) {
+  using P = PrefillTile;
+  if (m_max <= 0) return hipSuccess;
+  constexpr int BN = SW ? P::BNW / 2 : P::BNW;
+  const int n_tiles = (N_out + BN - 1) / BN;
+  const int group_n = n_tiles < 8 ? n_tiles : 8;
+  const int n_groups = (n_tiles + group_n - 1) / group_n;
+  const int64_t logical = m_max * group_n * n_groups;
+  const int64_t grid = (logical + 7) / 8 * 8;
+  const size_t lds = (size_t)P::kStages * P::kStageBytes;
+  hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  prefill_gemm_kernel<T, SW><<<(unsigned)grid, P::kThreads, lds, s>>>(
+      A, B0, B1, b_stride, C, K, N_out, offsets, table, (int)m_max, n_tiles, group_n,
+      (int)logical);
+  return hipGetLastError();
+}
+
 hipError_t launch_table(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   if (p.m_max <= 0) return hipSuccess;
   tile_table_kernel<<<1, 1024, 0, s>>>(a.offsets, (int)a.E, p.bm, (int)p.m_max, a.sched);
@@ -273,8 +498,8 @@ hipError_t run_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
     return launch_gemm<T, 1, 4, 1, 8, true>(xp, (const T*)a.w_gate, (const T*)a.w_up, stride,
                                             h, (int)a.d, (int)a.F, a.offsets, a.sched,
                                             p.m_max, s);
-  return launch_gemm<T, 2, 2, 4, 8, true>(xp, (const T*)a.w_gate, (const T*)a.w_up, stride, h,
-                                          (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s);
+  return launch_prefill<T, true>(xp, (const T*)a.w_gate, (const T*)a.w_up, stride, h,
+                                 (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s);
 }
 
 template <class T>
@@ -286,8 +511,8 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
     return launch_gemm<T, 1, 4, 1, 8, false>(h, (const T*)a.w_down, nullptr, stride, y,
                                              (int)a.F, (int)a.d, a.offsets, a.sched, p.m_max,
                                              s);
-  return launch_gemm<T, 2, 2, 4, 8, false>(h, (const T*)a.w_down, nullptr, stride, y,
-                                           (int)a.F, (int)a.d, a.offsets, a.sched, p.m_max, s);
+  return launch_prefill<T, false>(h, (const T*)a.w_down, nullptr, stride, y, (int)a.F,
+                                  (int)a.d, a.offsets, a.sched, p.m_max, s);
 }
 
 }  // namespace

@@ -30,21 +30,25 @@ hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
 // ---------------------------------------------------------------------------------------
 // S1: L[t, e] = sum_i x[t, i] w[e, i] + b[e]
 //
-// The router GEMM is skinny (E = 8 or 256 columns) and, for E = 8, bound by reading x
-// once from HBM.  Each wave computes a 16-token x (16 * NT)-expert tile with MFMA straight
-// from global memory (no LDS): per 128-byte k-step a lane loads 32 contiguous bytes of its
-// token row and of each expert row.  Both operands use the same k-chunk assignment
-// (lane group g takes chunks 2g and 2g+1), so the products pair up correctly.
-// Block: 4 waves over 64 tokens; grid.y over groups of 16 * NT experts.
+// The router GEMM is skinny (E = 8 or 256 columns) and bound by reading x (and, for
+// E = 256, w) once.  A block computes a 16-token x (16 * NT)-expert tile with MFMA straight
+// from global memory (no LDS staging); its 8 waves split the reduction axis in 128-byte
+// steps (wave w takes steps w, w + 8, ...), so enough loads are in flight, and their
+// partial tiles are summed in LDS in wave order, which keeps the result deterministic.
+// Per 128-byte step a lane loads 32 contiguous bytes of its token row and of each expert
+// row; both operands use the same k-chunk assignment (lane group g takes chunks 2g and
+// 2g + 1), so the products pair up.  grid = (ceil(T / 16), ceil(E / (16 * NT))).
 // ---------------------------------------------------------------------------------------
+constexpr int kRouterWaves = 8;
+
 template <class T, int NT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kRouterWaves* kWave)
 router_logits_kernel(const T* __restrict__ x, const T* __restrict__ w,
                      const float* __restrict__ bias, float* __restrict__ logits, int T_,
                      int d, int E) {
+  __shared__ float part[kRouterWaves][NT][4][kWave];
   const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int t0 = blockIdx.x * 64 + wave * 16;
-  if (t0 >= T_) return;
+  const int t0 = blockIdx.x * 16;
   const int e0 = blockIdx.y * NT * 16;
   const int r = lane & 15, g = lane >> 4;
   const int t = min(t0 + r, T_ - 1);  // clamped rows are computed but never stored
@@ -58,8 +62,9 @@ router_logits_kernel(const T* __restrict__ x, const T* __restrict__ w,
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int row_bytes = d * (int)sizeof(T);
-  for (int kb = 0; kb < row_bytes; kb += 128) {
+  const int steps = d * (int)sizeof(T) / 128;
+  for (int st = wave; st < steps; st += kRouterWaves) {
+    const int kb = st * 128;
     const u32x4 a0 = ld16(xa + kb), a1 = ld16(xa + kb + 16);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -69,41 +74,44 @@ router_logits_kernel(const T* __restrict__ x, const T* __restrict__ w,
     }
   }
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int e = e0 + n * 16 + r;
-    if (e >= E) continue;
-    const float be = bias ? bias[e] : 0.f;
+  for (int n = 0; n < NT; ++n)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = t0 + 4 * g + i;
-      if (tt < T_) logits[(int64_t)tt * E + e] = acc[n][i] + be;
-    }
+    for (int i = 0; i < 4; ++i) part[wave][n][i][lane] = acc[n][i];
+  __syncthreads();
+  // thread -> (n, i, lane) of the tile; sum the 8 partial tiles in wave order
+  for (int o = threadIdx.x; o < NT * 4 * kWave; o += blockDim.x) {
+    const int n = o / (4 * kWave), i = (o / kWave) % 4, l = o % kWave;
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kRouterWaves; ++ww) v += part[ww][n][i][l];
+    const int e = e0 + n * 16 + (l & 15);
+    const int tt = t0 + 4 * (l >> 4) + i;
+    if (e < E && tt < T_) logits[(int64_t)tt * E + e] = v + (bias ? bias[e] : 0.f);
   }
+}
+
+template <class T>
+hipError_t launch_router_typed(const T* x, const T* w, const float* b, float* logits,
+                               int64_t T_, int64_t d, int64_t E, hipStream_t s) {
+  const unsigned gx = (unsigned)((T_ + 15) / 16);
+  // 64-expert tiles when there are enough token tiles to fill the GPU, else 16-expert ones
+  if (E > 16 && gx * ((E + 63) / 64) >= 512) {
+    router_logits_kernel<T, 4><<<dim3(gx, (unsigned)((E + 63) / 64)), kRouterWaves * kWave,
+                                 0, s>>>(x, w, b, logits, (int)T_, (int)d, (int)E);
+  } else {
+    router_logits_kernel<T, 1><<<dim3(gx, (unsigned)((E + 15) / 16)), kRouterWaves * kWave,
+                                 0, s>>>(x, w, b, logits, (int)T_, (int)d, (int)E);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_router_logits(int dtype, const void* x, const void* w, const float* b,
                                 float* logits, int64_t T, int64_t d, int64_t E,
                                 hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const unsigned gx = (unsigned)((T + 63) / 64);
-  if (E <= 16) {
-    dim3 grid(gx, 1);
-    if (dtype == 1)
-      router_logits_kernel<bf16, 1><<<grid, 256, 0, s>>>((const bf16*)x, (const bf16*)w, b,
-                                                         logits, (int)T, (int)d, (int)E);
-    else
-      router_logits_kernel<float, 1><<<grid, 256, 0, s>>>((const float*)x, (const float*)w, b,
-                                                          logits, (int)T, (int)d, (int)E);
-  } else {
-    dim3 grid(gx, (unsigned)((E + 63) / 64));
-    if (dtype == 1)
-      router_logits_kernel<bf16, 4><<<grid, 256, 0, s>>>((const bf16*)x, (const bf16*)w, b,
-                                                         logits, (int)T, (int)d, (int)E);
-    else
-      router_logits_kernel<float, 4><<<grid, 256, 0, s>>>((const float*)x, (const float*)w, b,
-                                                          logits, (int)T, (int)d, (int)E);
-  }
-  return hipGetLastError();
+  if (dtype == 1)
+    return launch_router_typed<bf16>((const bf16*)x, (const bf16*)w, b, logits, T, d, E, s);
+  return launch_router_typed<float>((const float*)x, (const float*)w, b, logits, T, d, E, s);
 }
 
 // ---------------------------------------------------------------------------------------
