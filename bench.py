@@ -46,7 +46,78 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=None,
                    help="tokens in the oracle's timed sample (default per workload)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a device copy of known size (for rocprofv3 --pmc scaling)")
+    p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                        "script into profiles/traffic_<workload>.json and exit")
     return p.parse_args()
+
+
+COPY_BYTES = 512 << 20  # bytes read (and written) by the calibration copy
+TRAFFIC_KERNELS = {True: "prefill_gemm_kernel", False: "grouped_gemm_kernel"}
+KERNEL_SOURCES = ["routing_expert_ffn_router_amd/csrc/expert_ffn.hip",
+                  "routing_expert_ffn_router_amd/csrc/common.h"]
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_traffic(fetch_dir, write_dir, workload):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant kernel, scaled by what the
+    same counters read for the calibration copy of COPY_BYTES."""
+    import statistics as st
+
+    out = {"workload": workload, "kernel_source_sha": kernel_source_sha(),
+           "copy_bytes": COPY_BYTES}
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = [r for r in _pmc_rows(d) if r["Counter_Name"] == counter]
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        # the gate/up GEMM is the grouped GEMM instantiated with SwiGLU on (the down GEMM's
+        # name carries the false / Lb0E template argument)
+        gate_up = [r for r in rows if ("prefill_gemm_kernel" in r["Kernel_Name"] or
+                                       "grouped_gemm_kernel" in r["Kernel_Name"]) and
+                   "Lb0E" not in r["Kernel_Name"] and "false" not in r["Kernel_Name"]]
+        if not copy or not gate_up:
+            raise SystemExit(f"{counter}: no copy or gate/up kernel rows in {d}")
+        kib_copy = max(copy)  # the calibration copies are the largest copies of the run
+        factor = kib_copy * 1024.0 / COPY_BYTES
+        kib = st.median(float(r["Counter_Value"]) for r in gate_up)
+        out[f"{key}_kib_per_dispatch"] = kib
+        out[f"{key}_copy_kib"] = kib_copy
+        out[f"{key}_copy_factor"] = round(factor, 4)
+        out[f"{key}_bytes_scaled"] = kib * 1024.0 / factor
+        out["kernel"] = gate_up[0]["Kernel_Name"][:120]
+    out["traffic_bytes"] = out["fetch_bytes_scaled"] + out["write_bytes_scaled"]
+    return out
+
+
+def traffic_for(workload):
+    """Scaled HBM bytes per gate/up launch from the committed summary, or None when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t["traffic_bytes"]
 
 
 def build_if_missing():
@@ -100,6 +171,12 @@ def _cpu_model() -> str:
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        t = summarize_traffic(*args.summarize_traffic, args.workload)
+        path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+        json.dump(t, open(path, "w"), indent=1)
+        print(json.dumps(t))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU's share of the MoE layer (expert parallel size 1); "
@@ -165,6 +242,14 @@ def main():
             prev = e
     stage_ms = {n: statistics.mean(v) for n, v in stage_times.items()}
 
+    if args.copy_calibration:  # a plain device copy of known size, for counter scaling
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---- routing statistics of the last call ------------------------------------------------
     routed = lay.routed_counts.cpu().numpy().astype(np.int64)
     kept = lay.tokens_per_expert.cpu().numpy().astype(np.int64)
@@ -194,7 +279,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(bytes_gu / t_gu / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = traffic_for(w.name)
     roof["kernel"] = "grouped_gemm_kernel (gate/up + SwiGLU), incl. its tile-table launch"
     roof["kernel_ms"] = round(stage_ms["gate_up"], 4)
 

@@ -58,6 +58,30 @@ __device__ inline void mma_chunk(f32x4& acc, const u32x4& a, const u32x4& b, flo
 }
 
 // ---------------------------------------------------------------------------------------
+// 32x32 output tile, one 16-byte chunk of A and of B per lane per call.
+//
+// Lane l supplies row (l % 32) of A and of B (B stored [n][k]) and the chunk at k-chunk
+// position (l / 32) of the current 32-byte k-step.  The result tile holds
+// C[8 * (i / 4) + 4 * (l / 32) + (i % 4)][l % 32] in acc[i], i < 16.
+//   bf16: one v_mfma_f32_32x32x16_bf16.  On gfx950 this instruction sustains the full
+//         dense bf16 rate (measured 2.48 PFLOP/s over the chip), while the 16x16x32 form
+//         sustains about 1.4 PFLOP/s, so compute-bound GEMMs use this tile.
+//   fp32: four v_mfma_f32_32x32x2_f32, element i of the chunk in the i-th one.
+// ---------------------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ inline void mma32_chunk(f32x16& acc, const u32x4& a, const u32x4& b, bf16) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+__device__ inline void mma32_chunk(f32x16& acc, const u32x4& a, const u32x4& b, float) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i]), __uint_as_float(b[i]),
+                                               acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------------
 // wave helpers
 // ---------------------------------------------------------------------------------------
 __device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -218,17 +218,17 @@ grouped_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
 }
 
 // ---------------------------------------------------------------------------------------
-// Prefill-sized experts: 256 x 256 block tile, 8 waves, 4-stage LDS pipeline fed by
-// direct global -> LDS loads (global_load_lds_dwordx4).
+// Prefill-sized experts: 256 x 256 block tile, 8 waves, 32x32 MFMA tiles, 4-stage LDS
+// pipeline fed by direct global -> LDS loads (global_load_lds_dwordx4).
 //
 // Each stage holds 32 reduction elements (64 bytes) of the block's 256 A rows and 256
 // weight rows: 512 LDS rows of 64 bytes = 32 KB; four stages use 128 KB of the CU's 160 KB.
 // A wave's direct-load instruction writes 64 lanes x 16 bytes = 16 consecutive LDS rows,
 // lane L landing at row L / 4, slot L % 4 of them.  The slot holding k-chunk c of row r is
-// c ^ f(r) with f(r) = ((r >> 1) ^ (r >> 3)) & 1 | (r >> 1) & 2: for 8 consecutive rows
-// read at one chunk position the 16-byte slots cover all 128 bytes of a 32-bank cycle,
-// and for 16 consecutive rows all 256 bytes of a 64-bank cycle, so the MFMA fragment
-// reads are conflict-free either way.  The lane therefore fetches chunk (L % 4) ^ f(r).
+// c ^ ((r >> 2) & 3).  A 32x32 fragment read (32 rows at one chunk position in each half
+// of the wave) then runs at the full LDS rate of gfx950: measured 4.75 cycles per 64-lane
+// 16-byte read on one CU with 8 waves, against 16.2 without a swizzle.  The lane therefore
+// fetches chunk (L % 4) ^ ((r >> 2) & 3).
 //
 // Pipeline: stages k+1 and k+2 are in flight while stage k is multiplied; at the top of
 // step k a wave waits until its own loads of stage k have landed (vmcnt counts the 4
@@ -237,28 +237,39 @@ grouped_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
 // buffers are distinct __restrict__ pointers of an inlined function so the compiler keeps
 // these explicit waits instead of inserting a full wait before every LDS read.
 //
-// Waves form a 2 (rows) x 4 (weight rows) grid; each owns 128 x 64 of the tile (8 x 4
-// MFMA tiles of 16 x 16).  With SwiGLU a wave's 64 weight rows are 32 gate rows followed
+// Waves form a 2 (rows) x 4 (weight rows) grid; each owns 128 x 64 of the tile (4 x 2
+// MFMA tiles of 32 x 32).  With SwiGLU a wave's 64 weight rows are 32 gate rows followed
 // by the 32 up rows of the same output columns, so a block produces 256 x 128 of h.
 // ---------------------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) char lds_char;
 typedef const __attribute__((address_space(1))) void gbl_void;
 
-struct PrefillTile {
+// ROWB: bytes of each row per stage (64 or 128); STAGES: LDS stages (4 or 2).
+template <int ROWB, int STAGES>
+struct PrefillTileT {
   static constexpr int BM = 256, BNW = 256, kWaves = 8, kThreads = 512;
-  static constexpr int WM = 2, WN = 4, MT = 8, NT = 4;
-  static constexpr int kRowBytes = 64;
+  static constexpr int WM = 2, WN = 4, MT = 4, NT = 2;  // 32x32 tiles per wave
+  static constexpr int kRowBytes = ROWB;
+  static constexpr int kChunks = ROWB / 16;                  // 16-byte chunks per row
+  static constexpr int kKSteps = ROWB / 32;                  // 32-byte MFMA k-steps
   static constexpr int kStageBytes = (BM + BNW) * kRowBytes;
-  static constexpr int kStages = 4;
-  static constexpr int kDmaPerWave = (BM + BNW) / 16 / kWaves;  // 16 LDS rows per load
+  static constexpr int kStages = STAGES;
+  static constexpr int kRowsPerLoad = 1024 / ROWB;           // rows per direct load
+  static constexpr int kDmaPerWave = (BM + BNW) / kRowsPerLoad / kWaves;
+  // slot of k-chunk c in row r: c ^ swz(r); conflict-free 32x32 fragment reads (measured)
+  __device__ static inline int swz(int r) {
+    return ROWB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+  }
 };
+using PrefillTile = PrefillTileT<128, 2>;
 
-__device__ inline int swz64(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
-
+// wait until at most N direct loads of this wave are outstanding, then block barrier
 template <int N>
 __device__ inline void wait_vm_barrier() {
-  static_assert(N == 0 || N == 4 || N == 8, "vmcnt immediate");
-  if (N == 8)
+  static_assert(N == 0 || N == 4 || N == 8 || N == 16, "vmcnt immediate");
+  if (N == 16)
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  else if (N == 8)
     asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
   else if (N == 4)
     asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
@@ -266,14 +277,13 @@ __device__ inline void wait_vm_barrier() {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <class T, bool SWIGLU>
+template <class T, bool SWIGLU, class P>
 __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     const T* __restrict__ A, const T* __restrict__ B0, const T* __restrict__ B1,
     int64_t b_expert_stride, T* __restrict__ C, int K, int N_out,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ table,
     int m_tiles_max, int n_tiles, int group_n, int grid_logical, lds_char* __restrict__ s0,
     lds_char* __restrict__ s1, lds_char* __restrict__ s2, lds_char* __restrict__ s3) {
-  using P = PrefillTile;
   constexpr int BN = SWIGLU ? P::BNW / 2 : P::BNW;
   const int bid = blockIdx.x;
   const int per_xcd = gridDim.x >> 3;
@@ -299,8 +309,8 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   const T* B1e = SWIGLU ? B1 + (int64_t)e * b_expert_stride : nullptr;
 #pragma unroll
   for (int i = 0; i < P::kDmaPerWave; ++i) {
-    const int r = (wave * P::kDmaPerWave + i) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ swz64(r);
+    const int r = (wave * P::kDmaPerWave + i) * P::kRowsPerLoad + lane / P::kChunks;
+    const int c = (lane % P::kChunks) ^ P::swz(r);
     const char* rowp;
     if (r < P::BM) {
       const int gr = min(m_begin + r, m_end - 1);  // rows past the expert: never stored
@@ -319,18 +329,20 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   }
   const int dma_lds = wave * P::kDmaPerWave * 1024;
 
-  f32x4 acc[P::MT][P::NT];
+  f32x16 acc[P::MT][P::NT];
 #pragma unroll
   for (int i = 0; i < P::MT; ++i)
 #pragma unroll
-    for (int j = 0; j < P::NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < P::NT; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   // a wave whose 128-row band lies past the expert's rows skips its MFMAs
-  const bool band_live = m_begin + wm * P::MT * 16 < m_end;
-  const int frag_row = lane & 15, frag_grp = lane >> 4;
-  const int frag_off = frag_row * P::kRowBytes + ((frag_grp ^ swz64(frag_row)) << 4);
-  const int a_frag = wm * P::MT * 16 * P::kRowBytes + frag_off;
-  const int b_frag = (P::BM + wn * P::NT * 16) * P::kRowBytes + frag_off;
+  const bool band_live = m_begin + wm * P::MT * 32 < m_end;
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  const int a_frag = (wm * P::MT * 32 + frag_row) * P::kRowBytes;
+  const int b_frag = (P::BM + wn * P::NT * 32 + frag_row) * P::kRowBytes;
+  const int swz = P::swz(frag_row);
 
   auto issue = [&](int kt, lds_char* buf) {
     const int64_t koff = (int64_t)kt * P::kRowBytes;
@@ -339,67 +351,91 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
       __builtin_amdgcn_global_load_lds((gbl_void*)(src[i] + koff), buf + dma_lds + i * 1024, 16,
                                        0, 0);
   };
-  auto compute = [&](const lds_char* buf) {
-    if (!band_live) return;
-    // all fragment reads first (B, then A in the order the MFMAs consume them), so the
-    // MFMAs wait progressively instead of after each read
-    u32x4 fa[P::MT], fb[P::NT];
+  // Fragments of one 32-byte k-step: 4 A tiles + 2 B tiles.  The reads of k-step s+1 are
+  // issued before the MFMAs of k-step s (two register sets), and the scheduling groups
+  // pin that order, so each k-step's 8 MFMAs cover the next k-step's LDS latency.
+  auto load_frags = [&](const lds_char* buf, int ks, u32x4* fa, u32x4* fb) {
+    const int slot = ((ks * 2 + frag_half) ^ swz) << 4;
 #pragma unroll
     for (int j = 0; j < P::NT; ++j)
       fb[j] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          buf + b_frag + j * 16 * P::kRowBytes);
+          buf + b_frag + j * 32 * P::kRowBytes + slot);
 #pragma unroll
     for (int i = 0; i < P::MT; ++i)
       fa[i] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          buf + a_frag + i * 16 * P::kRowBytes);
-    __builtin_amdgcn_sched_barrier(0);
+          buf + a_frag + i * 32 * P::kRowBytes + slot);
+  };
+  auto compute = [&](const lds_char* buf) {
+    if (!band_live) return;
+    u32x4 fa[2][P::MT], fb[2][P::NT];
+    load_frags(buf, 0, fa[0], fb[0]);
 #pragma unroll
-    for (int i = 0; i < P::MT; ++i)
+    for (int ks = 0; ks < P::kKSteps; ++ks) {
+      if (ks + 1 < P::kKSteps) load_frags(buf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
 #pragma unroll
-      for (int j = 0; j < P::NT; ++j) mma_chunk(acc[i][j], fa[i], fb[j], T());
+      for (int i = 0; i < P::MT; ++i)
+#pragma unroll
+        for (int j = 0; j < P::NT; ++j)
+          mma32_chunk(acc[i][j], fa[ks & 1][i], fb[ks & 1][j], T());
+      // order: [6 LDS reads of step 0] then per step: 6 reads of the next step, 8 MFMAs
+      if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x100, P::MT + P::NT, 0);
+      if (ks + 1 < P::kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, P::MT + P::NT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, P::MT * P::NT, 0);
+    }
   };
   const int KT = (int)(row_bytes / P::kRowBytes);
+  constexpr int D = P::kStages - 1;  // stages in flight ahead of the one multiplied
   auto step = [&](int kt, const lds_char* cur, lds_char* nxt) {
     if (kt >= KT) return;
-    if (kt + 2 < KT)
-      wait_vm_barrier<8>();
-    else if (kt + 1 < KT)
-      wait_vm_barrier<4>();
+    // stage kt must have landed; stages kt+1 .. kt+D-1 may still be in flight
+    if (D >= 3 && kt + 2 < KT)
+      wait_vm_barrier<2 * P::kDmaPerWave * (D >= 3)>();
+    else if (D >= 2 && kt + 1 < KT)
+      wait_vm_barrier<P::kDmaPerWave * (D >= 2)>();
     else
       wait_vm_barrier<0>();
-    if (kt + 3 < KT) issue(kt + 3, nxt);
+    if (kt + D < KT) issue(kt + D, nxt);
     compute(cur);
   };
 
-  issue(0, s0);
-  if (KT > 1) issue(1, s1);
-  if (KT > 2) issue(2, s2);
-  for (int kt = 0; kt < KT; kt += 4) {
-    step(kt + 0, s0, s3);
-    step(kt + 1, s1, s0);
-    step(kt + 2, s2, s1);
-    step(kt + 3, s3, s2);
+  if (P::kStages == 4) {
+    issue(0, s0);
+    if (KT > 1) issue(1, s1);
+    if (KT > 2) issue(2, s2);
+    for (int kt = 0; kt < KT; kt += 4) {
+      step(kt + 0, s0, s3);
+      step(kt + 1, s1, s0);
+      step(kt + 2, s2, s1);
+      step(kt + 3, s3, s2);
+    }
+  } else {
+    issue(0, s0);
+    for (int kt = 0; kt < KT; kt += 2) {
+      step(kt + 0, s0, s1);
+      step(kt + 1, s1, s0);
+    }
   }
 
   if (!band_live) return;
+  // lane holds column (lane % 32) and rows 8 * (q / 4) + 4 * (lane / 32) + q % 4 of a tile
   constexpr int NOUT = SWIGLU ? P::NT / 2 : P::NT;
 #pragma unroll
   for (int i = 0; i < P::MT; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = m_begin + wm * P::MT * 16 + i * 16 + frag_grp * 4 + r;
+    for (int q = 0; q < 16; ++q) {
+      const int row = m_begin + wm * P::MT * 32 + i * 32 + 8 * (q >> 2) + 4 * frag_half + (q & 3);
       if (row >= m_end) continue;
-      const int col0 = nt * BN + wn * NOUT * 16 + frag_row;
+      const int col0 = nt * BN + wn * NOUT * 32 + frag_row;
       T* crow = C + (int64_t)row * N_out + col0;
 #pragma unroll
       for (int j = 0; j < NOUT; ++j) {
-        if (col0 + j * 16 >= N_out) continue;
+        if (col0 + j * 32 >= N_out) continue;
         float v;
         if (SWIGLU)
-          v = silu_f32(acc[i][j][r]) * acc[i][j + NOUT][r];
+          v = silu_f32(acc[i][j][q]) * acc[i][j + NOUT][q];
         else
-          v = acc[i][j][r];
-        crow[j * 16] = Elt<T>::from_f32(v);
+          v = acc[i][j][q];
+        crow[j * 32] = Elt<T>::from_f32(v);
       }
     }
   }
@@ -415,9 +451,11 @@ prefill_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
   extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
   lds_char* base = (lds_char*)smem_dyn;
   constexpr int S = PrefillTile::kStageBytes;
-  prefill_gemm_body<T, SWIGLU>(A, B0, B1, b_expert_stride, C, K, N_out, offsets, table,
-                               m_tiles_max, n_tiles, group_n, grid_logical, base, base + S,
-                               base + 2 * S, base + 3 * S);
+  // with two stages, s2 and s3 are never used
+  prefill_gemm_body<T, SWIGLU, PrefillTile>(
+      A, B0, B1, b_expert_stride, C, K, N_out, offsets, table, m_tiles_max, n_tiles, group_n,
+      grid_logical, base, base + S, base + (PrefillTile::kStages > 2 ? 2 * S : 0),
+      base + (PrefillTile::kStages > 3 ? 3 * S : 0));
 }
 
 // ---------------------------------------------------------------------------------------
