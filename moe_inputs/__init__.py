@@ -196,6 +196,8 @@ def host_lib():
 def dev_lib():
     global _dev_lib
     if _dev_lib is None:
+        import torch  # noqa: F401  (bind to the HIP runtime torch loaded; see load_library)
+
         lib = _load("libmoe_inputs_dev.so")
         lib.moe_inputs_fill_device.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64,
                                                ctypes.c_uint64, ctypes.c_uint32,

@@ -59,6 +59,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    # torch ships its own HIP runtime with the same soname as the system one; importing
+    # torch first makes libmoe.so bind to that copy, so tensors, streams and kernels all
+    # live in one runtime (two copies in one process break launches on torch's streams).
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(path)
     i64, i32, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     sig = {
