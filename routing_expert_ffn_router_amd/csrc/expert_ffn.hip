@@ -13,13 +13,15 @@
 //     one-block kernel writes the table tile -> (expert, first row) on the device from the
 //     expert offsets, so the host never waits for the routing.  The grid is sized from an
 //     upper bound on the tile count and surplus blocks exit at once.
-//   - Block tile BM x BN_W weight rows, K in 128-byte steps staged through LDS (two stages,
-//     global loads of step k+1 in flight while step k is multiplied).  LDS rows are 128
-//     bytes with the 16-byte chunks XOR-swizzled by (row & 7), so the MFMA fragment reads
-//     (16 rows x one chunk column) hit distinct banks.
-//   - SwiGLU: the B tile of a wave holds NT/2 tiles of gate rows followed by the NT/2 tiles
-//     of up rows for the same output columns, so gate and up accumulators of one output
-//     element sit in the same lane and the epilogue computes silu(g) * u in registers.
+//   - Operands reach LDS by direct global -> LDS loads in 128-byte row pieces, in a ring of
+//     stages; fragments are read with a measured bank-conflict-free swizzle and fed to
+//     32x32x16 MFMAs (the bf16 form that runs at the full dense rate on gfx950).
+//   - Two tile shapes of the same template: prefill-sized experts (mean > 32 rows) use
+//     256 x 256 tiles (128 flop per loaded byte); decode-sized experts stream weights with
+//     64 x 256 tiles and three stages, keeping 80 KB of weight reads in flight per CU.
+//   - SwiGLU: each wave's weight rows are 32 gate rows followed by the 32 up rows of the
+//     same output columns, so gate and up accumulators of one output element sit in the
+//     same lane and the epilogue computes silu(g) * u in registers.
 //   - Block order: blocks are dealt round-robin to the 8 XCDs; the logical tile index is
 //     remapped so each XCD walks a contiguous range in which neighbouring tiles share the
 //     A rows (same m-tile) and the B rows (same n-group), keeping both in that XCD's L2.
@@ -29,22 +31,6 @@
 namespace moe {
 
 __device__ inline float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
-
-template <int WAVES_M, int WAVES_N, int MT, int NT, bool SWIGLU>
-struct GemmShape {
-  static constexpr int kThreads = WAVES_M * WAVES_N * kWave;
-  static constexpr int BM = WAVES_M * MT * 16;
-  static constexpr int kWaveRows = NT * 16;             // weight rows per wave
-  static constexpr int BNW = WAVES_N * kWaveRows;       // weight rows per block
-  static constexpr int BN = SWIGLU ? BNW / 2 : BNW;     // output columns per block
-  // 16-byte chunks per thread and stage (A: the last round may leave threads idle)
-  static constexpr int kAChunks = (BM * 8 + kThreads - 1) / kThreads;
-  static constexpr bool kAPartial = BM * 8 % kThreads != 0;
-  static constexpr int kBChunks = BNW * 8 / kThreads;
-  static constexpr int kStageBytes = (BM + BNW) * 128;
-  static_assert(BNW * 8 % kThreads == 0, "tile / thread mismatch");
-  static_assert(!SWIGLU || NT % 2 == 0, "SwiGLU needs gate and up halves");
-};
 
 // Tile table for one row-tile height BM: table[0] = number of m-tiles over all experts;
 // entry i (i < table[0]) is (expert, first row) at table[1 + 2i], table[2 + 2i].  Experts
@@ -76,147 +62,6 @@ tile_table_kernel(const int32_t* __restrict__ offsets, int E, int bm, int m_max,
   }
 }
 
-template <class T, int WAVES_M, int WAVES_N, int MT, int NT, bool SWIGLU>
-__global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
-grouped_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
-                    const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C,
-                    int K, int N_out, const int32_t* __restrict__ offsets,
-                    const int32_t* __restrict__ table, int m_tiles_max, int n_tiles,
-                    int group_n, int grid_logical) {
-  using S = GemmShape<WAVES_M, WAVES_N, MT, NT, SWIGLU>;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-
-  // ---- block -> (expert, m-tile, n-tile) ------------------------------------------------
-  const int bid = blockIdx.x;
-  const int per_xcd = gridDim.x >> 3;
-  const int logical = (bid & 7) * per_xcd + (bid >> 3);
-  if (logical >= grid_logical) return;
-  const int per_group = m_tiles_max * group_n;
-  const int grp = logical / per_group, rem = logical - grp * per_group;
-  const int mt = rem / group_n, nt = grp * group_n + (rem - (rem / group_n) * group_n);
-  if (nt >= n_tiles) return;
-  if (mt >= table[0]) return;
-  const int e = table[1 + 2 * mt];
-  const int m_begin = table[2 + 2 * mt];
-  const int m_end = offsets[e + 1];
-
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int64_t row_bytes = (int64_t)K * sizeof(T);
-
-  // ---- per-thread global source rows (fixed over k) ---------------------------------------
-  const char* a_src[S::kAChunks];
-  int a_lds[S::kAChunks];
-#pragma unroll
-  for (int i = 0; i < S::kAChunks; ++i) {
-    const int c0 = tid + i * S::kThreads;
-    const int c = (S::kAPartial && c0 >= S::BM * 8) ? c0 % (S::BM * 8) : c0;  // duplicate load
-    const int r = c >> 3, ch = c & 7;
-    const int gr = min(m_begin + r, m_end - 1);  // rows past the expert: computed, not stored
-    a_src[i] = reinterpret_cast<const char*>(A) + (int64_t)gr * row_bytes + ch * 16;
-    a_lds[i] = r * 128 + ((ch ^ (r & 7)) << 4);
-  }
-  const char* b_src[S::kBChunks];
-  int b_lds[S::kBChunks];
-  const T* B0e = B0 + (int64_t)e * b_expert_stride;
-  const T* B1e = SWIGLU ? B1 + (int64_t)e * b_expert_stride : nullptr;
-#pragma unroll
-  for (int i = 0; i < S::kBChunks; ++i) {
-    const int c = tid + i * S::kThreads, r = c >> 3, ch = c & 7;
-    const T* rowp;
-    if (SWIGLU) {
-      const int w = r / S::kWaveRows, within = r % S::kWaveRows, half = S::kWaveRows / 2;
-      // columns past N_out (last n-tile) are clamped: computed, never stored
-      const int col = min(nt * S::BN + w * half + (within % half), N_out - 1);
-      rowp = (within < half ? B0e : B1e) + (int64_t)col * K;
-    } else {
-      rowp = B0e + (int64_t)min(nt * S::BN + r, N_out - 1) * K;
-    }
-    b_src[i] = reinterpret_cast<const char*>(rowp) + ch * 16;
-    b_lds[i] = S::BM * 128 + r * 128 + ((ch ^ (r & 7)) << 4);
-  }
-
-  f32x4 acc[MT][NT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 ra[S::kAChunks], rb[S::kBChunks];
-  auto load_global = [&](int kt) {
-    const int64_t off = (int64_t)kt * 128;
-#pragma unroll
-    for (int i = 0; i < S::kAChunks; ++i) ra[i] = ld16(a_src[i] + off);
-#pragma unroll
-    for (int i = 0; i < S::kBChunks; ++i) rb[i] = ld16(b_src[i] + off);
-  };
-  auto store_lds = [&](int stage) {
-    char* base = smem + stage * S::kStageBytes;
-#pragma unroll
-    for (int i = 0; i < S::kAChunks; ++i) st16(base + a_lds[i], ra[i]);
-#pragma unroll
-    for (int i = 0; i < S::kBChunks; ++i) st16(base + b_lds[i], rb[i]);
-  };
-
-  // fragment addresses: row (lane & 15) of each 16-row tile, chunk (ks * 4 + lane / 16)
-  // swizzled by (row & 7) == (lane & 7)
-  const int frag_row = lane & 15, frag_grp = lane >> 4, swz = lane & 7;
-  const int a_frag = (wm * MT * 16 + frag_row) * 128;
-  const int b_frag = S::BM * 128 + (wn * NT * 16 + frag_row) * 128;
-
-  auto compute = [&](int stage) {
-    const char* base = smem + stage * S::kStageBytes;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int chunk_off = ((ks * 4 + frag_grp) ^ swz) << 4;
-      u32x4 fa[MT], fb[NT];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) fa[i] = ld16(base + a_frag + i * 16 * 128 + chunk_off);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) fb[j] = ld16(base + b_frag + j * 16 * 128 + chunk_off);
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) mma_chunk(acc[i][j], fa[i], fb[j], T());
-    }
-  };
-
-  const int KT = (int)(row_bytes / 128);
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    if (more) load_global(kt + 1);
-    compute(kt & 1);
-    if (more) store_lds((kt + 1) & 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue ----------------------------------------------------------------------------
-  constexpr int NOUT = SWIGLU ? NT / 2 : NT;
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = m_begin + wm * MT * 16 + i * 16 + frag_grp * 4 + r;
-      if (row >= m_end) continue;
-      const int col0 = nt * S::BN + wn * NOUT * 16 + frag_row;
-      T* crow = C + (int64_t)row * N_out + col0;
-#pragma unroll
-      for (int j = 0; j < NOUT; ++j) {
-        if (col0 + j * 16 >= N_out) continue;
-        float v;
-        if (SWIGLU)
-          v = silu_f32(acc[i][j][r]) * acc[i][j + NOUT][r];
-        else
-          v = acc[i][j][r];
-        crow[j * 16] = Elt<T>::from_f32(v);
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------------------
 // Prefill-sized experts: 256 x 256 block tile, 8 waves, 32x32 MFMA tiles, 4-stage LDS
 // pipeline fed by direct global -> LDS loads (global_load_lds_dwordx4).
@@ -244,11 +89,14 @@ grouped_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
 typedef __attribute__((address_space(3))) char lds_char;
 typedef const __attribute__((address_space(1))) void gbl_void;
 
-// ROWB: bytes of each row per stage (64 or 128); STAGES: LDS stages (4 or 2).
-template <int ROWB, int STAGES>
+// ROWB: bytes of each row per stage (64 or 128); STAGES: LDS stages (2, 3 or 4);
+// BM_ activation rows and BNW_ weight rows per block; the 8 waves split it WM_ x WN_.
+template <int ROWB, int STAGES, int BM_, int BNW_, int WM_, int WN_>
 struct PrefillTileT {
-  static constexpr int BM = 256, BNW = 256, kWaves = 8, kThreads = 512;
-  static constexpr int WM = 2, WN = 4, MT = 4, NT = 2;  // 32x32 tiles per wave
+  static constexpr int BM = BM_, BNW = BNW_, kWaves = 8, kThreads = 512;
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int MT = BM / WM / 32, NT = BNW / WN / 32;  // 32x32 tiles per wave
+  static constexpr int kWaveCols = NT * 32;                    // weight rows per wave
   static constexpr int kRowBytes = ROWB;
   static constexpr int kChunks = ROWB / 16;                  // 16-byte chunks per row
   static constexpr int kKSteps = ROWB / 32;                  // 32-byte MFMA k-steps
@@ -256,25 +104,24 @@ struct PrefillTileT {
   static constexpr int kStages = STAGES;
   static constexpr int kRowsPerLoad = 1024 / ROWB;           // rows per direct load
   static constexpr int kDmaPerWave = (BM + BNW) / kRowsPerLoad / kWaves;
+  static_assert(WM * WN == kWaves && NT % 2 == 0 && MT >= 1, "wave grid");
+  static_assert((BM + BNW) % (kRowsPerLoad * kWaves) == 0, "direct loads per wave");
   // slot of k-chunk c in row r: c ^ swz(r); conflict-free 32x32 fragment reads (measured)
   __device__ static inline int swz(int r) {
     return ROWB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
   }
 };
-using PrefillTile = PrefillTileT<128, 2>;
+// Prefill: 256 x 256 tile, two 64 KB stages of 128-byte row pieces.
+using PrefillTile = PrefillTileT<128, 2, 256, 256, 2, 4>;
+// Decode: weight streaming.  64 x 256 tile, three 40 KB stages, so two stages (80 KB per
+// CU) of weight reads are in flight while one is multiplied.
+using DecodeDmaTile = PrefillTileT<128, 3, 64, 256, 2, 4>;
 
 // wait until at most N direct loads of this wave are outstanding, then block barrier
 template <int N>
 __device__ inline void wait_vm_barrier() {
-  static_assert(N == 0 || N == 4 || N == 8 || N == 16, "vmcnt immediate");
-  if (N == 16)
-    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-  else if (N == 8)
-    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-  else if (N == 4)
-    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 template <class T, bool SWIGLU, class P>
@@ -318,9 +165,10 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     } else {
       const int br = r - P::BM;
       if (SWIGLU) {
-        const int w = br / 64, within = br % 64;
-        const int col = min(nt * BN + w * 32 + (within % 32), N_out - 1);
-        rowp = reinterpret_cast<const char*>((within < 32 ? B0e : B1e) + (int64_t)col * K);
+        constexpr int half = P::kWaveCols / 2;
+        const int w = br / P::kWaveCols, within = br % P::kWaveCols;
+        const int col = min(nt * BN + w * half + (within % half), N_out - 1);
+        rowp = reinterpret_cast<const char*>((within < half ? B0e : B1e) + (int64_t)col * K);
       } else {
         rowp = reinterpret_cast<const char*>(B0e + (int64_t)min(nt * BN + br, N_out - 1) * K);
       }
@@ -344,16 +192,17 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   const int b_frag = (P::BM + wn * P::NT * 32 + frag_row) * P::kRowBytes;
   const int swz = P::swz(frag_row);
 
-  auto issue = [&](int kt, lds_char* buf) {
-    const int64_t koff = (int64_t)kt * P::kRowBytes;
-#pragma unroll
-    for (int i = 0; i < P::kDmaPerWave; ++i)
-      __builtin_amdgcn_global_load_lds((gbl_void*)(src[i] + koff), buf + dma_lds + i * 1024, 16,
-                                       0, 0);
+  const int KT = (int)(row_bytes / P::kRowBytes);
+  constexpr int D = P::kStages - 1;  // stages in flight ahead of the one multiplied
+  // Direct load i of stage kt into buffer buf.  Stages past the end re-read the last stage
+  // (k offset clamped, always in bounds) into a buffer nobody reads again, so every step
+  // issues the same number of loads and the wait count below is a constant.
+  auto dma = [&](int i, int kt, lds_char* buf) {
+    const int64_t koff = (int64_t)min(kt, KT - 1) * P::kRowBytes;
+    __builtin_amdgcn_global_load_lds((gbl_void*)(src[i] + koff), buf + dma_lds + i * 1024, 16,
+                                     0, 0);
   };
-  // Fragments of one 32-byte k-step: 4 A tiles + 2 B tiles.  The reads of k-step s+1 are
-  // issued before the MFMAs of k-step s (two register sets), and the scheduling groups
-  // pin that order, so each k-step's 8 MFMAs cover the next k-step's LDS latency.
+  // Fragments of one 32-byte k-step: MT A tiles + NT B tiles.
   auto load_frags = [&](const lds_char* buf, int ks, u32x4* fa, u32x4* fb) {
     const int slot = ((ks * 2 + frag_half) ^ swz) << 4;
 #pragma unroll
@@ -365,6 +214,8 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
       fa[i] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
           buf + a_frag + i * 32 * P::kRowBytes + slot);
   };
+  // Multiply stage `buf`.  The reads of k-step s+1 go out before the MFMAs of k-step s
+  // (two register sets), so each k-step's MFMAs cover the next k-step's LDS latency.
   auto compute = [&](const lds_char* buf) {
     if (!band_live) return;
     u32x4 fa[2][P::MT], fb[2][P::NT];
@@ -377,44 +228,57 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
 #pragma unroll
         for (int j = 0; j < P::NT; ++j)
           mma32_chunk(acc[i][j], fa[ks & 1][i], fb[ks & 1][j], T());
-      // order: [6 LDS reads of step 0] then per step: 6 reads of the next step, 8 MFMAs
+      // order: [reads of step 0]; per step: reads of the next step, then its MFMAs
       if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x100, P::MT + P::NT, 0);
       if (ks + 1 < P::kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, P::MT + P::NT, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, P::MT * P::NT, 0);
     }
   };
-  const int KT = (int)(row_bytes / P::kRowBytes);
-  constexpr int D = P::kStages - 1;  // stages in flight ahead of the one multiplied
+  // One step: wait for stage kt (the D-1 later stages may still be in flight), make every
+  // wave's loads visible, issue stage kt + D into the buffer step kt-1 finished reading,
+  // then multiply.  Issuing the stage's loads together here lets the other wave of the
+  // SIMD keep the MFMA pipe busy while this one waits on the address FIFO; spreading them
+  // between the MFMAs measured slower.
   auto step = [&](int kt, const lds_char* cur, lds_char* nxt) {
     if (kt >= KT) return;
-    // stage kt must have landed; stages kt+1 .. kt+D-1 may still be in flight
-    if (D >= 3 && kt + 2 < KT)
-      wait_vm_barrier<2 * P::kDmaPerWave * (D >= 3)>();
-    else if (D >= 2 && kt + 1 < KT)
-      wait_vm_barrier<P::kDmaPerWave * (D >= 2)>();
-    else
-      wait_vm_barrier<0>();
-    if (kt + D < KT) issue(kt + D, nxt);
+    wait_vm_barrier<(D - 1) * P::kDmaPerWave>();
+#pragma unroll
+    for (int i = 0; i < P::kDmaPerWave; ++i) dma(i, kt + D, nxt);
     compute(cur);
   };
 
+  // prologue: stages 0 .. D-1
+#pragma unroll
+  for (int i = 0; i < P::kDmaPerWave; ++i) dma(i, 0, s0);
+  if (D >= 2) {
+#pragma unroll
+    for (int i = 0; i < P::kDmaPerWave; ++i) dma(i, 1, s1);
+  }
+  if (D >= 3) {
+#pragma unroll
+    for (int i = 0; i < P::kDmaPerWave; ++i) dma(i, 2, s2);
+  }
   if (P::kStages == 4) {
-    issue(0, s0);
-    if (KT > 1) issue(1, s1);
-    if (KT > 2) issue(2, s2);
     for (int kt = 0; kt < KT; kt += 4) {
       step(kt + 0, s0, s3);
       step(kt + 1, s1, s0);
       step(kt + 2, s2, s1);
       step(kt + 3, s3, s2);
     }
+  } else if (P::kStages == 3) {
+    for (int kt = 0; kt < KT; kt += 3) {
+      step(kt + 0, s0, s2);
+      step(kt + 1, s1, s0);
+      step(kt + 2, s2, s1);
+    }
   } else {
-    issue(0, s0);
     for (int kt = 0; kt < KT; kt += 2) {
       step(kt + 0, s0, s1);
       step(kt + 1, s1, s0);
     }
   }
+  // drain the loads issued past the last stage before the block's LDS can be reassigned
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (!band_live) return;
   // lane holds column (lane % 32) and rows 8 * (q / 4) + 4 * (lane / 32) + q % 4 of a tile
@@ -441,8 +305,8 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   }
 }
 
-template <class T, bool SWIGLU>
-__global__ void __launch_bounds__(PrefillTile::kThreads)
+template <class T, bool SWIGLU, class P>
+__global__ void __launch_bounds__(P::kThreads)
 prefill_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
                     const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C, int K,
                     int N_out, const int32_t* __restrict__ offsets,
@@ -450,23 +314,23 @@ prefill_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
                     int group_n, int grid_logical) {
   extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
   lds_char* base = (lds_char*)smem_dyn;
-  constexpr int S = PrefillTile::kStageBytes;
-  // with two stages, s2 and s3 are never used
-  prefill_gemm_body<T, SWIGLU, PrefillTile>(
-      A, B0, B1, b_expert_stride, C, K, N_out, offsets, table, m_tiles_max, n_tiles, group_n,
-      grid_logical, base, base + S, base + (PrefillTile::kStages > 2 ? 2 * S : 0),
-      base + (PrefillTile::kStages > 3 ? 3 * S : 0));
+  constexpr int S = P::kStageBytes;
+  // stage buffers past kStages are never used
+  prefill_gemm_body<T, SWIGLU, P>(A, B0, B1, b_expert_stride, C, K, N_out, offsets, table,
+                                  m_tiles_max, n_tiles, group_n, grid_logical, base, base + S,
+                                  base + (P::kStages > 2 ? 2 * S : 0),
+                                  base + (P::kStages > 3 ? 3 * S : 0));
 }
 
 // ---------------------------------------------------------------------------------------
 // launch configurations
 // ---------------------------------------------------------------------------------------
 // Row-tile heights: prefill-sized experts (mean > 32 rows) use the 256-row prefill kernel,
-// decode-sized ones 16-row tiles.
+// decode-sized ones the 32-row weight-streaming kernel.
 FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R) {
   FfnPlan p;
   p.small = T * k <= 32 * E;
-  p.bm = p.small ? 16 : PrefillTile::BM;
+  p.bm = p.small ? DecodeDmaTile::BM : PrefillTile::BM;
   int64_t m_max = (R + E * (p.bm - 1)) / p.bm;
   const int64_t m_cap = E * ((C + p.bm - 1) / p.bm);
   p.m_max = m_cap < m_max ? m_cap : m_max;
@@ -476,34 +340,10 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R) {
 
 namespace {
 
-template <class T, int WM, int WN, int MT, int NT, bool SW>
-hipError_t launch_gemm(const T* A, const T* B0, const T* B1, int64_t b_stride, T* C, int K,
-                       int N_out, const int32_t* offsets, const int32_t* table, int64_t m_max,
-                       hipStream_t s) {
-  using S = GemmShape<WM, WN, MT, NT, SW>;
-  if (m_max <= 0) return hipSuccess;
-  const int n_tiles = (N_out + S::BN - 1) / S::BN;
-  const int group_n = n_tiles < 8 ? n_tiles : 8;
-  const int n_groups = (n_tiles + group_n - 1) / group_n;
-  const int64_t logical = m_max * group_n * n_groups;
-  const int64_t grid = (logical + 7) / 8 * 8;
-  const size_t lds = 2 * S::kStageBytes;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_kernel<T, WM, WN, MT, NT, SW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  grouped_gemm_kernel<T, WM, WN, MT, NT, SW><<<(unsigned)grid, S::kThreads, lds, s>>>(
-      A, B0, B1, b_stride, C, K, N_out, offsets, table, (int)m_max, n_tiles, group_n,
-      (int)logical);
-  return hipGetLastError();
-}
-
-template <class T, bool SW>
+template <class T, bool SW, class P = PrefillTile>
 hipError_t launch_prefill(const T* A, const T* B0, const T* B1, int64_t b_stride, T* C, int K,
                           int N_out, const int32_t* offsets, const int32_t* table,
                           int64_t m_max, hipStream_t s) {
-  using P = PrefillTile;
   if (m_max <= 0) return hipSuccess;
   constexpr int BN = SW ? P::BNW / 2 : P::BNW;
   const int n_tiles = (N_out + BN - 1) / BN;
@@ -512,10 +352,10 @@ hipError_t launch_prefill(const T* A, const T* B0, const T* B1, int64_t b_stride
   const int64_t logical = m_max * group_n * n_groups;
   const int64_t grid = (logical + 7) / 8 * 8;
   const size_t lds = (size_t)P::kStages * P::kStageBytes;
-  hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW>,
+  hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW, P>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  prefill_gemm_kernel<T, SW><<<(unsigned)grid, P::kThreads, lds, s>>>(
+  prefill_gemm_kernel<T, SW, P><<<(unsigned)grid, P::kThreads, lds, s>>>(
       A, B0, B1, b_stride, C, K, N_out, offsets, table, (int)m_max, n_tiles, group_n,
       (int)logical);
   return hipGetLastError();
@@ -533,9 +373,9 @@ hipError_t run_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   T* h = (T*)a.h;
   const int64_t stride = a.F * a.d;
   if (p.small)
-    return launch_gemm<T, 1, 4, 1, 8, true>(xp, (const T*)a.w_gate, (const T*)a.w_up, stride,
-                                            h, (int)a.d, (int)a.F, a.offsets, a.sched,
-                                            p.m_max, s);
+    return launch_prefill<T, true, DecodeDmaTile>(xp, (const T*)a.w_gate, (const T*)a.w_up,
+                                                  stride, h, (int)a.d, (int)a.F, a.offsets,
+                                                  a.sched, p.m_max, s);
   return launch_prefill<T, true>(xp, (const T*)a.w_gate, (const T*)a.w_up, stride, h,
                                  (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s);
 }
@@ -546,9 +386,9 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   T* y = (T*)a.y_perm;
   const int64_t stride = a.d * a.F;
   if (p.small)
-    return launch_gemm<T, 1, 4, 1, 8, false>(h, (const T*)a.w_down, nullptr, stride, y,
-                                             (int)a.F, (int)a.d, a.offsets, a.sched, p.m_max,
-                                             s);
+    return launch_prefill<T, false, DecodeDmaTile>(h, (const T*)a.w_down, nullptr, stride, y,
+                                                   (int)a.F, (int)a.d, a.offsets, a.sched,
+                                                   p.m_max, s);
   return launch_prefill<T, false>(h, (const T*)a.w_down, nullptr, stride, y, (int)a.F,
                                   (int)a.d, a.offsets, a.sched, p.m_max, s);
 }
