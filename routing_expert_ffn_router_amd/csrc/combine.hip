@@ -10,49 +10,55 @@
 
 namespace moe {
 
+// One wave per (token, 64-chunk column segment): lane l of segment s sums chunk
+// s * 64 + l of the token's k expert rows.  Splitting each row over several waves keeps
+// enough loads in flight when T is small (a decode step of 256 tokens x 14 segments).
 template <class T>
 __global__ void __launch_bounds__(256)
 combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ dest,
-               const float* __restrict__ w, T* __restrict__ out, int64_t T_, int d, int k) {
+               const float* __restrict__ w, T* __restrict__ out, int64_t T_, int d, int k,
+               int segs) {
   constexpr int P = Elt<T>::kPerChunk;
   const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t t = gw / segs;
   if (t >= T_) return;
-  const int nchunks = d / P;
+  const int c = (int)(gw % segs) * kWave + lane;  // 16-byte chunk of the row
+  if (c >= d / P) return;
   const int32_t* dt = dest + t * k;
   const float* wt = w + t * k;
-  for (int c = lane; c < nchunks; c += kWave) {
-    float acc[P];
+  float acc[P];
 #pragma unroll
-    for (int i = 0; i < P; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int r = dt[j];
-      if (r < 0) continue;
-      const float g = wt[j];
-      const u32x4 v = ld16(y + (int64_t)r * d + (int64_t)c * P);
-      const T* e = reinterpret_cast<const T*>(&v);
+  for (int i = 0; i < P; ++i) acc[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int r = dt[j];
+    if (r < 0) continue;
+    const float g = wt[j];
+    const u32x4 v = ld16(y + (int64_t)r * d + (int64_t)c * P);
+    const T* e = reinterpret_cast<const T*>(&v);
 #pragma unroll
-      for (int i = 0; i < P; ++i) acc[i] = fmaf(g, Elt<T>::to_f32(e[i]), acc[i]);
-    }
-    u32x4 o;
-    T* oe = reinterpret_cast<T*>(&o);
-#pragma unroll
-    for (int i = 0; i < P; ++i) oe[i] = Elt<T>::from_f32(acc[i]);
-    st16(out + t * d + (int64_t)c * P, o);
+    for (int i = 0; i < P; ++i) acc[i] = fmaf(g, Elt<T>::to_f32(e[i]), acc[i]);
   }
+  u32x4 o;
+  T* oe = reinterpret_cast<T*>(&o);
+#pragma unroll
+  for (int i = 0; i < P; ++i) oe[i] = Elt<T>::from_f32(acc[i]);
+  st16(out + t * d + (int64_t)c * P, o);
 }
 
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* dest_row,
                           const float* topk_w, void* out, int64_t T, int64_t d, int64_t k,
                           hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((T + 3) / 4);
+  const int per_chunk = dtype == 1 ? 8 : 4;
+  const int segs = (int)((d / per_chunk + kWave - 1) / kWave);
+  const unsigned blocks = (unsigned)((T * segs + 3) / 4);
   if (dtype == 1)
     combine_kernel<bf16><<<blocks, 256, 0, s>>>((const bf16*)y_perm, dest_row, topk_w,
-                                                (bf16*)out, T, (int)d, (int)k);
+                                                (bf16*)out, T, (int)d, (int)k, segs);
   else
     combine_kernel<float><<<blocks, 256, 0, s>>>((const float*)y_perm, dest_row, topk_w,
-                                                 (float*)out, T, (int)d, (int)k);
+                                                 (float*)out, T, (int)d, (int)k, segs);
   return hipGetLastError();
 }
 

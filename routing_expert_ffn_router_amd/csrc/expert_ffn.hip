@@ -39,26 +39,17 @@ __global__ void __launch_bounds__(1024)
 tile_table_kernel(const int32_t* __restrict__ offsets, int E, int bm, int m_max,
                   int32_t* __restrict__ table) {
   __shared__ int smem[17];
-  __shared__ int s_pre[1024];
-  __shared__ int s_cnt[1024];
   const int e = threadIdx.x;
-  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int row0 = e < E ? offsets[e] : 0;
+  const int c = e < E ? offsets[e + 1] - row0 : 0;
   const int tiles = (c + bm - 1) / bm;
   int total;
   const int pre = block_exclusive_scan(tiles, smem, &total);
-  if (e < E) {
-    s_pre[e] = pre;
-    s_cnt[e] = tiles;
-  }
   if (threadIdx.x == 0) table[0] = total < m_max ? total : m_max;
-  __syncthreads();
-  for (int x = 0; x < E; ++x) {
-    const int n = s_cnt[x], p0 = s_pre[x], row0 = offsets[x];
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      if (p0 + i >= m_max) break;
-      table[1 + 2 * (p0 + i)] = x;
-      table[2 + 2 * (p0 + i)] = row0 + i * bm;
-    }
+  // each thread writes its own expert's tiles (E <= 1024 = blockDim)
+  for (int i = 0; i < tiles && pre + i < m_max; ++i) {
+    table[1 + 2 * (pre + i)] = e;
+    table[2 + 2 * (pre + i)] = row0 + i * bm;
   }
 }
 
@@ -113,6 +104,8 @@ struct PrefillTileT {
 };
 // Prefill: 256 x 256 tile, two 64 KB stages of 128-byte row pieces.
 using PrefillTile = PrefillTileT<128, 2, 256, 256, 2, 4>;
+// Prefill with tall experts: 320 x 256 tile, two 72 KB stages (142 flop per loaded byte).
+using PrefillTallTile = PrefillTileT<128, 2, 320, 256, 2, 4>;
 // Decode: weight streaming.  64 x 256 tile, three 40 KB stages, so two stages (80 KB per
 // CU) of weight reads are in flight while one is multiplied.
 using DecodeDmaTile = PrefillTileT<128, 3, 64, 256, 2, 4>;
@@ -325,12 +318,26 @@ prefill_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
 // ---------------------------------------------------------------------------------------
 // launch configurations
 // ---------------------------------------------------------------------------------------
-// Row-tile heights: prefill-sized experts (mean > 32 rows) use the 256-row prefill kernel,
-// decode-sized ones the 32-row weight-streaming kernel.
+// Row-tile heights: decode-sized experts (mean <= 32 rows) stream weights with 64-row tiles;
+// prefill-sized ones use 256- or 320-row tiles.
 FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R) {
   FfnPlan p;
   p.small = T * k <= 32 * E;
-  p.bm = p.small ? DecodeDmaTile::BM : PrefillTile::BM;
+  if (p.small) {
+    p.tile = 0;
+    p.bm = DecodeDmaTile::BM;
+  } else {
+    // Rows an expert will probably hold: a little above the mean, at most the capacity.
+    // Take the tile height that needs fewer row tiles (each one re-reads the expert's
+    // weight panel), then the one that pads fewer rows.
+    const int64_t mean = (T * k + E - 1) / E;
+    int64_t r = mean + mean / 20;
+    if (r > C) r = C;
+    const int64_t t256 = (r + 255) / 256, t320 = (r + 319) / 320;
+    const bool tall = t320 < t256 || (t320 == t256 && t320 * 320 < t256 * 256);
+    p.tile = tall ? 2 : 1;
+    p.bm = tall ? PrefillTallTile::BM : PrefillTile::BM;
+  }
   int64_t m_max = (R + E * (p.bm - 1)) / p.bm;
   const int64_t m_cap = E * ((C + p.bm - 1) / p.bm);
   p.m_max = m_cap < m_max ? m_cap : m_max;
@@ -376,6 +383,10 @@ hipError_t run_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
     return launch_prefill<T, true, DecodeDmaTile>(xp, (const T*)a.w_gate, (const T*)a.w_up,
                                                   stride, h, (int)a.d, (int)a.F, a.offsets,
                                                   a.sched, p.m_max, s);
+  if (p.tile == 2)
+    return launch_prefill<T, true, PrefillTallTile>(xp, (const T*)a.w_gate, (const T*)a.w_up,
+                                                    stride, h, (int)a.d, (int)a.F, a.offsets,
+                                                    a.sched, p.m_max, s);
   return launch_prefill<T, true>(xp, (const T*)a.w_gate, (const T*)a.w_up, stride, h,
                                  (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s);
 }
@@ -389,6 +400,10 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
     return launch_prefill<T, false, DecodeDmaTile>(h, (const T*)a.w_down, nullptr, stride, y,
                                                    (int)a.F, (int)a.d, a.offsets, a.sched,
                                                    p.m_max, s);
+  if (p.tile == 2)
+    return launch_prefill<T, false, PrefillTallTile>(h, (const T*)a.w_down, nullptr, stride, y,
+                                                     (int)a.F, (int)a.d, a.offsets, a.sched,
+                                                     p.m_max, s);
   return launch_prefill<T, false>(h, (const T*)a.w_down, nullptr, stride, y, (int)a.F,
                                   (int)a.d, a.offsets, a.sched, p.m_max, s);
 }

@@ -48,7 +48,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 // S6-S7.  The grouped GEMMs run over a device-side tile table (expert, first row) of
 // row-tile height bm with at most m_max entries.
 struct FfnPlan {
-  bool small;     // decode-sized experts: 16-row tiles
+  bool small;     // decode-sized experts (weight streaming)
+  int tile;       // 0 decode, 1 prefill 256 rows, 2 prefill 320 rows
   int bm;
   int64_t m_max;  // upper bound on m-tiles over all experts
 };
