@@ -55,7 +55,6 @@ def parse():
 
 
 COPY_BYTES = 512 << 20  # bytes read (and written) by the calibration copy
-TRAFFIC_KERNELS = {True: "prefill_gemm_kernel", False: "grouped_gemm_kernel"}
 KERNEL_SOURCES = ["routing_expert_ffn_router_amd/csrc/expert_ffn.hip",
                   "routing_expert_ffn_router_amd/csrc/common.h"]
 
@@ -91,8 +90,7 @@ def summarize_traffic(fetch_dir, write_dir, workload):
         copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         # the gate/up GEMM is the grouped GEMM instantiated with SwiGLU on (the down GEMM's
         # name carries the false / Lb0E template argument)
-        gate_up = [r for r in rows if ("prefill_gemm_kernel" in r["Kernel_Name"] or
-                                       "grouped_gemm_kernel" in r["Kernel_Name"]) and
+        gate_up = [r for r in rows if "prefill_gemm_kernel" in r["Kernel_Name"] and
                    "Lb0E" not in r["Kernel_Name"] and "false" not in r["Kernel_Name"]]
         if not copy or not gate_up:
             raise SystemExit(f"{counter}: no copy or gate/up kernel rows in {d}")
@@ -280,7 +278,7 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = traffic_for(w.name)
-    roof["kernel"] = "grouped_gemm_kernel (gate/up + SwiGLU), incl. its tile-table launch"
+    roof["kernel"] = "prefill_gemm_kernel (gate/up + SwiGLU), incl. its tile-table launch"
     roof["kernel_ms"] = round(stage_ms["gate_up"], 4)
 
     # whole-layer roofline: algorithmic work of the layer against both peaks

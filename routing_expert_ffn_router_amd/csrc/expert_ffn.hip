@@ -13,15 +13,17 @@
 //     one-block kernel writes the table tile -> (expert, first row) on the device from the
 //     expert offsets, so the host never waits for the routing.  The grid is sized from an
 //     upper bound on the tile count and surplus blocks exit at once.
-//   - Operands reach LDS by direct global -> LDS loads in 128-byte row pieces, in a ring of
+//   - Operands reach LDS by direct buffer -> LDS loads in 128-byte row pieces, in a ring of
 //     stages; fragments are read with a measured bank-conflict-free swizzle and fed to
 //     32x32x16 MFMAs (the bf16 form that runs at the full dense rate on gfx950).
-//   - Two tile shapes of the same template: prefill-sized experts (mean > 32 rows) use
-//     256 x 256 tiles (128 flop per loaded byte); decode-sized experts stream weights with
-//     64 x 256 tiles and three stages, keeping 80 KB of weight reads in flight per CU.
-//   - SwiGLU: each wave's weight rows are 32 gate rows followed by the 32 up rows of the
-//     same output columns, so gate and up accumulators of one output element sit in the
-//     same lane and the epilogue computes silu(g) * u in registers.
+//   - Three tile shapes of the same template: prefill-sized experts (mean > 32 rows) use
+//     256 x 256 tiles (128 flop per loaded byte) or, when that needs fewer row tiles or
+//     pads fewer rows, 320 x 256 tiles (142 flop per byte); decode-sized experts stream
+//     weights with 64 x 256 tiles and three stages, keeping 80 KB of weight reads in
+//     flight per CU.
+//   - SwiGLU: the gate and up rows of the same output columns are loaded side by side, so
+//     the gate and up accumulators of one output element sit in the same lane and the
+//     epilogue computes silu(g) * u in registers.
 //   - Block order: blocks are dealt round-robin to the 8 XCDs; the logical tile index is
 //     remapped so each XCD walks a contiguous range in which neighbouring tiles share the
 //     A rows (same m-tile) and the B rows (same n-group), keeping both in that XCD's L2.
@@ -54,38 +56,44 @@ tile_table_kernel(const int32_t* __restrict__ offsets, int E, int bm, int m_max,
 }
 
 // ---------------------------------------------------------------------------------------
-// Prefill-sized experts: 256 x 256 block tile, 8 waves, 32x32 MFMA tiles, 4-stage LDS
-// pipeline fed by direct global -> LDS loads (global_load_lds_dwordx4).
+// Block tile GEMM: 8 waves, 32x32 MFMA tiles, a ring of LDS stages fed by direct
+// buffer -> LDS loads (buffer_load_dwordx4 ... lds).
 //
-// Each stage holds 32 reduction elements (64 bytes) of the block's 256 A rows and 256
-// weight rows: 512 LDS rows of 64 bytes = 32 KB; four stages use 128 KB of the CU's 160 KB.
-// A wave's direct-load instruction writes 64 lanes x 16 bytes = 16 consecutive LDS rows,
-// lane L landing at row L / 4, slot L % 4 of them.  The slot holding k-chunk c of row r is
-// c ^ ((r >> 2) & 3).  A 32x32 fragment read (32 rows at one chunk position in each half
-// of the wave) then runs at the full LDS rate of gfx950: measured 4.75 cycles per 64-lane
-// 16-byte read on one CU with 8 waves, against 16.2 without a swizzle.  The lane therefore
-// fetches chunk (L % 4) ^ ((r >> 2) & 3).
+// A stage holds ROWB bytes of the reduction axis of each of the tile's rows: first the BM
+// activation rows, then the weight rows (with SwiGLU the BNW/2 gate rows, then the BNW/2
+// up rows of the same output columns).  One direct load writes 64 lanes x 16 bytes, i.e.
+// 1024 / ROWB consecutive LDS rows, lane L landing at row L / (ROWB/16), slot
+// L % (ROWB/16).  The slot holding k-chunk c of row r is c ^ swz(r); the lane therefore
+// fetches chunk (L % (ROWB/16)) ^ swz(r).  With this swizzle a 32x32 fragment read (32
+// rows at one chunk position in each half of the wave) runs at the full LDS rate of gfx950
+// (measured 4.75 cycles per 64-lane 16-byte read on one CU with 8 waves, against 16.2
+// without it).  Row pieces of 128 bytes (whole cache lines) measured clearly faster than
+// 64-byte pieces with more stages.
 //
-// Pipeline: stages k+1 and k+2 are in flight while stage k is multiplied; at the top of
-// step k a wave waits until its own loads of stage k have landed (vmcnt counts the 4
-// direct loads per wave per stage) and a barrier makes every wave's loads visible; then
-// stage k+3 is issued into the buffer that step k-1 just finished reading.  The stage
-// buffers are distinct __restrict__ pointers of an inlined function so the compiler keeps
-// these explicit waits instead of inserting a full wait before every LDS read.
+// Pipeline: STAGES - 1 stages are in flight while one is multiplied.  At the top of step k
+// a wave waits until its own loads of stage k have landed (vmcnt counts its direct loads)
+// and a barrier makes every wave's loads visible; then stage k + STAGES - 1 is issued into
+// the buffer that step k-1 finished reading.  The stage buffers are distinct __restrict__
+// pointers of an inlined function so the compiler keeps these explicit waits instead of
+// inserting a full wait before every LDS read.
 //
-// Waves form a 2 (rows) x 4 (weight rows) grid; each owns 128 x 64 of the tile (4 x 2
-// MFMA tiles of 32 x 32).  With SwiGLU a wave's 64 weight rows are 32 gate rows followed
-// by the 32 up rows of the same output columns, so a block produces 256 x 128 of h.
+// Waves form a WM (rows) x WN (weight rows) grid; wave (wm, wn) owns BM/WM activation rows
+// and BNW/WN weight rows (MT x NT MFMA tiles).  With SwiGLU the wave's weight rows are
+// NT/2 tiles of gate rows and the NT/2 tiles of up rows of the same output columns, so
+// the gate and up accumulators of one output element sit in the same lane.
 // ---------------------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) char lds_char;
-typedef const __attribute__((address_space(1))) void gbl_void;
 
 // ROWB: bytes of each row per stage (64 or 128); STAGES: LDS stages (2, 3 or 4);
 // BM_ activation rows and BNW_ weight rows per block; the 8 waves split it WM_ x WN_.
-template <int ROWB, int STAGES, int BM_, int BNW_, int WM_, int WN_>
+// DSEL_: which waves issue the direct loads: 0 = all eight, 1 = the odd waves (one per
+// SIMD, so each SIMD keeps a wave that never waits on the address unit).
+template <int ROWB, int STAGES, int BM_, int BNW_, int WM_, int WN_, int DSEL_ = 0>
 struct PrefillTileT {
   static constexpr int BM = BM_, BNW = BNW_, kWaves = 8, kThreads = 512;
   static constexpr int WM = WM_, WN = WN_;
+  static constexpr int kDmaSel = DSEL_;
+  static constexpr int kDmaWaves = DSEL_ == 0 ? 8 : 4;
   static constexpr int MT = BM / WM / 32, NT = BNW / WN / 32;  // 32x32 tiles per wave
   static constexpr int kWaveCols = NT * 32;                    // weight rows per wave
   static constexpr int kRowBytes = ROWB;
@@ -94,9 +102,19 @@ struct PrefillTileT {
   static constexpr int kStageBytes = (BM + BNW) * kRowBytes;
   static constexpr int kStages = STAGES;
   static constexpr int kRowsPerLoad = 1024 / ROWB;           // rows per direct load
-  static constexpr int kDmaPerWave = (BM + BNW) / kRowsPerLoad / kWaves;
+  static constexpr int kDmaPerWave = (BM + BNW) / kRowsPerLoad / kDmaWaves;
   static_assert(WM * WN == kWaves && NT % 2 == 0 && MT >= 1, "wave grid");
-  static_assert((BM + BNW) % (kRowsPerLoad * kWaves) == 0, "direct loads per wave");
+  // load i of every issuing wave reads the same operand: 0 activations, 1 the first weight
+  // operand (gate with SwiGLU), 2 the up weights
+  static_assert((BM / kRowsPerLoad) % kDmaWaves == 0 &&
+                    (BNW / 2 / kRowsPerLoad) % kDmaWaves == 0,
+                "direct loads per wave: each load index stays within one operand");
+  template <bool SWIGLU>
+  __device__ static constexpr int kind_of(int i) {
+    return i * kDmaWaves * kRowsPerLoad < BM                                ? 0
+           : !SWIGLU || i * kDmaWaves * kRowsPerLoad < BM + BNW / 2 ? 1
+                                                                          : 2;
+  }
   // slot of k-chunk c in row r: c ^ swz(r); conflict-free 32x32 fragment reads (measured)
   __device__ static inline int swz(int r) {
     return ROWB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
@@ -109,6 +127,23 @@ using PrefillTallTile = PrefillTileT<128, 2, 320, 256, 2, 4>;
 // Decode: weight streaming.  64 x 256 tile, three 40 KB stages, so two stages (80 KB per
 // CU) of weight reads are in flight while one is multiplied.
 using DecodeDmaTile = PrefillTileT<128, 3, 64, 256, 2, 4>;
+
+// A wave-uniform 64-bit address, moved to scalar registers.
+__device__ inline uint64_t uniform_u64(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+// Raw buffer resource for byte offsets below 2^31 from a uniform base address.  Selecting
+// between bases (scalar) rather than between descriptors keeps the descriptor in scalar
+// registers; a descriptor the compiler cannot prove uniform turns every buffer load into a
+// serialised per-lane loop.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(uint64_t base) {
+  constexpr int kFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0, 0x7fffffff,
+                                           kFlags);
+}
 
 // wait until at most N direct loads of this wave are outstanding, then block barrier
 template <int N>
@@ -142,33 +177,35 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   const int wm = wave / P::WN, wn = wave % P::WN;
   const int64_t row_bytes = (int64_t)K * sizeof(T);
 
-  // per-lane source of each direct load (k offset 0); LDS row of load i of this wave:
-  // (wave * kDmaPerWave + i) * 16 + lane / 4
-  const char* src[P::kDmaPerWave];
+  // Direct loads.  LDS rows of a stage: the BM activation rows, then the weight rows; with
+  // SwiGLU the BNW/2 gate rows come first and the BNW/2 up rows of the same output columns
+  // after them.  Each load fills one block of kRowsPerLoad rows; load i of issuing wave
+  // `dslot` fills block i * kDmaWaves + dslot, so the operand a load reads (kind_of(i)) is
+  // the same for every issuing wave and known at compile time.  Each operand is addressed
+  // through a buffer resource based at the tile's first row: a lane's source is a 32-bit
+  // offset (row within the tile, clamped to the valid rows, times the row pitch, plus its
+  // swizzled chunk) and the stage's k offset is a scalar.  Clamped rows are loaded but
+  // their results never stored.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool issuer = P::kDmaSel == 0 || (wave_u & 1);
+  const int dslot = P::kDmaSel == 0 ? wave_u : wave_u >> 1;
   const T* B0e = B0 + (int64_t)e * b_expert_stride;
   const T* B1e = SWIGLU ? B1 + (int64_t)e * b_expert_stride : nullptr;
+  const uint64_t base[3] = {uniform_u64(A + (int64_t)m_begin * K),
+                            uniform_u64(B0e + (int64_t)nt * BN * K),
+                            SWIGLU ? uniform_u64(B1e + (int64_t)nt * BN * K) : 0};
+  constexpr int kBRows = SWIGLU ? P::BNW / 2 : P::BNW;  // rows of one weight operand
+  uint32_t voff[P::kDmaPerWave];
 #pragma unroll
   for (int i = 0; i < P::kDmaPerWave; ++i) {
-    const int r = (wave * P::kDmaPerWave + i) * P::kRowsPerLoad + lane / P::kChunks;
+    const int r = (i * P::kDmaWaves + dslot) * P::kRowsPerLoad + lane / P::kChunks;
     const int c = (lane % P::kChunks) ^ P::swz(r);
-    const char* rowp;
-    if (r < P::BM) {
-      const int gr = min(m_begin + r, m_end - 1);  // rows past the expert: never stored
-      rowp = reinterpret_cast<const char*>(A) + (int64_t)gr * row_bytes;
-    } else {
-      const int br = r - P::BM;
-      if (SWIGLU) {
-        constexpr int half = P::kWaveCols / 2;
-        const int w = br / P::kWaveCols, within = br % P::kWaveCols;
-        const int col = min(nt * BN + w * half + (within % half), N_out - 1);
-        rowp = reinterpret_cast<const char*>((within < half ? B0e : B1e) + (int64_t)col * K);
-      } else {
-        rowp = reinterpret_cast<const char*>(B0e + (int64_t)min(nt * BN + br, N_out - 1) * K);
-      }
-    }
-    src[i] = rowp + c * 16;
+    const int kind = P::template kind_of<SWIGLU>(i);
+    const int row = kind == 0 ? min(r, m_end - 1 - m_begin)
+                              : min(r - P::BM - (kind - 1) * kBRows, N_out - 1 - nt * BN);
+    voff[i] = (uint32_t)row * (uint32_t)row_bytes + (uint32_t)(c * 16);
   }
-  const int dma_lds = wave * P::kDmaPerWave * 1024;
+  const int dma_lds = dslot * 1024;
 
   f32x16 acc[P::MT][P::NT];
 #pragma unroll
@@ -182,7 +219,10 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   const bool band_live = m_begin + wm * P::MT * 32 < m_end;
   const int frag_row = lane & 31, frag_half = lane >> 5;
   const int a_frag = (wm * P::MT * 32 + frag_row) * P::kRowBytes;
-  const int b_frag = (P::BM + wn * P::NT * 32 + frag_row) * P::kRowBytes;
+  // weight rows of this wave: NT tiles of 32; with SwiGLU NT/2 gate tiles (from the gate
+  // half of the stage) and the NT/2 up tiles of the same output columns
+  constexpr int kNG = SWIGLU ? P::NT / 2 : P::NT;
+  const int b_frag = (P::BM + wn * kNG * 32 + frag_row) * P::kRowBytes;
   const int swz = P::swz(frag_row);
 
   const int KT = (int)(row_bytes / P::kRowBytes);
@@ -191,9 +231,15 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // (k offset clamped, always in bounds) into a buffer nobody reads again, so every step
   // issues the same number of loads and the wait count below is a constant.
   auto dma = [&](int i, int kt, lds_char* buf) {
-    const int64_t koff = (int64_t)min(kt, KT - 1) * P::kRowBytes;
-    __builtin_amdgcn_global_load_lds((gbl_void*)(src[i] + koff), buf + dma_lds + i * 1024, 16,
-                                     0, 0);
+    const uint32_t koff = (uint32_t)min(kt, KT - 1) * P::kRowBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(base[P::template kind_of<SWIGLU>(i)]),
+                                             buf + dma_lds + i * P::kDmaWaves * 1024, 16,
+                                             voff[i], koff, 0, 0);
+  };
+  auto dma_stage = [&](int kt, lds_char* buf) {
+    if (!issuer) return;
+#pragma unroll
+    for (int i = 0; i < P::kDmaPerWave; ++i) dma(i, kt, buf);
   };
   // Fragments of one 32-byte k-step: MT A tiles + NT B tiles.
   auto load_frags = [&](const lds_char* buf, int ks, u32x4* fa, u32x4* fb) {
@@ -201,7 +247,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
 #pragma unroll
     for (int j = 0; j < P::NT; ++j)
       fb[j] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          buf + b_frag + j * 32 * P::kRowBytes + slot);
+          buf + b_frag + ((j < kNG ? 0 : kBRows - kNG * 32) + j * 32) * P::kRowBytes + slot);
 #pragma unroll
     for (int i = 0; i < P::MT; ++i)
       fa[i] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
@@ -235,22 +281,14 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   auto step = [&](int kt, const lds_char* cur, lds_char* nxt) {
     if (kt >= KT) return;
     wait_vm_barrier<(D - 1) * P::kDmaPerWave>();
-#pragma unroll
-    for (int i = 0; i < P::kDmaPerWave; ++i) dma(i, kt + D, nxt);
+    dma_stage(kt + D, nxt);
     compute(cur);
   };
 
   // prologue: stages 0 .. D-1
-#pragma unroll
-  for (int i = 0; i < P::kDmaPerWave; ++i) dma(i, 0, s0);
-  if (D >= 2) {
-#pragma unroll
-    for (int i = 0; i < P::kDmaPerWave; ++i) dma(i, 1, s1);
-  }
-  if (D >= 3) {
-#pragma unroll
-    for (int i = 0; i < P::kDmaPerWave; ++i) dma(i, 2, s2);
-  }
+  dma_stage(0, s0);
+  if (D >= 2) dma_stage(1, s1);
+  if (D >= 3) dma_stage(2, s2);
   if (P::kStages == 4) {
     for (int kt = 0; kt < KT; kt += 4) {
       step(kt + 0, s0, s3);
