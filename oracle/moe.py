@@ -46,7 +46,8 @@ def router_logits(x: np.ndarray, w_router: np.ndarray,
 # ------------------------------------------------------------------------------------------
 # S2  top-k selection and gates
 # ------------------------------------------------------------------------------------------
-def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
+def select_topk(logits: np.ndarray, k: int, n_groups: int = 1,
+                topk_groups: Optional[int] = None) -> np.ndarray:
     """idx[t, j] = the (j+1)-th best expert of token t.
 
     [EP-serving] "Deep dive": the router picks the top-k experts (often 1 or 2) per token.
@@ -54,14 +55,46 @@ def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
     go to the lower index; -0.0 and +0.0 are equal.  Softmax is strictly increasing, so this
     is the top-k of the softmax probabilities as well.  A stable sort of the negated logits
     is exactly that order.
+
+    Group-limited selection ([EP-checks] "Routing is a system-level decision": routing that
+    limits how many nodes a token may reach shapes the exchange).  The pages fix neither
+    the group count nor the limit, so both are parameters.  READING: the E experts form
+    n_groups groups of E / n_groups consecutive indices; a group's score is its best logit;
+    a token keeps the topk_groups groups of highest score (ties to the lower group index)
+    and picks its k experts among theirs in the order above.
     """
     L = np.asarray(logits, dtype=np.float32)
     assert np.all(np.isfinite(L)), "non-finite logits are outside the oracle's contract"
     T, E = L.shape
     assert 1 <= k <= E
     canon = L + np.float32(0.0)  # -0.0 + 0.0 == +0.0
+    if n_groups > 1 and topk_groups is not None and topk_groups < n_groups:
+        assert E % n_groups == 0 and 1 <= topk_groups
+        gs = E // n_groups
+        assert k <= topk_groups * gs
+        score = canon.reshape(T, n_groups, gs).max(axis=2)
+        chosen = np.argsort(-score, axis=1, kind="stable")[:, :topk_groups]
+        allowed = np.zeros((T, n_groups), dtype=bool)
+        np.put_along_axis(allowed, chosen, True, axis=1)
+        canon = np.where(np.repeat(allowed, gs, axis=1), canon.astype(np.float64), -np.inf)
     order = np.argsort(-canon, axis=1, kind="stable")
     return order[:, :k].astype(np.int32)
+
+
+def selection_logits(logits: np.ndarray, b_router: Optional[np.ndarray]) -> np.ndarray:
+    """Logits that decide the selection when the bias shifts the selection only: the fp32
+    sum L + b, rounded to fp32 like every logit the selection sees.
+
+    [EP-serving] "Deep dive" (the router's choice decides which experts run) with
+    [EP-checks] "Routing is a system-level decision" (balancing the load is part of
+    routing).  READING: with a selection-only bias (the auxiliary-loss-free balancing
+    style) the bias moves which experts are chosen but the gates come from the unbiased
+    logits.
+    """
+    L = np.asarray(logits, dtype=np.float32)
+    if b_router is None:
+        return L
+    return (L + np.asarray(b_router, dtype=np.float32)[None, :]).astype(np.float32)
 
 
 def gate_weights(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
@@ -104,65 +137,87 @@ def effective_capacity(T: int, C: int) -> int:
 # ------------------------------------------------------------------------------------------
 # S3-S5  dispatch: counts, capacity truncation, offsets, permutation
 # ------------------------------------------------------------------------------------------
-def dispatch(idx: np.ndarray, E: int, C: int) -> dict:
+def dispatch(idx: np.ndarray, E: int, C: int, slot_major: bool = False,
+             pad_to_capacity: bool = False) -> dict:
     """Routing tables for the single-GPU stand-in of the dispatch all-to-all.
 
     [EP-serving] "Technical details": tokens are sent to their experts, experts get
     capacity-limited buffers and overflow tokens are dropped.  [EP-checks] "Capacity factor
     changes quality, memory and tail latency": in capacity mode overflow is dropped before
     the exchange, so every keep/drop decision here is made before any row moves.
-    READING (drop priority, not on the pages): first come, first kept, in token order.  The
-    assignment (t, j) -> e has position pos = number of earlier assignments to e in the
-    token-major list (t, j); it is kept iff pos < C.  Kept rows of an expert are stored
-    contiguously in token order; experts follow each other in index order.
+    READING (drop priority, not on the pages): first come, first kept.  Assignments are
+    visited in token-major order (t, j) by default, or slot-major order (j, t) -- every
+    first choice before any second choice -- when slot_major; the assignment (t, j) -> e
+    has position pos = number of assignments to e visited before it, and it is kept iff
+    pos < C.  Kept rows of an expert are stored in visit order.
+
+    Buffers: packed (default), expert e's rows are [off_e, off_{e+1}) with off the exclusive
+    scan of the kept counts; with pad_to_capacity every expert owns C slots, rows
+    [e * C, (e + 1) * C), and the slots past its kept count stay empty (src_token -1, zero
+    rows).  [EP-serving] "Technical details" (fixed-capacity expert buffers keep the GEMM
+    shapes regular) and [EP-checks] "Capacity factor changes quality, memory and tail
+    latency" (padding to capacity spends memory and compute on empty slots).
 
     Returns routed_counts n_e, tokens_per_expert c_e = min(n_e, C), expert_offsets [E+1],
-    pos, dest_row [T, k] (-1 when dropped), src_token / src_slot [T*k] (-1 past N),
-    drops (total, per slot, tokens with every slot dropped).
+    pos, dest_row [T, k] (-1 when dropped), src_token / src_slot over the row slots (-1
+    where no row), n_kept N = sum c_e, n_rows (row slots: T*k packed, E*C padded), and drops
+    (total, per slot, tokens with every slot dropped).
     """
     idx = np.asarray(idx, dtype=np.int64)
     T, k = idx.shape
     Ceff = effective_capacity(T, C)
-    flat = idx.reshape(-1)
-    pos = np.empty(T * k, dtype=np.int64)
+    pos = np.empty((T, k), dtype=np.int64)
     seen = [0] * E
-    for f in range(T * k):  # token-major walk: f = t * k + j
-        e = int(flat[f])
-        pos[f] = seen[e]
+    walk = ([(t, j) for j in range(k) for t in range(T)] if slot_major
+            else [(t, j) for t in range(T) for j in range(k)])
+    for t, j in walk:
+        e = int(idx[t, j])
+        pos[t, j] = seen[e]
         seen[e] += 1
     routed = np.array(seen, dtype=np.int64)
     kept_counts = np.minimum(routed, Ceff)
-    offsets = np.zeros(E + 1, dtype=np.int64)
-    offsets[1:] = np.cumsum(kept_counts)
+    if pad_to_capacity:
+        offsets = np.arange(E + 1, dtype=np.int64) * Ceff
+        n_rows = E * Ceff
+    else:
+        offsets = np.zeros(E + 1, dtype=np.int64)
+        offsets[1:] = np.cumsum(kept_counts)
+        n_rows = T * k
     kept = pos < Ceff
-    dest = np.where(kept, offsets[flat] + pos, -1)
-    N = int(offsets[E])
-    src_token = np.full(T * k, -1, dtype=np.int64)
-    src_slot = np.full(T * k, -1, dtype=np.int64)
-    fk = np.nonzero(kept)[0]
-    src_token[dest[fk]] = fk // k
-    src_slot[dest[fk]] = fk % k
-    dropped = ~kept.reshape(T, k)
+    dest = np.where(kept, offsets[idx] + pos, -1)
+    src_token = np.full(n_rows, -1, dtype=np.int64)
+    src_slot = np.full(n_rows, -1, dtype=np.int64)
+    for t, j in zip(*np.nonzero(kept)):
+        src_token[dest[t, j]] = t
+        src_slot[dest[t, j]] = j
+    dropped = ~kept
     return {
         "routed_counts": routed,
         "tokens_per_expert": kept_counts,
         "expert_offsets": offsets,
         "capacity": Ceff,
-        "pos": pos.reshape(T, k),
-        "dest_row": dest.reshape(T, k),
+        "pos": pos,
+        "dest_row": dest,
         "src_token": src_token,
         "src_slot": src_slot,
-        "n_kept": N,
+        "n_kept": int(kept_counts.sum()),
+        "n_rows": int(n_rows),
         "drops_total": int(dropped.sum()),
         "drops_per_slot": dropped.sum(axis=0).astype(np.int64),
         "fully_dropped_tokens": int(dropped.all(axis=1).sum()),
     }
 
 
-def permute(x: np.ndarray, src_token: np.ndarray, n_kept: int) -> np.ndarray:
-    """X_perm[r] = x[src_token[r]] for the n_kept kept rows (the pack step of [EP-checks]
-    "All-to-all must be profiled separately from compute")."""
-    return np.asarray(x)[np.asarray(src_token[:n_kept], dtype=np.int64)]
+def permute(x: np.ndarray, src_token: np.ndarray, n_rows: int) -> np.ndarray:
+    """X_perm[r] = x[src_token[r]] for the first n_rows row slots, a zero row where
+    src_token[r] = -1 (the pack step of [EP-checks] "All-to-all must be profiled separately
+    from compute")."""
+    x = np.asarray(x)
+    src = np.asarray(src_token[:n_rows], dtype=np.int64)
+    out = np.zeros((n_rows, x.shape[1]), dtype=x.dtype)
+    has = src >= 0
+    out[has] = x[src[has]]
+    return out
 
 
 # ------------------------------------------------------------------------------------------
@@ -260,24 +315,95 @@ def expert_stats(routed_counts: np.ndarray, T: int, k: int,
     return rec
 
 
+def routing_record(idx: np.ndarray, dest_row: np.ndarray, E: int,
+                   placement: Optional[np.ndarray] = None,
+                   ranks_per_node: Optional[int] = None) -> dict:
+    """Observability record of one layer's routing beyond the expert counts.
+
+    [EP-checks] "Mean expert load proves almost nothing" (the share held by the busiest
+    experts, the distribution of the second choice), "Capacity factor changes quality,
+    memory and tail latency" (which choices get dropped) and "Routing is a system-level
+    decision" (load per GPU and per node under a given expert placement).  READINGS:
+      routed_by_slot[j][e] = assignments of slot j to expert e; kept_by_slot likewise for
+        kept ones;
+      top_5_percent_expert_share = routed assignments of the ceil(0.05 E) busiest experts
+        over all routed assignments;
+      slot_max_to_mean[j] = max_e routed_by_slot[j][e] / (T / E), the imbalance of the
+        (j+1)-th choice alone;
+      drop_share_per_slot[j] = dropped assignments of slot j over all dropped (0 when
+        nothing is dropped);
+      with placement[e] = the rank holding expert e: rank_load[r] = assignments routed to
+        rank r's experts, node_load[n] = sum over ranks n * ranks_per_node ... + ranks_per_node
+        - 1, each with its max / mean.
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    dest = np.asarray(dest_row, dtype=np.int64)
+    T, k = idx.shape
+    routed_by_slot = np.zeros((k, E), dtype=np.int64)
+    kept_by_slot = np.zeros((k, E), dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            routed_by_slot[j, idx[t, j]] += 1
+            if dest[t, j] >= 0:
+                kept_by_slot[j, idx[t, j]] += 1
+    n = routed_by_slot.sum(axis=0)
+    top = int(math.ceil(0.05 * E))
+    busiest = np.sort(n)[::-1][:top]
+    total = int(n.sum())
+    dropped_by_slot = routed_by_slot.sum(axis=1) - kept_by_slot.sum(axis=1)
+    dropped = int(dropped_by_slot.sum())
+    rec = {
+        "routed_by_slot": routed_by_slot.tolist(),
+        "kept_by_slot": kept_by_slot.tolist(),
+        "top_5_percent_experts": top,
+        "top_5_percent_expert_share": float(busiest.sum() / total) if total else 0.0,
+        "slot_max_to_mean": [float(routed_by_slot[j].max() / (T / E)) if T else 0.0
+                             for j in range(k)],
+        "drop_share_per_slot": [float(dropped_by_slot[j] / dropped) if dropped else 0.0
+                                for j in range(k)],
+    }
+    if placement is not None:
+        pl = np.asarray(placement, dtype=np.int64)
+        n_ranks = int(pl.max()) + 1
+        rank_load = np.zeros(n_ranks, dtype=np.int64)
+        for e in range(E):
+            rank_load[pl[e]] += n[e]
+        rec["rank_load"] = rank_load.tolist()
+        rec["rank_max_to_mean"] = float(rank_load.max() / rank_load.mean()) if total else 0.0
+        if ranks_per_node:
+            n_nodes = (n_ranks + ranks_per_node - 1) // ranks_per_node
+            node_load = np.zeros(n_nodes, dtype=np.int64)
+            for r in range(n_ranks):
+                node_load[r // ranks_per_node] += rank_load[r]
+            rec["node_load"] = node_load.tolist()
+            rec["node_max_to_mean"] = float(node_load.max() / node_load.mean()) if total else 0.0
+    return rec
+
+
 # ------------------------------------------------------------------------------------------
 # the whole layer
 # ------------------------------------------------------------------------------------------
 def moe_layer(x, w_router, b_router, w_gate, w_up, w_down, k: int, C: int,
-              logits: Optional[np.ndarray] = None) -> dict:
+              logits: Optional[np.ndarray] = None, bias_selection_only: bool = False,
+              n_groups: int = 1, topk_groups: Optional[int] = None,
+              slot_major: bool = False, pad_to_capacity: bool = False) -> dict:
     """Router -> dispatch -> expert FFN -> combine on one GPU's share (expert parallel size
     1: every expert is local and no all-to-all runs, the control run of [EP-checks]
     "All-to-all must be profiled separately from compute").
 
-    If `logits` is given the oracle routes from it instead of computing S1.
+    If `logits` is given the oracle routes from it instead of computing S1 (with
+    bias_selection_only these are the unbiased logits and b_router still shifts the
+    selection).
     """
     if logits is None:
-        logits = router_logits(x, w_router, b_router)
+        logits = router_logits(x, w_router, None if bias_selection_only else b_router)
     E = logits.shape[1]
-    idx = select_topk(logits, k)
+    sel = selection_logits(logits, b_router) if bias_selection_only else logits
+    idx = select_topk(sel, k, n_groups, topk_groups)
     gates = gate_weights(logits, idx)
-    tab = dispatch(idx, E, C)
-    xp = permute(x, tab["src_token"], tab["n_kept"])
+    tab = dispatch(idx, E, C, slot_major=slot_major, pad_to_capacity=pad_to_capacity)
+    n_rows = tab["n_rows"] if pad_to_capacity else tab["n_kept"]
+    xp = permute(x, tab["src_token"], n_rows)
     Y = expert_ffn(xp, tab["expert_offsets"], w_gate, w_up, w_down)
     out = combine(Y, tab["dest_row"], gates)
     res = dict(tab)
