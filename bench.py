@@ -46,6 +46,17 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=None,
                    help="tokens in the oracle's timed sample (default per workload)")
+    p.add_argument("--pad", action="store_true",
+                   help="pad-to-capacity dispatch: every expert owns C row slots")
+    p.add_argument("--slot-major", action="store_true",
+                   help="slot-major drop priority (first choices before second choices)")
+    p.add_argument("--bias-selection-only", action="store_true",
+                   help="the router bias shifts the selection only, not the gates")
+    p.add_argument("--groups", default=None, metavar="G:M",
+                   help="group-limited top-k: G expert groups, M kept per token")
+    p.add_argument("--ep", type=int, default=8,
+                   help="ranks of the expert placement in the routing record (contiguous)")
+    p.add_argument("--ranks-per-node", type=int, default=8)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a device copy of known size (for rocprofv3 --pmc scaling)")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -191,7 +202,11 @@ def main():
     w = mi.WORKLOADS[args.workload]
     C = moe.capacity(w.T, w.k, w.E, w.capacity_factor)
     dtype = moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32
-    s = moe.shape(w.T, w.d, w.E, w.k, w.F, C, dtype)
+    flags = ((moe.MOE_FLAG_PAD_TO_CAPACITY if args.pad else 0) |
+             (moe.MOE_FLAG_SLOT_MAJOR if args.slot_major else 0) |
+             (moe.MOE_FLAG_BIAS_SELECTION_ONLY if args.bias_selection_only else 0))
+    G, M = (int(v) for v in args.groups.split(":")) if args.groups else (0, 0)
+    s = moe.shape(w.T, w.d, w.E, w.k, w.F, C, dtype, flags=flags, n_groups=G, topk_groups=M)
     b_elt = w.elt_bytes
     print(f"# workload {w.name}: {s}", file=sys.stderr, flush=True)
 
@@ -263,6 +278,25 @@ def main():
              "dropped_tokens": int(drops[0]), "dropped_per_slot": drops[1:w.k + 1].tolist(),
              "fully_dropped_tokens": int(drops[w.k + 1]), "kept_rows": N,
              "active_experts": E_active}
+    if args.pad:
+        R = moe.max_rows(s)
+        stats["padded_rows"] = R
+        stats["pad_fraction"] = round(1.0 - N / R, 4)
+    # per-slot counts on the device, summarised on the host, under a contiguous placement of
+    # the experts over --ep ranks
+    rbs = torch.empty((w.k, w.E), dtype=torch.int32, device="cuda")
+    kbs = torch.empty_like(rbs)
+    moe.slot_counts(s, lay.view("topk_idx"), lay.view("dest_row"), rbs, kbs)
+    placement = np.arange(w.E) * args.ep // w.E
+    rec = moe.routing_record(rbs.cpu().numpy(), kbs.cpu().numpy(), placement,
+                             args.ranks_per_node)
+    stats["routing"] = {
+        "top_5_percent_expert_share": round(rec["top_5_percent_expert_share"], 4),
+        "slot_max_to_mean": [round(v, 3) for v in rec["slot_max_to_mean"]],
+        "drop_share_per_slot": [round(v, 4) for v in rec["drop_share_per_slot"]],
+        "ep_ranks": args.ep, "rank_load": rec["rank_load"],
+        "rank_max_to_mean": round(rec["rank_max_to_mean"], 4),
+        "node_load": rec["node_load"], "node_max_to_mean": round(rec["node_max_to_mean"], 4)}
 
     # ---- roofline of the dominant kernel (gate/up grouped GEMM) ------------------------------
     t_gu = stage_ms["gate_up"] * 1e-3
@@ -302,7 +336,11 @@ def main():
         "data": "synthetic (seeded Philox inputs, random-init weights)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F,
                    "capacity_factor": w.capacity_factor, "capacity": C,
-                   "router_bias_zipf_s": w.zipf_s},
+                   "router_bias_zipf_s": w.zipf_s,
+                   "dispatch": "pad_to_capacity" if args.pad else "packed",
+                   "drop_order": "slot_major" if args.slot_major else "token_major",
+                   "bias": "selection_only" if args.bias_selection_only else "logits",
+                   "groups": [G, M] if G > 1 else None},
         "roofline": roof,
         "layer_roofline_frac": round(layer_frac, 4),
         "step_ms_p50_p95_p99": [round(percentile(step_ms, q), 4) for q in (0.5, 0.95, 0.99)],
@@ -315,7 +353,7 @@ def main():
         "expert_stats": stats,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not (flags or G > 1):
         ntok = args.cpu_tokens or CPU_SAMPLE_TOKENS.get(w.name, 256)
         print(f"# cpu baseline: oracle on {ntok} tokens", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, ntok)

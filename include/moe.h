@@ -53,6 +53,28 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Variants of routing and dispatch, or-ed into moe_shape.flags; 0 selects the defaults
+ * described at each entry point.
+ *   MOE_FLAG_PAD_TO_CAPACITY  every expert owns C row slots: the kept rows of expert e are
+ *       rows e*C + pos of x_perm / y_perm (expert_offsets[e] = e*C) and the slots past its
+ *       kept count are zero rows, so the expert GEMMs run on E*C uniform rows.  Pages:
+ *       [EP-serving] "Technical details" (fixed expert buffers keep the GEMM shapes
+ *       regular) and [EP-checks] "Capacity factor changes quality, memory and tail
+ *       latency" (padding spends memory and compute on empty slots).  Needs E*C < 2^31.
+ *   MOE_FLAG_SLOT_MAJOR  drop priority visits assignments slot-major, (j, t): every first
+ *       choice before any second choice, each slot in token order; kept rows of an expert
+ *       are stored in that order.  [EP-checks] "Capacity factor changes quality, memory
+ *       and tail latency" (which choices are dropped matters).
+ *   MOE_FLAG_BIAS_SELECTION_ONLY  b_router shifts the selection only: logits = x w^T
+ *       (no bias), the top-k uses the fp32 sums logits + b_router, and the gates use the
+ *       unbiased logits of the selected experts.  [EP-checks] "Routing is a system-level
+ *       decision" (balancing the load is part of routing). */
+enum {
+  MOE_FLAG_PAD_TO_CAPACITY = 1,
+  MOE_FLAG_SLOT_MAJOR = 2,
+  MOE_FLAG_BIAS_SELECTION_ONLY = 4
+};
+
 typedef struct {
   int64_t T;        /* tokens (rows of x) */
   int64_t d;        /* model width */
@@ -61,7 +83,16 @@ typedef struct {
   int64_t F;        /* expert FFN width */
   int64_t capacity; /* per-expert capacity C; <= 0 means no limit (C = T) */
   int32_t dtype;    /* moe_dtype */
-  int32_t reserved; /* must be 0 */
+  int32_t flags;    /* MOE_FLAG_* bits; unknown bits are rejected */
+  /* Group-limited top-k ([EP-checks] "Routing is a system-level decision": limiting how
+   * many nodes a token reaches shapes the exchange).  With n_groups > 1 the experts form
+   * n_groups groups of E / n_groups consecutive indices; a group's score is its best
+   * selection logit; each token keeps its topk_groups best groups (ties to the lower
+   * group) and picks its k experts among theirs.  n_groups 0 or 1: no limit (topk_groups
+   * must then be 0).  Limits: n_groups <= 64 and divides E, 1 <= topk_groups <=
+   * n_groups, k <= topk_groups * E / n_groups. */
+  int32_t n_groups;
+  int32_t topk_groups;
 } moe_shape;
 
 /* Drop counters written by moe_dispatch / moe_layer: drops[0] = dropped assignments,
@@ -97,8 +128,8 @@ typedef enum {
  * k < 1 or E < 1 or cf is not finite.  Host function. */
 int64_t moe_capacity(int64_t T, int64_t k, int64_t E, double cf);
 
-/* Upper bound R on kept rows: min(T*k, E*C) with C = T when unlimited.  x_perm, y_perm
- * and src_token hold R rows.  Returns -1 for an invalid shape.  Host function. */
+/* Row slots R of x_perm, y_perm and src_token: min(T*k, E*C) with C = T when unlimited,
+ * or E*C with MOE_FLAG_PAD_TO_CAPACITY.  Returns -1 for an invalid shape.  Host function. */
 int64_t moe_max_rows(const moe_shape* shape);
 
 /* Bytes of device workspace that any call below needs for this shape (the same size
@@ -118,7 +149,8 @@ const char* moe_status_string(int status);
  * Layer specification: logits L = x w_router^T + b_router (fp32); the k largest logits
  * per token under (value descending, expert index ascending), -0.0 equal to +0.0; gates
  * w_j = exp(L_j - L_max) / sum over the k selected exp(L_i - L_max) (softmax restricted to
- * the selection and renormalised).
+ * the selection and renormalised).  With MOE_FLAG_BIAS_SELECTION_ONLY the bias enters the
+ * selection only; with n_groups > 1 the selection is group-limited (see moe_shape).
  *   x          [T, d] dtype          (unused when logits_given)
  *   w_router   [E, d] dtype          (unused when logits_given)
  *   b_router   [E] float, nullable
@@ -138,16 +170,18 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router,
  * capacity-limited buffers; overflow is dropped) and [EP-checks] "Capacity factor changes
  * quality, memory and tail latency" (overflow is dropped before the exchange).
  * Drop priority: first come, first kept in token order.  The assignment (t, j) -> e is
- * kept iff fewer than C earlier assignments (token-major order) went to e.  Kept rows of
- * expert e fill rows [expert_offsets[e], expert_offsets[e+1]) of x_perm in token order.
- * Entries of topk_idx outside [0, E) are dropped.
+ * kept iff fewer than C earlier assignments (token-major order, or slot-major with
+ * MOE_FLAG_SLOT_MAJOR) went to e.  Kept rows of expert e fill rows [expert_offsets[e],
+ * expert_offsets[e] + tokens_per_expert[e]) of x_perm in that order; expert_offsets is
+ * the exclusive scan of tokens_per_expert, or e*C with MOE_FLAG_PAD_TO_CAPACITY (then the
+ * other slots of x_perm are zero rows).  Entries of topk_idx outside [0, E) are dropped.
  *   topk_idx          [T, k] int32 in
  *   x                 [T, d] dtype in
  *   workspace         moe_workspace_size() bytes; workspace_bytes its size
  *   routed_counts     [E] int32 out: n_e, assignments routed to e
  *   tokens_per_expert [E] int32 out: c_e = min(n_e, C)
  *   expert_offsets    [E+1] int32 out: exclusive scan of c_e
- *   src_token         [R] int32 out: token of each kept row, -1 for rows >= N = sum c_e
+ *   src_token         [R] int32 out: token of each kept row, -1 for every other slot
  *   dest_row          [T, k] int32 out: row of each assignment in x_perm, -1 if dropped
  *   drops             [k+2] int32 out (see above)
  *   x_perm            [R, d] dtype out: x_perm[r] = x[src_token[r]] for r < N
@@ -207,6 +241,18 @@ int moe_expert_down(const moe_shape* shape, const void* h, const int32_t* expert
  */
 int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* dest_row,
                 const float* topk_w, void* out, hipStream_t stream);
+
+/*
+ * moe_slot_counts -- routing observability ([EP-checks] "Mean expert load proves almost
+ * nothing": look past the mean, at the second choice and at what gets dropped).
+ * routed_by_slot[j * E + e] = tokens whose slot j chose expert e; kept_by_slot likewise
+ * for assignments with dest_row >= 0.  Entries of topk_idx outside [0, E) are not
+ * counted.
+ *   topk_idx [T, k] int32 in; dest_row [T, k] int32 in
+ *   routed_by_slot, kept_by_slot [k, E] int32 out
+ */
+int moe_slot_counts(const moe_shape* shape, const int32_t* topk_idx, const int32_t* dest_row,
+                    int32_t* routed_by_slot, int32_t* kept_by_slot, hipStream_t stream);
 
 /*
  * moe_layer -- the whole layer: moe_route, moe_dispatch, moe_expert_ffn, moe_combine on one

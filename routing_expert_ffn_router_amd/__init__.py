@@ -26,6 +26,10 @@ MOE_ERR_HIP = -5
 MOE_F32 = 0
 MOE_BF16 = 1
 
+MOE_FLAG_PAD_TO_CAPACITY = 1
+MOE_FLAG_SLOT_MAJOR = 2
+MOE_FLAG_BIAS_SELECTION_ONLY = 4
+
 WS_REGIONS = ["logits", "topk_idx", "topk_w", "routed", "kept", "offsets", "src_token",
               "dest_row", "drops", "status", "tile_hist", "tile_base", "sched", "x_perm", "h",
               "y_perm"]
@@ -34,11 +38,14 @@ WS_REGIONS = ["logits", "topk_idx", "topk_w", "routed", "kept", "offsets", "src_
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64),
                 ("k", ctypes.c_int64), ("F", ctypes.c_int64), ("capacity", ctypes.c_int64),
-                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"MoeShape(T={self.T}, d={self.d}, E={self.E}, k={self.k}, F={self.F}, "
-                f"capacity={self.capacity}, dtype={'bf16' if self.dtype == 1 else 'f32'})")
+                f"capacity={self.capacity}, dtype={'bf16' if self.dtype == 1 else 'f32'}, "
+                f"flags={self.flags}, n_groups={self.n_groups}, "
+                f"topk_groups={self.topk_groups})")
 
 
 class MoeError(RuntimeError):
@@ -78,6 +85,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_expert_gate_up": (i32, [_S, _P, _P, _P, _P, _P, sz, _P, _P]),
         "moe_expert_down": (i32, [_S, _P, _P, _P, _P, sz, _P, _P]),
         "moe_combine": (i32, [_S, _P, _P, _P, _P, _P]),
+        "moe_slot_counts": (i32, [_S, _P, _P, _P, _P, _P]),
         "moe_layer": (i32, [_S, _P, _P, _P, _P, _P, _P, _P, sz, _P, _P, _P, _P, _P, _P]),
     }
     for name, (res, args) in sig.items():
@@ -100,8 +108,9 @@ def status_string(status: int) -> str:
 
 
 def shape(T: int, d: int, E: int, k: int, F: int, capacity: int = 0,
-          dtype: int = MOE_BF16) -> MoeShape:
-    return MoeShape(T, d, E, k, F, capacity, dtype, 0)
+          dtype: int = MOE_BF16, flags: int = 0, n_groups: int = 0,
+          topk_groups: int = 0) -> MoeShape:
+    return MoeShape(T, d, E, k, F, capacity, dtype, flags, n_groups, topk_groups)
 
 
 def capacity(T: int, k: int, E: int, cf: Optional[float]) -> int:
@@ -188,6 +197,52 @@ def combine(s: MoeShape, y_perm, dest_row, topk_w, out, stream=None) -> None:
     _check("moe_combine", load_library().moe_combine(
         ctypes.byref(s), _ptr(y_perm), _ptr(dest_row), _ptr(topk_w), _ptr(out),
         _stream(stream)))
+
+
+def slot_counts(s: MoeShape, topk_idx, dest_row, routed_by_slot, kept_by_slot,
+                stream=None) -> None:
+    _check("moe_slot_counts", load_library().moe_slot_counts(
+        ctypes.byref(s), _ptr(topk_idx), _ptr(dest_row), _ptr(routed_by_slot),
+        _ptr(kept_by_slot), _stream(stream)))
+
+
+def routing_record(routed_by_slot, kept_by_slot, placement=None,
+                   ranks_per_node: Optional[int] = None) -> dict:
+    """Host summary of moe_slot_counts' per-slot counts (arrays [k, E]): the share of the
+    busiest ceil(5 % of E) experts, each slot's max-to-mean, how the drops split over the
+    slots and, for an expert -> rank placement, the load per rank and per node."""
+    import math
+
+    import numpy as np
+
+    rbs = np.asarray(routed_by_slot, dtype=np.int64)
+    kbs = np.asarray(kept_by_slot, dtype=np.int64)
+    k, E = rbs.shape
+    n = rbs.sum(axis=0)
+    total = int(n.sum())
+    top = int(math.ceil(0.05 * E))
+    dropped = rbs.sum(axis=1) - kbs.sum(axis=1)
+    T = int(rbs[0].sum())
+    rec = {
+        "routed_by_slot": rbs.tolist(),
+        "kept_by_slot": kbs.tolist(),
+        "top_5_percent_experts": top,
+        "top_5_percent_expert_share": float(np.sort(n)[-top:].sum() / total) if total else 0.0,
+        "slot_max_to_mean": [float(r.max() * E / T) if T else 0.0 for r in rbs],
+        "drop_share_per_slot": [float(v / dropped.sum()) if dropped.sum() else 0.0
+                                for v in dropped],
+    }
+    if placement is not None:
+        pl = np.asarray(placement, dtype=np.int64)
+        rank_load = np.bincount(pl, weights=n, minlength=int(pl.max()) + 1).astype(np.int64)
+        rec["rank_load"] = rank_load.tolist()
+        rec["rank_max_to_mean"] = float(rank_load.max() / rank_load.mean()) if total else 0.0
+        if ranks_per_node:
+            nodes = np.arange(rank_load.size) // ranks_per_node
+            node_load = np.bincount(nodes, weights=rank_load).astype(np.int64)
+            rec["node_load"] = node_load.tolist()
+            rec["node_max_to_mean"] = float(node_load.max() / node_load.mean()) if total else 0.0
+    return rec
 
 
 def layer(s: MoeShape, x, w_router, b_router, w_gate, w_up, w_down, workspace, out,

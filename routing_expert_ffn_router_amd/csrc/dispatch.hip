@@ -7,31 +7,41 @@
 // tail latency": the overflow is dropped before the exchange, so every keep/drop decision
 // below is final before a single row moves.
 //
-// Drop priority is first come, first kept in token order: the flat assignment list
-// f = t * k + j is stably counting-sorted by expert, and an assignment is kept iff its
-// position among its expert's assignments is below the capacity C.
+// Drop priority is first come, first kept: the assignments are visited in priority order
+// -- token-major p = t * k + j by default, slot-major p = j * T + t (every first choice
+// before any second choice) on request -- the visit list is stably counting-sorted by
+// expert, and an assignment is kept iff its position among its expert's assignments is
+// below the capacity C.
 //
-//   K3 tile_hist   per tile of flat assignments, an LDS histogram over experts
+//   K3 tile_hist   per tile of the visit list, an LDS histogram over experts
 //   K4 scan        per expert, the exclusive scan over tiles, then counts, capacity,
-//                  offsets (exclusive scan over experts) and zeroed drop counters
+//                  offsets (exclusive scan over experts, or e * C when every expert owns C
+//                  padded slots) and zeroed drop counters
 //   K5 rank        per assignment, its position = tile base + earlier waves of the tile
 //                  + rank inside the wave (wave ballots on the expert id bits); keep/drop,
 //                  dest_row, src_token and drop counters
-//   K5b gather     x_perm[r] = x[src_token[r]] with 16-byte vector copies
+//   K5c token_drop (slot-major only) tokens whose k assignments were all dropped
+//   K5b gather     x_perm[r] = x[src_token[r]] with 16-byte vector copies; empty slots
+//                  get src_token -1 (and, when padded, a zero row)
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
+// Index into topk_idx / dest_row [T, k] of visit position p.
+__device__ inline int64_t visit_entry(int64_t p, int64_t T, int k, bool slot_major) {
+  return slot_major ? (p % T) * k + p / T : p;
+}
+
 __global__ void __launch_bounds__(kTileMax)
-tile_hist_kernel(const int32_t* __restrict__ idx, int64_t total, int te, int E,
-                 int32_t* __restrict__ hist) {
+tile_hist_kernel(const int32_t* __restrict__ idx, int64_t total, int64_t T, int te, int k,
+                 int E, bool slot_major, int32_t* __restrict__ hist) {
   extern __shared__ int32_t s_cnt[];  // [E]
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_cnt[e] = 0;
   __syncthreads();
-  const int64_t f = (int64_t)blockIdx.x * te + threadIdx.x;
-  if ((int)threadIdx.x < te && f < total) {
-    const int e = idx[f];
+  const int64_t p = (int64_t)blockIdx.x * te + threadIdx.x;
+  if ((int)threadIdx.x < te && p < total) {
+    const int e = idx[visit_entry(p, T, k, slot_major)];
     if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
   }
   __syncthreads();
@@ -39,7 +49,7 @@ tile_hist_kernel(const int32_t* __restrict__ idx, int64_t total, int te, int E,
 }
 
 __global__ void __launch_bounds__(1024)
-scan_kernel(const int32_t* __restrict__ hist, int ntiles, int E, int C, int k,
+scan_kernel(const int32_t* __restrict__ hist, int ntiles, int E, int C, int k, bool pad,
             int32_t* __restrict__ tile_base, int32_t* __restrict__ routed,
             int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
             int32_t* __restrict__ drops) {
@@ -60,14 +70,14 @@ scan_kernel(const int32_t* __restrict__ hist, int ntiles, int E, int C, int k,
   }
   int total;
   const int ex = block_exclusive_scan(c, smem, &total);
-  if (e < E) offsets[e] = ex;
-  if (threadIdx.x == 0) offsets[E] = total;
+  if (e < E) offsets[e] = pad ? e * C : ex;
+  if (threadIdx.x == 0) offsets[E] = pad ? E * C : total;
   for (int i = threadIdx.x; i < k + 2; i += blockDim.x) drops[i] = 0;
 }
 
 __global__ void __launch_bounds__(kTileMax)
-rank_kernel(const int32_t* __restrict__ idx, int64_t total, int te, int k, int E, int C,
-            int nbits, const int32_t* __restrict__ tile_base,
+rank_kernel(const int32_t* __restrict__ idx, int64_t total, int64_t T, int te, int k, int E,
+            int C, int nbits, bool slot_major, const int32_t* __restrict__ tile_base,
             const int32_t* __restrict__ offsets, int32_t* __restrict__ dest_row,
             int32_t* __restrict__ src_token, int32_t* __restrict__ drops) {
   extern __shared__ int32_t sm[];
@@ -81,8 +91,9 @@ rank_kernel(const int32_t* __restrict__ idx, int64_t total, int te, int k, int E
   for (int i = tid; i < k + 2; i += blockDim.x) s_drop[i] = 0;
   __syncthreads();
 
-  const int64_t f = (int64_t)blockIdx.x * te + tid;
-  const bool active = tid < te && f < total;
+  const int64_t p = (int64_t)blockIdx.x * te + tid;
+  const bool active = tid < te && p < total;
+  const int64_t f = active ? visit_entry(p, T, k, slot_major) : 0;  // entry t * k + j
   const int e = active ? idx[f] : -1;
   const bool valid = active && e >= 0 && e < E;
 
@@ -115,24 +126,55 @@ rank_kernel(const int32_t* __restrict__ idx, int64_t total, int te, int k, int E
     atomicAdd(&s_tokdrop[tid / k], 1);
   }
   __syncthreads();
-  // the tile starts at a multiple of k, so token-local index is tid / k
-  if (active && (tid % k) == 0 && s_tokdrop[tid / k] == k) atomicAdd(&s_drop[k + 1], 1);
+  // token-major: the tile starts at a multiple of k, so token-local index is tid / k (the
+  // slot-major count runs in token_drop_kernel)
+  if (!slot_major && active && (tid % k) == 0 && s_tokdrop[tid / k] == k)
+    atomicAdd(&s_drop[k + 1], 1);
   __syncthreads();
   for (int i = tid; i < k + 2; i += blockDim.x)
     if (s_drop[i]) atomicAdd(&drops[i], s_drop[i]);
 }
 
-// One wave per row, four rows per block, grid-stride over the R row slots.  Rows past
-// N = offsets[E] only get src_token = -1.
+// Tokens whose k assignments were all dropped, for the slot-major order (there a token's
+// assignments lie in k different tiles of the rank kernel).
+__global__ void __launch_bounds__(256)
+token_drop_kernel(const int32_t* __restrict__ dest_row, int64_t T, int k,
+                  int32_t* __restrict__ drops) {
+  __shared__ int s_n;
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < T) {
+    bool all = true;
+    for (int j = 0; j < k; ++j) all = all && dest_row[t * k + j] < 0;
+    if (all) atomicAdd(&s_n, 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && s_n) atomicAdd(&drops[k + 1], s_n);
+}
+
+// One wave per row, four rows per block, grid-stride over the R row slots.  Packed rows:
+// slots past N = offsets[E] only get src_token = -1.  Padded (C slots per expert): slot
+// r belongs to expert r / C and is empty when r % C >= kept[r / C]; it gets src_token -1
+// and a zero row.
 __global__ void __launch_bounds__(256)
 gather_rows_kernel(const char* __restrict__ x, int32_t* __restrict__ src_token,
-                   const int32_t* __restrict__ offsets, int E, int64_t R, int64_t row_bytes,
+                   const int32_t* __restrict__ offsets, const int32_t* __restrict__ kept,
+                   int E, int C, bool pad, int64_t R, int64_t row_bytes,
                    char* __restrict__ x_perm) {
   const int64_t N = offsets[E];
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int64_t nchunks = row_bytes / 16;
   for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < R; r += (int64_t)gridDim.x * 4) {
-    if (r >= N) {
+    if (pad) {
+      if (r % C >= kept[r / C]) {
+        if (lane == 0) src_token[r] = -1;
+        char* dst = x_perm + r * row_bytes;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int64_t c = lane; c < nchunks; c += kWave) st16(dst + c * 16, z);
+        continue;
+      }
+    } else if (r >= N) {
       if (lane == 0) src_token[r] = -1;
       continue;
     }
@@ -152,6 +194,35 @@ gather_rows_kernel(const char* __restrict__ x, int32_t* __restrict__ src_token,
   }
 }
 
+// Observability: per-slot routed and kept counts, [k, E] each.  One thread per assignment
+// adds into the global counters (up to 64 x 1024 of them, too many for an LDS histogram);
+// integer adds make the result independent of their order.
+__global__ void __launch_bounds__(256)
+slot_counts_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ dest_row,
+                   int64_t total, int k, int E, int32_t* __restrict__ routed_by_slot,
+                   int32_t* __restrict__ kept_by_slot) {
+  const int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (f >= total) return;
+  const int e = idx[f];
+  if (e < 0 || e >= E) return;
+  const int64_t c = (int64_t)(f % k) * E + e;
+  atomicAdd(&routed_by_slot[c], 1);
+  if (dest_row[f] >= 0) atomicAdd(&kept_by_slot[c], 1);
+}
+
+hipError_t launch_slot_counts(const int32_t* idx, const int32_t* dest_row, int64_t T,
+                              int64_t k, int64_t E, int32_t* routed_by_slot,
+                              int32_t* kept_by_slot, hipStream_t s) {
+  hipError_t err;
+  if ((err = launch_zero_i32(routed_by_slot, k * E, s)) != hipSuccess) return err;
+  if ((err = launch_zero_i32(kept_by_slot, k * E, s)) != hipSuccess) return err;
+  const int64_t total = T * k;
+  if (total == 0) return hipSuccess;
+  slot_counts_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
+      idx, dest_row, total, (int)k, (int)E, routed_by_slot, kept_by_slot);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int64_t total = a.T * a.k;
   const int te = (int)dispatch_tile_entries(a.k);
@@ -160,26 +231,31 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   while ((1ll << nbits) < a.E) ++nbits;
   hipError_t err;
   if (ntiles > 0) {
-    tile_hist_kernel<<<ntiles, kTileMax, a.E * sizeof(int32_t), s>>>(a.topk_idx, total, te,
-                                                                     (int)a.E, a.tile_hist);
+    tile_hist_kernel<<<ntiles, kTileMax, a.E * sizeof(int32_t), s>>>(
+        a.topk_idx, total, a.T, te, (int)a.k, (int)a.E, a.slot_major, a.tile_hist);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  scan_kernel<<<1, 1024, 0, s>>>(a.tile_hist, ntiles, (int)a.E, (int)a.C, (int)a.k,
+  scan_kernel<<<1, 1024, 0, s>>>(a.tile_hist, ntiles, (int)a.E, (int)a.C, (int)a.k, a.pad,
                                  a.tile_base, a.routed, a.kept, a.offsets, a.drops);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ntiles > 0) {
     const size_t lds = ((kTileMax / kWave) * a.E + kTileMax + a.k + 2) * sizeof(int32_t);
-    rank_kernel<<<ntiles, kTileMax, lds, s>>>(a.topk_idx, total, te, (int)a.k, (int)a.E,
-                                              (int)a.C, nbits, a.tile_base, a.offsets,
-                                              a.dest_row, a.src_token, a.drops);
+    rank_kernel<<<ntiles, kTileMax, lds, s>>>(a.topk_idx, total, a.T, te, (int)a.k, (int)a.E,
+                                              (int)a.C, nbits, a.slot_major, a.tile_base,
+                                              a.offsets, a.dest_row, a.src_token, a.drops);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.slot_major) {
+      token_drop_kernel<<<(unsigned)((a.T + 255) / 256), 256, 0, s>>>(a.dest_row, a.T,
+                                                                       (int)a.k, a.drops);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
   }
   if (a.R > 0) {
     int64_t blocks = (a.R + 3) / 4;
     if (blocks > 4096) blocks = 4096;
     gather_rows_kernel<<<(unsigned)blocks, 256, 0, s>>>(
-        (const char*)a.x, a.src_token, a.offsets, (int)a.E, a.R, a.d * a.elt_bytes,
-        (char*)a.x_perm);
+        (const char*)a.x, a.src_token, a.offsets, a.kept, (int)a.E, (int)a.C, a.pad, a.R,
+        a.d * a.elt_bytes, (char*)a.x_perm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;

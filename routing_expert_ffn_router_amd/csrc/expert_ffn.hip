@@ -86,8 +86,9 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 // ROWB: bytes of each row per stage (64 or 128); STAGES: LDS stages (2, 3 or 4);
 // BM_ activation rows and BNW_ weight rows per block; the 8 waves split it WM_ x WN_.
-// DSEL_: which waves issue the direct loads: 0 = all eight, 1 = the odd waves (one per
-// SIMD, so each SIMD keeps a wave that never waits on the address unit).
+// DSEL_: which waves issue the direct loads: 0 = all eight; 1 = waves 4-7, one per SIMD
+// (waves are placed on the SIMDs round-robin), so each SIMD keeps one wave that never
+// waits on the address unit (measured about 2.5% faster on the prefill tiles).
 template <int ROWB, int STAGES, int BM_, int BNW_, int WM_, int WN_, int DSEL_ = 0>
 struct PrefillTileT {
   static constexpr int BM = BM_, BNW = BNW_, kWaves = 8, kThreads = 512;
@@ -121,9 +122,9 @@ struct PrefillTileT {
   }
 };
 // Prefill: 256 x 256 tile, two 64 KB stages of 128-byte row pieces.
-using PrefillTile = PrefillTileT<128, 2, 256, 256, 2, 4>;
+using PrefillTile = PrefillTileT<128, 2, 256, 256, 2, 4, 1>;
 // Prefill with tall experts: 320 x 256 tile, two 72 KB stages (142 flop per loaded byte).
-using PrefillTallTile = PrefillTileT<128, 2, 320, 256, 2, 4>;
+using PrefillTallTile = PrefillTileT<128, 2, 320, 256, 2, 4, 1>;
 // Decode: weight streaming.  64 x 256 tile, three 40 KB stages, so two stages (80 KB per
 // CU) of weight reads are in flight while one is multiplied.
 using DecodeDmaTile = PrefillTileT<128, 3, 64, 256, 2, 4>;
@@ -187,8 +188,8 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // swizzled chunk) and the stage's k offset is a scalar.  Clamped rows are loaded but
   // their results never stored.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const bool issuer = P::kDmaSel == 0 || (wave_u & 1);
-  const int dslot = P::kDmaSel == 0 ? wave_u : wave_u >> 1;
+  const bool issuer = P::kDmaSel == 0 || wave_u >= 4;
+  const int dslot = P::kDmaSel == 0 ? wave_u : wave_u - 4;
   const T* B0e = B0 + (int64_t)e * b_expert_stride;
   const T* B1e = SWIGLU ? B1 + (int64_t)e * b_expert_stride : nullptr;
   const uint64_t base[3] = {uniform_u64(A + (int64_t)m_begin * K),
@@ -358,9 +359,9 @@ prefill_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
 // ---------------------------------------------------------------------------------------
 // Row-tile heights: decode-sized experts (mean <= 32 rows) stream weights with 64-row tiles;
 // prefill-sized ones use 256- or 320-row tiles.
-FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R) {
+FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad) {
   FfnPlan p;
-  p.small = T * k <= 32 * E;
+  p.small = pad ? C <= 32 : T * k <= 32 * E;
   if (p.small) {
     p.tile = 0;
     p.bm = DecodeDmaTile::BM;
@@ -369,7 +370,7 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R) {
     // Take the tile height that needs fewer row tiles (each one re-reads the expert's
     // weight panel), then the one that pads fewer rows.
     const int64_t mean = (T * k + E - 1) / E;
-    int64_t r = mean + mean / 20;
+    int64_t r = pad ? C : mean + mean / 20;
     if (r > C) r = C;
     const int64_t t256 = (r + 255) / 256, t320 = (r + 319) / 320;
     const bool tall = t320 < t256 || (t320 == t256 && t320 * 320 < t256 * 256);
@@ -450,7 +451,7 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
 
 hipError_t launch_expert_ffn(const FfnArgs& a, int which, hipStream_t s) {
   if (a.R <= 0) return hipSuccess;
-  const FfnPlan p = ffn_plan(a.T, a.E, a.k, a.C, a.R);
+  const FfnPlan p = ffn_plan(a.T, a.E, a.k, a.C, a.R, a.pad);
   hipError_t err = launch_table(a, p, s);
   if (err != hipSuccess) return err;
   if (which & 1) {

@@ -24,8 +24,11 @@ hipError_t launch_router_logits(int dtype, const void* x, const void* w, const f
                                 float* logits, int64_t T, int64_t d, int64_t E,
                                 hipStream_t s);
 // S2
-hipError_t launch_topk(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* idx,
-                       float* w, int32_t* status, hipStream_t s);
+// sel_bias (nullable): selection-only bias.  n_groups > 1: group-limited selection keeping
+// topk_groups groups (n_groups <= min(E, 64), dividing E).
+hipError_t launch_topk(const float* logits, const float* sel_bias, int64_t T, int64_t E,
+                       int64_t k, int n_groups, int topk_groups, int32_t* idx, float* w,
+                       int32_t* status, hipStream_t s);
 
 // S3-S5.  C is the effective capacity (1 <= C <= T when T > 0); R the row bound.
 struct DispatchArgs {
@@ -33,6 +36,8 @@ struct DispatchArgs {
   const void* x;
   int64_t T, d, E, k, C, R;
   int elt_bytes;
+  bool slot_major;     // visit assignments slot-major instead of token-major
+  bool pad;            // C slots per expert (offsets e * C, empty slots zero rows)
   int32_t* tile_hist;  // [ntiles, E]
   int32_t* tile_base;  // [ntiles, E]
   int32_t* routed;     // [E]
@@ -53,7 +58,8 @@ struct FfnPlan {
   int bm;
   int64_t m_max;  // upper bound on m-tiles over all experts
 };
-FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R);
+// pad: every expert holds exactly C rows (offsets e * C).
+FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad);
 inline int64_t ffn_table_ints(const FfnPlan& p) { return 1 + 2 * p.m_max; }
 
 struct FfnArgs {
@@ -64,6 +70,7 @@ struct FfnArgs {
   const void* w_up;
   const void* w_down;
   int64_t T, d, E, k, F, C, R;
+  bool pad;
   void* h;               // [R, F]
   int32_t* sched;        // ffn_table_ints() ints
   void* y_perm;          // [R, d]
@@ -76,5 +83,10 @@ hipError_t launch_expert_ffn(const FfnArgs& a, int which, hipStream_t s);
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* dest_row,
                           const float* topk_w, void* out, int64_t T, int64_t d, int64_t k,
                           hipStream_t s);
+
+// Observability: routed_by_slot / kept_by_slot [k, E] (zeroed here first).
+hipError_t launch_slot_counts(const int32_t* idx, const int32_t* dest_row, int64_t T,
+                              int64_t k, int64_t E, int32_t* routed_by_slot,
+                              int32_t* kept_by_slot, hipStream_t s);
 
 }  // namespace moe

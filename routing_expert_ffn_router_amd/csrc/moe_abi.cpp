@@ -23,21 +23,40 @@ int64_t eff_capacity(const moe_shape* s) {
   return (s->capacity <= 0 || s->capacity > s->T) ? s->T : s->capacity;
 }
 
+constexpr int32_t kKnownFlags =
+    MOE_FLAG_PAD_TO_CAPACITY | MOE_FLAG_SLOT_MAJOR | MOE_FLAG_BIAS_SELECTION_ONLY;
+constexpr int64_t kMaxGroups = 64;
+
+bool padded(const moe_shape* s) { return (s->flags & MOE_FLAG_PAD_TO_CAPACITY) != 0; }
+bool grouped(const moe_shape* s) { return s->n_groups > 1 && s->topk_groups < s->n_groups; }
+
 int check_shape(const moe_shape* s) {
   if (!s) return MOE_ERR_INVALID_ARG;
-  if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->F <= 0 || s->reserved != 0)
-    return MOE_ERR_INVALID_ARG;
+  if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->F <= 0) return MOE_ERR_INVALID_ARG;
+  if (s->flags & ~kKnownFlags) return MOE_ERR_INVALID_ARG;
   if (s->k > s->E) return MOE_ERR_INVALID_ARG;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (s->E > kMaxE || s->k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (s->d % 128 != 0 || s->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (s->T * s->k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   if (s->d > ((int64_t)1 << 20) || s->F > ((int64_t)1 << 20)) return MOE_ERR_UNSUPPORTED;
+  if (padded(s) && s->E * eff_capacity(s) >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  // group-limited selection
+  if (s->n_groups < 0 || s->topk_groups < 0) return MOE_ERR_INVALID_ARG;
+  if (s->n_groups <= 1) {
+    if (s->topk_groups != 0) return MOE_ERR_INVALID_ARG;
+  } else {
+    if (s->n_groups > kMaxGroups || s->n_groups > s->E) return MOE_ERR_UNSUPPORTED;
+    if (s->E % s->n_groups != 0) return MOE_ERR_INVALID_ARG;
+    if (s->topk_groups < 1 || s->topk_groups > s->n_groups) return MOE_ERR_INVALID_ARG;
+    if (s->k > (int64_t)s->topk_groups * (s->E / s->n_groups)) return MOE_ERR_INVALID_ARG;
+  }
   return MOE_OK;
 }
 
 int64_t max_rows(const moe_shape* s) {
   const int64_t a = s->T * s->k, b = s->E * eff_capacity(s);
+  if (padded(s)) return b;
   return a < b ? a : b;
 }
 
@@ -64,7 +83,7 @@ Layout make_layout(const moe_shape* s) {
   L.size[MOE_WS_TILE_HIST] = ntiles * E * 4;
   L.size[MOE_WS_TILE_BASE] = ntiles * E * 4;
   L.size[MOE_WS_SCHED] =
-      moe::ffn_table_ints(moe::ffn_plan(T, E, k, eff_capacity(s), R)) * 4;
+      moe::ffn_table_ints(moe::ffn_plan(T, E, k, eff_capacity(s), R, padded(s))) * 4;
   L.size[MOE_WS_X_PERM] = R * s->d * b;
   L.size[MOE_WS_H] = R * s->F * b;
   L.size[MOE_WS_Y_PERM] = R * s->d * b;
@@ -99,12 +118,16 @@ int route_impl(const moe_shape* s, const void* x, const void* w_router, const fl
   hipError_t e;
   if (status && (e = moe::launch_zero_i32(status, 1, st)) != hipSuccess) return MOE_ERR_HIP;
   if (s->T == 0) return MOE_OK;
+  // with a selection-only bias the logits stay unbiased and the bias goes to the top-k
+  const bool sel_only = (s->flags & MOE_FLAG_BIAS_SELECTION_ONLY) != 0;
   if (!logits_given) {
-    e = moe::launch_router_logits(s->dtype, x, w_router, b_router, logits, s->T, s->d, s->E,
-                                  st);
+    e = moe::launch_router_logits(s->dtype, x, w_router, sel_only ? nullptr : b_router, logits,
+                                  s->T, s->d, s->E, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
-  return hip_status(moe::launch_topk(logits, s->T, s->E, s->k, idx, gates, status, st));
+  const int ng = grouped(s) ? s->n_groups : 1, mg = grouped(s) ? s->topk_groups : 1;
+  return hip_status(moe::launch_topk(logits, sel_only ? b_router : nullptr, s->T, s->E, s->k,
+                                     ng, mg, idx, gates, status, st));
 }
 
 }  // namespace
@@ -185,6 +208,8 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, voi
   a.C = eff_capacity(s);
   a.R = max_rows(s);
   a.elt_bytes = elt_bytes(s->dtype);
+  a.slot_major = (s->flags & MOE_FLAG_SLOT_MAJOR) != 0;
+  a.pad = padded(s);
   a.tile_hist = region<int32_t>(ws, L, MOE_WS_TILE_HIST);
   a.tile_base = region<int32_t>(ws, L, MOE_WS_TILE_BASE);
   a.routed = routed_counts;
@@ -231,6 +256,7 @@ int expert_ffn_impl(const moe_shape* s, int which, const void* x_perm, void* h,
   a.F = s->F;
   a.C = eff_capacity(s);
   a.R = max_rows(s);
+  a.pad = padded(s);
   a.h = h;
   a.sched = region<int32_t>(ws, L, MOE_WS_SCHED);
   a.y_perm = y_perm;
@@ -276,6 +302,16 @@ int moe_combine(const moe_shape* s, const void* y_perm, const int32_t* dest_row,
   if (!aligned16(y_perm) || !aligned16(out)) return MOE_ERR_ALIGNMENT;
   return hip_status(
       moe::launch_combine(s->dtype, y_perm, dest_row, topk_w, out, s->T, s->d, s->k, st));
+}
+
+int moe_slot_counts(const moe_shape* s, const int32_t* topk_idx, const int32_t* dest_row,
+                    int32_t* routed_by_slot, int32_t* kept_by_slot, hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!routed_by_slot || !kept_by_slot) return MOE_ERR_INVALID_ARG;
+  if (s->T > 0 && (!topk_idx || !dest_row)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_slot_counts(topk_idx, dest_row, s->T, s->k, s->E,
+                                            routed_by_slot, kept_by_slot, st));
 }
 
 int moe_layer(const moe_shape* s, const void* x, const void* w_router, const float* b_router,

@@ -123,7 +123,17 @@ hipError_t launch_router_logits(int dtype, const void* x, const void* w, const f
 // where ordered() maps fp32 to an unsigned integer of the same order (after turning -0.0
 // into +0.0).  Larger key = better expert; equal values compare by the low word, which
 // prefers the lower index.  k rounds of a group max-reduction pick the experts in order.
-// Non-finite logits are counted into *status (one per token) and get key 0.
+// Non-finite logits are counted into *status (one per token) and get key 0 (every finite
+// logit's key is non-zero, its low word alone being at least 0xFFFFFC00).
+//
+// The selection value is the logit, or the fp32 sum logit + sel_bias[e] when a
+// selection-only bias is given; the gates always use the logits.
+//
+// Group-limited selection (NG > 1 groups of E / NG consecutive experts, keep M groups): a
+// group's key is the largest key of its experts (its best value; equal values favour the
+// lower expert index and so the lower group).  NG rounds of a group reduction leave group
+// g's key on lane g (NG <= G); M rounds of a max-reduction over those pick the groups, and
+// the keys of experts outside them are cleared before the k rounds.
 // ---------------------------------------------------------------------------------------
 __device__ inline uint32_t ordered_f32(float v) {
   if (v == 0.0f) v = 0.0f;  // -0.0 == +0.0
@@ -131,11 +141,20 @@ __device__ inline uint32_t ordered_f32(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// max of v over the G lanes of this lane group (G a power of two <= 64)
+__device__ inline uint64_t group_max_u64(uint64_t v, int G) {
+  for (int msk = G >> 1; msk > 0; msk >>= 1) {
+    const uint64_t o = shfl_xor_u64(v, msk);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
 template <int V>
 __global__ void __launch_bounds__(256)
-topk_kernel(const float* __restrict__ logits, int T_, int E, int k, int G,
-            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-            int32_t* __restrict__ status) {
+topk_kernel(const float* __restrict__ logits, const float* __restrict__ sel_bias, int T_,
+            int E, int k, int G, int NG, int M, int32_t* __restrict__ topk_idx,
+            float* __restrict__ topk_w, int32_t* __restrict__ status) {
   const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
   const int tok = gtid / G, sub = gtid % G;
   const bool active = tok < T_;
@@ -149,8 +168,9 @@ topk_kernel(const float* __restrict__ logits, int T_, int E, int k, int G,
     key[v] = 0;
     if (active && e < E) {
       const float val = row[e];
-      if (__builtin_isfinite(val))
-        key[v] = ((uint64_t)ordered_f32(val) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+      const float sv = sel_bias ? val + sel_bias[e] : val;
+      if (__builtin_isfinite(val) && __builtin_isfinite(sv))
+        key[v] = ((uint64_t)ordered_f32(sv) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
       else
         bad = 1;
     }
@@ -159,17 +179,43 @@ topk_kernel(const float* __restrict__ logits, int T_, int E, int k, int G,
   for (int m = G >> 1; m > 0; m >>= 1) bad |= __shfl_xor(bad, m, kWave);
   if (active && sub == 0 && bad && status) atomicAdd(status, 1);
 
-  // Slot 0 holds the largest logit m, so the renormalised gates are exp(L_j - m) / sum.
-  // The owner lane writes the indices first and re-reads the selected logits afterwards.
-  float m = 0.f, sum = 0.f;
+  if (NG > 1 && M < NG) {
+    const int gs = E / NG;
+    uint64_t gkey = 0;  // lane g: key of group g
+    for (int g = 0; g < NG; ++g) {
+      uint64_t b = 0;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int e = sub + v * G;
+        if (e < E && e / gs == g && key[v] > b) b = key[v];
+      }
+      b = group_max_u64(b, G);
+      if (sub == g) gkey = b;
+    }
+    uint64_t chosen = 0;  // bit g: group g kept
+    for (int r = 0; r < M; ++r) {
+      const uint64_t b = group_max_u64(gkey, G);
+      if (b == 0) break;  // only tokens with non-finite logits get here
+      const int g = (int)(0xFFFFFFFFu - (uint32_t)b) / gs;
+      chosen |= 1ull << g;
+      if (sub == g) gkey = 0;
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = sub + v * G;
+      if (e < E && !((chosen >> (e / gs)) & 1ull)) key[v] = 0;
+    }
+  }
+
+  // Slot 0 holds the best selection; the gates are exp(L_j - m) / sum with m the largest
+  // selected logit.  The owner lane writes the indices first and re-reads the selected
+  // logits afterwards.
+  float m = -__builtin_huge_valf(), sum = 0.f;
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
     for (int v = 0; v < V; ++v) best = key[v] > best ? key[v] : best;
-    for (int msk = G >> 1; msk > 0; msk >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, msk);
-      best = o > best ? o : best;
-    }
+    best = group_max_u64(best, G);
     // the unique owner retires the winning key
 #pragma unroll
     for (int v = 0; v < V; ++v)
@@ -177,12 +223,11 @@ topk_kernel(const float* __restrict__ logits, int T_, int E, int k, int G,
     if (sub == 0 && active) {
       const int e = best ? (int)(0xFFFFFFFFu - (uint32_t)best) : 0;
       topk_idx[(int64_t)tok * k + j] = e;
-      const float val = row[e];
-      if (j == 0) m = val;
-      sum += expf(val - m);
+      m = fmaxf(m, row[e]);
     }
   }
   if (sub == 0 && active) {
+    for (int j = 0; j < k; ++j) sum += expf(row[topk_idx[(int64_t)tok * k + j]] - m);
     const float inv = 1.0f / sum;
     for (int j = 0; j < k; ++j) {
       const int e = topk_idx[(int64_t)tok * k + j];
@@ -191,16 +236,18 @@ topk_kernel(const float* __restrict__ logits, int T_, int E, int k, int G,
   }
 }
 
-hipError_t launch_topk(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* idx,
-                       float* w, int32_t* status, hipStream_t s) {
+hipError_t launch_topk(const float* logits, const float* sel_bias, int64_t T, int64_t E,
+                       int64_t k, int n_groups, int topk_groups, int32_t* idx, float* w,
+                       int32_t* status, hipStream_t s) {
   if (T == 0) return hipSuccess;
   int G = 1;
   while (G < E && G < 64) G <<= 1;
   const int V = (int)((E + G - 1) / G);
   const int64_t threads = T * G;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-#define MOE_TOPK(VV)                                                                        \
-  topk_kernel<VV><<<blocks, 256, 0, s>>>(logits, (int)T, (int)E, (int)k, G, idx, w, status)
+#define MOE_TOPK(VV)                                                                     \
+  topk_kernel<VV><<<blocks, 256, 0, s>>>(logits, sel_bias, (int)T, (int)E, (int)k, G,    \
+                                         n_groups, topk_groups, idx, w, status)
   if (V <= 1)
     MOE_TOPK(1);
   else if (V <= 2)

@@ -72,14 +72,26 @@ BAD_SHAPES = [
     (dict(E=2048, k=2), moe.MOE_ERR_UNSUPPORTED),
     (dict(E=128, k=65), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=1 << 30, k=2), moe.MOE_ERR_UNSUPPORTED),
+    # variant fields
+    (dict(flags=8), moe.MOE_ERR_INVALID_ARG),
+    (dict(flags=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=0, topk_groups=1), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=-2, topk_groups=1), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=3, topk_groups=1), moe.MOE_ERR_INVALID_ARG),       # 3 does not divide 8
+    (dict(n_groups=4, topk_groups=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=4, topk_groups=5), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=8, topk_groups=1, k=2), moe.MOE_ERR_INVALID_ARG),  # k > 1 group of 1
+    (dict(E=256, k=2, n_groups=128, topk_groups=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 22, E=1024, k=1, capacity=0, flags=1), moe.MOE_ERR_UNSUPPORTED),  # E*C
 ]
 
 
 def _shape(**kw):
-    base = dict(T=64, d=128, E=8, k=2, F=256, capacity=32, dtype=moe.MOE_F32)
+    base = dict(T=64, d=128, E=8, k=2, F=256, capacity=32, dtype=moe.MOE_F32, flags=0,
+                n_groups=0, topk_groups=0)
     base.update(kw)
     return moe.shape(base["T"], base["d"], base["E"], base["k"], base["F"], base["capacity"],
-                     base["dtype"])
+                     base["dtype"], base["flags"], base["n_groups"], base["topk_groups"])
 
 
 FAKE = 1 << 40  # an aligned address that is never dereferenced: calls fail validation first
@@ -95,8 +107,65 @@ def test_bad_shapes_rejected_everywhere(kw, err):
     assert lib.moe_dispatch(s, p, p, p, 1 << 40, p, p, p, p, p, p, p, None) == err
     assert lib.moe_expert_ffn(s, p, p, p, p, p, p, 1 << 40, p, None) == err
     assert lib.moe_combine(s, p, p, p, p, None) == err
+    assert lib.moe_slot_counts(s, p, p, p, p, None) == err
     assert lib.moe_layer(s, p, p, None, p, p, p, p, 1 << 40, p, None, None, None, None,
                          None) == err
+
+
+GOOD_VARIANTS = [dict(flags=moe.MOE_FLAG_PAD_TO_CAPACITY), dict(flags=moe.MOE_FLAG_SLOT_MAJOR),
+                 dict(flags=moe.MOE_FLAG_BIAS_SELECTION_ONLY), dict(flags=7),
+                 dict(n_groups=4, topk_groups=1), dict(n_groups=4, topk_groups=4),
+                 dict(n_groups=1, topk_groups=0), dict(n_groups=8, topk_groups=2),
+                 dict(E=256, k=8, n_groups=64, topk_groups=4)]
+
+
+@pytest.mark.parametrize("kw", GOOD_VARIANTS)
+def test_variant_shapes_accepted(kw):
+    sh = _shape(**kw)
+    assert moe.workspace_size(sh) > 0 and moe.max_rows(sh) > 0
+
+
+def test_pad_to_capacity_rows_and_workspace():
+    for C, want in ((32, 8 * 32), (0, 8 * 64), (100, 8 * 64)):  # C > T means C = T
+        packed = _shape(capacity=C)
+        padded = _shape(capacity=C, flags=moe.MOE_FLAG_PAD_TO_CAPACITY)
+        assert moe.max_rows(padded) == want
+        assert moe.max_rows(packed) == min(64 * 2, want)
+        lay = moe.workspace_layout(padded)
+        assert lay["h"] - lay["x_perm"] >= want * 128 * 4
+    # C = 8: padded rows E*C = 64 are fewer than T*k = 128 packed row slots
+    assert moe.max_rows(_shape(capacity=8, flags=1)) == 64 == moe.max_rows(_shape(capacity=8))
+
+
+def test_slot_counts_null_outputs_rejected():
+    s = ctypes.byref(_shape())
+    p = FAKE
+    assert lib.moe_slot_counts(s, p, p, None, p, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_slot_counts(s, None, p, p, p, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_routing_record_from_counts_matches_oracle():
+    # host summary of per-slot counts against the oracle's record built from the routing
+    import oracle
+
+    rng = np.random.default_rng(7)
+    T, E, k, C = 300, 16, 4, 70
+    L = (rng.standard_normal((T, E)) - 0.5 * np.log(np.arange(1, E + 1))).astype(np.float32)
+    idx = oracle.select_topk(L, k)
+    tab = oracle.dispatch(idx, E, C)
+    rbs = np.zeros((k, E), np.int64)
+    kbs = np.zeros((k, E), np.int64)
+    for j in range(k):
+        np.add.at(rbs[j], idx[:, j], 1)
+        np.add.at(kbs[j], idx[:, j][tab["dest_row"][:, j] >= 0], 1)
+    pl = np.arange(E) % 4
+    got = moe.routing_record(rbs, kbs, pl, ranks_per_node=2)
+    want = oracle.routing_record(idx, tab["dest_row"], E, pl, ranks_per_node=2)
+    for key, v in want.items():
+        if isinstance(v, list) and v and isinstance(v[0], list):
+            assert got[key] == v, key
+        else:
+            assert got[key] == pytest.approx(v), key
 
 
 def test_null_shape():
