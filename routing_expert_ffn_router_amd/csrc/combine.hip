@@ -30,14 +30,27 @@ combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ dest,
   float acc[P];
 #pragma unroll
   for (int i = 0; i < P; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int r = dt[j];
-    if (r < 0) continue;
-    const float g = wt[j];
-    const u32x4 v = ld16(y + (int64_t)r * d + (int64_t)c * P);
-    const T* e = reinterpret_cast<const T*>(&v);
+  // slots in groups of four: the group's row loads go out together, the sums still run
+  // in slot order
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    u32x4 v[4];
+    float g[4];
+    bool live[4];
 #pragma unroll
-    for (int i = 0; i < P; ++i) acc[i] = fmaf(g, Elt<T>::to_f32(e[i]), acc[i]);
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u;
+      const int r = j < k ? dt[j] : -1;
+      live[u] = r >= 0;
+      g[u] = live[u] ? wt[j] : 0.f;
+      v[u] = live[u] ? ld16(y + (int64_t)r * d + (int64_t)c * P) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (!live[u]) continue;  // dropped slots add nothing
+      const T* e = reinterpret_cast<const T*>(&v[u]);
+#pragma unroll
+      for (int i = 0; i < P; ++i) acc[i] = fmaf(g[u], Elt<T>::to_f32(e[i]), acc[i]);
+    }
   }
   u32x4 o;
   T* oe = reinterpret_cast<T*>(&o);

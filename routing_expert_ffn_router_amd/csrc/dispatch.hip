@@ -48,31 +48,53 @@ tile_hist_kernel(const int32_t* __restrict__ idx, int64_t total, int64_t T, int 
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(int64_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
+// One block of 1024 threads.  Thread tid = part * E + e scans part `part` of expert e's
+// tile counts (q parts per expert, q the largest power of two with q * E <= 1024), so the
+// per-expert scans over many tiles run q-wide; partial sums meet in LDS.  The threads with
+// part 0 (tid = e) then hold the kept counts in expert order for the offsets scan.
 __global__ void __launch_bounds__(1024)
 scan_kernel(const int32_t* __restrict__ hist, int ntiles, int E, int C, int k, bool pad,
             int32_t* __restrict__ tile_base, int32_t* __restrict__ routed,
             int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
             int32_t* __restrict__ drops) {
   __shared__ int smem[17];
-  const int e = threadIdx.x;
-  int c = 0;
-  if (e < E) {
-    int run = 0;
-    for (int t = 0; t < ntiles; ++t) {
+  __shared__ int s_part[1024];
+  int q = 1;
+  while (q * 2 * E <= 1024) q *= 2;
+  const int tid = threadIdx.x, part = tid / E, e = tid - part * E;
+  const bool live = part < q;
+  const int chunk = (ntiles + q - 1) / q;
+  const int t_begin = part * chunk, t_end = min(ntiles, t_begin + chunk);
+  int sum = 0;
+  if (live)
+    for (int t = t_begin; t < t_end; ++t) sum += hist[(int64_t)t * E + e];
+  s_part[tid] = sum;
+  __syncthreads();
+  int run = 0, total_e = 0;
+  if (live) {
+    for (int p = 0; p < q; ++p) {
+      const int v = s_part[p * E + e];
+      if (p < part) run += v;
+      total_e += v;
+    }
+    for (int t = t_begin; t < t_end; ++t) {
       const int64_t i = (int64_t)t * E + e;
       const int h = hist[i];
       tile_base[i] = run;
       run += h;
     }
-    routed[e] = run;
-    c = run < C ? run : C;
+  }
+  int c = 0;
+  if (live && part == 0) {
+    routed[e] = total_e;
+    c = total_e < C ? total_e : C;
     kept[e] = c;
   }
   int total;
   const int ex = block_exclusive_scan(c, smem, &total);
-  if (e < E) offsets[e] = pad ? e * C : ex;
-  if (threadIdx.x == 0) offsets[E] = pad ? E * C : total;
-  for (int i = threadIdx.x; i < k + 2; i += blockDim.x) drops[i] = 0;
+  if (live && part == 0) offsets[e] = pad ? e * C : ex;
+  if (tid == 0) offsets[E] = pad ? E * C : total;
+  for (int i = tid; i < k + 2; i += blockDim.x) drops[i] = 0;
 }
 
 __global__ void __launch_bounds__(kTileMax)

@@ -27,6 +27,9 @@
 //   - Block order: blocks are dealt round-robin to the 8 XCDs; the logical tile index is
 //     remapped so each XCD walks a contiguous range in which neighbouring tiles share the
 //     A rows (same m-tile) and the B rows (same n-group), keeping both in that XCD's L2.
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -89,7 +92,8 @@ typedef __attribute__((address_space(3))) char lds_char;
 // DSEL_: which waves issue the direct loads: 0 = all eight; 1 = waves 4-7, one per SIMD
 // (waves are placed on the SIMDs round-robin), so each SIMD keeps one wave that never
 // waits on the address unit (measured about 2.5% faster on the prefill tiles).
-template <int ROWB, int STAGES, int BM_, int BNW_, int WM_, int WN_, int DSEL_ = 0>
+template <int ROWB, int STAGES, int BM_, int BNW_, int WM_, int WN_, int DSEL_ = 0,
+          int BSTAGES_ = 0>
 struct PrefillTileT {
   static constexpr int BM = BM_, BNW = BNW_, kWaves = 8, kThreads = 512;
   static constexpr int WM = WM_, WN = WN_;
@@ -100,11 +104,17 @@ struct PrefillTileT {
   static constexpr int kRowBytes = ROWB;
   static constexpr int kChunks = ROWB / 16;                  // 16-byte chunks per row
   static constexpr int kKSteps = ROWB / 32;                  // 32-byte MFMA k-steps
-  static constexpr int kStageBytes = (BM + BNW) * kRowBytes;
-  static constexpr int kStages = STAGES;
+  // separate rings: activation rows (kAStages) and weight rows (kBStages)
+  static constexpr int kAStages = STAGES, kBStages = BSTAGES_ ? BSTAGES_ : STAGES;
+  static constexpr int kABytes = BM * kRowBytes, kBBytes = BNW * kRowBytes;
+  static constexpr int kLdsBytes = kAStages * kABytes + kBStages * kBBytes;
   static constexpr int kRowsPerLoad = 1024 / ROWB;           // rows per direct load
-  static constexpr int kDmaPerWave = (BM + BNW) / kRowsPerLoad / kDmaWaves;
+  static constexpr int kALoads = BM / kRowsPerLoad / kDmaWaves;   // per issuing wave
+  static constexpr int kBLoads = BNW / kRowsPerLoad / kDmaWaves;
+  static constexpr int kDmaPerWave = kALoads + kBLoads;
   static_assert(WM * WN == kWaves && NT % 2 == 0 && MT >= 1, "wave grid");
+  static_assert(kAStages >= 2 && kAStages <= 3 && kBStages >= 2 && kBStages <= 4, "rings");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
   // load i of every issuing wave reads the same operand: 0 activations, 1 the first weight
   // operand (gate with SwiGLU), 2 the up weights
   static_assert((BM / kRowsPerLoad) % kDmaWaves == 0 &&
@@ -112,9 +122,7 @@ struct PrefillTileT {
                 "direct loads per wave: each load index stays within one operand");
   template <bool SWIGLU>
   __device__ static constexpr int kind_of(int i) {
-    return i * kDmaWaves * kRowsPerLoad < BM                                ? 0
-           : !SWIGLU || i * kDmaWaves * kRowsPerLoad < BM + BNW / 2 ? 1
-                                                                          : 2;
+    return i < kALoads ? 0 : !SWIGLU || (i - kALoads) * kDmaWaves * kRowsPerLoad < BNW / 2 ? 1 : 2;
   }
   // slot of k-chunk c in row r: c ^ swz(r); conflict-free 32x32 fragment reads (measured)
   __device__ static inline int swz(int r) {
@@ -122,7 +130,7 @@ struct PrefillTileT {
   }
 };
 // Prefill: 256 x 256 tile, two 64 KB stages of 128-byte row pieces.
-using PrefillTile = PrefillTileT<128, 2, 256, 256, 2, 4, 1>;
+using PrefillTile = PrefillTileT<128, 2, 256, 256, 2, 4, 1, 3>;
 // Prefill with tall experts: 320 x 256 tile, two 72 KB stages (142 flop per loaded byte).
 using PrefillTallTile = PrefillTileT<128, 2, 320, 256, 2, 4, 1>;
 // Decode: weight streaming.  64 x 256 tile, three 40 KB stages, so two stages (80 KB per
@@ -146,6 +154,18 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(uint64_t base) {
                                            kFlags);
 }
 
+template <int N>
+using IntC = std::integral_constant<int, N>;
+// f(IntC<0>{}), ..., f(IntC<L-1>{}), with compile-time indices
+template <class F, int... Is>
+__device__ inline void unroll_steps_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(IntC<Is>{}), ...);
+}
+template <int L, class F>
+__device__ inline void unroll_steps(F&& f) {
+  unroll_steps_impl(f, std::make_integer_sequence<int, L>{});
+}
+
 // wait until at most N direct loads of this wave are outstanding, then block barrier
 template <int N>
 __device__ inline void wait_vm_barrier() {
@@ -158,8 +178,9 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     const T* __restrict__ A, const T* __restrict__ B0, const T* __restrict__ B1,
     int64_t b_expert_stride, T* __restrict__ C, int K, int N_out,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ table,
-    int m_tiles_max, int n_tiles, int group_n, int grid_logical, lds_char* __restrict__ s0,
-    lds_char* __restrict__ s1, lds_char* __restrict__ s2, lds_char* __restrict__ s3) {
+    int m_tiles_max, int n_tiles, int group_n, int grid_logical, lds_char* __restrict__ a0,
+    lds_char* __restrict__ a1, lds_char* __restrict__ a2, lds_char* __restrict__ b0,
+    lds_char* __restrict__ b1, lds_char* __restrict__ b2, lds_char* __restrict__ b3) {
   constexpr int BN = SWIGLU ? P::BNW / 2 : P::BNW;
   const int bid = blockIdx.x;
   const int per_xcd = gridDim.x >> 3;
@@ -178,11 +199,12 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   const int wm = wave / P::WN, wn = wave % P::WN;
   const int64_t row_bytes = (int64_t)K * sizeof(T);
 
-  // Direct loads.  LDS rows of a stage: the BM activation rows, then the weight rows; with
-  // SwiGLU the BNW/2 gate rows come first and the BNW/2 up rows of the same output columns
-  // after them.  Each load fills one block of kRowsPerLoad rows; load i of issuing wave
-  // `dslot` fills block i * kDmaWaves + dslot, so the operand a load reads (kind_of(i)) is
-  // the same for every issuing wave and known at compile time.  Each operand is addressed
+  // Direct loads.  A stage of the activation ring holds the BM activation rows; a stage of
+  // the weight ring the weight rows, with SwiGLU the BNW/2 gate rows first and the BNW/2
+  // up rows of the same output columns after them.  Each load fills one block of
+  // kRowsPerLoad rows; load i of issuing wave `dslot` fills block i * kDmaWaves + dslot of
+  // the concatenated rows (activations, then weights), so the operand a load reads
+  // (kind_of(i)) is the same for every issuing wave and known at compile time.  Each operand is addressed
   // through a buffer resource based at the tile's first row: a lane's source is a 32-bit
   // offset (row within the tile, clamped to the valid rows, times the row pitch, plus its
   // swizzled chunk) and the stage's k offset is a scalar.  Clamped rows are loaded but
@@ -199,11 +221,13 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   uint32_t voff[P::kDmaPerWave];
 #pragma unroll
   for (int i = 0; i < P::kDmaPerWave; ++i) {
-    const int r = (i * P::kDmaWaves + dslot) * P::kRowsPerLoad + lane / P::kChunks;
-    const int c = (lane % P::kChunks) ^ P::swz(r);
     const int kind = P::template kind_of<SWIGLU>(i);
+    // row of the lane within its ring's stage buffer
+    const int r = ((kind == 0 ? i : i - P::kALoads) * P::kDmaWaves + dslot) * P::kRowsPerLoad +
+                  lane / P::kChunks;
+    const int c = (lane % P::kChunks) ^ P::swz(r);
     const int row = kind == 0 ? min(r, m_end - 1 - m_begin)
-                              : min(r - P::BM - (kind - 1) * kBRows, N_out - 1 - nt * BN);
+                              : min(r - (kind - 1) * kBRows, N_out - 1 - nt * BN);
     voff[i] = (uint32_t)row * (uint32_t)row_bytes + (uint32_t)(c * 16);
   }
   const int dma_lds = dslot * 1024;
@@ -223,46 +247,71 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // weight rows of this wave: NT tiles of 32; with SwiGLU NT/2 gate tiles (from the gate
   // half of the stage) and the NT/2 up tiles of the same output columns
   constexpr int kNG = SWIGLU ? P::NT / 2 : P::NT;
-  const int b_frag = (P::BM + wn * kNG * 32 + frag_row) * P::kRowBytes;
+  const int b_frag = (wn * kNG * 32 + frag_row) * P::kRowBytes;
   const int swz = P::swz(frag_row);
 
   const int KT = (int)(row_bytes / P::kRowBytes);
-  constexpr int D = P::kStages - 1;  // stages in flight ahead of the one multiplied
-  // Direct load i of stage kt into buffer buf.  Stages past the end re-read the last stage
-  // (k offset clamped, always in bounds) into a buffer nobody reads again, so every step
-  // issues the same number of loads and the wait count below is a constant.
+  constexpr int SA = P::kAStages, SB = P::kBStages;
+  constexpr int DA = SA - 1, DB = SB - 1;  // stages of each ring in flight ahead
+  constexpr int nA = P::kALoads, nB = P::kBLoads;
+  // Loads a wave may leave outstanding at the top of step k, when stage k of both rings must
+  // have landed: each step issues its activation loads, then its weight loads, and with
+  // DA < DB the activation stage k is the later of the two to be issued.
+  constexpr int kWait = DA == DB ? (DA - 1) * (nA + nB)
+                        : DA < DB ? nB + (DA - 1) * (nA + nB)
+                                  : (DB - 1) * (nA + nB);
+  // Stage buffers by compile-time index (indices fold to the distinct pointers).
+  auto ring_a = [&](auto I) -> lds_char* {
+    constexpr int j = decltype(I)::value % SA;
+    return j == 0 ? a0 : j == 1 ? a1 : a2;
+  };
+  auto ring_b = [&](auto I) -> lds_char* {
+    constexpr int j = decltype(I)::value % SB;
+    return j == 0 ? b0 : j == 1 ? b1 : j == 2 ? b2 : b3;
+  };
+  // Direct load i of stage kt into its ring's buffer.  Stages past the end re-read the last
+  // stage (k offset clamped, always in bounds) into a buffer nobody reads again, so every
+  // step issues the same number of loads and the wait count is a constant.
   auto dma = [&](int i, int kt, lds_char* buf) {
     const uint32_t koff = (uint32_t)min(kt, KT - 1) * P::kRowBytes;
+    const int blk = (i < nA ? i : i - nA) * P::kDmaWaves;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(base[P::template kind_of<SWIGLU>(i)]),
-                                             buf + dma_lds + i * P::kDmaWaves * 1024, 16,
-                                             voff[i], koff, 0, 0);
+                                             buf + dma_lds + blk * 1024, 16, voff[i], koff, 0,
+                                             0);
   };
-  auto dma_stage = [&](int kt, lds_char* buf) {
+  auto dma_a = [&](int kt, lds_char* buf) {
     if (!issuer) return;
 #pragma unroll
-    for (int i = 0; i < P::kDmaPerWave; ++i) dma(i, kt, buf);
+    for (int i = 0; i < nA; ++i) dma(i, kt, buf);
   };
-  // Fragments of one 32-byte k-step: MT A tiles + NT B tiles.
-  auto load_frags = [&](const lds_char* buf, int ks, u32x4* fa, u32x4* fb) {
+  auto dma_b = [&](int kt, lds_char* buf) {
+    if (!issuer) return;
+#pragma unroll
+    for (int i = nA; i < nA + nB; ++i) dma(i, kt, buf);
+  };
+  // Fragments of one 32-byte k-step: MT activation tiles + NT weight tiles.
+  auto load_frags = [&](const lds_char* abuf, const lds_char* bbuf, int ks, u32x4* fa,
+                        u32x4* fb) {
     const int slot = ((ks * 2 + frag_half) ^ swz) << 4;
 #pragma unroll
     for (int j = 0; j < P::NT; ++j)
       fb[j] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          buf + b_frag + ((j < kNG ? 0 : kBRows - kNG * 32) + j * 32) * P::kRowBytes + slot);
+          bbuf + b_frag + ((j < kNG ? 0 : kBRows - kNG * 32) + j * 32) * P::kRowBytes + slot);
 #pragma unroll
     for (int i = 0; i < P::MT; ++i)
       fa[i] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          buf + a_frag + i * 32 * P::kRowBytes + slot);
+          abuf + a_frag + i * 32 * P::kRowBytes + slot);
   };
-  // Multiply stage `buf`.  The reads of k-step s+1 go out before the MFMAs of k-step s
-  // (two register sets), so each k-step's MFMAs cover the next k-step's LDS latency.
-  auto compute = [&](const lds_char* buf) {
+  // Multiply one stage.  The reads of k-step s+1 go out before the MFMAs of k-step s (two
+  // register sets), so each k-step's MFMAs cover the next k-step's LDS latency.
+  auto compute = [&](const lds_char* abuf, const lds_char* bbuf) {
     if (!band_live) return;
     u32x4 fa[2][P::MT], fb[2][P::NT];
-    load_frags(buf, 0, fa[0], fb[0]);
+    load_frags(abuf, bbuf, 0, fa[0], fb[0]);
 #pragma unroll
     for (int ks = 0; ks < P::kKSteps; ++ks) {
-      if (ks + 1 < P::kKSteps) load_frags(buf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      if (ks + 1 < P::kKSteps)
+        load_frags(abuf, bbuf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < P::MT; ++i)
 #pragma unroll
@@ -274,41 +323,29 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
       __builtin_amdgcn_sched_group_barrier(0x008, P::MT * P::NT, 0);
     }
   };
-  // One step: wait for stage kt (the D-1 later stages may still be in flight), make every
-  // wave's loads visible, issue stage kt + D into the buffer step kt-1 finished reading,
-  // then multiply.  Issuing the stage's loads together here lets the other wave of the
-  // SIMD keep the MFMA pipe busy while this one waits on the address FIFO; spreading them
-  // between the MFMAs measured slower.
-  auto step = [&](int kt, const lds_char* cur, lds_char* nxt) {
+  // Step kt (I = kt modulo the unroll): wait until stage kt of both rings has landed, make
+  // every wave's loads visible, issue activation stage kt + DA and weight stage kt + DB into
+  // the buffers step kt-1 finished reading, then multiply.  The loads of a step go out
+  // together after the barrier (spreading them between the MFMAs measured no faster).
+  auto step = [&](int kt, auto I) {
     if (kt >= KT) return;
-    wait_vm_barrier<(D - 1) * P::kDmaPerWave>();
-    dma_stage(kt + D, nxt);
-    compute(cur);
+    wait_vm_barrier<kWait>();
+    dma_a(kt + DA, ring_a(IntC<decltype(I)::value + DA>{}));
+    dma_b(kt + DB, ring_b(IntC<decltype(I)::value + DB>{}));
+    compute(ring_a(I), ring_b(I));
   };
 
-  // prologue: stages 0 .. D-1
-  dma_stage(0, s0);
-  if (D >= 2) dma_stage(1, s1);
-  if (D >= 3) dma_stage(2, s2);
-  if (P::kStages == 4) {
-    for (int kt = 0; kt < KT; kt += 4) {
-      step(kt + 0, s0, s3);
-      step(kt + 1, s1, s0);
-      step(kt + 2, s2, s1);
-      step(kt + 3, s3, s2);
-    }
-  } else if (P::kStages == 3) {
-    for (int kt = 0; kt < KT; kt += 3) {
-      step(kt + 0, s0, s2);
-      step(kt + 1, s1, s0);
-      step(kt + 2, s2, s1);
-    }
-  } else {
-    for (int kt = 0; kt < KT; kt += 2) {
-      step(kt + 0, s0, s1);
-      step(kt + 1, s1, s0);
-    }
-  }
+  // prologue: the loads of steps -max(DA, DB) .. -1, issued as those steps would
+  constexpr int DM = DA > DB ? DA : DB;
+  unroll_steps<DM>([&](auto V) {
+    constexpr int v = decltype(V)::value - DM;
+    if constexpr (v + DA >= 0) dma_a(v + DA, ring_a(IntC<v + DA>{}));
+    if constexpr (v + DB >= 0) dma_b(v + DB, ring_b(IntC<v + DB>{}));
+  });
+  constexpr int L = SA == SB ? SA : SB % SA == 0 ? SB : SA * SB;  // the rings repeat
+  for (int kt = 0; kt < KT; kt += L) unroll_steps<L>([&](auto I) {
+    step(kt + decltype(I)::value, I);
+  });
   // drain the loads issued past the last stage before the block's LDS can be reassigned
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -346,12 +383,14 @@ prefill_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
                     int group_n, int grid_logical) {
   extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
   lds_char* base = (lds_char*)smem_dyn;
-  constexpr int S = P::kStageBytes;
-  // stage buffers past kStages are never used
+  constexpr int SA = P::kABytes, SB = P::kBBytes;
+  lds_char* bb = base + P::kAStages * SA;
+  // buffers past a ring's stage count are never used
   prefill_gemm_body<T, SWIGLU, P>(A, B0, B1, b_expert_stride, C, K, N_out, offsets, table,
-                                  m_tiles_max, n_tiles, group_n, grid_logical, base, base + S,
-                                  base + (P::kStages > 2 ? 2 * S : 0),
-                                  base + (P::kStages > 3 ? 3 * S : 0));
+                                  m_tiles_max, n_tiles, group_n, grid_logical, base, base + SA,
+                                  base + (P::kAStages > 2 ? 2 * SA : 0), bb, bb + SB,
+                                  bb + (P::kBStages > 2 ? 2 * SB : 0),
+                                  bb + (P::kBStages > 3 ? 3 * SB : 0));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -397,7 +436,7 @@ hipError_t launch_prefill(const T* A, const T* B0, const T* B1, int64_t b_stride
   const int n_groups = (n_tiles + group_n - 1) / group_n;
   const int64_t logical = m_max * group_n * n_groups;
   const int64_t grid = (logical + 7) / 8 * 8;
-  const size_t lds = (size_t)P::kStages * P::kStageBytes;
+  const size_t lds = (size_t)P::kLdsBytes;
   hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW, P>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

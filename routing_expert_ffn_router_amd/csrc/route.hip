@@ -31,78 +31,113 @@ hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
 // S1: L[t, e] = sum_i x[t, i] w[e, i] + b[e]
 //
 // The router GEMM is skinny (E = 8 or 256 columns) and bound by reading x (and, for
-// E = 256, w) once.  A block computes a 16-token x (16 * NT)-expert tile with MFMA straight
-// from global memory (no LDS staging); its 8 waves split the reduction axis in 128-byte
-// steps (wave w takes steps w, w + 8, ...), so enough loads are in flight, and their
-// partial tiles are summed in LDS in wave order, which keeps the result deterministic.
-// Per 128-byte step a lane loads 32 contiguous bytes of its token row and of each expert
-// row; both operands use the same k-chunk assignment (lane group g takes chunks 2g and
-// 2g + 1), so the products pair up.  grid = (ceil(T / 16), ceil(E / (16 * NT))).
+// E = 256, w) once.  A block computes a (16 * MT)-token x (16 * NT)-expert tile with MFMA
+// straight from global memory (no LDS staging); its 8 waves split the reduction axis in
+// 128-byte steps (wave w takes steps w, w + 8, ...), so enough loads are in flight, and
+// their partial tiles are summed in LDS in wave order, which keeps the result
+// deterministic.  Per 128-byte step a lane loads 32 contiguous bytes of each of its MT
+// token rows and NT expert rows; both operands use the same k-chunk assignment (lane group
+// g takes chunks 2g and 2g + 1), so the products pair up.  Larger tiles cut the re-reads:
+// with many experts and tokens a 64 x 64 tile reads x E / 64 times and w T / 64 times.
+// grid = (ceil(T / (16 MT)), ceil(E / (16 NT))).
 // ---------------------------------------------------------------------------------------
 constexpr int kRouterWaves = 8;
 
-template <class T, int NT>
+template <class T, int MT, int NT>
 __global__ void __launch_bounds__(kRouterWaves* kWave)
 router_logits_kernel(const T* __restrict__ x, const T* __restrict__ w,
                      const float* __restrict__ bias, float* __restrict__ logits, int T_,
                      int d, int E) {
-  __shared__ float part[kRouterWaves][NT][4][kWave];
+  extern __shared__ float part[];  // [kRouterWaves][MT][NT][4][kWave]
   const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int t0 = blockIdx.x * 16;
+  const int t0 = blockIdx.x * MT * 16;
   const int e0 = blockIdx.y * NT * 16;
   const int r = lane & 15, g = lane >> 4;
-  const int t = min(t0 + r, T_ - 1);  // clamped rows are computed but never stored
-  const char* xa = reinterpret_cast<const char*>(x + (int64_t)t * d) + g * 32;
+  const char* xa[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int t = min(t0 + m * 16 + r, T_ - 1);  // clamped rows are computed, never stored
+    xa[m] = reinterpret_cast<const char*>(x + (int64_t)t * d) + g * 32;
+  }
   const char* wb[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int e = min(e0 + n * 16 + r, E - 1);
     wb[n] = reinterpret_cast<const char*>(w + (int64_t)e * d) + g * 32;
   }
-  f32x4 acc[NT];
+  f32x4 acc[MT][NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int steps = d * (int)sizeof(T) / 128;
   for (int st = wave; st < steps; st += kRouterWaves) {
     const int kb = st * 128;
-    const u32x4 a0 = ld16(xa + kb), a1 = ld16(xa + kb + 16);
+    u32x4 a0[MT], a1[MT], b0[NT], b1[NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      a0[m] = ld16(xa[m] + kb);
+      a1[m] = ld16(xa[m] + kb + 16);
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const u32x4 b0 = ld16(wb[n] + kb), b1 = ld16(wb[n] + kb + 16);
-      mma_chunk(acc[n], a0, b0, T());
-      mma_chunk(acc[n], a1, b1, T());
+      b0[n] = ld16(wb[n] + kb);
+      b1[n] = ld16(wb[n] + kb + 16);
     }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        mma_chunk(acc[m][n], a0[m], b0[n], T());
+        mma_chunk(acc[m][n], a1[m], b1[n], T());
+      }
   }
+  constexpr int kTile = MT * NT * 4 * kWave;  // floats of one wave's partial tile
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][n][i][lane] = acc[n][i];
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[wave * kTile + ((m * NT + n) * 4 + i) * kWave + lane] = acc[m][n][i];
   __syncthreads();
-  // thread -> (n, i, lane) of the tile; sum the 8 partial tiles in wave order
-  for (int o = threadIdx.x; o < NT * 4 * kWave; o += blockDim.x) {
-    const int n = o / (4 * kWave), i = (o / kWave) % 4, l = o % kWave;
+  // thread -> (m, n, i, lane) of the tile; sum the 8 partial tiles in wave order
+  for (int o = threadIdx.x; o < kTile; o += blockDim.x) {
+    const int mn = o / (4 * kWave), i = (o / kWave) % 4, l = o % kWave;
+    const int m = mn / NT, n = mn % NT;
     float v = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kRouterWaves; ++ww) v += part[ww][n][i][l];
+    for (int ww = 0; ww < kRouterWaves; ++ww) v += part[ww * kTile + o];
     const int e = e0 + n * 16 + (l & 15);
-    const int tt = t0 + 4 * (l >> 4) + i;
+    const int tt = t0 + m * 16 + 4 * (l >> 4) + i;
     if (e < E && tt < T_) logits[(int64_t)tt * E + e] = v + (bias ? bias[e] : 0.f);
   }
+}
+
+template <class T, int MT, int NT>
+hipError_t launch_router_tile(const T* x, const T* w, const float* b, float* logits,
+                              int64_t T_, int64_t d, int64_t E, hipStream_t s) {
+  const size_t lds = (size_t)kRouterWaves * MT * NT * 4 * kWave * sizeof(float);
+  hipError_t e = hipFuncSetAttribute((const void*)router_logits_kernel<T, MT, NT>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((T_ + 16 * MT - 1) / (16 * MT)),
+                  (unsigned)((E + 16 * NT - 1) / (16 * NT)));
+  router_logits_kernel<T, MT, NT><<<grid, kRouterWaves * kWave, lds, s>>>(
+      x, w, b, logits, (int)T_, (int)d, (int)E);
+  return hipGetLastError();
 }
 
 template <class T>
 hipError_t launch_router_typed(const T* x, const T* w, const float* b, float* logits,
                                int64_t T_, int64_t d, int64_t E, hipStream_t s) {
-  const unsigned gx = (unsigned)((T_ + 15) / 16);
-  // 64-expert tiles when there are enough token tiles to fill the GPU, else 16-expert ones
-  if (E > 16 && gx * ((E + 63) / 64) >= 512) {
-    router_logits_kernel<T, 4><<<dim3(gx, (unsigned)((E + 63) / 64)), kRouterWaves * kWave,
-                                 0, s>>>(x, w, b, logits, (int)T_, (int)d, (int)E);
-  } else {
-    router_logits_kernel<T, 1><<<dim3(gx, (unsigned)((E + 15) / 16)), kRouterWaves * kWave,
-                                 0, s>>>(x, w, b, logits, (int)T_, (int)d, (int)E);
-  }
-  return hipGetLastError();
+  // The largest tile that still gives at least 512 blocks (two per CU): 64 x 64, then
+  // 16 x 64, else 16 x 16.
+  const int64_t t16 = (T_ + 15) / 16, t64 = (T_ + 63) / 64;
+  if (E > 16 && t64 * ((E + 63) / 64) >= 512)
+    return launch_router_tile<T, 4, 4>(x, w, b, logits, T_, d, E, s);
+  if (E > 16 && t16 * ((E + 63) / 64) >= 512)
+    return launch_router_tile<T, 1, 4>(x, w, b, logits, T_, d, E, s);
+  return launch_router_tile<T, 1, 1>(x, w, b, logits, T_, d, E, s);
 }
 
 hipError_t launch_router_logits(int dtype, const void* x, const void* w, const float* b,

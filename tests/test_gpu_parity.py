@@ -114,6 +114,31 @@ def test_router_logits(name):
     assert err <= logits_tol(ref)
 
 
+@pytest.mark.parametrize("T,d,E,dtype", [(2048, 256, 1024, "bf16"), (2047, 128, 1024, "f32"),
+                                         (600, 256, 1000, "bf16"), (8192, 128, 64, "f32"),
+                                         (1000, 128, 512, "bf16")])
+def test_router_logits_tile_shapes(T, d, E, dtype):
+    # sizes that select each router tile (64 x 64, 16 x 64, 16 x 16 tokens x experts),
+    # with ragged token and expert tails
+    log(f"router tiles T={T} d={d} E={E} {dtype}")
+    rng = np.random.default_rng(T + E)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = (rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)
+    b = rng.standard_normal(E).astype(np.float32)
+    if dtype == "bf16":
+        x, wr = (mi.bf16_bits_to_f32(mi.bf16_rne_np(a)) for a in (x, wr))
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    s = moe.shape(T, d, E, 1, 128, 0, moe.MOE_BF16 if dtype == "bf16" else moe.MOE_F32)
+    L = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx, gw = _i32(0, T, 1), torch.empty((T, 1), device="cuda")
+    moe.route(s, to_device(x, dt), to_device(wr, dt), to_device(b, torch.float32), L, idx, gw)
+    torch.cuda.synchronize()
+    ref = oracle.router_logits(x, wr, b)
+    err = float(np.max(np.abs(L.cpu().numpy() - ref)))
+    log(f"  max|dL| = {err:.3e}, tol {logits_tol(ref):.3e}")
+    assert err <= logits_tol(ref)
+
+
 # ------------------------------------------------------------------------------- S3-S5
 DISPATCH_CASES = [
     # T, E, k, C, d, dtype, bias s
