@@ -133,6 +133,9 @@ struct PrefillTileT {
 using PrefillTile = PrefillTileT<128, 2, 256, 256, 2, 4, 1, 3>;
 // Prefill with tall experts: 320 x 256 tile, two 72 KB stages (142 flop per loaded byte).
 using PrefillTallTile = PrefillTileT<128, 2, 320, 256, 2, 4, 1>;
+// An expert's last row tile when it holds at most 128 rows: 128 x 256, the weight ring
+// three deep (the same weight columns as the full tiles).
+using PrefillTailTile = PrefillTileT<128, 2, 128, 256, 2, 4, 1, 3>;
 // Decode: weight streaming.  64 x 256 tile, three 40 KB stages, so two stages (80 KB per
 // CU) of weight reads are in flight while one is multiplied.
 using DecodeDmaTile = PrefillTileT<128, 3, 64, 256, 2, 4>;
@@ -176,24 +179,11 @@ __device__ inline void wait_vm_barrier() {
 template <class T, bool SWIGLU, class P>
 __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     const T* __restrict__ A, const T* __restrict__ B0, const T* __restrict__ B1,
-    int64_t b_expert_stride, T* __restrict__ C, int K, int N_out,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ table,
-    int m_tiles_max, int n_tiles, int group_n, int grid_logical, lds_char* __restrict__ a0,
-    lds_char* __restrict__ a1, lds_char* __restrict__ a2, lds_char* __restrict__ b0,
-    lds_char* __restrict__ b1, lds_char* __restrict__ b2, lds_char* __restrict__ b3) {
+    int64_t b_expert_stride, T* __restrict__ C, int K, int N_out, int e, int m_begin,
+    int m_end, int nt, lds_char* __restrict__ a0, lds_char* __restrict__ a1,
+    lds_char* __restrict__ a2, lds_char* __restrict__ b0, lds_char* __restrict__ b1,
+    lds_char* __restrict__ b2, lds_char* __restrict__ b3) {
   constexpr int BN = SWIGLU ? P::BNW / 2 : P::BNW;
-  const int bid = blockIdx.x;
-  const int per_xcd = gridDim.x >> 3;
-  const int logical = (bid & 7) * per_xcd + (bid >> 3);
-  if (logical >= grid_logical) return;
-  const int per_group = m_tiles_max * group_n;
-  const int grp = logical / per_group, rem = logical - grp * per_group;
-  const int mt = rem / group_n, nt = grp * group_n + (rem - (rem / group_n) * group_n);
-  if (nt >= n_tiles) return;
-  if (mt >= table[0]) return;
-  const int e = table[1 + 2 * mt];
-  const int m_begin = table[2 + 2 * mt];
-  const int m_end = offsets[e + 1];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int wm = wave / P::WN, wn = wave % P::WN;
@@ -374,23 +364,55 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   }
 }
 
+// Stage buffers of tile P in the block's LDS, then its body.
 template <class T, bool SWIGLU, class P>
+__device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
+    const T* __restrict__ A, const T* __restrict__ B0, const T* __restrict__ B1,
+    int64_t b_expert_stride, T* __restrict__ C, int K, int N_out, int e, int m_begin,
+    int m_end, int nt, lds_char* base) {
+  constexpr int SA = P::kABytes, SB = P::kBBytes;
+  lds_char* bb = base + P::kAStages * SA;
+  // buffers past a ring's stage count are never used
+  prefill_gemm_body<T, SWIGLU, P>(A, B0, B1, b_expert_stride, C, K, N_out, e, m_begin, m_end,
+                                  nt, base, base + SA, base + (P::kAStages > 2 ? 2 * SA : 0),
+                                  bb, bb + SB, bb + (P::kBStages > 2 ? 2 * SB : 0),
+                                  bb + (P::kBStages > 3 ? 3 * SB : 0));
+}
+
+// One block per (m-tile, n-tile).  Blocks are dealt round-robin to the 8 XCDs; the logical
+// tile index is remapped so each XCD walks a contiguous range of logical tiles, n fastest
+// within groups of group_n n-tiles.  An m-tile with at most PT::BM rows (an expert's last,
+// partly filled tile) runs the shorter tile PT with the same weight columns: fewer loads
+// and MFMAs instead of a full tile of mostly clamped rows.
+template <class T, bool SWIGLU, class P, class PT>
 __global__ void __launch_bounds__(P::kThreads)
 prefill_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
                     const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C, int K,
                     int N_out, const int32_t* __restrict__ offsets,
                     const int32_t* __restrict__ table, int m_tiles_max, int n_tiles,
                     int group_n, int grid_logical) {
+  static_assert(PT::BNW == P::BNW && PT::kThreads == P::kThreads && PT::BM <= P::BM,
+                "the shorter tile shares the n-tiling and the block size");
   extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
+  const int bid = blockIdx.x;
+  const int per_xcd = gridDim.x >> 3;
+  const int logical = (bid & 7) * per_xcd + (bid >> 3);
+  if (logical >= grid_logical) return;
+  const int per_group = m_tiles_max * group_n;
+  const int grp = logical / per_group, rem = logical - grp * per_group;
+  const int mt = rem / group_n, nt = grp * group_n + (rem - (rem / group_n) * group_n);
+  if (nt >= n_tiles) return;
+  if (mt >= table[0]) return;
+  const int e = table[1 + 2 * mt];
+  const int m_begin = table[2 + 2 * mt];
+  const int m_end = offsets[e + 1];
   lds_char* base = (lds_char*)smem_dyn;
-  constexpr int SA = P::kABytes, SB = P::kBBytes;
-  lds_char* bb = base + P::kAStages * SA;
-  // buffers past a ring's stage count are never used
-  prefill_gemm_body<T, SWIGLU, P>(A, B0, B1, b_expert_stride, C, K, N_out, offsets, table,
-                                  m_tiles_max, n_tiles, group_n, grid_logical, base, base + SA,
-                                  base + (P::kAStages > 2 ? 2 * SA : 0), bb, bb + SB,
-                                  bb + (P::kBStages > 2 ? 2 * SB : 0),
-                                  bb + (P::kBStages > 3 ? 3 * SB : 0));
+  if (PT::BM < P::BM && m_end - m_begin <= PT::BM)
+    prefill_gemm_tile<T, SWIGLU, PT>(A, B0, B1, b_expert_stride, C, K, N_out, e, m_begin,
+                                     m_end, nt, base);
+  else
+    prefill_gemm_tile<T, SWIGLU, P>(A, B0, B1, b_expert_stride, C, K, N_out, e, m_begin,
+                                    m_end, nt, base);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -425,7 +447,7 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad
 
 namespace {
 
-template <class T, bool SW, class P = PrefillTile>
+template <class T, bool SW, class P = PrefillTile, class PT = PrefillTailTile>
 hipError_t launch_prefill(const T* A, const T* B0, const T* B1, int64_t b_stride, T* C, int K,
                           int N_out, const int32_t* offsets, const int32_t* table,
                           int64_t m_max, hipStream_t s) {
@@ -436,11 +458,11 @@ hipError_t launch_prefill(const T* A, const T* B0, const T* B1, int64_t b_stride
   const int n_groups = (n_tiles + group_n - 1) / group_n;
   const int64_t logical = m_max * group_n * n_groups;
   const int64_t grid = (logical + 7) / 8 * 8;
-  const size_t lds = (size_t)P::kLdsBytes;
-  hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW, P>,
+  const size_t lds = (size_t)(P::kLdsBytes > PT::kLdsBytes ? P::kLdsBytes : PT::kLdsBytes);
+  hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW, P, PT>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  prefill_gemm_kernel<T, SW, P><<<(unsigned)grid, P::kThreads, lds, s>>>(
+  prefill_gemm_kernel<T, SW, P, PT><<<(unsigned)grid, P::kThreads, lds, s>>>(
       A, B0, B1, b_stride, C, K, N_out, offsets, table, (int)m_max, n_tiles, group_n,
       (int)logical);
   return hipGetLastError();
@@ -458,7 +480,7 @@ hipError_t run_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   T* h = (T*)a.h;
   const int64_t stride = a.F * a.d;
   if (p.small)
-    return launch_prefill<T, true, DecodeDmaTile>(xp, (const T*)a.w_gate, (const T*)a.w_up,
+    return launch_prefill<T, true, DecodeDmaTile, DecodeDmaTile>(xp, (const T*)a.w_gate, (const T*)a.w_up,
                                                   stride, h, (int)a.d, (int)a.F, a.offsets,
                                                   a.sched, p.m_max, s);
   if (p.tile == 2)
@@ -475,7 +497,7 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   T* y = (T*)a.y_perm;
   const int64_t stride = a.d * a.F;
   if (p.small)
-    return launch_prefill<T, false, DecodeDmaTile>(h, (const T*)a.w_down, nullptr, stride, y,
+    return launch_prefill<T, false, DecodeDmaTile, DecodeDmaTile>(h, (const T*)a.w_down, nullptr, stride, y,
                                                    (int)a.F, (int)a.d, a.offsets, a.sched,
                                                    p.m_max, s);
   if (p.tile == 2)
