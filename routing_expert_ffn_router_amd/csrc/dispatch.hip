@@ -49,7 +49,8 @@ tile_hist_kernel(const int32_t* __restrict__ idx, int64_t total, int64_t T, int 
 }
 
 // One block of 1024 threads.  Thread tid = part * E + e scans part `part` of expert e's
-// tile counts (q parts per expert, q the largest power of two with q * E <= 1024), so the
+// tile counts (q parts per expert, q the smallest power of two >= the tile count, at most
+// the largest with q * E <= 1024), so the
 // per-expert scans over many tiles run q-wide; partial sums meet in LDS.  The threads with
 // part 0 (tid = e) then hold the kept counts in expert order for the offsets scan.
 __global__ void __launch_bounds__(1024)
@@ -60,7 +61,7 @@ scan_kernel(const int32_t* __restrict__ hist, int ntiles, int E, int C, int k, b
   __shared__ int smem[17];
   __shared__ int s_part[1024];
   int q = 1;
-  while (q * 2 * E <= 1024) q *= 2;
+  while (q * 2 * E <= 1024 && q < ntiles) q *= 2;
   const int tid = threadIdx.x, part = tid / E, e = tid - part * E;
   const bool live = part < q;
   const int chunk = (ntiles + q - 1) / q;
