@@ -71,11 +71,17 @@ KERNEL_SOURCES = ["routing_expert_ffn_router_amd/csrc/expert_ffn.hip",
 
 
 def kernel_source_sha() -> str:
+    """Hash of the GEMM kernel's code with comments and whitespace removed, so the traffic
+    counters stay attached to the kernel across comment edits."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        src = open(os.path.join(ROOT, f)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

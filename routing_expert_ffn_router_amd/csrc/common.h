@@ -1,5 +1,5 @@
 // Internal building blocks of the MoE kernels for gfx950 (CDNA4): 16-byte memory chunks,
-// the 16x16 MFMA tile shared by every GEMM here, bf16 conversion and wave reductions.
+// the 16x16 (router) and 32x32 (expert GEMM) MFMA tiles, bf16 conversion and wave scans.
 #pragma once
 
 #include <hip/hip_runtime.h>
