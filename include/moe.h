@@ -184,7 +184,9 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router,
  *   src_token         [R] int32 out: token of each kept row, -1 for every other slot
  *   dest_row          [T, k] int32 out: row of each assignment in x_perm, -1 if dropped
  *   drops             [k+2] int32 out (see above)
- *   x_perm            [R, d] dtype out: x_perm[r] = x[src_token[r]] for r < N
+ *   x_perm            [R, d] dtype out: x_perm[r] = x[src_token[r]] for kept rows; nullable:
+ *                     NULL builds the tables only (no row is copied, x may then be NULL),
+ *                     for moe_expert_gate_up_gathered
  */
 int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const void* x,
                  void* workspace, size_t workspace_bytes, int32_t* routed_counts,
@@ -217,6 +219,21 @@ int moe_expert_ffn(const moe_shape* shape, const void* x_perm, const int32_t* ex
 int moe_expert_gate_up(const moe_shape* shape, const void* x_perm,
                        const int32_t* expert_offsets, const void* w_gate, const void* w_up,
                        void* workspace, size_t workspace_bytes, void* h, hipStream_t stream);
+
+/*
+ * moe_expert_gate_up_gathered -- S6 reading the token rows straight from x: h[r] =
+ * silu(x[src_token[r]] w_gate[e]^T) * (x[src_token[r]] w_up[e]^T) for the rows of each
+ * expert (the pack step of [EP-checks] "All-to-all must be profiled separately from
+ * compute" fused into the GEMM's loads, so x_perm is neither written nor read).
+ *   x          [T, d] dtype in; src_token [R] int32 in (from moe_dispatch)
+ *   h          [R, F] dtype out (rows >= expert_offsets[E], and empty padded slots, whose
+ *              src_token is -1, are unspecified)
+ * Needs T * d * sizeof(dtype) < 2^31 (MOE_ERR_UNSUPPORTED otherwise).
+ */
+int moe_expert_gate_up_gathered(const moe_shape* shape, const void* x,
+                                const int32_t* src_token, const int32_t* expert_offsets,
+                                const void* w_gate, const void* w_up, void* workspace,
+                                size_t workspace_bytes, void* h, hipStream_t stream);
 
 /*
  * moe_expert_down -- S7 alone: y_perm[r] = h[r] w_down[e]^T for the rows of each expert
@@ -255,10 +272,13 @@ int moe_slot_counts(const moe_shape* shape, const int32_t* topk_idx, const int32
                     int32_t* routed_by_slot, int32_t* kept_by_slot, hipStream_t stream);
 
 /*
- * moe_layer -- the whole layer: moe_route, moe_dispatch, moe_expert_ffn, moe_combine on one
- * stream, with every intermediate in the workspace (regions in moe_ws_region).  This is
- * the expert-parallel-size-1 configuration of [EP-checks] "All-to-all must be profiled
- * separately from compute": every expert is local and no all-to-all runs.
+ * moe_layer -- the whole layer: moe_route, moe_dispatch, the expert GEMMs and moe_combine on
+ * one stream, with every intermediate in the workspace (regions in moe_ws_region).  This
+ * is the expert-parallel-size-1 configuration of [EP-checks] "All-to-all must be profiled
+ * separately from compute": every expert is local and no all-to-all runs.  With packed
+ * rows (no MOE_FLAG_PAD_TO_CAPACITY) and T * d * sizeof(dtype) < 2^31 the gate/up GEMM
+ * gathers the token rows itself (moe_expert_gate_up_gathered) and the x_perm region is
+ * left unwritten.
  *   out               [T, d] dtype out
  *   routed_counts, tokens_per_expert [E] int32 out, nullable (then kept in the workspace)
  *   drops             [k+2] int32 out, nullable

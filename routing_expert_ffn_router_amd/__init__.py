@@ -83,6 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_dispatch": (i32, [_S, _P, _P, _P, sz, _P, _P, _P, _P, _P, _P, _P, _P]),
         "moe_expert_ffn": (i32, [_S, _P, _P, _P, _P, _P, _P, sz, _P, _P]),
         "moe_expert_gate_up": (i32, [_S, _P, _P, _P, _P, _P, sz, _P, _P]),
+        "moe_expert_gate_up_gathered": (i32, [_S, _P, _P, _P, _P, _P, _P, sz, _P, _P]),
         "moe_expert_down": (i32, [_S, _P, _P, _P, _P, sz, _P, _P]),
         "moe_combine": (i32, [_S, _P, _P, _P, _P, _P]),
         "moe_slot_counts": (i32, [_S, _P, _P, _P, _P, _P]),
@@ -184,6 +185,20 @@ def expert_gate_up(s: MoeShape, x_perm, expert_offsets, w_gate, w_up, workspace,
     _check("moe_expert_gate_up", load_library().moe_expert_gate_up(
         ctypes.byref(s), _ptr(x_perm), _ptr(expert_offsets), _ptr(w_gate), _ptr(w_up),
         _ptr(workspace), _nbytes(workspace), _ptr(h), _stream(stream)))
+
+
+def expert_gate_up_gathered(s: MoeShape, x, src_token, expert_offsets, w_gate, w_up,
+                            workspace, h, stream=None) -> None:
+    _check("moe_expert_gate_up_gathered", load_library().moe_expert_gate_up_gathered(
+        ctypes.byref(s), _ptr(x), _ptr(src_token), _ptr(expert_offsets), _ptr(w_gate),
+        _ptr(w_up), _ptr(workspace), _nbytes(workspace), _ptr(h), _stream(stream)))
+
+
+def gathered_layer(s: MoeShape) -> bool:
+    """Whether moe_layer lets the gate/up GEMM gather the token rows (packed rows and x
+    addressable with 32-bit offsets); x_perm is then not written."""
+    esz = 2 if s.dtype == MOE_BF16 else 4
+    return not (s.flags & MOE_FLAG_PAD_TO_CAPACITY) and s.T * s.d * esz < (1 << 31)
 
 
 def expert_down(s: MoeShape, h, expert_offsets, w_down, workspace, y_perm,
@@ -305,18 +320,25 @@ class MoELayer:
 
     def stages(self, x, w_router, b_router, w_gate, w_up, w_down, stream=None):
         """The same layer as __call__, as the five ABI calls moe_layer makes internally
-        (route, dispatch, gate/up GEMM, down GEMM, combine), yielding after each one so a
-        caller can record events between stages."""
+        (route, dispatch, gate/up GEMM, down GEMM, combine; the dispatch builds the tables
+        only and the gate/up GEMM gathers the rows when moe_layer does so), yielding after
+        each one so a caller can record events between stages."""
         s, ws = self.shape, self.workspace
         v = self.view
         route(s, x, w_router, b_router, v("logits"), v("topk_idx"), v("topk_w"), self.status,
               stream=stream)
         yield "router"
+        gathered = gathered_layer(s)
         dispatch(s, v("topk_idx"), x, ws, self.routed_counts, self.tokens_per_expert,
-                 v("offsets"), v("src_token"), v("dest_row"), self.drops, v("x_perm"),
-                 stream=stream)
+                 v("offsets"), v("src_token"), v("dest_row"), self.drops,
+                 None if gathered else v("x_perm"), stream=stream)
         yield "dispatch"
-        expert_gate_up(s, v("x_perm"), v("offsets"), w_gate, w_up, ws, v("h"), stream=stream)
+        if gathered:
+            expert_gate_up_gathered(s, x, v("src_token"), v("offsets"), w_gate, w_up, ws, v("h"),
+                                    stream=stream)
+        else:
+            expert_gate_up(s, v("x_perm"), v("offsets"), w_gate, w_up, ws, v("h"),
+                           stream=stream)
         yield "gate_up"
         expert_down(s, v("h"), v("offsets"), w_down, ws, v("y_perm"), stream=stream)
         yield "down"

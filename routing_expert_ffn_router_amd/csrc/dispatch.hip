@@ -176,7 +176,8 @@ token_drop_kernel(const int32_t* __restrict__ dest_row, int64_t T, int k,
   if (threadIdx.x == 0 && s_n) atomicAdd(&drops[k + 1], s_n);
 }
 
-// One wave per row, four rows per block, grid-stride over the R row slots.  Packed rows:
+// One wave per row, four rows per block, grid-stride over the R row slots (with x_perm
+// null only the src_token entries of empty slots are written).  Packed rows:
 // slots past N = offsets[E] only get src_token = -1.  Padded (C slots per expert): slot
 // r belongs to expert r / C and is empty when r % C >= kept[r / C]; it gets src_token -1
 // and a zero row.
@@ -192,6 +193,7 @@ gather_rows_kernel(const char* __restrict__ x, int32_t* __restrict__ src_token,
     if (pad) {
       if (r % C >= kept[r / C]) {
         if (lane == 0) src_token[r] = -1;
+        if (!x_perm) continue;
         char* dst = x_perm + r * row_bytes;
         const u32x4 z = {0u, 0u, 0u, 0u};
         for (int64_t c = lane; c < nchunks; c += kWave) st16(dst + c * 16, z);
@@ -201,6 +203,7 @@ gather_rows_kernel(const char* __restrict__ x, int32_t* __restrict__ src_token,
       if (lane == 0) src_token[r] = -1;
       continue;
     }
+    if (!x_perm) continue;  // tables only
     const int64_t t = src_token[r];
     const char* src = x + t * row_bytes;
     char* dst = x_perm + r * row_bytes;

@@ -178,9 +178,9 @@ __device__ inline void wait_vm_barrier() {
 
 template <class T, bool SWIGLU, class P>
 __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
-    const T* __restrict__ A, const T* __restrict__ B0, const T* __restrict__ B1,
-    int64_t b_expert_stride, T* __restrict__ C, int K, int N_out, int e, int m_begin,
-    int m_end, int nt, lds_char* __restrict__ a0, lds_char* __restrict__ a1,
+    const T* __restrict__ A, const int32_t* __restrict__ a_rows, const T* __restrict__ B0,
+    const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C, int K, int N_out,
+    int e, int m_begin, int m_end, int nt, lds_char* __restrict__ a0, lds_char* __restrict__ a1,
     lds_char* __restrict__ a2, lds_char* __restrict__ b0, lds_char* __restrict__ b1,
     lds_char* __restrict__ b2, lds_char* __restrict__ b3) {
   constexpr int BN = SWIGLU ? P::BNW / 2 : P::BNW;
@@ -204,7 +204,8 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   const int dslot = P::kDmaSel == 0 ? wave_u : wave_u - 4;
   const T* B0e = B0 + (int64_t)e * b_expert_stride;
   const T* B1e = SWIGLU ? B1 + (int64_t)e * b_expert_stride : nullptr;
-  const uint64_t base[3] = {uniform_u64(A + (int64_t)m_begin * K),
+  // activation rows: rows m_begin.. of A, or (gathered) the A rows a_rows[m_begin..]
+  const uint64_t base[3] = {uniform_u64(a_rows ? A : A + (int64_t)m_begin * K),
                             uniform_u64(B0e + (int64_t)nt * BN * K),
                             SWIGLU ? uniform_u64(B1e + (int64_t)nt * BN * K) : 0};
   constexpr int kBRows = SWIGLU ? P::BNW / 2 : P::BNW;  // rows of one weight operand
@@ -216,8 +217,12 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     const int r = ((kind == 0 ? i : i - P::kALoads) * P::kDmaWaves + dslot) * P::kRowsPerLoad +
                   lane / P::kChunks;
     const int c = (lane % P::kChunks) ^ P::swz(r);
-    const int row = kind == 0 ? min(r, m_end - 1 - m_begin)
-                              : min(r - (kind - 1) * kBRows, N_out - 1 - nt * BN);
+    int row = kind == 0 ? min(r, m_end - 1 - m_begin)
+                        : min(r - (kind - 1) * kBRows, N_out - 1 - nt * BN);
+    if (kind == 0 && a_rows) {  // an empty padded slot (-1) reads row 0; never stored
+      const int src = a_rows[m_begin + row];
+      row = src < 0 ? 0 : src;
+    }
     voff[i] = (uint32_t)row * (uint32_t)row_bytes + (uint32_t)(c * 16);
   }
   const int dma_lds = dslot * 1024;
@@ -367,14 +372,14 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
 // Stage buffers of tile P in the block's LDS, then its body.
 template <class T, bool SWIGLU, class P>
 __device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
-    const T* __restrict__ A, const T* __restrict__ B0, const T* __restrict__ B1,
-    int64_t b_expert_stride, T* __restrict__ C, int K, int N_out, int e, int m_begin,
-    int m_end, int nt, lds_char* base) {
+    const T* __restrict__ A, const int32_t* __restrict__ a_rows, const T* __restrict__ B0,
+    const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C, int K, int N_out,
+    int e, int m_begin, int m_end, int nt, lds_char* base) {
   constexpr int SA = P::kABytes, SB = P::kBBytes;
   lds_char* bb = base + P::kAStages * SA;
   // buffers past a ring's stage count are never used
-  prefill_gemm_body<T, SWIGLU, P>(A, B0, B1, b_expert_stride, C, K, N_out, e, m_begin, m_end,
-                                  nt, base, base + SA, base + (P::kAStages > 2 ? 2 * SA : 0),
+  prefill_gemm_body<T, SWIGLU, P>(A, a_rows, B0, B1, b_expert_stride, C, K, N_out, e, m_begin,
+                                  m_end, nt, base, base + SA, base + (P::kAStages > 2 ? 2 * SA : 0),
                                   bb, bb + SB, bb + (P::kBStages > 2 ? 2 * SB : 0),
                                   bb + (P::kBStages > 3 ? 3 * SB : 0));
 }
@@ -386,8 +391,9 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
 // and MFMAs instead of a full tile of mostly clamped rows.
 template <class T, bool SWIGLU, class P, class PT>
 __global__ void __launch_bounds__(P::kThreads)
-prefill_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
-                    const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C, int K,
+prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
+                    const T* __restrict__ B0, const T* __restrict__ B1,
+                    int64_t b_expert_stride, T* __restrict__ C, int K,
                     int N_out, const int32_t* __restrict__ offsets,
                     const int32_t* __restrict__ table, int m_tiles_max, int n_tiles,
                     int group_n, int grid_logical) {
@@ -408,11 +414,11 @@ prefill_gemm_kernel(const T* __restrict__ A, const T* __restrict__ B0,
   const int m_end = offsets[e + 1];
   lds_char* base = (lds_char*)smem_dyn;
   if (PT::BM < P::BM && m_end - m_begin <= PT::BM)
-    prefill_gemm_tile<T, SWIGLU, PT>(A, B0, B1, b_expert_stride, C, K, N_out, e, m_begin,
-                                     m_end, nt, base);
+    prefill_gemm_tile<T, SWIGLU, PT>(A, a_rows, B0, B1, b_expert_stride, C, K, N_out, e,
+                                     m_begin, m_end, nt, base);
   else
-    prefill_gemm_tile<T, SWIGLU, P>(A, B0, B1, b_expert_stride, C, K, N_out, e, m_begin,
-                                    m_end, nt, base);
+    prefill_gemm_tile<T, SWIGLU, P>(A, a_rows, B0, B1, b_expert_stride, C, K, N_out, e,
+                                    m_begin, m_end, nt, base);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -448,9 +454,9 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad
 namespace {
 
 template <class T, bool SW, class P = PrefillTile, class PT = PrefillTailTile>
-hipError_t launch_prefill(const T* A, const T* B0, const T* B1, int64_t b_stride, T* C, int K,
-                          int N_out, const int32_t* offsets, const int32_t* table,
-                          int64_t m_max, hipStream_t s) {
+hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const T* B1,
+                          int64_t b_stride, T* C, int K, int N_out, const int32_t* offsets,
+                          const int32_t* table, int64_t m_max, hipStream_t s) {
   if (m_max <= 0) return hipSuccess;
   constexpr int BN = SW ? P::BNW / 2 : P::BNW;
   const int n_tiles = (N_out + BN - 1) / BN;
@@ -463,7 +469,7 @@ hipError_t launch_prefill(const T* A, const T* B0, const T* B1, int64_t b_stride
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   prefill_gemm_kernel<T, SW, P, PT><<<(unsigned)grid, P::kThreads, lds, s>>>(
-      A, B0, B1, b_stride, C, K, N_out, offsets, table, (int)m_max, n_tiles, group_n,
+      A, a_rows, B0, B1, b_stride, C, K, N_out, offsets, table, (int)m_max, n_tiles, group_n,
       (int)logical);
   return hipGetLastError();
 }
@@ -476,18 +482,20 @@ hipError_t launch_table(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
 
 template <class T>
 hipError_t run_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
-  const T* xp = (const T*)a.x_perm;
+  // activations: x_perm, or x with the rows gathered through a.src_rows
+  const T* xp = (const T*)(a.src_rows ? a.x : a.x_perm);
+  const int32_t* rows = a.src_rows;
   T* h = (T*)a.h;
   const int64_t stride = a.F * a.d;
   if (p.small)
-    return launch_prefill<T, true, DecodeDmaTile, DecodeDmaTile>(xp, (const T*)a.w_gate, (const T*)a.w_up,
+    return launch_prefill<T, true, DecodeDmaTile, DecodeDmaTile>(xp, rows, (const T*)a.w_gate, (const T*)a.w_up,
                                                   stride, h, (int)a.d, (int)a.F, a.offsets,
                                                   a.sched, p.m_max, s);
   if (p.tile == 2)
-    return launch_prefill<T, true, PrefillTallTile>(xp, (const T*)a.w_gate, (const T*)a.w_up,
+    return launch_prefill<T, true, PrefillTallTile>(xp, rows, (const T*)a.w_gate, (const T*)a.w_up,
                                                     stride, h, (int)a.d, (int)a.F, a.offsets,
                                                     a.sched, p.m_max, s);
-  return launch_prefill<T, true>(xp, (const T*)a.w_gate, (const T*)a.w_up, stride, h,
+  return launch_prefill<T, true>(xp, rows, (const T*)a.w_gate, (const T*)a.w_up, stride, h,
                                  (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s);
 }
 
@@ -497,14 +505,14 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   T* y = (T*)a.y_perm;
   const int64_t stride = a.d * a.F;
   if (p.small)
-    return launch_prefill<T, false, DecodeDmaTile, DecodeDmaTile>(h, (const T*)a.w_down, nullptr, stride, y,
+    return launch_prefill<T, false, DecodeDmaTile, DecodeDmaTile>(h, nullptr, (const T*)a.w_down, nullptr, stride, y,
                                                    (int)a.F, (int)a.d, a.offsets, a.sched,
                                                    p.m_max, s);
   if (p.tile == 2)
-    return launch_prefill<T, false, PrefillTallTile>(h, (const T*)a.w_down, nullptr, stride, y,
+    return launch_prefill<T, false, PrefillTallTile>(h, nullptr, (const T*)a.w_down, nullptr, stride, y,
                                                      (int)a.F, (int)a.d, a.offsets, a.sched,
                                                      p.m_max, s);
-  return launch_prefill<T, false>(h, (const T*)a.w_down, nullptr, stride, y, (int)a.F,
+  return launch_prefill<T, false>(h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F,
                                   (int)a.d, a.offsets, a.sched, p.m_max, s);
 }
 

@@ -46,7 +46,7 @@ struct DispatchArgs {
   int32_t* src_token;  // [R]
   int32_t* dest_row;   // [T*k]
   int32_t* drops;      // [k+2]
-  void* x_perm;        // [R, d]
+  void* x_perm;        // [R, d]; null: tables only, no row copies
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 
@@ -65,6 +65,8 @@ inline int64_t ffn_table_ints(const FfnPlan& p) { return 1 + 2 * p.m_max; }
 struct FfnArgs {
   int dtype;
   const void* x_perm;
+  const void* x;            // with src_rows: the gate/up GEMM reads x[src_rows[r]] for row r
+  const int32_t* src_rows;  // nullable; [R] token of each row (-1: empty padded slot)
   const int32_t* offsets;  // [E+1]
   const void* w_gate;
   const void* w_up;

@@ -193,9 +193,9 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, voi
   if (rc != MOE_OK) return rc;
   if (!routed_counts || !tokens_per_expert || !expert_offsets || !drops)
     return MOE_ERR_INVALID_ARG;
-  if (s->T > 0 && (!topk_idx || !x || !src_token || !dest_row || !x_perm))
+  if (s->T > 0 && (!topk_idx || !src_token || !dest_row || (x_perm && !x)))
     return MOE_ERR_INVALID_ARG;
-  if (s->T > 0 && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_ALIGNMENT;
+  if (s->T > 0 && x_perm && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_ALIGNMENT;
   Layout L;
   if ((rc = check_workspace(s, ws, ws_bytes, &L)) != MOE_OK) return rc;
   moe::DispatchArgs a;
@@ -226,25 +226,35 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, voi
 
 namespace {
 
-// Shared body of the three expert-FFN entry points; which = 1 (gate/up), 2 (down), 3 (both).
-int expert_ffn_impl(const moe_shape* s, int which, const void* x_perm, void* h,
-                    const int32_t* expert_offsets, const void* w_gate, const void* w_up,
-                    const void* w_down, void* ws, size_t ws_bytes, void* y_perm,
-                    hipStream_t st) {
+// Rows of x addressed by 32-bit byte offsets in the gathered gate/up GEMM.
+bool gather_fits(const moe_shape* s) {
+  return s->T * s->d * elt_bytes(s->dtype) < ((int64_t)1 << 31);
+}
+
+// Shared body of the expert-FFN entry points; which = 1 (gate/up), 2 (down), 3 (both).  The
+// gate/up activations are x_perm, or, with src_rows, the rows src_rows[r] of x.
+int expert_ffn_impl(const moe_shape* s, int which, const void* x_perm, const void* x,
+                    const int32_t* src_rows, void* h, const int32_t* expert_offsets,
+                    const void* w_gate, const void* w_up, const void* w_down, void* ws,
+                    size_t ws_bytes, void* y_perm, hipStream_t st) {
   int rc = check_shape(s);
   if (rc != MOE_OK) return rc;
   if (s->T == 0) return MOE_OK;
   if (!expert_offsets) return MOE_ERR_INVALID_ARG;
-  if ((which & 1) && (!x_perm || !w_gate || !w_up || !h)) return MOE_ERR_INVALID_ARG;
+  const void* act = src_rows ? x : x_perm;
+  if ((which & 1) && (!act || !w_gate || !w_up || !h)) return MOE_ERR_INVALID_ARG;
   if ((which & 2) && (!w_down || !y_perm || !h)) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x_perm) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+  if (!aligned16(act) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
       !aligned16(y_perm) || !aligned16(h))
     return MOE_ERR_ALIGNMENT;
+  if (src_rows && !gather_fits(s)) return MOE_ERR_UNSUPPORTED;
   Layout L;
   if ((rc = check_workspace(s, ws, ws_bytes, &L)) != MOE_OK) return rc;
   moe::FfnArgs a;
   a.dtype = s->dtype;
   a.x_perm = x_perm;
+  a.x = x;
+  a.src_rows = src_rows;
   a.offsets = expert_offsets;
   a.w_gate = w_gate;
   a.w_up = w_up;
@@ -275,22 +285,33 @@ int moe_expert_ffn(const moe_shape* s, const void* x_perm, const int32_t* expert
   Layout L;
   if (s->T > 0 && (rc = check_workspace(s, ws, ws_bytes, &L)) != MOE_OK) return rc;
   void* h = s->T > 0 ? region<void>(ws, L, MOE_WS_H) : nullptr;
-  return expert_ffn_impl(s, 3, x_perm, h, expert_offsets, w_gate, w_up, w_down, ws, ws_bytes,
-                         y_perm, st);
+  return expert_ffn_impl(s, 3, x_perm, nullptr, nullptr, h, expert_offsets, w_gate, w_up,
+                         w_down, ws, ws_bytes, y_perm, st);
 }
 
 int moe_expert_gate_up(const moe_shape* s, const void* x_perm, const int32_t* expert_offsets,
                        const void* w_gate, const void* w_up, void* ws, size_t ws_bytes,
                        void* h, hipStream_t st) {
-  return expert_ffn_impl(s, 1, x_perm, h, expert_offsets, w_gate, w_up, nullptr, ws, ws_bytes,
-                         nullptr, st);
+  return expert_ffn_impl(s, 1, x_perm, nullptr, nullptr, h, expert_offsets, w_gate, w_up,
+                         nullptr, ws, ws_bytes, nullptr, st);
+}
+
+int moe_expert_gate_up_gathered(const moe_shape* s, const void* x, const int32_t* src_token,
+                                const int32_t* expert_offsets, const void* w_gate,
+                                const void* w_up, void* ws, size_t ws_bytes, void* h,
+                                hipStream_t st) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (s->T > 0 && !src_token) return MOE_ERR_INVALID_ARG;
+  return expert_ffn_impl(s, 1, nullptr, x, src_token, h, expert_offsets, w_gate, w_up,
+                         nullptr, ws, ws_bytes, nullptr, st);
 }
 
 int moe_expert_down(const moe_shape* s, const void* h, const int32_t* expert_offsets,
                     const void* w_down, void* ws, size_t ws_bytes, void* y_perm,
                     hipStream_t st) {
-  return expert_ffn_impl(s, 2, nullptr, const_cast<void*>(h), expert_offsets, nullptr, nullptr,
-                         w_down, ws, ws_bytes, y_perm, st);
+  return expert_ffn_impl(s, 2, nullptr, nullptr, nullptr, const_cast<void*>(h), expert_offsets,
+                         nullptr, nullptr, w_down, ws, ws_bytes, y_perm, st);
 }
 
 int moe_combine(const moe_shape* s, const void* y_perm, const int32_t* dest_row,
@@ -342,9 +363,17 @@ int moe_layer(const moe_shape* s, const void* x, const void* w_router, const flo
 
   rc = route_impl(s, x, w_router, b_router, logits, 0, idx, gates, stt, st);
   if (rc != MOE_OK) return rc;
-  rc = moe_dispatch(s, idx, x, ws, ws_bytes, routed, kept, offsets, src, dest, dr, x_perm, st);
+  // packed rows: the gate/up GEMM gathers the token rows itself (x_perm is not written)
+  const bool gathered = !padded(s) && gather_fits(s);
+  rc = moe_dispatch(s, idx, x, ws, ws_bytes, routed, kept, offsets, src, dest, dr,
+                    gathered ? nullptr : x_perm, st);
   if (rc != MOE_OK) return rc;
-  rc = moe_expert_ffn(s, x_perm, offsets, w_gate, w_up, w_down, ws, ws_bytes, y_perm, st);
+  void* h = region<void>(ws, L, MOE_WS_H);
+  rc = gathered ? moe_expert_gate_up_gathered(s, x, src, offsets, w_gate, w_up, ws, ws_bytes,
+                                              h, st)
+                : moe_expert_gate_up(s, x_perm, offsets, w_gate, w_up, ws, ws_bytes, h, st);
+  if (rc != MOE_OK) return rc;
+  rc = moe_expert_down(s, h, offsets, w_down, ws, ws_bytes, y_perm, st);
   if (rc != MOE_OK) return rc;
   return moe_combine(s, y_perm, dest, gates, out, st);
 }

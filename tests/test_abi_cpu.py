@@ -137,6 +137,31 @@ def test_pad_to_capacity_rows_and_workspace():
     assert moe.max_rows(_shape(capacity=8, flags=1)) == 64 == moe.max_rows(_shape(capacity=8))
 
 
+def test_gathered_gate_up_checks():
+    s = ctypes.byref(_shape())
+    p = FAKE
+    f = lib.moe_expert_gate_up_gathered
+    assert f(s, p, None, p, p, p, p, 1 << 40, p, None) == moe.MOE_ERR_INVALID_ARG  # src_token
+    assert f(s, None, p, p, p, p, p, 1 << 40, p, None) == moe.MOE_ERR_INVALID_ARG  # x
+    assert f(s, p + 8, p, p, p, p, p, 1 << 40, p, None) == moe.MOE_ERR_ALIGNMENT
+    assert f(s, p, p, p, p, p, None, 1 << 40, p, None) == moe.MOE_ERR_WORKSPACE
+    big = _shape(T=1 << 20, d=1 << 11, k=1, dtype=moe.MOE_BF16)  # x is 4 GiB: no 32-bit rows
+    assert f(ctypes.byref(big), p, p, p, p, p, p, 1 << 40, p, None) == moe.MOE_ERR_UNSUPPORTED
+    assert not moe.gathered_layer(big) and moe.gathered_layer(_shape())
+    assert not moe.gathered_layer(_shape(flags=moe.MOE_FLAG_PAD_TO_CAPACITY))
+
+
+def test_dispatch_tables_only_accepts_null_x_perm():
+    s = ctypes.byref(_shape())
+    p = FAKE
+    # x_perm NULL: x is not needed either; the call fails only at the workspace check
+    assert lib.moe_dispatch(s, p, None, p, 16, p, p, p, p, p, p, None, None) == \
+        moe.MOE_ERR_WORKSPACE
+    # x_perm given without x
+    assert lib.moe_dispatch(s, p, None, p, 1 << 40, p, p, p, p, p, p, p, None) == \
+        moe.MOE_ERR_INVALID_ARG
+
+
 def test_slot_counts_null_outputs_rejected():
     s = ctypes.byref(_shape())
     p = FAKE

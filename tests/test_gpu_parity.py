@@ -263,6 +263,55 @@ def test_expert_ffn(name):
     assert np.all(np.isfinite(to_host(y[:N])))
 
 
+@pytest.mark.parametrize("name,pad", [("bf16_e8_big_tiles", False), ("bf16_e8_zipf_drops", False),
+                                      ("bf16_e256_k8_decode", False), ("f32_e4_big_tiles", False),
+                                      ("bf16_e8_zipf_drops", True), ("bf16_e3_k3", True)])
+def test_gate_up_gathered_equals_packed(name, pad):
+    # the GEMM that gathers x rows through src_token computes the same h, bit for bit, as
+    # the GEMM over x_perm (same row values, same arithmetic), on the kept rows
+    w = SMALL[name]
+    log(f"gathered gate/up {w} pad={pad}")
+    d_in = device_inputs(w)
+    C = moe.capacity(w.T, w.k, w.E, w.capacity_factor)
+    s = moe.shape(w.T, w.d, w.E, w.k, w.F, C, moe.MOE_BF16 if w.dtype == "bf16" else
+                  moe.MOE_F32, flags=moe.MOE_FLAG_PAD_TO_CAPACITY if pad else 0)
+    lay = moe.MoELayer(s)
+    v = lay.view
+    moe.route(s, d_in["x"], d_in["w_router"], d_in["b_router"], v("logits"), v("topk_idx"),
+              v("topk_w"))
+    moe.dispatch(s, v("topk_idx"), d_in["x"], lay.workspace, lay.routed_counts,
+                 lay.tokens_per_expert, v("offsets"), v("src_token"), v("dest_row"), lay.drops,
+                 v("x_perm"))
+    moe.expert_gate_up(s, v("x_perm"), v("offsets"), d_in["w_gate"], d_in["w_up"],
+                       lay.workspace, v("h"))
+    h1 = v("h").clone()
+    v("h").fill_(0)
+    moe.expert_gate_up_gathered(s, d_in["x"], v("src_token"), v("offsets"), d_in["w_gate"],
+                                d_in["w_up"], lay.workspace, v("h"))
+    torch.cuda.synchronize()
+    rows = torch.nonzero(v("src_token") >= 0).flatten()
+    assert rows.numel() == int(lay.tokens_per_expert.sum())
+    assert torch.equal(h1[rows], v("h")[rows])
+
+
+def test_dispatch_tables_only():
+    T, E, k, C, d = 1000, 8, 2, 250, 256
+    rng = np.random.default_rng(21)
+    idx = oracle.select_topk(rng.standard_normal((T, E)).astype(np.float32), k)
+    s = moe.shape(T, d, E, k, 128, C, moe.MOE_BF16)
+    R = moe.max_rows(s)
+    ws = torch.empty(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
+    g = dict(routed=_i32(E), kept=_i32(E), offsets=_i32(E + 1), src=_i32(R), dest=_i32(0, T, k),
+             drops=_i32(k + 2))
+    moe.dispatch(s, to_device(idx, torch.int32), None, ws, g["routed"], g["kept"], g["offsets"],
+                 g["src"], g["dest"], g["drops"], None)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(idx, E, C)
+    assert np.array_equal(g["dest"].cpu().numpy(), ref["dest_row"])
+    assert np.array_equal(g["src"].cpu().numpy(), ref["src_token"][:R])
+    assert np.array_equal(g["offsets"].cpu().numpy(), ref["expert_offsets"])
+
+
 # ------------------------------------------------------------------------------- S8
 @pytest.mark.parametrize("T,E,k,C,d,dtype", [(500, 8, 2, 110, 256, "bf16"),
                                              (300, 256, 8, 10, 128, "bf16"),
@@ -372,13 +421,13 @@ def test_layer_deterministic():
     d_in = device_inputs(w)
     lay, out1 = _layer_gpu(w, d_in, s)
     N = int(lay.view("offsets")[-1])
-    first = (out1.clone(), lay.view("dest_row").clone(), lay.view("x_perm")[:N].clone(),
+    first = (out1.clone(), lay.view("dest_row").clone(), lay.view("h")[:N].clone(),
              lay.view("y_perm")[:N].clone())
     lay2, out2 = _layer_gpu(w, d_in, s)
     assert int(lay2.view("offsets")[-1]) == N
     assert torch.equal(first[0], out2)
     assert torch.equal(first[1], lay2.view("dest_row"))
-    assert torch.equal(first[2], lay2.view("x_perm")[:N])
+    assert torch.equal(first[2], lay2.view("h")[:N])
     assert torch.equal(first[3], lay2.view("y_perm")[:N])
 
 
