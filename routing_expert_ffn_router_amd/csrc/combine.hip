@@ -13,7 +13,7 @@ namespace moe {
 // One wave per (token, 64-chunk column segment): lane l of segment s sums chunk
 // s * 64 + l of the token's k expert rows.  Splitting each row over several waves keeps
 // enough loads in flight when T is small (a decode step of 256 tokens x 14 segments).
-template <class T>
+template <class T, int G>
 __global__ void __launch_bounds__(256)
 combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ dest,
                const float* __restrict__ w, T* __restrict__ out, int64_t T_, int d, int k,
@@ -30,14 +30,14 @@ combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ dest,
   float acc[P];
 #pragma unroll
   for (int i = 0; i < P; ++i) acc[i] = 0.f;
-  // slots in groups of four: the group's row loads go out together, the sums still run
-  // in slot order
-  for (int j0 = 0; j0 < k; j0 += 4) {
-    u32x4 v[4];
-    float g[4];
-    bool live[4];
+  // slots in groups of G: the group's row loads go out together, the sums still run in
+  // slot order
+  for (int j0 = 0; j0 < k; j0 += G) {
+    u32x4 v[G];
+    float g[G];
+    bool live[G];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < G; ++u) {
       const int j = j0 + u;
       const int r = j < k ? dt[j] : -1;
       live[u] = r >= 0;
@@ -45,7 +45,7 @@ combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ dest,
       v[u] = live[u] ? ld16(y + (int64_t)r * d + (int64_t)c * P) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < G; ++u) {
       if (!live[u]) continue;  // dropped slots add nothing
       const T* e = reinterpret_cast<const T*>(&v[u]);
 #pragma unroll
@@ -66,12 +66,19 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* dest_row
   const int per_chunk = dtype == 1 ? 8 : 4;
   const int segs = (int)((d / per_chunk + kWave - 1) / kWave);
   const unsigned blocks = (unsigned)((T * segs + 3) / 4);
-  if (dtype == 1)
-    combine_kernel<bf16><<<blocks, 256, 0, s>>>((const bf16*)y_perm, dest_row, topk_w,
-                                                (bf16*)out, T, (int)d, (int)k, segs);
+  // slot groups of 8 when k is large enough to fill them, else 4
+  if (dtype == 1 && k > 4)
+    combine_kernel<bf16, 8><<<blocks, 256, 0, s>>>((const bf16*)y_perm, dest_row, topk_w,
+                                                   (bf16*)out, T, (int)d, (int)k, segs);
+  else if (dtype == 1)
+    combine_kernel<bf16, 4><<<blocks, 256, 0, s>>>((const bf16*)y_perm, dest_row, topk_w,
+                                                   (bf16*)out, T, (int)d, (int)k, segs);
+  else if (k > 4)
+    combine_kernel<float, 8><<<blocks, 256, 0, s>>>((const float*)y_perm, dest_row, topk_w,
+                                                    (float*)out, T, (int)d, (int)k, segs);
   else
-    combine_kernel<float><<<blocks, 256, 0, s>>>((const float*)y_perm, dest_row, topk_w,
-                                                 (float*)out, T, (int)d, (int)k, segs);
+    combine_kernel<float, 4><<<blocks, 256, 0, s>>>((const float*)y_perm, dest_row, topk_w,
+                                                    (float*)out, T, (int)d, (int)k, segs);
   return hipGetLastError();
 }
 

@@ -32,23 +32,21 @@ hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
 //
 // The router GEMM is skinny (E = 8 or 256 columns) and bound by reading x (and, for
 // E = 256, w) once.  A block computes a (16 * MT)-token x (16 * NT)-expert tile with MFMA
-// straight from global memory (no LDS staging); its 8 waves split the reduction axis in
-// 128-byte steps (wave w takes steps w, w + 8, ...), so enough loads are in flight, and
-// their partial tiles are summed in LDS in wave order, which keeps the result
-// deterministic.  Per 128-byte step a lane loads 32 contiguous bytes of each of its MT
+// straight from global memory (no LDS staging); its W waves split the reduction axis in
+// 128-byte steps (wave w takes steps w, w + W, ...), each wave loading its next step while
+// multiplying the current one, and their partial tiles are summed in LDS in wave order,
+// which keeps the result deterministic.  Per 128-byte step a lane loads 32 contiguous bytes of each of its MT
 // token rows and NT expert rows; both operands use the same k-chunk assignment (lane group
 // g takes chunks 2g and 2g + 1), so the products pair up.  Larger tiles cut the re-reads:
 // with many experts and tokens a 64 x 64 tile reads x E / 64 times and w T / 64 times.
 // grid = (ceil(T / (16 MT)), ceil(E / (16 NT))).
 // ---------------------------------------------------------------------------------------
-constexpr int kRouterWaves = 8;
-
-template <class T, int MT, int NT>
+template <class T, int MT, int NT, int kRouterWaves>
 __global__ void __launch_bounds__(kRouterWaves* kWave)
 router_logits_kernel(const T* __restrict__ x, const T* __restrict__ w,
                      const float* __restrict__ bias, float* __restrict__ logits, int T_,
                      int d, int E) {
-  extern __shared__ float part[];  // [kRouterWaves][MT][NT][4][kWave]
+  extern __shared__ float part[];  // [W][MT][NT][4][kWave]
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int t0 = blockIdx.x * MT * 16;
   const int e0 = blockIdx.y * NT * 16;
@@ -71,26 +69,37 @@ router_logits_kernel(const T* __restrict__ x, const T* __restrict__ w,
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int steps = d * (int)sizeof(T) / 128;
-  for (int st = wave; st < steps; st += kRouterWaves) {
+  // operands of one 128-byte step; the next step's loads go out before this step's MFMAs
+  u32x4 a0[2][MT], a1[2][MT], b0[2][NT], b1[2][NT];
+  auto load = [&](int st, int set) {
     const int kb = st * 128;
-    u32x4 a0[MT], a1[MT], b0[NT], b1[NT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      a0[m] = ld16(xa[m] + kb);
-      a1[m] = ld16(xa[m] + kb + 16);
+      a0[set][m] = ld16(xa[m] + kb);
+      a1[set][m] = ld16(xa[m] + kb + 16);
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      b0[n] = ld16(wb[n] + kb);
-      b1[n] = ld16(wb[n] + kb + 16);
+      b0[set][n] = ld16(wb[n] + kb);
+      b1[set][n] = ld16(wb[n] + kb + 16);
     }
+  };
+  auto mfma = [&](int set) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        mma_chunk(acc[m][n], a0[m], b0[n], T());
-        mma_chunk(acc[m][n], a1[m], b1[n], T());
+        mma_chunk(acc[m][n], a0[set][m], b0[set][n], T());
+        mma_chunk(acc[m][n], a1[set][m], b1[set][n], T());
       }
+  };
+  if (wave < steps) load(wave, 0);
+  for (int st = wave; st < steps; st += 2 * kRouterWaves) {
+    if (st + kRouterWaves < steps) load(st + kRouterWaves, 1);
+    mfma(0);
+    if (st + kRouterWaves >= steps) break;
+    if (st + 2 * kRouterWaves < steps) load(st + 2 * kRouterWaves, 0);
+    mfma(1);
   }
   constexpr int kTile = MT * NT * 4 * kWave;  // floats of one wave's partial tile
 #pragma unroll
@@ -113,17 +122,17 @@ router_logits_kernel(const T* __restrict__ x, const T* __restrict__ w,
   }
 }
 
-template <class T, int MT, int NT>
+template <class T, int MT, int NT, int W>
 hipError_t launch_router_tile(const T* x, const T* w, const float* b, float* logits,
                               int64_t T_, int64_t d, int64_t E, hipStream_t s) {
-  const size_t lds = (size_t)kRouterWaves * MT * NT * 4 * kWave * sizeof(float);
-  hipError_t e = hipFuncSetAttribute((const void*)router_logits_kernel<T, MT, NT>,
+  const size_t lds = (size_t)W * MT * NT * 4 * kWave * sizeof(float);
+  hipError_t e = hipFuncSetAttribute((const void*)router_logits_kernel<T, MT, NT, W>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((T_ + 16 * MT - 1) / (16 * MT)),
                   (unsigned)((E + 16 * NT - 1) / (16 * NT)));
-  router_logits_kernel<T, MT, NT><<<grid, kRouterWaves * kWave, lds, s>>>(
-      x, w, b, logits, (int)T_, (int)d, (int)E);
+  router_logits_kernel<T, MT, NT, W><<<grid, W * kWave, lds, s>>>(x, w, b, logits, (int)T_,
+                                                                  (int)d, (int)E);
   return hipGetLastError();
 }
 
@@ -133,11 +142,13 @@ hipError_t launch_router_typed(const T* x, const T* w, const float* b, float* lo
   // The largest tile that still gives at least 512 blocks (two per CU): 64 x 64, then
   // 16 x 64, else 16 x 16.
   const int64_t t16 = (T_ + 15) / 16, t64 = (T_ + 63) / 64;
+  // The 64 x 64 tile runs 4 waves per block (one per SIMD, registers for two operand sets
+  // of 16 rows), the others 8.
   if (E > 16 && t64 * ((E + 63) / 64) >= 512)
-    return launch_router_tile<T, 4, 4>(x, w, b, logits, T_, d, E, s);
+    return launch_router_tile<T, 4, 4, 4>(x, w, b, logits, T_, d, E, s);
   if (E > 16 && t16 * ((E + 63) / 64) >= 512)
-    return launch_router_tile<T, 1, 4>(x, w, b, logits, T_, d, E, s);
-  return launch_router_tile<T, 1, 1>(x, w, b, logits, T_, d, E, s);
+    return launch_router_tile<T, 1, 4, 8>(x, w, b, logits, T_, d, E, s);
+  return launch_router_tile<T, 1, 1, 8>(x, w, b, logits, T_, d, E, s);
 }
 
 hipError_t launch_router_logits(int dtype, const void* x, const void* w, const float* b,

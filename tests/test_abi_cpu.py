@@ -108,6 +108,7 @@ def test_bad_shapes_rejected_everywhere(kw, err):
     assert lib.moe_expert_ffn(s, p, p, p, p, p, p, 1 << 40, p, None) == err
     assert lib.moe_combine(s, p, p, p, p, None) == err
     assert lib.moe_slot_counts(s, p, p, p, p, None) == err
+    assert lib.moe_expert_gate_up_gathered(s, p, p, p, p, p, p, 1 << 40, p, None) == err
     assert lib.moe_layer(s, p, p, None, p, p, p, p, 1 << 40, p, None, None, None, None,
                          None) == err
 
