@@ -113,6 +113,15 @@ def test_fullsize_layer_sampled(name):
     gates = oracle.gate_weights(L, idx)
     ref = oracle.dispatch(idx, w.E, s.capacity)
     idx_gpu = lay.view("topk_idx").cpu().numpy()
+    # routing from the GPU's own fp32 logits is bit-exact: selection, gates, every table
+    idx_own = oracle.select_topk(L_gpu, w.k)
+    assert np.array_equal(idx_gpu, idx_own)
+    assert np.max(np.abs(lay.view("topk_w").cpu().numpy() - oracle.gate_weights(L_gpu, idx_own))) <= 1e-6
+    own = oracle.dispatch(idx_own, w.E, s.capacity)
+    assert np.array_equal(lay.view("dest_row").cpu().numpy(), own["dest_row"])
+    assert np.array_equal(lay.view("offsets").cpu().numpy(), own["expert_offsets"])
+    assert np.array_equal(lay.tokens_per_expert.cpu().numpy(), own["tokens_per_expert"])
+    assert np.array_equal(lay.drops.cpu().numpy()[1:w.k + 1], own["drops_per_slot"])
     bad, unexplained = near_tie_ok(L, idx_gpu, idx, tol)
     log(f"  selection differs on {len(bad)} tokens (all near-ties: {not unexplained})")
     assert not unexplained
