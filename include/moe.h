@@ -125,7 +125,7 @@ typedef enum {
  * quality, memory and tail latency": mean tokens per expert times the factor; the mean is
  * T*k/E by the section "Mean expert load proves almost nothing").  Returns
  * ceil(((cf * T) * k) / E) evaluated in IEEE double; 0 (no limit) when cf <= 0; -1 when T < 0,
- * k < 1 or E < 1 or cf is not finite.  Host function. */
+ * k < 1 or E < 1, cf is not finite or the result does not fit int64.  Host function. */
 int64_t moe_capacity(int64_t T, int64_t k, int64_t E, double cf);
 
 /* Row slots R of x_perm, y_perm and src_token: min(T*k, E*C) with C = T when unlimited,

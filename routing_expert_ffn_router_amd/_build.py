@@ -27,29 +27,43 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer (device code is not
+# instrumented): the library's argument checks, workspace layout and capacity arithmetic run
+# under them in a CPU test.  Each sanitizer flag applies to the host compilation only.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-shared-libasan",
+            "-Xarch_host", "-fno-omit-frame-pointer"]
+LIB_SANITIZED = os.path.join(OBJ, "libmoe_sanitized.so")
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    out = os.path.join(OBJ, "sanitized") if sanitize else OBJ
+    obj = os.path.join(out, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = SANITIZE if sanitize else []
+    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile and link libmoe.so (or, with sanitize, the host-sanitized copy in _build/)."""
+    os.makedirs(os.path.join(OBJ, "sanitized") if sanitize else OBJ, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+    lib = LIB_SANITIZED if sanitize else LIB
+    tmp = lib + ".tmp"
+    extra = SANITIZE if sanitize else []
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -38,7 +38,7 @@ int check_shape(const moe_shape* s) {
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (s->E > kMaxE || s->k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (s->d % 128 != 0 || s->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  if (s->T * s->k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (s->T > ((((int64_t)1 << 31) - 1) / s->k)) return MOE_ERR_UNSUPPORTED;  // T * k < 2^31
   if (s->d > ((int64_t)1 << 20) || s->F > ((int64_t)1 << 20)) return MOE_ERR_UNSUPPORTED;
   if (padded(s) && s->E * eff_capacity(s) >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   // group-limited selection
@@ -137,7 +137,9 @@ extern "C" {
 int64_t moe_capacity(int64_t T, int64_t k, int64_t E, double cf) {
   if (T < 0 || k < 1 || E < 1 || !isfinite(cf)) return -1;
   if (!(cf > 0)) return 0;
-  return (int64_t)ceil(((cf * (double)T) * (double)k) / (double)E);
+  const double c = ceil(((cf * (double)T) * (double)k) / (double)E);
+  if (!(c < 9.2233720368547758e18)) return -1;  // does not fit int64
+  return (int64_t)c;
 }
 
 int64_t moe_max_rows(const moe_shape* s) {
