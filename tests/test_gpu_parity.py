@@ -28,6 +28,10 @@ SMALL = {
     "bf16_e256_k8_decode": W("bf16_e256_k8_decode", 37, 512, 256, 8, 384, None, "bf16"),
     "f32_e4_big_tiles": W("f32_e4_big_tiles", 600, 256, 4, 2, 384, 1.0, "f32"),
     "bf16_e3_k3": W("bf16_e3_k3", 333, 128, 3, 3, 256, None, "bf16"),
+    # the ABI's maximum experts and slots per token, capacity-bound
+    "bf16_e1024_k64_max": W("bf16_e1024_k64_max", 96, 128, 1024, 64, 128, 1.0, "bf16", 0.02),
+    # one expert: every token takes it, the gate is exactly 1
+    "f32_e1_k1": W("f32_e1_k1", 300, 128, 1, 1, 256, None, "f32"),
 }
 
 
