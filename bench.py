@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--ep", type=int, default=8,
                    help="ranks of the expert placement in the routing record (contiguous)")
     p.add_argument("--ranks-per-node", type=int, default=8)
+    p.add_argument("--graph", action="store_true",
+                   help="time replays of a HIP graph that captured one moe_layer call")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a device copy of known size (for rocprofv3 --pmc scaling)")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -226,6 +228,16 @@ def main():
     for _ in range(args.warmup):
         lay(*args_l)
     torch.cuda.synchronize()
+    run_step = lambda: lay(*args_l)  # noqa: E731
+    if args.graph:  # the same launches, replayed from a captured HIP graph
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            lay(*args_l)
+        run_step = graph.replay
+        for _ in range(args.warmup):
+            run_step()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
 
     # ---- timed region: exactly K moe_layer calls ------------------------------------------
     K = args.steps
@@ -234,7 +246,7 @@ def main():
     wall0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(K):
-        lay(*args_l)
+        run_step()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -346,7 +358,8 @@ def main():
                    "dispatch": "pad_to_capacity" if args.pad else "packed",
                    "drop_order": "slot_major" if args.slot_major else "token_major",
                    "bias": "selection_only" if args.bias_selection_only else "logits",
-                   "groups": [G, M] if G > 1 else None},
+                   "groups": [G, M] if G > 1 else None,
+                   "launch": "hip_graph_replay" if args.graph else "stream"},
         "roofline": roof,
         "layer_roofline_frac": round(layer_frac, 4),
         "step_ms_p50_p95_p99": [round(percentile(step_ms, q), 4) for q in (0.5, 0.95, 0.99)],

@@ -449,3 +449,38 @@ def test_device_generator_matches_host():
     for name in ("x", "w_gate", "w_down"):
         dev = to_host(mi.device_tensor(w, name))
         assert np.array_equal(dev, mi.host_tensor_f32(w, name))
+
+
+# ------------------------------------------------------------------------------- graphs
+@pytest.mark.parametrize("name,flags", [("bf16_e8_zipf_drops", 0), ("bf16_e256_k8_drops", 0),
+                                        ("bf16_e8_zipf_drops", moe.MOE_FLAG_PAD_TO_CAPACITY)])
+def test_layer_graph_replay_matches_eager(name, flags):
+    # moe_layer only enqueues kernels (no allocation, memset or host synchronisation), so a
+    # captured HIP graph replays it; every replay, with eager work of the program between
+    # replays, must reproduce the eager result bit for bit
+    w = SMALL[name]
+    d_in = device_inputs(w)
+    C = moe.capacity(w.T, w.k, w.E, w.capacity_factor)
+    s = moe.shape(w.T, w.d, w.E, w.k, w.F, C, moe.MOE_BF16, flags=flags)
+    args = (d_in["x"], d_in["w_router"], d_in["b_router"], d_in["w_gate"], d_in["w_up"],
+            d_in["w_down"])
+    eager = moe.MoELayer(s)
+    eager(*args)
+    torch.cuda.synchronize()
+    lay = moe.MoELayer(s)
+    lay(*args)  # warm-up outside the capture (kernel attributes are set on first use)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lay(*args)
+    for rep in range(3):
+        lay.out.fill_(0)
+        lay.routed_counts.fill_(-1)
+        eager(*args)  # eager work of the program between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lay.out, eager.out), f"replay {rep}"
+        assert torch.equal(lay.routed_counts, eager.routed_counts)
+        assert torch.equal(lay.drops, eager.drops)
+        assert torch.equal(lay.view("dest_row"), eager.view("dest_row"))
