@@ -61,6 +61,9 @@ def parse():
                    help="time replays of a HIP graph that captured one moe_layer call")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a device copy of known size (for rocprofv3 --pmc scaling)")
+    p.add_argument("--summarize-clock", metavar="GRBM_DIR",
+                   help="print each kernel's average shader clock from a rocprofv3 run with "
+                        "--pmc GRBM_COUNT --kernel-trace (GRBM_COUNT summed over the XCDs)")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                         "script into profiles/traffic_<workload>.json and exit")
@@ -123,6 +126,47 @@ def summarize_traffic(fetch_dir, write_dir, workload):
         out["kernel"] = gate_up[0]["Kernel_Name"][:120]
     out["traffic_bytes"] = out["fetch_bytes_scaled"] + out["write_bytes_scaled"]
     return out
+
+
+def summarize_clock(d):
+    """Median duration and average shader clock per kernel: GRBM_COUNT counts GPU clocks
+    on every XCD while a dispatch runs, so clock = GRBM_COUNT / XCDs / duration."""
+    import csv
+    import glob
+    import statistics as st
+
+    def rows(pattern):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pattern), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    agents = [r for r in rows("*agent_info.csv") if r.get("Name", "").startswith("gfx")]
+    if not agents:
+        raise SystemExit(f"no GPU agent in {d}")
+    n_xcc = int(agents[0]["Num_Xcc"])
+    span = {r["Dispatch_Id"]: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            for r in rows("*kernel_trace.csv")}
+    per = {}
+    for r in rows("*counter_collection.csv"):
+        if r["Counter_Name"] != "GRBM_COUNT" or r["Dispatch_Id"] not in span:
+            continue
+        ns = span[r["Dispatch_Id"]]
+        if ns <= 0:
+            continue
+        name = r["Kernel_Name"]
+        if "prefill_gemm_kernel" in name:
+            name = "prefill_gemm_kernel (" + (
+                "down" if "Lb0E" in name or "false" in name else "gate/up+SwiGLU") + ")"
+        else:
+            name = name.split("(")[0].split("<")[0].replace("void ", "")
+        per.setdefault(name, []).append((ns, float(r["Counter_Value"]) / n_xcc / ns))
+    out = []
+    for name, v in sorted(per.items(), key=lambda kv: -sum(a for a, _ in kv[1])):
+        out.append({"kernel": name, "dispatches": len(v),
+                    "median_us": round(st.median(a for a, _ in v) / 1e3, 1),
+                    "clock_ghz": round(st.median(c for _, c in v), 3)})
+    return {"xcds": n_xcc, "kernels": out}
 
 
 def traffic_for(workload):
@@ -188,6 +232,9 @@ def _cpu_model() -> str:
 
 def main():
     args = parse()
+    if args.summarize_clock:
+        print(json.dumps(summarize_clock(args.summarize_clock), indent=1))
+        return
     if args.summarize_traffic:
         t = summarize_traffic(*args.summarize_traffic, args.workload)
         path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
@@ -197,7 +244,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU's share of the MoE layer (expert parallel size 1); "
-              "multi-GPU runs are not part of this build.", file=sys.stderr)
+              "it does not run on several GPUs.", file=sys.stderr)
         sys.exit(2)
     build_if_missing()
     import numpy as np

@@ -1,0 +1,73 @@
+# Host logic of bench.py's rocprofv3 summaries, on small synthetic CSV files in the layout
+# rocprofv3 writes (agent info, kernel trace, counter collection).
+import csv
+import importlib.util
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GATE_UP = "void moe::prefill_gemm_kernel<__bf16, true, moe::PrefillTileT<128, 2, 320>>(x)"
+DOWN = "void moe::prefill_gemm_kernel<__bf16, false, moe::PrefillTileT<128, 2, 320>>(x)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _write(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_clock_summary(bench, tmp_path):
+    _write(tmp_path / "run_agent_info.csv",
+           [{"Name": "AMD EPYC", "Cu_Count": "16", "Num_Xcc": "1"},
+            {"Name": "gfx950", "Cu_Count": "256", "Num_Xcc": "8"}])
+    # dispatch 1: 1 ms at 1.7 GHz on 8 XCDs; 2: 0.5 ms at 2.4 GHz; 3: 2 ms at 1.8 GHz
+    trace = [{"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Start_Timestamp": "0", "End_Timestamp": "1000000"},
+             {"Dispatch_Id": "2", "Kernel_Name": DOWN, "Start_Timestamp": "0", "End_Timestamp": "500000"},
+             {"Dispatch_Id": "3", "Kernel_Name": GATE_UP, "Start_Timestamp": "0", "End_Timestamp": "2000000"}]
+    _write(tmp_path / "run_kernel_trace.csv", trace)
+    cc = [{"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Counter_Name": "GRBM_COUNT", "Counter_Value": str(1.7e6 * 8)},
+          {"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": "1"},
+          {"Dispatch_Id": "2", "Kernel_Name": DOWN, "Counter_Name": "GRBM_COUNT", "Counter_Value": str(2.4e6 / 2 * 8)},
+          {"Dispatch_Id": "3", "Kernel_Name": GATE_UP, "Counter_Name": "GRBM_COUNT", "Counter_Value": str(1.8e6 * 2 * 8)}]
+    _write(tmp_path / "run_counter_collection.csv", cc)
+    out = bench.summarize_clock(str(tmp_path))
+    assert out["xcds"] == 8
+    by = {k["kernel"]: k for k in out["kernels"]}
+    gu = by["prefill_gemm_kernel (gate/up+SwiGLU)"]
+    assert gu["dispatches"] == 2 and gu["median_us"] == 1500.0
+    assert gu["clock_ghz"] == pytest.approx(1.75)
+    dn = by["prefill_gemm_kernel (down)"]
+    assert dn["clock_ghz"] == pytest.approx(2.4) and dn["median_us"] == 500.0
+    # the kernel with the most total time comes first
+    assert out["kernels"][0]["kernel"] == "prefill_gemm_kernel (gate/up+SwiGLU)"
+
+
+def test_traffic_summary(bench, tmp_path):
+    kib_copy = bench.COPY_BYTES / 1024 * 0.5  # the counter reads half the copy's bytes
+    for counter, sub, gate_kib in (("FETCH_SIZE", "fetch", [100.0, 300.0, 200.0]),
+                                   ("WRITE_SIZE", "write", [50.0, 50.0, 50.0])):
+        d = tmp_path / sub
+        d.mkdir()
+        rows = [{"Kernel_Name": COPY, "Counter_Name": counter, "Counter_Value": str(kib_copy)},
+                {"Kernel_Name": COPY, "Counter_Name": counter, "Counter_Value": "4.0"},
+                {"Kernel_Name": DOWN, "Counter_Name": counter, "Counter_Value": "9999.0"}]
+        rows += [{"Kernel_Name": GATE_UP, "Counter_Name": counter, "Counter_Value": str(v)}
+                 for v in gate_kib]
+        _write(d / "run_counter_collection.csv", rows)
+    out = bench.summarize_traffic(str(tmp_path / "fetch"), str(tmp_path / "write"), "wl")
+    assert out["fetch_copy_factor"] == pytest.approx(0.5)
+    # median 200 KiB, scaled by 1 / 0.5; the down GEMM's rows are not counted
+    assert out["fetch_bytes_scaled"] == pytest.approx(200 * 1024 * 2)
+    assert out["write_bytes_scaled"] == pytest.approx(50 * 1024 * 2)
+    assert out["traffic_bytes"] == pytest.approx((200 + 50) * 1024 * 2)
