@@ -61,9 +61,11 @@ def parse():
                    help="time replays of a HIP graph that captured one moe_layer call")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a device copy of known size (for rocprofv3 --pmc scaling)")
-    p.add_argument("--summarize-clock", metavar="GRBM_DIR",
-                   help="print each kernel's average shader clock from a rocprofv3 run with "
-                        "--pmc GRBM_COUNT --kernel-trace (GRBM_COUNT summed over the XCDs)")
+    p.add_argument("--summarize-counters", metavar="PMC_DIR",
+                   help="per kernel of a rocprofv3 --pmc ... --kernel-trace run: shader clock "
+                        "(GRBM_COUNT), MFMA busy share (SQ_VALU_MFMA_BUSY_CYCLES over "
+                        "GRBM_GUI_ACTIVE) and bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16), "
+                        "for whichever of these counters the run holds")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                         "script into profiles/traffic_<workload>.json and exit")
@@ -128,9 +130,14 @@ def summarize_traffic(fetch_dir, write_dir, workload):
     return out
 
 
-def summarize_clock(d):
-    """Median duration and average shader clock per kernel: GRBM_COUNT counts GPU clocks
-    on every XCD while a dispatch runs, so clock = GRBM_COUNT / XCDs / duration."""
+def summarize_counters(d):
+    """Per kernel, medians over its dispatches of the derived figures the run's counters
+    allow.  GRBM_COUNT and GRBM_GUI_ACTIVE count GPU clocks on every XCD (rocprofv3 reports
+    the sum), SQ_VALU_MFMA_BUSY_CYCLES counts busy cycles of every SIMD's MFMA unit, and
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 counts bf16 MFMA work in units of 512 flops:
+        clock_ghz     = GRBM_COUNT / XCDs / duration
+        mfma_busy_pct = 100 * SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs * SIMDs)
+        mfma_tflops   = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16 / duration."""
     import csv
     import glob
     import statistics as st
@@ -144,29 +151,47 @@ def summarize_clock(d):
     agents = [r for r in rows("*agent_info.csv") if r.get("Name", "").startswith("gfx")]
     if not agents:
         raise SystemExit(f"no GPU agent in {d}")
-    n_xcc = int(agents[0]["Num_Xcc"])
+    n_xcc, n_simd = int(agents[0]["Num_Xcc"]), int(agents[0]["Simd_Count"])
     span = {r["Dispatch_Id"]: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
             for r in rows("*kernel_trace.csv")}
-    per = {}
+    disp = {}
     for r in rows("*counter_collection.csv"):
-        if r["Counter_Name"] != "GRBM_COUNT" or r["Dispatch_Id"] not in span:
+        did = r["Dispatch_Id"]
+        if did not in span or span[did] <= 0:
             continue
-        ns = span[r["Dispatch_Id"]]
-        if ns <= 0:
-            continue
-        name = r["Kernel_Name"]
+        e = disp.setdefault(did, {"name": r["Kernel_Name"], "ns": span[did]})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+
+    def short(name):
         if "prefill_gemm_kernel" in name:
-            name = "prefill_gemm_kernel (" + (
+            return "prefill_gemm_kernel (" + (
                 "down" if "Lb0E" in name or "false" in name else "gate/up+SwiGLU") + ")"
-        else:
-            name = name.split("(")[0].split("<")[0].replace("void ", "")
-        per.setdefault(name, []).append((ns, float(r["Counter_Value"]) / n_xcc / ns))
+        return name.split("(")[0].split("<")[0].replace("void ", "")
+
+    per = {}
+    for e in disp.values():
+        ns = e["ns"]
+        f = {"ns": ns}
+        if "GRBM_COUNT" in e:
+            f["clock_ghz"] = e["GRBM_COUNT"] / n_xcc / ns
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in e and e.get("GRBM_GUI_ACTIVE"):
+            f["mfma_busy_pct"] = (100.0 * e["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                  (e["GRBM_GUI_ACTIVE"] / n_xcc * n_simd))
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in e:
+            f["mfma_tflops"] = 512.0 * e["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / ns / 1e3
+            f["mfma_gflop_per_dispatch"] = 512.0 * e["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / 1e9
+        per.setdefault(short(e["name"]), []).append(f)
     out = []
-    for name, v in sorted(per.items(), key=lambda kv: -sum(a for a, _ in kv[1])):
-        out.append({"kernel": name, "dispatches": len(v),
-                    "median_us": round(st.median(a for a, _ in v) / 1e3, 1),
-                    "clock_ghz": round(st.median(c for _, c in v), 3)})
-    return {"xcds": n_xcc, "kernels": out}
+    for name, v in sorted(per.items(), key=lambda kv: -sum(f["ns"] for f in kv[1])):
+        k = {"kernel": name, "dispatches": len(v),
+             "median_us": round(st.median(f["ns"] for f in v) / 1e3, 1)}
+        for key, nd in (("clock_ghz", 3), ("mfma_busy_pct", 1), ("mfma_tflops", 1),
+                        ("mfma_gflop_per_dispatch", 2)):
+            vals = [f[key] for f in v if key in f]
+            if vals:
+                k[key] = round(st.median(vals), nd)
+        out.append(k)
+    return {"xcds": n_xcc, "simds": n_simd, "kernels": out}
 
 
 def traffic_for(workload):
@@ -232,8 +257,8 @@ def _cpu_model() -> str:
 
 def main():
     args = parse()
-    if args.summarize_clock:
-        print(json.dumps(summarize_clock(args.summarize_clock), indent=1))
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
         return
     if args.summarize_traffic:
         t = summarize_traffic(*args.summarize_traffic, args.workload)

@@ -32,7 +32,7 @@ MOE_FLAG_BIAS_SELECTION_ONLY = 4
 
 WS_REGIONS = ["logits", "topk_idx", "topk_w", "routed", "kept", "offsets", "src_token",
               "dest_row", "drops", "status", "tile_hist", "tile_base", "sched", "x_perm", "h",
-              "y_perm"]
+              "y_perm", "down_acc"]
 
 
 class MoeShape(ctypes.Structure):

@@ -27,6 +27,7 @@
 //   - Block order: blocks are dealt round-robin to the 8 XCDs; the logical tile index is
 //     remapped so each XCD walks a contiguous range in which neighbouring tiles share the
 //     A rows (same m-tile) and the B rows (same n-group), keeping both in that XCD's L2.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -179,8 +180,9 @@ __device__ inline void wait_vm_barrier() {
 template <class T, bool SWIGLU, class P>
 __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     const T* __restrict__ A, const int32_t* __restrict__ a_rows, const T* __restrict__ B0,
-    const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C, int K, int N_out,
-    int e, int m_begin, int m_end, int nt, lds_char* __restrict__ a0, lds_char* __restrict__ a1,
+    const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C,
+    float* __restrict__ Cacc, int K, int N_out, int e, int m_begin, int m_end, int nt,
+    int k_first, int k_steps, lds_char* __restrict__ a0, lds_char* __restrict__ a1,
     lds_char* __restrict__ a2, lds_char* __restrict__ b0, lds_char* __restrict__ b1,
     lds_char* __restrict__ b2, lds_char* __restrict__ b3) {
   constexpr int BN = SWIGLU ? P::BNW / 2 : P::BNW;
@@ -245,7 +247,8 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   const int b_frag = (wn * kNG * 32 + frag_row) * P::kRowBytes;
   const int swz = P::swz(frag_row);
 
-  const int KT = (int)(row_bytes / P::kRowBytes);
+  // stages k_first .. k_first + k_steps - 1 of the reduction (all of it, or one half)
+  const int KT = k_steps;
   constexpr int SA = P::kAStages, SB = P::kBStages;
   constexpr int DA = SA - 1, DB = SB - 1;  // stages of each ring in flight ahead
   constexpr int nA = P::kALoads, nB = P::kBLoads;
@@ -268,7 +271,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // stage (k offset clamped, always in bounds) into a buffer nobody reads again, so every
   // step issues the same number of loads and the wait count is a constant.
   auto dma = [&](int i, int kt, lds_char* buf) {
-    const uint32_t koff = (uint32_t)min(kt, KT - 1) * P::kRowBytes;
+    const uint32_t koff = (uint32_t)(k_first + min(kt, KT - 1)) * P::kRowBytes;
     const int blk = (i < nA ? i : i - nA) * P::kDmaWaves;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(base[P::template kind_of<SWIGLU>(i)]),
                                              buf + dma_lds + blk * 1024, 16, voff[i], koff, 0,
@@ -363,7 +366,10 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
           v = silu_f32(acc[i][j][q]) * acc[i][j + NOUT][q];
         else
           v = acc[i][j][q];
-        crow[j * 32] = Elt<T>::from_f32(v);
+        if (!SWIGLU && Cacc)  // one half of a split reduction: add into the fp32 sums
+          unsafeAtomicAdd(Cacc + (int64_t)row * N_out + col0 + j * 32, v);
+        else
+          crow[j * 32] = Elt<T>::from_f32(v);
       }
     }
   }
@@ -373,37 +379,45 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
 template <class T, bool SWIGLU, class P>
 __device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
     const T* __restrict__ A, const int32_t* __restrict__ a_rows, const T* __restrict__ B0,
-    const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C, int K, int N_out,
-    int e, int m_begin, int m_end, int nt, lds_char* base) {
+    const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C,
+    float* __restrict__ Cacc, int K, int N_out, int e, int m_begin, int m_end, int nt,
+    int k_first, int k_steps, lds_char* base) {
   constexpr int SA = P::kABytes, SB = P::kBBytes;
   lds_char* bb = base + P::kAStages * SA;
   // buffers past a ring's stage count are never used
-  prefill_gemm_body<T, SWIGLU, P>(A, a_rows, B0, B1, b_expert_stride, C, K, N_out, e, m_begin,
-                                  m_end, nt, base, base + SA, base + (P::kAStages > 2 ? 2 * SA : 0),
-                                  bb, bb + SB, bb + (P::kBStages > 2 ? 2 * SB : 0),
+  prefill_gemm_body<T, SWIGLU, P>(A, a_rows, B0, B1, b_expert_stride, C, Cacc, K, N_out, e,
+                                  m_begin, m_end, nt, k_first, k_steps, base, base + SA,
+                                  base + (P::kAStages > 2 ? 2 * SA : 0), bb, bb + SB,
+                                  bb + (P::kBStages > 2 ? 2 * SB : 0),
                                   bb + (P::kBStages > 3 ? 3 * SB : 0));
 }
 
-// One block per (m-tile, n-tile).  Blocks are dealt round-robin to the 8 XCDs; the logical
-// tile index is remapped so each XCD walks a contiguous range of logical tiles, n fastest
-// within groups of group_n n-tiles.  An m-tile with at most PT::BM rows (an expert's last,
-// partly filled tile) runs the shorter tile PT with the same weight columns: fewer loads
-// and MFMAs instead of a full tile of mostly clamped rows.
+// One block per (m-tile, n-tile), or per (m-tile, n-tile, half of the reduction) when the
+// reduction is split in ksplit = 2 halves (then the halves add their fp32 partial sums into
+// Cacc, which must be zero before the launch: with exactly two addends on +0.0 the sum is
+// the same in either order).  Blocks are dealt round-robin to the 8 XCDs; the logical tile
+// index is remapped so each XCD walks a contiguous range of logical tiles, n fastest within
+// groups of group_n n-tiles.  An m-tile with at most PT::BM rows (an expert's last, partly
+// filled tile) runs the shorter tile PT with the same weight columns: fewer loads and MFMAs
+// instead of a full tile of mostly clamped rows.
 template <class T, bool SWIGLU, class P, class PT>
 __global__ void __launch_bounds__(P::kThreads)
 prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
                     const T* __restrict__ B0, const T* __restrict__ B1,
-                    int64_t b_expert_stride, T* __restrict__ C, int K,
-                    int N_out, const int32_t* __restrict__ offsets,
+                    int64_t b_expert_stride, T* __restrict__ C, float* __restrict__ Cacc,
+                    int K, int N_out, const int32_t* __restrict__ offsets,
                     const int32_t* __restrict__ table, int m_tiles_max, int n_tiles,
-                    int group_n, int grid_logical) {
+                    int group_n, int grid_logical, int ksplit) {
   static_assert(PT::BNW == P::BNW && PT::kThreads == P::kThreads && PT::BM <= P::BM,
                 "the shorter tile shares the n-tiling and the block size");
   extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
   const int bid = blockIdx.x;
   const int per_xcd = gridDim.x >> 3;
-  const int logical = (bid & 7) * per_xcd + (bid >> 3);
-  if (logical >= grid_logical) return;
+  const int logical_all = (bid & 7) * per_xcd + (bid >> 3);
+  if (logical_all >= grid_logical * ksplit) return;
+  const int half = logical_all / grid_logical;
+  const int logical = logical_all - half * grid_logical;
+  const int k_steps = K * (int)sizeof(T) / P::kRowBytes / ksplit;
   const int per_group = m_tiles_max * group_n;
   const int grp = logical / per_group, rem = logical - grp * per_group;
   const int mt = rem / group_n, nt = grp * group_n + (rem - (rem / group_n) * group_n);
@@ -414,11 +428,33 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
   const int m_end = offsets[e + 1];
   lds_char* base = (lds_char*)smem_dyn;
   if (PT::BM < P::BM && m_end - m_begin <= PT::BM)
-    prefill_gemm_tile<T, SWIGLU, PT>(A, a_rows, B0, B1, b_expert_stride, C, K, N_out, e,
-                                     m_begin, m_end, nt, base);
+    prefill_gemm_tile<T, SWIGLU, PT>(A, a_rows, B0, B1, b_expert_stride, C, Cacc, K, N_out,
+                                     e, m_begin, m_end, nt, half * k_steps, k_steps, base);
   else
-    prefill_gemm_tile<T, SWIGLU, P>(A, a_rows, B0, B1, b_expert_stride, C, K, N_out, e,
-                                    m_begin, m_end, nt, base);
+    prefill_gemm_tile<T, SWIGLU, P>(A, a_rows, B0, B1, b_expert_stride, C, Cacc, K, N_out, e,
+                                    m_begin, m_end, nt, half * k_steps, k_steps, base);
+}
+
+// Rows [0, offsets[E]) of the fp32 partial sums of a split down GEMM: zeroed before it,
+// converted to the output type after it (d is a multiple of 4).
+__global__ void __launch_bounds__(256)
+zero_rows_f32_kernel(float* __restrict__ acc, const int32_t* __restrict__ offsets, int E,
+                     int64_t d) {
+  const int64_t n = (int64_t)offsets[E] * d / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    reinterpret_cast<f32x4*>(acc)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+template <class T>
+__global__ void __launch_bounds__(256)
+rows_from_f32_kernel(const float* __restrict__ acc, const int32_t* __restrict__ offsets, int E,
+                     int64_t d, T* __restrict__ y) {
+  const int64_t n = (int64_t)offsets[E] * d / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(acc)[i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) y[4 * i + c] = Elt<T>::from_f32(v[c]);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -426,7 +462,8 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
 // ---------------------------------------------------------------------------------------
 // Row-tile heights: decode-sized experts (mean <= 32 rows) stream weights with 64-row tiles;
 // prefill-sized ones use 256- or 320-row tiles.
-FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad) {
+FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad, int64_t d,
+                 int64_t F, int64_t elt) {
   FfnPlan p;
   p.small = pad ? C <= 32 : T * k <= 32 * E;
   if (p.small) {
@@ -448,6 +485,17 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad
   const int64_t m_cap = E * ((C + p.bm - 1) / p.bm);
   p.m_max = m_cap < m_max ? m_cap : m_max;
   if (p.m_max < 0) p.m_max = 0;
+  // Down GEMM with few, long tiles: when the tile count (at most m_max x ceil(d / 256)) just
+  // exceeds a multiple of the 256 CUs, half the chip idles through the last round.  Split
+  // the reduction in two halves when that fills the rounds clearly better (in whole-tile
+  // time, rounds(2t) / 2 <= 0.85 rounds(t)), the reduction has an even number of at least
+  // 32 128-byte stages, and the tiles are prefill tiles.
+  p.down_split = 1;
+  const int64_t tiles = p.m_max * ((d + 255) / 256), stages = F * elt / 128, cus = 256;
+  const auto rounds = [&](int64_t t) { return (t + cus - 1) / cus; };
+  if (!p.small && tiles > 0 && F * elt % 256 == 0 && stages >= 32 &&
+      100 * rounds(2 * tiles) <= 170 * rounds(tiles))
+    p.down_split = 2;
   return p;
 }
 
@@ -456,21 +504,22 @@ namespace {
 template <class T, bool SW, class P = PrefillTile, class PT = PrefillTailTile>
 hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const T* B1,
                           int64_t b_stride, T* C, int K, int N_out, const int32_t* offsets,
-                          const int32_t* table, int64_t m_max, hipStream_t s) {
+                          const int32_t* table, int64_t m_max, hipStream_t s,
+                          int ksplit = 1, float* c_acc = nullptr) {
   if (m_max <= 0) return hipSuccess;
   constexpr int BN = SW ? P::BNW / 2 : P::BNW;
   const int n_tiles = (N_out + BN - 1) / BN;
   const int group_n = n_tiles < 8 ? n_tiles : 8;
   const int n_groups = (n_tiles + group_n - 1) / group_n;
   const int64_t logical = m_max * group_n * n_groups;
-  const int64_t grid = (logical + 7) / 8 * 8;
+  const int64_t grid = (logical * ksplit + 7) / 8 * 8;
   const size_t lds = (size_t)(P::kLdsBytes > PT::kLdsBytes ? P::kLdsBytes : PT::kLdsBytes);
   hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW, P, PT>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   prefill_gemm_kernel<T, SW, P, PT><<<(unsigned)grid, P::kThreads, lds, s>>>(
-      A, a_rows, B0, B1, b_stride, C, K, N_out, offsets, table, (int)m_max, n_tiles, group_n,
-      (int)logical);
+      A, a_rows, B0, B1, b_stride, C, c_acc, K, N_out, offsets, table, (int)m_max, n_tiles,
+      group_n, (int)logical, ksplit);
   return hipGetLastError();
 }
 
@@ -508,19 +557,35 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
     return launch_prefill<T, false, DecodeDmaTile, DecodeDmaTile>(h, nullptr, (const T*)a.w_down, nullptr, stride, y,
                                                    (int)a.F, (int)a.d, a.offsets, a.sched,
                                                    p.m_max, s);
-  if (p.tile == 2)
-    return launch_prefill<T, false, PrefillTallTile>(h, nullptr, (const T*)a.w_down, nullptr, stride, y,
-                                                     (int)a.F, (int)a.d, a.offsets, a.sched,
-                                                     p.m_max, s);
-  return launch_prefill<T, false>(h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F,
-                                  (int)a.d, a.offsets, a.sched, p.m_max, s);
+  // split reduction: zero the fp32 sums of rows [0, N), let both halves add into them,
+  // then convert the rows to the output type
+  const int ks = p.down_split;
+  float* acc = ks > 1 ? a.down_acc : nullptr;
+  const unsigned ew_blocks = (unsigned)std::min<int64_t>((a.R * a.d / 4 + 255) / 256, 4096);
+  if (ks > 1) {
+    zero_rows_f32_kernel<<<ew_blocks, 256, 0, s>>>(acc, a.offsets, (int)a.E, a.d);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e =
+      p.tile == 2
+          ? launch_prefill<T, false, PrefillTallTile>(h, nullptr, (const T*)a.w_down, nullptr,
+                                                      stride, y, (int)a.F, (int)a.d, a.offsets,
+                                                      a.sched, p.m_max, s, ks, acc)
+          : launch_prefill<T, false>(h, nullptr, (const T*)a.w_down, nullptr, stride, y,
+                                     (int)a.F, (int)a.d, a.offsets, a.sched, p.m_max, s, ks,
+                                     acc);
+  if (e != hipSuccess || ks == 1) return e;
+  rows_from_f32_kernel<T><<<ew_blocks, 256, 0, s>>>(acc, a.offsets, (int)a.E, a.d, y);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_expert_ffn(const FfnArgs& a, int which, hipStream_t s) {
   if (a.R <= 0) return hipSuccess;
-  const FfnPlan p = ffn_plan(a.T, a.E, a.k, a.C, a.R, a.pad);
+  const FfnPlan p = ffn_plan(a.T, a.E, a.k, a.C, a.R, a.pad, a.d, a.F, a.dtype == 1 ? 2 : 4);
+  if (p.down_split > 1 && (which & 2) && !a.down_acc) return hipErrorInvalidValue;
   hipError_t err = launch_table(a, p, s);
   if (err != hipSuccess) return err;
   if (which & 1) {

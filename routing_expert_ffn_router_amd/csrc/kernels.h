@@ -53,14 +53,21 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 // S6-S7.  The grouped GEMMs run over a device-side tile table (expert, first row) of
 // row-tile height bm with at most m_max entries.
 struct FfnPlan {
-  bool small;     // decode-sized experts (weight streaming)
-  int tile;       // 0 decode, 1 prefill 256 rows, 2 prefill 320 rows
+  bool small;      // decode-sized experts (weight streaming)
+  int tile;        // 0 decode, 1 prefill 256 rows, 2 prefill 320 rows
   int bm;
-  int64_t m_max;  // upper bound on m-tiles over all experts
+  int64_t m_max;   // upper bound on m-tiles over all experts
+  int down_split;  // 1, or 2: the down GEMM splits its reduction in two halves
 };
-// pad: every expert holds exactly C rows (offsets e * C).
-FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad);
+// pad: every expert holds exactly C rows (offsets e * C).  d, F and the element size
+// decide whether the down GEMM splits its reduction.
+FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad, int64_t d,
+                 int64_t F, int64_t elt);
 inline int64_t ffn_table_ints(const FfnPlan& p) { return 1 + 2 * p.m_max; }
+// fp32 [R, d] partial sums of a split down GEMM (0 bytes when it does not split)
+inline int64_t ffn_down_acc_bytes(const FfnPlan& p, int64_t R, int64_t d) {
+  return p.down_split > 1 ? R * d * 4 : 0;
+}
 
 struct FfnArgs {
   int dtype;
@@ -76,6 +83,7 @@ struct FfnArgs {
   void* h;               // [R, F]
   int32_t* sched;        // ffn_table_ints() ints
   void* y_perm;          // [R, d]
+  float* down_acc;       // [R, d] fp32, used when the plan splits the down GEMM
 };
 // which: 1 = gate/up GEMM (x_perm -> h), 2 = down GEMM (h -> y_perm), 3 = both.  Each
 // call first rebuilds the tile table from `offsets`.

@@ -82,11 +82,13 @@ Layout make_layout(const moe_shape* s) {
   L.size[MOE_WS_STATUS] = 4;
   L.size[MOE_WS_TILE_HIST] = ntiles * E * 4;
   L.size[MOE_WS_TILE_BASE] = ntiles * E * 4;
-  L.size[MOE_WS_SCHED] =
-      moe::ffn_table_ints(moe::ffn_plan(T, E, k, eff_capacity(s), R, padded(s))) * 4;
+  const moe::FfnPlan plan =
+      moe::ffn_plan(T, E, k, eff_capacity(s), R, padded(s), s->d, s->F, b);
+  L.size[MOE_WS_SCHED] = moe::ffn_table_ints(plan) * 4;
   L.size[MOE_WS_X_PERM] = R * s->d * b;
   L.size[MOE_WS_H] = R * s->F * b;
   L.size[MOE_WS_Y_PERM] = R * s->d * b;
+  L.size[MOE_WS_DOWN_ACC] = moe::ffn_down_acc_bytes(plan, R, s->d);
   int64_t o = 0;
   for (int i = 0; i < MOE_WS_COUNT; ++i) {
     L.off[i] = o;
@@ -272,6 +274,7 @@ int expert_ffn_impl(const moe_shape* s, int which, const void* x_perm, const voi
   a.h = h;
   a.sched = region<int32_t>(ws, L, MOE_WS_SCHED);
   a.y_perm = y_perm;
+  a.down_acc = region<float>(ws, L, MOE_WS_DOWN_ACC);
   return hip_status(moe::launch_expert_ffn(a, which, st));
 }
 

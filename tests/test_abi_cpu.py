@@ -61,6 +61,32 @@ def test_max_rows_and_workspace():
     assert lay["y_perm"] - lay["h"] >= R * F * 2
 
 
+def _down_acc_bytes(s):
+    return moe.workspace_size(s) - moe.workspace_layout(s)["down_acc"]
+
+
+def test_down_split_region():
+    # The down GEMM splits its reduction when ceil(2t / 256) / 2 <= 0.85 ceil(t / 256) for
+    # t = m-tiles (upper bound) x ceil(d / 256), with an even number of >= 32 128-byte
+    # stages; then the workspace holds fp32 [R, d] partial sums (last region).
+    # Mixtral-8x22B-shaped, C = 640: t <= 16 x 24 = 384 (2 rounds), split 768 (3 half
+    # rounds = 1.5) -> splits.
+    s = moe.shape(2048, 6144, 8, 2, 16384, 640)
+    assert _down_acc_bytes(s) == 4096 * 6144 * 4
+    # Mixtral-8x7B-shaped: t <= 32 x 16 = 512 = 2 rounds exactly -> no split
+    assert _down_acc_bytes(moe.shape(4096, 4096, 8, 2, 14336, 1280)) == 0
+    # decode-sized experts stream weights: never split
+    assert _down_acc_bytes(moe.shape(256, 7168, 256, 8, 2048, 0)) == 0
+    # DeepSeek-V3 mixed batch: t = 256 x 28 = 28 rounds -> no split
+    assert _down_acc_bytes(moe.shape(8192, 7168, 256, 8, 2048, 256)) == 0
+    # a short reduction (F * 2 / 128 = 6 stages) does not split; a long one does
+    assert _down_acc_bytes(moe.shape(700, 256, 8, 2, 384, 219)) == 0
+    assert _down_acc_bytes(moe.shape(700, 256, 8, 2, 2048, 219)) == 1400 * 256 * 4
+    # fp32: 4-byte elements, F = 1024 is 32 stages; F = 896 is 28 -> none
+    assert _down_acc_bytes(moe.shape(600, 256, 4, 2, 1024, 300, moe.MOE_F32)) == 1200 * 256 * 4
+    assert _down_acc_bytes(moe.shape(600, 256, 4, 2, 896, 300, moe.MOE_F32)) == 0
+
+
 BAD_SHAPES = [
     (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
     (dict(k=9), moe.MOE_ERR_INVALID_ARG),

@@ -27,26 +27,33 @@ def _write(path, rows):
         w.writerows(rows)
 
 
-def test_clock_summary(bench, tmp_path):
+def test_counter_summary(bench, tmp_path):
     _write(tmp_path / "run_agent_info.csv",
-           [{"Name": "AMD EPYC", "Cu_Count": "16", "Num_Xcc": "1"},
-            {"Name": "gfx950", "Cu_Count": "256", "Num_Xcc": "8"}])
+           [{"Name": "AMD EPYC", "Cu_Count": "16", "Num_Xcc": "1", "Simd_Count": "0"},
+            {"Name": "gfx950", "Cu_Count": "256", "Num_Xcc": "8", "Simd_Count": "1024"}])
     # dispatch 1: 1 ms at 1.7 GHz on 8 XCDs; 2: 0.5 ms at 2.4 GHz; 3: 2 ms at 1.8 GHz
     trace = [{"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Start_Timestamp": "0", "End_Timestamp": "1000000"},
              {"Dispatch_Id": "2", "Kernel_Name": DOWN, "Start_Timestamp": "0", "End_Timestamp": "500000"},
              {"Dispatch_Id": "3", "Kernel_Name": GATE_UP, "Start_Timestamp": "0", "End_Timestamp": "2000000"}]
     _write(tmp_path / "run_kernel_trace.csv", trace)
+    # dispatch 1 also: MFMA units busy 60 % of the active clocks, 1.2e12 bf16 MFMA flops
     cc = [{"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Counter_Name": "GRBM_COUNT", "Counter_Value": str(1.7e6 * 8)},
-          {"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": "1"},
+          {"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": str(1.7e6 * 8)},
+          {"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES", "Counter_Value": str(0.6 * 1.7e6 * 1024)},
+          {"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Counter_Name": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "Counter_Value": str(1.2e12 / 512)},
           {"Dispatch_Id": "2", "Kernel_Name": DOWN, "Counter_Name": "GRBM_COUNT", "Counter_Value": str(2.4e6 / 2 * 8)},
           {"Dispatch_Id": "3", "Kernel_Name": GATE_UP, "Counter_Name": "GRBM_COUNT", "Counter_Value": str(1.8e6 * 2 * 8)}]
     _write(tmp_path / "run_counter_collection.csv", cc)
-    out = bench.summarize_clock(str(tmp_path))
-    assert out["xcds"] == 8
+    out = bench.summarize_counters(str(tmp_path))
+    assert out["xcds"] == 8 and out["simds"] == 1024
     by = {k["kernel"]: k for k in out["kernels"]}
     gu = by["prefill_gemm_kernel (gate/up+SwiGLU)"]
     assert gu["dispatches"] == 2 and gu["median_us"] == 1500.0
     assert gu["clock_ghz"] == pytest.approx(1.75)
+    # only dispatch 1 carries the MFMA counters
+    assert gu["mfma_busy_pct"] == pytest.approx(60.0)
+    assert gu["mfma_gflop_per_dispatch"] == pytest.approx(1200.0)
+    assert gu["mfma_tflops"] == pytest.approx(1200.0, rel=1e-3)  # 1.2e12 flop in 1 ms
     dn = by["prefill_gemm_kernel (down)"]
     assert dn["clock_ghz"] == pytest.approx(2.4) and dn["median_us"] == 500.0
     # the kernel with the most total time comes first
