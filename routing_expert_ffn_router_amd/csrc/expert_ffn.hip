@@ -177,11 +177,11 @@ __device__ inline void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <class T, bool SWIGLU, class P>
+template <class T, bool SWIGLU, class P, class OutT>
 __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     const T* __restrict__ A, const int32_t* __restrict__ a_rows, const T* __restrict__ B0,
-    const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C,
-    float* __restrict__ Cacc, int K, int N_out, int e, int m_begin, int m_end, int nt,
+    const T* __restrict__ B1, int64_t b_expert_stride, OutT* __restrict__ C,
+    const float* __restrict__ col_bias, float* __restrict__ Cacc, int K, int N_out, int e, int m_begin, int m_end, int nt,
     int k_first, int k_steps, lds_char* __restrict__ a0, lds_char* __restrict__ a1,
     lds_char* __restrict__ a2, lds_char* __restrict__ b0, lds_char* __restrict__ b1,
     lds_char* __restrict__ b2, lds_char* __restrict__ b3) {
@@ -357,7 +357,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
       const int row = m_begin + wm * P::MT * 32 + i * 32 + 8 * (q >> 2) + 4 * frag_half + (q & 3);
       if (row >= m_end) continue;
       const int col0 = nt * BN + wn * NOUT * 32 + frag_row;
-      T* crow = C + (int64_t)row * N_out + col0;
+      OutT* crow = C + (int64_t)row * N_out + col0;
 #pragma unroll
       for (int j = 0; j < NOUT; ++j) {
         if (col0 + j * 32 >= N_out) continue;
@@ -368,6 +368,8 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
           v = acc[i][j][q];
         if (!SWIGLU && Cacc)  // one half of a split reduction: add into the fp32 sums
           unsafeAtomicAdd(Cacc + (int64_t)row * N_out + col0 + j * 32, v);
+        else if constexpr (std::is_same<OutT, float>::value)  // fp32 output (router logits)
+          crow[j * 32] = col_bias ? v + col_bias[col0 + j * 32] : v;
         else
           crow[j * 32] = Elt<T>::from_f32(v);
       }
@@ -376,16 +378,17 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
 }
 
 // Stage buffers of tile P in the block's LDS, then its body.
-template <class T, bool SWIGLU, class P>
+template <class T, bool SWIGLU, class P, class OutT>
 __device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
     const T* __restrict__ A, const int32_t* __restrict__ a_rows, const T* __restrict__ B0,
-    const T* __restrict__ B1, int64_t b_expert_stride, T* __restrict__ C,
-    float* __restrict__ Cacc, int K, int N_out, int e, int m_begin, int m_end, int nt,
+    const T* __restrict__ B1, int64_t b_expert_stride, OutT* __restrict__ C,
+    const float* __restrict__ col_bias, float* __restrict__ Cacc, int K, int N_out, int e, int m_begin, int m_end, int nt,
     int k_first, int k_steps, lds_char* base) {
   constexpr int SA = P::kABytes, SB = P::kBBytes;
   lds_char* bb = base + P::kAStages * SA;
   // buffers past a ring's stage count are never used
-  prefill_gemm_body<T, SWIGLU, P>(A, a_rows, B0, B1, b_expert_stride, C, Cacc, K, N_out, e,
+  prefill_gemm_body<T, SWIGLU, P, OutT>(A, a_rows, B0, B1, b_expert_stride, C, col_bias, Cacc,
+                                        K, N_out, e,
                                   m_begin, m_end, nt, k_first, k_steps, base, base + SA,
                                   base + (P::kAStages > 2 ? 2 * SA : 0), bb, bb + SB,
                                   bb + (P::kBStages > 2 ? 2 * SB : 0),
@@ -400,14 +403,18 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
 // groups of group_n n-tiles.  An m-tile with at most PT::BM rows (an expert's last, partly
 // filled tile) runs the shorter tile PT with the same weight columns: fewer loads and MFMAs
 // instead of a full tile of mostly clamped rows.
-template <class T, bool SWIGLU, class P, class PT>
+//
+// Dense mode (table == nullptr, used for the router logits): one operand A of dense_rows
+// rows and one B of N_out rows, m-tile mt covering rows mt * P::BM ...
+template <class T, bool SWIGLU, class P, class PT, class OutT>
 __global__ void __launch_bounds__(P::kThreads)
 prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
                     const T* __restrict__ B0, const T* __restrict__ B1,
-                    int64_t b_expert_stride, T* __restrict__ C, float* __restrict__ Cacc,
-                    int K, int N_out, const int32_t* __restrict__ offsets,
+                    int64_t b_expert_stride, OutT* __restrict__ C,
+                    const float* __restrict__ col_bias, float* __restrict__ Cacc, int K,
+                    int N_out, const int32_t* __restrict__ offsets,
                     const int32_t* __restrict__ table, int m_tiles_max, int n_tiles,
-                    int group_n, int grid_logical, int ksplit) {
+                    int group_n, int grid_logical, int ksplit, int dense_rows) {
   static_assert(PT::BNW == P::BNW && PT::kThreads == P::kThreads && PT::BM <= P::BM,
                 "the shorter tile shares the n-tiling and the block size");
   extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
@@ -422,16 +429,26 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
   const int grp = logical / per_group, rem = logical - grp * per_group;
   const int mt = rem / group_n, nt = grp * group_n + (rem - (rem / group_n) * group_n);
   if (nt >= n_tiles) return;
-  if (mt >= table[0]) return;
-  const int e = table[1 + 2 * mt];
-  const int m_begin = table[2 + 2 * mt];
-  const int m_end = offsets[e + 1];
+  int e, m_begin, m_end;
+  if (table) {
+    if (mt >= table[0]) return;
+    e = table[1 + 2 * mt];
+    m_begin = table[2 + 2 * mt];
+    m_end = offsets[e + 1];
+  } else {
+    e = 0;
+    m_begin = mt * P::BM;
+    m_end = min(dense_rows, m_begin + P::BM);
+    if (m_begin >= m_end) return;
+  }
   lds_char* base = (lds_char*)smem_dyn;
   if (PT::BM < P::BM && m_end - m_begin <= PT::BM)
-    prefill_gemm_tile<T, SWIGLU, PT>(A, a_rows, B0, B1, b_expert_stride, C, Cacc, K, N_out,
+    prefill_gemm_tile<T, SWIGLU, PT, OutT>(A, a_rows, B0, B1, b_expert_stride, C, col_bias,
+                                           Cacc, K, N_out,
                                      e, m_begin, m_end, nt, half * k_steps, k_steps, base);
   else
-    prefill_gemm_tile<T, SWIGLU, P>(A, a_rows, B0, B1, b_expert_stride, C, Cacc, K, N_out, e,
+    prefill_gemm_tile<T, SWIGLU, P, OutT>(A, a_rows, B0, B1, b_expert_stride, C, col_bias, Cacc,
+                                          K, N_out, e,
                                     m_begin, m_end, nt, half * k_steps, k_steps, base);
 }
 
@@ -501,11 +518,12 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad
 
 namespace {
 
-template <class T, bool SW, class P = PrefillTile, class PT = PrefillTailTile>
+template <class T, bool SW, class P = PrefillTile, class PT = PrefillTailTile, class OutT = T>
 hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const T* B1,
-                          int64_t b_stride, T* C, int K, int N_out, const int32_t* offsets,
+                          int64_t b_stride, OutT* C, int K, int N_out, const int32_t* offsets,
                           const int32_t* table, int64_t m_max, hipStream_t s,
-                          int ksplit = 1, float* c_acc = nullptr) {
+                          int ksplit = 1, float* c_acc = nullptr,
+                          const float* col_bias = nullptr, int dense_rows = 0) {
   if (m_max <= 0) return hipSuccess;
   constexpr int BN = SW ? P::BNW / 2 : P::BNW;
   const int n_tiles = (N_out + BN - 1) / BN;
@@ -514,12 +532,12 @@ hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const 
   const int64_t logical = m_max * group_n * n_groups;
   const int64_t grid = (logical * ksplit + 7) / 8 * 8;
   const size_t lds = (size_t)(P::kLdsBytes > PT::kLdsBytes ? P::kLdsBytes : PT::kLdsBytes);
-  hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW, P, PT>,
+  hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW, P, PT, OutT>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  prefill_gemm_kernel<T, SW, P, PT><<<(unsigned)grid, P::kThreads, lds, s>>>(
-      A, a_rows, B0, B1, b_stride, C, c_acc, K, N_out, offsets, table, (int)m_max, n_tiles,
-      group_n, (int)logical, ksplit);
+  prefill_gemm_kernel<T, SW, P, PT, OutT><<<(unsigned)grid, P::kThreads, lds, s>>>(
+      A, a_rows, B0, B1, b_stride, C, col_bias, c_acc, K, N_out, offsets, table, (int)m_max,
+      n_tiles, group_n, (int)logical, ksplit, dense_rows);
   return hipGetLastError();
 }
 
@@ -581,6 +599,27 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
 }
 
 }  // namespace
+
+// Router logits L = x w^T (+ b) through the same pipeline in dense mode: 64-token x
+// 256-expert tiles, fp32 output with the bias added in the epilogue.  Used when there are
+// enough tiles to spread over the CUs.
+bool router_gemm_suits(int64_t T, int64_t E) {
+  const int64_t tiles = ((T + DecodeDmaTile::BM - 1) / DecodeDmaTile::BM) *
+                        ((E + DecodeDmaTile::BNW - 1) / DecodeDmaTile::BNW);
+  return E >= 64 && tiles >= 96;
+}
+
+hipError_t launch_router_gemm(int dtype, const void* x, const void* w, const float* b,
+                              float* logits, int64_t T, int64_t d, int64_t E, hipStream_t s) {
+  const int64_t m_tiles = (T + DecodeDmaTile::BM - 1) / DecodeDmaTile::BM;
+  if (dtype == 1)
+    return launch_prefill<bf16, false, DecodeDmaTile, DecodeDmaTile, float>(
+        (const bf16*)x, nullptr, (const bf16*)w, nullptr, 0, logits, (int)d, (int)E, nullptr,
+        nullptr, m_tiles, s, 1, nullptr, b, (int)T);
+  return launch_prefill<float, false, DecodeDmaTile, DecodeDmaTile, float>(
+      (const float*)x, nullptr, (const float*)w, nullptr, 0, logits, (int)d, (int)E, nullptr,
+      nullptr, m_tiles, s, 1, nullptr, b, (int)T);
+}
 
 hipError_t launch_expert_ffn(const FfnArgs& a, int which, hipStream_t s) {
   if (a.R <= 0) return hipSuccess;

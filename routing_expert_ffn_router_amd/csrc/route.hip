@@ -35,10 +35,11 @@ hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
 // straight from global memory (no LDS staging); its W waves split the reduction axis in
 // 128-byte steps (wave w takes steps w, w + W, ...), each wave loading its next step while
 // multiplying the current one, and their partial tiles are summed in LDS in wave order,
-// which keeps the result deterministic.  Per 128-byte step a lane loads 32 contiguous bytes of each of its MT
-// token rows and NT expert rows; both operands use the same k-chunk assignment (lane group
-// g takes chunks 2g and 2g + 1), so the products pair up.  Larger tiles cut the re-reads:
-// with many experts and tokens a 64 x 64 tile reads x E / 64 times and w T / 64 times.
+// which keeps the result deterministic.  Per 128-byte step a lane loads 32 contiguous bytes
+// of each of its MT token rows and NT expert rows; both operands use the same k-chunk
+// assignment (lane group g takes chunks 2g and 2g + 1), so the products pair up.  Each load
+// touches half of 16 cache lines, so shapes with many tokens and experts (enough 64 x 256
+// tiles to fill the CUs) go through the expert-GEMM pipeline instead.
 // grid = (ceil(T / (16 MT)), ceil(E / (16 NT))).
 // ---------------------------------------------------------------------------------------
 template <class T, int MT, int NT, int kRouterWaves>
@@ -139,13 +140,9 @@ hipError_t launch_router_tile(const T* x, const T* w, const float* b, float* log
 template <class T>
 hipError_t launch_router_typed(const T* x, const T* w, const float* b, float* logits,
                                int64_t T_, int64_t d, int64_t E, hipStream_t s) {
-  // The largest tile that still gives at least 512 blocks (two per CU): 64 x 64, then
-  // 16 x 64, else 16 x 16.
-  const int64_t t16 = (T_ + 15) / 16, t64 = (T_ + 63) / 64;
-  // The 64 x 64 tile runs 4 waves per block (one per SIMD, registers for two operand sets
-  // of 16 rows), the others 8.
-  if (E > 16 && t64 * ((E + 63) / 64) >= 512)
-    return launch_router_tile<T, 4, 4, 4>(x, w, b, logits, T_, d, E, s);
+  // 16 x 64 tiles when that still gives at least 512 blocks (two per CU), else 16 x 16
+  // (larger shapes take the GEMM pipeline, see launch_router_logits).
+  const int64_t t16 = (T_ + 15) / 16;
   if (E > 16 && t16 * ((E + 63) / 64) >= 512)
     return launch_router_tile<T, 1, 4, 8>(x, w, b, logits, T_, d, E, s);
   return launch_router_tile<T, 1, 1, 8>(x, w, b, logits, T_, d, E, s);
@@ -155,6 +152,9 @@ hipError_t launch_router_logits(int dtype, const void* x, const void* w, const f
                                 float* logits, int64_t T, int64_t d, int64_t E,
                                 hipStream_t s) {
   if (T == 0) return hipSuccess;
+  // many tokens and experts: full-line direct loads into LDS and 32x32 MFMA tiles (the
+  // expert-GEMM pipeline); the kernel below reads half cache lines per load
+  if (router_gemm_suits(T, E)) return launch_router_gemm(dtype, x, w, b, logits, T, d, E, s);
   if (dtype == 1)
     return launch_router_typed<bf16>((const bf16*)x, (const bf16*)w, b, logits, T, d, E, s);
   return launch_router_typed<float>((const float*)x, (const float*)w, b, logits, T, d, E, s);

@@ -121,12 +121,14 @@ def test_router_logits(name):
     assert err <= logits_tol(ref)
 
 
-@pytest.mark.parametrize("T,d,E,dtype", [(2048, 256, 1024, "bf16"), (2047, 128, 1024, "f32"),
-                                         (600, 256, 1000, "bf16"), (8192, 128, 64, "f32"),
-                                         (1000, 128, 512, "bf16")])
+@pytest.mark.parametrize("T,d,E,dtype", [(2048, 256, 1024, "bf16"), (2047, 128, 1000, "f32"),
+                                         (6100, 256, 64, "bf16"), (8192, 128, 72, "f32"),
+                                         (600, 256, 1000, "bf16"), (1000, 128, 512, "bf16"),
+                                         (300, 128, 40, "bf16"), (8200, 128, 40, "f32")])
 def test_router_logits_tile_shapes(T, d, E, dtype):
-    # sizes that select each router tile (64 x 64, 16 x 64, 16 x 16 tokens x experts),
-    # with ragged token and expert tails
+    # sizes that select each router path: the expert-GEMM pipeline in dense mode (64 x 256
+    # tiles, >= 96 of them; expert counts below, at and above one tile, ragged token
+    # tails), then the skinny kernel's 16 x 64 and 16 x 16 tiles
     log(f"router tiles T={T} d={d} E={E} {dtype}")
     rng = np.random.default_rng(T + E)
     x = rng.standard_normal((T, d)).astype(np.float32)
