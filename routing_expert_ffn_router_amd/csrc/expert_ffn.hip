@@ -182,7 +182,8 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     const T* __restrict__ A, const int32_t* __restrict__ a_rows, const T* __restrict__ B0,
     const T* __restrict__ B1, int64_t b_expert_stride, OutT* __restrict__ C,
     const float* __restrict__ col_bias, float* __restrict__ Cacc, int K, int N_out, int e, int m_begin, int m_end, int nt,
-    int k_first, int k_steps, lds_char* __restrict__ a0, lds_char* __restrict__ a1,
+    int k_first, int k_steps, bool stream_b, lds_char* __restrict__ a0,
+    lds_char* __restrict__ a1,
     lds_char* __restrict__ a2, lds_char* __restrict__ b0, lds_char* __restrict__ b1,
     lds_char* __restrict__ b2, lds_char* __restrict__ b3) {
   constexpr int BN = SWIGLU ? P::BNW / 2 : P::BNW;
@@ -270,12 +271,19 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // Direct load i of stage kt into its ring's buffer.  Stages past the end re-read the last
   // stage (k offset clamped, always in bounds) into a buffer nobody reads again, so every
   // step issues the same number of loads and the wait count is a constant.
+  // With stream_b the weight loads carry the non-temporal hint: the plan sets it when each
+  // weight line is read by about one tile, and then it keeps the streamed weights from
+  // displacing the activation rows the other tiles reuse.
   auto dma = [&](int i, int kt, lds_char* buf) {
     const uint32_t koff = (uint32_t)(k_first + min(kt, KT - 1)) * P::kRowBytes;
     const int blk = (i < nA ? i : i - nA) * P::kDmaWaves;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(base[P::template kind_of<SWIGLU>(i)]),
-                                             buf + dma_lds + blk * 1024, 16, voff[i], koff, 0,
-                                             0);
+    const auto rsrc = buffer_rsrc(base[P::template kind_of<SWIGLU>(i)]);
+    if (i >= nA && stream_b)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, buf + dma_lds + blk * 1024, 16, voff[i],
+                                               koff, 0, 2 /* non-temporal */);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, buf + dma_lds + blk * 1024, 16, voff[i],
+                                               koff, 0, 0);
   };
   auto dma_a = [&](int kt, lds_char* buf) {
     if (!issuer) return;
@@ -382,17 +390,15 @@ template <class T, bool SWIGLU, class P, class OutT>
 __device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
     const T* __restrict__ A, const int32_t* __restrict__ a_rows, const T* __restrict__ B0,
     const T* __restrict__ B1, int64_t b_expert_stride, OutT* __restrict__ C,
-    const float* __restrict__ col_bias, float* __restrict__ Cacc, int K, int N_out, int e, int m_begin, int m_end, int nt,
-    int k_first, int k_steps, lds_char* base) {
+    const float* __restrict__ col_bias, float* __restrict__ Cacc, int K, int N_out, int e,
+    int m_begin, int m_end, int nt, int k_first, int k_steps, bool stream_b, lds_char* base) {
   constexpr int SA = P::kABytes, SB = P::kBBytes;
   lds_char* bb = base + P::kAStages * SA;
   // buffers past a ring's stage count are never used
-  prefill_gemm_body<T, SWIGLU, P, OutT>(A, a_rows, B0, B1, b_expert_stride, C, col_bias, Cacc,
-                                        K, N_out, e,
-                                  m_begin, m_end, nt, k_first, k_steps, base, base + SA,
-                                  base + (P::kAStages > 2 ? 2 * SA : 0), bb, bb + SB,
-                                  bb + (P::kBStages > 2 ? 2 * SB : 0),
-                                  bb + (P::kBStages > 3 ? 3 * SB : 0));
+  prefill_gemm_body<T, SWIGLU, P, OutT>(
+      A, a_rows, B0, B1, b_expert_stride, C, col_bias, Cacc, K, N_out, e, m_begin, m_end, nt,
+      k_first, k_steps, stream_b, base, base + SA, base + (P::kAStages > 2 ? 2 * SA : 0), bb,
+      bb + SB, bb + (P::kBStages > 2 ? 2 * SB : 0), bb + (P::kBStages > 3 ? 3 * SB : 0));
 }
 
 // One block per (m-tile, n-tile), or per (m-tile, n-tile, half of the reduction) when the
@@ -414,7 +420,8 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
                     const float* __restrict__ col_bias, float* __restrict__ Cacc, int K,
                     int N_out, const int32_t* __restrict__ offsets,
                     const int32_t* __restrict__ table, int m_tiles_max, int n_tiles,
-                    int group_n, int grid_logical, int ksplit, int dense_rows) {
+                    int group_n, int grid_logical, int ksplit, int dense_rows,
+                    int stream_b) {
   static_assert(PT::BNW == P::BNW && PT::kThreads == P::kThreads && PT::BM <= P::BM,
                 "the shorter tile shares the n-tiling and the block size");
   extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
@@ -444,12 +451,12 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
   lds_char* base = (lds_char*)smem_dyn;
   if (PT::BM < P::BM && m_end - m_begin <= PT::BM)
     prefill_gemm_tile<T, SWIGLU, PT, OutT>(A, a_rows, B0, B1, b_expert_stride, C, col_bias,
-                                           Cacc, K, N_out,
-                                     e, m_begin, m_end, nt, half * k_steps, k_steps, base);
+                                           Cacc, K, N_out, e, m_begin, m_end, nt,
+                                           half * k_steps, k_steps, stream_b != 0, base);
   else
     prefill_gemm_tile<T, SWIGLU, P, OutT>(A, a_rows, B0, B1, b_expert_stride, C, col_bias, Cacc,
-                                          K, N_out, e,
-                                    m_begin, m_end, nt, half * k_steps, k_steps, base);
+                                          K, N_out, e, m_begin, m_end, nt, half * k_steps,
+                                          k_steps, stream_b != 0, base);
 }
 
 // Rows [0, offsets[E]) of the fp32 partial sums of a split down GEMM: zeroed before it,
@@ -486,6 +493,7 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad
   if (p.small) {
     p.tile = 0;
     p.bm = DecodeDmaTile::BM;
+    p.stream_b = true;  // a few rows per expert: every weight line is read by one tile
   } else {
     // Rows an expert will probably hold: a little above the mean, at most the capacity.
     // Take the tile height that needs fewer row tiles (each one re-reads the expert's
@@ -497,6 +505,11 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad
     const bool tall = t320 < t256 || (t320 == t256 && t320 * 320 < t256 * 256);
     p.tile = tall ? 2 : 1;
     p.bm = tall ? PrefillTallTile::BM : PrefillTile::BM;
+    // An expert's weight panel is re-read by each of its row tiles, through L2 while they
+    // run together.  With at most two row tiles per expert the weights are effectively
+    // streamed and take the non-temporal hint (measured: DeepSeek-V3 mixed batch -4 %,
+    // Mixtral-8x22B -3.5 %); with four (Mixtral-8x7B) the hint costs 7 %.
+    p.stream_b = (r + p.bm - 1) / p.bm <= 2;
   }
   int64_t m_max = (R + E * (p.bm - 1)) / p.bm;
   const int64_t m_cap = E * ((C + p.bm - 1) / p.bm);
@@ -523,7 +536,8 @@ hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const 
                           int64_t b_stride, OutT* C, int K, int N_out, const int32_t* offsets,
                           const int32_t* table, int64_t m_max, hipStream_t s,
                           int ksplit = 1, float* c_acc = nullptr,
-                          const float* col_bias = nullptr, int dense_rows = 0) {
+                          const float* col_bias = nullptr, int dense_rows = 0,
+                          bool stream_b = false) {
   if (m_max <= 0) return hipSuccess;
   constexpr int BN = SW ? P::BNW / 2 : P::BNW;
   const int n_tiles = (N_out + BN - 1) / BN;
@@ -537,7 +551,7 @@ hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const 
   if (e != hipSuccess) return e;
   prefill_gemm_kernel<T, SW, P, PT, OutT><<<(unsigned)grid, P::kThreads, lds, s>>>(
       A, a_rows, B0, B1, b_stride, C, col_bias, c_acc, K, N_out, offsets, table, (int)m_max,
-      n_tiles, group_n, (int)logical, ksplit, dense_rows);
+      n_tiles, group_n, (int)logical, ksplit, dense_rows, stream_b ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -554,16 +568,18 @@ hipError_t run_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   const int32_t* rows = a.src_rows;
   T* h = (T*)a.h;
   const int64_t stride = a.F * a.d;
+  const T* wg = (const T*)a.w_gate;
+  const T* wu = (const T*)a.w_up;
   if (p.small)
-    return launch_prefill<T, true, DecodeDmaTile, DecodeDmaTile>(xp, rows, (const T*)a.w_gate, (const T*)a.w_up,
-                                                  stride, h, (int)a.d, (int)a.F, a.offsets,
-                                                  a.sched, p.m_max, s);
+    return launch_prefill<T, true, DecodeDmaTile, DecodeDmaTile>(
+        xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s, 1,
+        nullptr, nullptr, 0, p.stream_b);
   if (p.tile == 2)
-    return launch_prefill<T, true, PrefillTallTile>(xp, rows, (const T*)a.w_gate, (const T*)a.w_up,
-                                                    stride, h, (int)a.d, (int)a.F, a.offsets,
-                                                    a.sched, p.m_max, s);
-  return launch_prefill<T, true>(xp, rows, (const T*)a.w_gate, (const T*)a.w_up, stride, h,
-                                 (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s);
+    return launch_prefill<T, true, PrefillTallTile>(xp, rows, wg, wu, stride, h, (int)a.d,
+                                                    (int)a.F, a.offsets, a.sched, p.m_max, s, 1,
+                                                    nullptr, nullptr, 0, p.stream_b);
+  return launch_prefill<T, true>(xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets,
+                                 a.sched, p.m_max, s, 1, nullptr, nullptr, 0, p.stream_b);
 }
 
 template <class T>
@@ -572,9 +588,9 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   T* y = (T*)a.y_perm;
   const int64_t stride = a.d * a.F;
   if (p.small)
-    return launch_prefill<T, false, DecodeDmaTile, DecodeDmaTile>(h, nullptr, (const T*)a.w_down, nullptr, stride, y,
-                                                   (int)a.F, (int)a.d, a.offsets, a.sched,
-                                                   p.m_max, s);
+    return launch_prefill<T, false, DecodeDmaTile, DecodeDmaTile>(
+        h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F, (int)a.d, a.offsets,
+        a.sched, p.m_max, s, 1, nullptr, nullptr, 0, p.stream_b);
   // split reduction: zero the fp32 sums of rows [0, N), let both halves add into them,
   // then convert the rows to the output type
   const int ks = p.down_split;
@@ -589,10 +605,11 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
       p.tile == 2
           ? launch_prefill<T, false, PrefillTallTile>(h, nullptr, (const T*)a.w_down, nullptr,
                                                       stride, y, (int)a.F, (int)a.d, a.offsets,
-                                                      a.sched, p.m_max, s, ks, acc)
+                                                      a.sched, p.m_max, s, ks, acc, nullptr, 0,
+                                                      p.stream_b)
           : launch_prefill<T, false>(h, nullptr, (const T*)a.w_down, nullptr, stride, y,
                                      (int)a.F, (int)a.d, a.offsets, a.sched, p.m_max, s, ks,
-                                     acc);
+                                     acc, nullptr, 0, p.stream_b);
   if (e != hipSuccess || ks == 1) return e;
   rows_from_f32_kernel<T><<<ew_blocks, 256, 0, s>>>(acc, a.offsets, (int)a.E, a.d, y);
   return hipGetLastError();
