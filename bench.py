@@ -164,6 +164,9 @@ def summarize_counters(d):
 
     def short(name):
         if "prefill_gemm_kernel" in name:
+            # bf16 operands with an fp32 output: the router logits in dense mode
+            if ("IDF16b" in name and "fEEvPKT_" in name) or ("__bf16" in name and ", float>" in name):
+                return "prefill_gemm_kernel (router logits, dense)"
             return "prefill_gemm_kernel (" + (
                 "down" if "Lb0E" in name or "false" in name else "gate/up+SwiGLU") + ")"
         return name.split("(")[0].split("<")[0].replace("void ", "")

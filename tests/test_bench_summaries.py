@@ -9,6 +9,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GATE_UP = "void moe::prefill_gemm_kernel<__bf16, true, moe::PrefillTileT<128, 2, 320>>(x)"
 DOWN = "void moe::prefill_gemm_kernel<__bf16, false, moe::PrefillTileT<128, 2, 320>>(x)"
+# the same template with bf16 operands and an fp32 output: router logits in dense mode
+ROUTER = ("_ZN3moe19prefill_gemm_kernelIDF16bLb0ENS_12PrefillTileTILi128ELi3ELi64ELi256ELi2ELi4"
+          "ELi0ELi0EEES2_fEEvPKT_PKiS5_S5_lPT3_PKfPfiiS7_S7_iiiiiii")
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -34,7 +37,8 @@ def test_counter_summary(bench, tmp_path):
     # dispatch 1: 1 ms at 1.7 GHz on 8 XCDs; 2: 0.5 ms at 2.4 GHz; 3: 2 ms at 1.8 GHz
     trace = [{"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Start_Timestamp": "0", "End_Timestamp": "1000000"},
              {"Dispatch_Id": "2", "Kernel_Name": DOWN, "Start_Timestamp": "0", "End_Timestamp": "500000"},
-             {"Dispatch_Id": "3", "Kernel_Name": GATE_UP, "Start_Timestamp": "0", "End_Timestamp": "2000000"}]
+             {"Dispatch_Id": "3", "Kernel_Name": GATE_UP, "Start_Timestamp": "0", "End_Timestamp": "2000000"},
+             {"Dispatch_Id": "4", "Kernel_Name": ROUTER, "Start_Timestamp": "0", "End_Timestamp": "100000"}]
     _write(tmp_path / "run_kernel_trace.csv", trace)
     # dispatch 1 also: MFMA units busy 60 % of the active clocks, 1.2e12 bf16 MFMA flops
     cc = [{"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Counter_Name": "GRBM_COUNT", "Counter_Value": str(1.7e6 * 8)},
@@ -42,7 +46,8 @@ def test_counter_summary(bench, tmp_path):
           {"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES", "Counter_Value": str(0.6 * 1.7e6 * 1024)},
           {"Dispatch_Id": "1", "Kernel_Name": GATE_UP, "Counter_Name": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "Counter_Value": str(1.2e12 / 512)},
           {"Dispatch_Id": "2", "Kernel_Name": DOWN, "Counter_Name": "GRBM_COUNT", "Counter_Value": str(2.4e6 / 2 * 8)},
-          {"Dispatch_Id": "3", "Kernel_Name": GATE_UP, "Counter_Name": "GRBM_COUNT", "Counter_Value": str(1.8e6 * 2 * 8)}]
+          {"Dispatch_Id": "3", "Kernel_Name": GATE_UP, "Counter_Name": "GRBM_COUNT", "Counter_Value": str(1.8e6 * 2 * 8)},
+          {"Dispatch_Id": "4", "Kernel_Name": ROUTER, "Counter_Name": "GRBM_COUNT", "Counter_Value": str(2.0e5 * 8)}]
     _write(tmp_path / "run_counter_collection.csv", cc)
     out = bench.summarize_counters(str(tmp_path))
     assert out["xcds"] == 8 and out["simds"] == 1024
@@ -56,6 +61,9 @@ def test_counter_summary(bench, tmp_path):
     assert gu["mfma_tflops"] == pytest.approx(1200.0, rel=1e-3)  # 1.2e12 flop in 1 ms
     dn = by["prefill_gemm_kernel (down)"]
     assert dn["clock_ghz"] == pytest.approx(2.4) and dn["median_us"] == 500.0
+    rt = by["prefill_gemm_kernel (router logits, dense)"]
+    assert rt["dispatches"] == 1 and rt["clock_ghz"] == pytest.approx(2.0)
+    assert by["prefill_gemm_kernel (down)"]["dispatches"] == 1  # not merged with the router
     # the kernel with the most total time comes first
     assert out["kernels"][0]["kernel"] == "prefill_gemm_kernel (gate/up+SwiGLU)"
 
