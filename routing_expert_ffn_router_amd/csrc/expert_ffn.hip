@@ -494,6 +494,7 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad
     p.tile = 0;
     p.bm = DecodeDmaTile::BM;
     p.stream_b = true;  // a few rows per expert: every weight line is read by one tile
+    p.group_cap = 4;
   } else {
     // Rows an expert will probably hold: a little above the mean, at most the capacity.
     // Take the tile height that needs fewer row tiles (each one re-reads the expert's
@@ -510,6 +511,11 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad
     // streamed and take the non-temporal hint (measured: DeepSeek-V3 mixed batch -4 %,
     // Mixtral-8x22B -3.5 %); with four (Mixtral-8x7B) the hint costs 7 %.
     p.stream_b = (r + p.bm - 1) / p.bm <= 2;
+    // Launch order: each XCD walks groups of (all m-tiles) x group_cap n-tiles.  When an
+    // expert fits one row tile and its weights stream, the activation rows are the only
+    // operand reused, so a group spans every n-tile (DeepSeek-V3 mixed batch -3 %);
+    // otherwise 8 n-tiles, which lets an expert's row tiles share its weight panel.
+    p.group_cap = p.stream_b && r <= p.bm ? (1 << 30) : 8;
   }
   int64_t m_max = (R + E * (p.bm - 1)) / p.bm;
   const int64_t m_cap = E * ((C + p.bm - 1) / p.bm);
@@ -537,11 +543,11 @@ hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const 
                           const int32_t* table, int64_t m_max, hipStream_t s,
                           int ksplit = 1, float* c_acc = nullptr,
                           const float* col_bias = nullptr, int dense_rows = 0,
-                          bool stream_b = false) {
+                          bool stream_b = false, int group_cap = 8) {
   if (m_max <= 0) return hipSuccess;
   constexpr int BN = SW ? P::BNW / 2 : P::BNW;
   const int n_tiles = (N_out + BN - 1) / BN;
-  const int group_n = n_tiles < 8 ? n_tiles : 8;
+  const int group_n = n_tiles < group_cap ? n_tiles : group_cap;
   const int n_groups = (n_tiles + group_n - 1) / group_n;
   const int64_t logical = m_max * group_n * n_groups;
   const int64_t grid = (logical * ksplit + 7) / 8 * 8;
@@ -573,13 +579,15 @@ hipError_t run_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   if (p.small)
     return launch_prefill<T, true, DecodeDmaTile, DecodeDmaTile>(
         xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s, 1,
-        nullptr, nullptr, 0, p.stream_b);
+        nullptr, nullptr, 0, p.stream_b, p.group_cap);
   if (p.tile == 2)
     return launch_prefill<T, true, PrefillTallTile>(xp, rows, wg, wu, stride, h, (int)a.d,
                                                     (int)a.F, a.offsets, a.sched, p.m_max, s, 1,
-                                                    nullptr, nullptr, 0, p.stream_b);
+                                                    nullptr, nullptr, 0, p.stream_b,
+                                                    p.group_cap);
   return launch_prefill<T, true>(xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets,
-                                 a.sched, p.m_max, s, 1, nullptr, nullptr, 0, p.stream_b);
+                                 a.sched, p.m_max, s, 1, nullptr, nullptr, 0, p.stream_b,
+                                 p.group_cap);
 }
 
 template <class T>
@@ -590,7 +598,7 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   if (p.small)
     return launch_prefill<T, false, DecodeDmaTile, DecodeDmaTile>(
         h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F, (int)a.d, a.offsets,
-        a.sched, p.m_max, s, 1, nullptr, nullptr, 0, p.stream_b);
+        a.sched, p.m_max, s, 1, nullptr, nullptr, 0, p.stream_b, p.group_cap);
   // split reduction: zero the fp32 sums of rows [0, N), let both halves add into them,
   // then convert the rows to the output type
   const int ks = p.down_split;
@@ -606,10 +614,10 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
           ? launch_prefill<T, false, PrefillTallTile>(h, nullptr, (const T*)a.w_down, nullptr,
                                                       stride, y, (int)a.F, (int)a.d, a.offsets,
                                                       a.sched, p.m_max, s, ks, acc, nullptr, 0,
-                                                      p.stream_b)
+                                                      p.stream_b, p.group_cap)
           : launch_prefill<T, false>(h, nullptr, (const T*)a.w_down, nullptr, stride, y,
                                      (int)a.F, (int)a.d, a.offsets, a.sched, p.m_max, s, ks,
-                                     acc, nullptr, 0, p.stream_b);
+                                     acc, nullptr, 0, p.stream_b, p.group_cap);
   if (e != hipSuccess || ks == 1) return e;
   rows_from_f32_kernel<T><<<ew_blocks, 256, 0, s>>>(acc, a.offsets, (int)a.E, a.d, y);
   return hipGetLastError();

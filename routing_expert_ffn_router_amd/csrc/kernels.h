@@ -59,6 +59,7 @@ struct FfnPlan {
   int64_t m_max;   // upper bound on m-tiles over all experts
   int down_split;  // 1, or 2: the down GEMM splits its reduction in two halves
   bool stream_b;   // weight loads carry the non-temporal hint (each line read by ~1 tile)
+  int group_cap;   // n-tiles per launch-order group (each XCD walks groups of m x group)
 };
 // pad: every expert holds exactly C rows (offsets e * C).  d, F and the element size
 // decide whether the down GEMM splits its reduction.
