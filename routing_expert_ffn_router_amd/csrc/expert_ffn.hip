@@ -27,6 +27,14 @@
 //   - Block order: blocks are dealt round-robin to the 8 XCDs; the logical tile index is
 //     remapped so each XCD walks a contiguous range in which neighbouring tiles share the
 //     A rows (same m-tile) and the B rows (same n-group), keeping both in that XCD's L2.
+//     The n-group width comes from the launch plan.
+//   - Weights that each tile reads alone (at most two row tiles per expert) are loaded with
+//     the non-temporal hint, so they do not displace the shared activation rows.
+//   - A down GEMM with few, long tiles splits its reduction in two halves that add fp32
+//     partial sums (deterministic with two addends), so the last round of tiles does not
+//     leave most CUs idle.
+//   - Dense mode (no tile table, fp32 output with a column bias) serves the router logits
+//     of shapes with many tokens and experts.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
