@@ -121,7 +121,7 @@ struct PrefillTileT {
   static constexpr int kALoads = BM / kRowsPerLoad / kDmaWaves;   // per issuing wave
   static constexpr int kBLoads = BNW / kRowsPerLoad / kDmaWaves;
   static constexpr int kDmaPerWave = kALoads + kBLoads;
-  static_assert(WM * WN == kWaves && NT % 2 == 0 && MT >= 1, "wave grid");
+  static_assert(WM * WN == kWaves && NT >= 1 && MT >= 1, "wave grid");
   static_assert(kAStages >= 2 && kAStages <= 3 && kBStages >= 2 && kBStages <= 4, "rings");
   static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
   // load i of every issuing wave reads the same operand: 0 activations, 1 the first weight
@@ -148,6 +148,9 @@ using PrefillTailTile = PrefillTileT<128, 2, 128, 256, 2, 4, 1, 3>;
 // Decode: weight streaming.  64 x 256 tile, three 40 KB stages, so two stages (80 KB per
 // CU) of weight reads are in flight while one is multiplied.
 using DecodeDmaTile = PrefillTileT<128, 3, 64, 256, 2, 4>;
+// Router logits in dense mode: 64 tokens x 128 experts, one 32x32 tile per wave, so a
+// DeepSeek-V3-sized router (8192 tokens, 256 experts) spreads over 256 blocks.
+using RouterTile = PrefillTileT<128, 3, 64, 128, 2, 4>;
 
 // A wave-uniform 64-bit address, moved to scalar registers.
 __device__ inline uint64_t uniform_u64(const void* p) {
@@ -195,6 +198,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     lds_char* __restrict__ a2, lds_char* __restrict__ b0, lds_char* __restrict__ b1,
     lds_char* __restrict__ b2, lds_char* __restrict__ b3) {
   constexpr int BN = SWIGLU ? P::BNW / 2 : P::BNW;
+  static_assert(!SWIGLU || P::NT % 2 == 0, "SwiGLU pairs gate and up tiles in each wave");
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int wm = wave / P::WN, wn = wave % P::WN;
@@ -634,22 +638,22 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
 }  // namespace
 
 // Router logits L = x w^T (+ b) through the same pipeline in dense mode: 64-token x
-// 256-expert tiles, fp32 output with the bias added in the epilogue.  Used when there are
+// 128-expert tiles, fp32 output with the bias added in the epilogue.  Used when there are
 // enough tiles to spread over the CUs.
 bool router_gemm_suits(int64_t T, int64_t E) {
-  const int64_t tiles = ((T + DecodeDmaTile::BM - 1) / DecodeDmaTile::BM) *
-                        ((E + DecodeDmaTile::BNW - 1) / DecodeDmaTile::BNW);
-  return E >= 64 && tiles >= 96;
+  const int64_t tiles = ((T + RouterTile::BM - 1) / RouterTile::BM) *
+                        ((E + RouterTile::BNW - 1) / RouterTile::BNW);
+  return E >= 64 && tiles >= 192;
 }
 
 hipError_t launch_router_gemm(int dtype, const void* x, const void* w, const float* b,
                               float* logits, int64_t T, int64_t d, int64_t E, hipStream_t s) {
-  const int64_t m_tiles = (T + DecodeDmaTile::BM - 1) / DecodeDmaTile::BM;
+  const int64_t m_tiles = (T + RouterTile::BM - 1) / RouterTile::BM;
   if (dtype == 1)
-    return launch_prefill<bf16, false, DecodeDmaTile, DecodeDmaTile, float>(
+    return launch_prefill<bf16, false, RouterTile, RouterTile, float>(
         (const bf16*)x, nullptr, (const bf16*)w, nullptr, 0, logits, (int)d, (int)E, nullptr,
         nullptr, m_tiles, s, 1, nullptr, b, (int)T);
-  return launch_prefill<float, false, DecodeDmaTile, DecodeDmaTile, float>(
+  return launch_prefill<float, false, RouterTile, RouterTile, float>(
       (const float*)x, nullptr, (const float*)w, nullptr, 0, logits, (int)d, (int)E, nullptr,
       nullptr, m_tiles, s, 1, nullptr, b, (int)T);
 }
