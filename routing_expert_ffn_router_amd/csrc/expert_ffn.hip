@@ -151,6 +151,10 @@ using DecodeDmaTile = PrefillTileT<128, 3, 64, 256, 2, 4>;
 // Router logits in dense mode: 64 tokens x 128 experts, one 32x32 tile per wave, so a
 // DeepSeek-V3-sized router (8192 tokens, 256 experts) spreads over 256 blocks.
 using RouterTile = PrefillTileT<128, 3, 64, 128, 2, 4>;
+// Down GEMM of decode-sized experts: the same 64 x 128 tile.  Its short reduction (F) makes
+// every tile start wait for a full HBM round trip; at 72 KB of LDS two blocks share a CU
+// and one streams while the other starts (decode layer -1.5 % against 64 x 256).
+using DecodeDownTile = PrefillTileT<128, 3, 64, 128, 2, 4>;
 
 // A wave-uniform 64-bit address, moved to scalar registers.
 __device__ inline uint64_t uniform_u64(const void* p) {
@@ -608,7 +612,7 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   T* y = (T*)a.y_perm;
   const int64_t stride = a.d * a.F;
   if (p.small)
-    return launch_prefill<T, false, DecodeDmaTile, DecodeDmaTile>(
+    return launch_prefill<T, false, DecodeDownTile, DecodeDownTile>(
         h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F, (int)a.d, a.offsets,
         a.sched, p.m_max, s, 1, nullptr, nullptr, 0, p.stream_b, p.group_cap);
   // split reduction: zero the fp32 sums of rows [0, N), let both halves add into them,
