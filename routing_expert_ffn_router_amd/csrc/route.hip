@@ -195,6 +195,14 @@ __device__ inline uint64_t group_max_u64(uint64_t v, int G) {
   }
   return v;
 }
+__device__ inline float group_max_f32(float v, int G) {
+  for (int msk = G >> 1; msk > 0; msk >>= 1) v = fmaxf(v, __shfl_xor(v, msk, kWave));
+  return v;
+}
+__device__ inline float group_sum_f32(float v, int G) {
+  for (int msk = G >> 1; msk > 0; msk >>= 1) v += __shfl_xor(v, msk, kWave);
+  return v;
+}
 
 template <int V>
 __global__ void __launch_bounds__(256)
@@ -207,13 +215,16 @@ topk_kernel(const float* __restrict__ logits, const float* __restrict__ sel_bias
   const float* row = logits + (int64_t)(active ? tok : 0) * E;
 
   uint64_t key[V];
+  float lg[V];  // the logits of this lane's experts (the gates use them)
   int bad = 0;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int e = sub + v * G;
     key[v] = 0;
+    lg[v] = 0.f;
     if (active && e < E) {
       const float val = row[e];
+      lg[v] = val;
       const float sv = sel_bias ? val + sel_bias[e] : val;
       if (__builtin_isfinite(val) && __builtin_isfinite(sv))
         key[v] = ((uint64_t)ordered_f32(sv) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
@@ -253,10 +264,13 @@ topk_kernel(const float* __restrict__ logits, const float* __restrict__ sel_bias
     }
   }
 
-  // Slot 0 holds the best selection; the gates are exp(L_j - m) / sum with m the largest
-  // selected logit.  The owner lane writes the indices first and re-reads the selected
-  // logits afterwards.
-  float m = -__builtin_huge_valf(), sum = 0.f;
+  // Slot 0 holds the best selection.  Round j's winner is expert e, held by lane e % G of
+  // the group as its entry e / G; that lane's logit reaches the group by one shuffle and
+  // lane j keeps slot j (k <= G).  The gates are exp(L_j - m) / sum with m the largest
+  // selected logit, computed by the k slot lanes together.
+  const int base = lane_id() & ~(G - 1);
+  int slot_e = 0;
+  float slot_l = -__builtin_huge_valf();
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
@@ -266,19 +280,23 @@ topk_kernel(const float* __restrict__ logits, const float* __restrict__ sel_bias
 #pragma unroll
     for (int v = 0; v < V; ++v)
       if (key[v] == best) key[v] = 0;
-    if (sub == 0 && active) {
-      const int e = best ? (int)(0xFFFFFFFFu - (uint32_t)best) : 0;
-      topk_idx[(int64_t)tok * k + j] = e;
-      m = fmaxf(m, row[e]);
+    const int e = best ? (int)(0xFFFFFFFFu - (uint32_t)best) : 0;
+    float mine = 0.f;  // this lane's logit of expert e's column
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (v == e / G) mine = lg[v];
+    const float l = __shfl(mine, base + e % G, kWave);
+    if (sub == j) {
+      slot_e = e;
+      slot_l = l;
     }
   }
-  if (sub == 0 && active) {
-    for (int j = 0; j < k; ++j) sum += expf(row[topk_idx[(int64_t)tok * k + j]] - m);
-    const float inv = 1.0f / sum;
-    for (int j = 0; j < k; ++j) {
-      const int e = topk_idx[(int64_t)tok * k + j];
-      topk_w[(int64_t)tok * k + j] = expf(row[e] - m) * inv;
-    }
+  const float m = group_max_f32(sub < k ? slot_l : -__builtin_huge_valf(), G);
+  const float ex = sub < k ? expf(slot_l - m) : 0.f;
+  const float inv = 1.0f / group_sum_f32(ex, G);
+  if (active && sub < k) {
+    topk_idx[(int64_t)tok * k + sub] = slot_e;
+    topk_w[(int64_t)tok * k + sub] = ex * inv;
   }
 }
 
