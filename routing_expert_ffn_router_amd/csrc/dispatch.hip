@@ -102,13 +102,20 @@ __global__ void __launch_bounds__(kTileMax)
 rank_kernel(const int32_t* __restrict__ idx, int64_t total, int64_t T, int te, int k, int E,
             int C, int nbits, bool slot_major, const int32_t* __restrict__ tile_base,
             const int32_t* __restrict__ offsets, int32_t* __restrict__ dest_row,
-            int32_t* __restrict__ src_token, int32_t* __restrict__ drops) {
+            int32_t* __restrict__ src_token, int32_t* __restrict__ drops, int64_t fill_R) {
   extern __shared__ int32_t sm[];
   constexpr int kWaves = kTileMax / kWave;
   int32_t* s_cnt = sm;                          // [kWaves][E] per-wave expert counts
   int32_t* s_tokdrop = sm + kWaves * E;         // [kTileMax] dropped slots per token
   int32_t* s_drop = s_tokdrop + kTileMax;       // [k + 2] block drop counters
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  // With fill_R > 0 the row slots [N, fill_R) past the kept rows get src_token = -1 here
+  // (when no rows are copied, this saves the separate row kernel); kept rows are < N, so
+  // no slot is written twice.
+  if (fill_R > 0)
+    for (int64_t r = offsets[E] + (int64_t)blockIdx.x * blockDim.x + tid; r < fill_R;
+         r += (int64_t)gridDim.x * blockDim.x)
+      src_token[r] = -1;
   for (int i = tid; i < kWaves * E; i += blockDim.x) s_cnt[i] = 0;
   s_tokdrop[tid] = 0;
   for (int i = tid; i < k + 2; i += blockDim.x) s_drop[i] = 0;
@@ -256,6 +263,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   int nbits = 0;
   while ((1ll << nbits) < a.E) ++nbits;
   hipError_t err;
+  // packed rows without a copy: the rank kernel marks the empty row slots itself
+  const bool tail_in_rank = !a.x_perm && !a.pad && ntiles > 0;
   if (ntiles > 0) {
     tile_hist_kernel<<<ntiles, kTileMax, a.E * sizeof(int32_t), s>>>(
         a.topk_idx, total, a.T, te, (int)a.k, (int)a.E, a.slot_major, a.tile_hist);
@@ -268,7 +277,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     const size_t lds = ((kTileMax / kWave) * a.E + kTileMax + a.k + 2) * sizeof(int32_t);
     rank_kernel<<<ntiles, kTileMax, lds, s>>>(a.topk_idx, total, a.T, te, (int)a.k, (int)a.E,
                                               (int)a.C, nbits, a.slot_major, a.tile_base,
-                                              a.offsets, a.dest_row, a.src_token, a.drops);
+                                              a.offsets, a.dest_row, a.src_token, a.drops,
+                                              tail_in_rank ? a.R : 0);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.slot_major) {
       token_drop_kernel<<<(unsigned)((a.T + 255) / 256), 256, 0, s>>>(a.dest_row, a.T,
@@ -276,7 +286,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
-  if (a.R > 0) {
+  if (a.R > 0 && !tail_in_rank) {
     int64_t blocks = (a.R + 3) / 4;
     if (blocks > 4096) blocks = 4096;
     gather_rows_kernel<<<(unsigned)blocks, 256, 0, s>>>(

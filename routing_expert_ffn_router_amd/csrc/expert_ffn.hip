@@ -666,7 +666,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, int which, hipStream_t s) {
   if (a.R <= 0) return hipSuccess;
   const FfnPlan p = ffn_plan(a.T, a.E, a.k, a.C, a.R, a.pad, a.d, a.F, a.dtype == 1 ? 2 : 4);
   if (p.down_split > 1 && (which & 2) && !a.down_acc) return hipErrorInvalidValue;
-  hipError_t err = launch_table(a, p, s);
+  hipError_t err = a.table_ready ? hipSuccess : launch_table(a, p, s);
   if (err != hipSuccess) return err;
   if (which & 1) {
     err = a.dtype == 1 ? run_gate_up<bf16>(a, p, s) : run_gate_up<float>(a, p, s);

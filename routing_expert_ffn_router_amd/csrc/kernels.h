@@ -86,6 +86,7 @@ struct FfnArgs {
   int32_t* sched;        // ffn_table_ints() ints
   void* y_perm;          // [R, d]
   float* down_acc;       // [R, d] fp32, used when the plan splits the down GEMM
+  bool table_ready;      // sched already holds this call's tile table (skip rebuilding it)
 };
 // S1 through the grouped-GEMM pipeline in dense mode (64 x 256 tiles, fp32 out + bias),
 // for shapes with enough tiles (router_gemm_suits).

@@ -237,10 +237,12 @@ bool gather_fits(const moe_shape* s) {
 
 // Shared body of the expert-FFN entry points; which = 1 (gate/up), 2 (down), 3 (both).  The
 // gate/up activations are x_perm, or, with src_rows, the rows src_rows[r] of x.
+// With table_ready the workspace already holds the tile table of these offsets (moe_layer's
+// down GEMM reuses the gate/up GEMM's).
 int expert_ffn_impl(const moe_shape* s, int which, const void* x_perm, const void* x,
                     const int32_t* src_rows, void* h, const int32_t* expert_offsets,
                     const void* w_gate, const void* w_up, const void* w_down, void* ws,
-                    size_t ws_bytes, void* y_perm, hipStream_t st) {
+                    size_t ws_bytes, void* y_perm, hipStream_t st, bool table_ready = false) {
   int rc = check_shape(s);
   if (rc != MOE_OK) return rc;
   if (s->T == 0) return MOE_OK;
@@ -275,6 +277,7 @@ int expert_ffn_impl(const moe_shape* s, int which, const void* x_perm, const voi
   a.sched = region<int32_t>(ws, L, MOE_WS_SCHED);
   a.y_perm = y_perm;
   a.down_acc = region<float>(ws, L, MOE_WS_DOWN_ACC);
+  a.table_ready = table_ready;
   return hip_status(moe::launch_expert_ffn(a, which, st));
 }
 
@@ -378,7 +381,9 @@ int moe_layer(const moe_shape* s, const void* x, const void* w_router, const flo
                                               h, st)
                 : moe_expert_gate_up(s, x_perm, offsets, w_gate, w_up, ws, ws_bytes, h, st);
   if (rc != MOE_OK) return rc;
-  rc = moe_expert_down(s, h, offsets, w_down, ws, ws_bytes, y_perm, st);
+  // the down GEMM reuses the tile table the gate/up GEMM just built from the same offsets
+  rc = expert_ffn_impl(s, 2, nullptr, nullptr, nullptr, h, offsets, nullptr, nullptr, w_down,
+                       ws, ws_bytes, y_perm, st, /*table_ready=*/true);
   if (rc != MOE_OK) return rc;
   return moe_combine(s, y_perm, dest, gates, out, st);
 }
