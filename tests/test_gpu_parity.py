@@ -303,15 +303,19 @@ def test_gate_up_gathered_equals_packed(name, pad):
     assert torch.equal(h1[rows], v("h")[rows])
 
 
-def test_dispatch_tables_only():
-    T, E, k, C, d = 1000, 8, 2, 250, 256
-    rng = np.random.default_rng(21)
+@pytest.mark.parametrize("T,E,k,C", [(1000, 8, 2, 250), (1000, 8, 2, 0), (3001, 64, 6, 290)])
+def test_dispatch_tables_only(T, E, k, C):
+    # packed rows without a copy: every row slot past the kept rows must read -1 afterwards,
+    # so the tables start out holding a sentinel
+    d = 256
+    rng = np.random.default_rng(21 + T + C)
     idx = oracle.select_topk(rng.standard_normal((T, E)).astype(np.float32), k)
     s = moe.shape(T, d, E, k, 128, C, moe.MOE_BF16)
     R = moe.max_rows(s)
     ws = torch.empty(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
     g = dict(routed=_i32(E), kept=_i32(E), offsets=_i32(E + 1), src=_i32(R), dest=_i32(0, T, k),
              drops=_i32(k + 2))
+    g["src"].fill_(0x5A5A5A5A)
     moe.dispatch(s, to_device(idx, torch.int32), None, ws, g["routed"], g["kept"], g["offsets"],
                  g["src"], g["dest"], g["drops"], None)
     torch.cuda.synchronize()
@@ -319,6 +323,7 @@ def test_dispatch_tables_only():
     assert np.array_equal(g["dest"].cpu().numpy(), ref["dest_row"])
     assert np.array_equal(g["src"].cpu().numpy(), ref["src_token"][:R])
     assert np.array_equal(g["offsets"].cpu().numpy(), ref["expert_offsets"])
+    assert C == 0 or ref["expert_offsets"][-1] < R  # the capped cases leave a tail to mark
 
 
 # ------------------------------------------------------------------------------- S8
