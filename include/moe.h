@@ -284,7 +284,7 @@ int moe_slot_counts(const moe_shape* shape, const int32_t* topk_idx, const int32
  * separately from compute": every expert is local and no all-to-all runs.  With packed
  * rows (no MOE_FLAG_PAD_TO_CAPACITY) and T * d * sizeof(dtype) < 2^31 the gate/up GEMM
  * gathers the token rows itself (moe_expert_gate_up_gathered) and the x_perm region is
- * left unwritten.
+ * left unwritten.  The down GEMM reuses the tile table the gate/up GEMM built.
  *   out               [T, d] dtype out
  *   routed_counts, tokens_per_expert [E] int32 out, nullable (then kept in the workspace)
  *   drops             [k+2] int32 out, nullable

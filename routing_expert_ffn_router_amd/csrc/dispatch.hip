@@ -22,7 +22,8 @@
 //                  dest_row, src_token and drop counters
 //   K5c token_drop (slot-major only) tokens whose k assignments were all dropped
 //   K5b gather     x_perm[r] = x[src_token[r]] with 16-byte vector copies; empty slots
-//                  get src_token -1 (and, when padded, a zero row)
+//                  get src_token -1 (and, when padded, a zero row).  With packed rows and
+//                  no copy requested, K5 marks the empty slots and K5b is not launched.
 #include "common.h"
 #include "kernels.h"
 

@@ -19,8 +19,8 @@
 //   - Three tile shapes of the same template: prefill-sized experts (mean > 32 rows) use
 //     256 x 256 tiles (128 flop per loaded byte) or, when that needs fewer row tiles or
 //     pads fewer rows, 320 x 256 tiles (142 flop per byte); decode-sized experts stream
-//     weights with 64 x 256 tiles and three stages, keeping 80 KB of weight reads in
-//     flight per CU.
+//     weights in three stages with 64 x 256 tiles for gate/up (80 KB of weight reads in
+//     flight per CU) and 64 x 128 tiles for down (two blocks per CU).
 //   - SwiGLU: the gate and up rows of the same output columns are loaded side by side, so
 //     the gate and up accumulators of one output element sit in the same lane and the
 //     epilogue computes silu(g) * u in registers.

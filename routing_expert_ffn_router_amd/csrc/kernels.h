@@ -88,14 +88,15 @@ struct FfnArgs {
   float* down_acc;       // [R, d] fp32, used when the plan splits the down GEMM
   bool table_ready;      // sched already holds this call's tile table (skip rebuilding it)
 };
-// S1 through the grouped-GEMM pipeline in dense mode (64 x 256 tiles, fp32 out + bias),
+// S1 through the grouped-GEMM pipeline in dense mode (64 x 128 tiles, fp32 out + bias),
 // for shapes with enough tiles (router_gemm_suits).
 bool router_gemm_suits(int64_t T, int64_t E);
 hipError_t launch_router_gemm(int dtype, const void* x, const void* w, const float* b,
                               float* logits, int64_t T, int64_t d, int64_t E, hipStream_t s);
 
 // which: 1 = gate/up GEMM (x_perm -> h), 2 = down GEMM (h -> y_perm), 3 = both.  Each
-// call first rebuilds the tile table from `offsets`.
+// call first rebuilds the tile table from `offsets`, unless a.table_ready says an earlier
+// call on the same stream built it from the same offsets.
 hipError_t launch_expert_ffn(const FfnArgs& a, int which, hipStream_t s);
 
 // S8

@@ -38,7 +38,7 @@ hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
 // which keeps the result deterministic.  Per 128-byte step a lane loads 32 contiguous bytes
 // of each of its MT token rows and NT expert rows; both operands use the same k-chunk
 // assignment (lane group g takes chunks 2g and 2g + 1), so the products pair up.  Each load
-// touches half of 16 cache lines, so shapes with many tokens and experts (enough 64 x 256
+// touches half of 16 cache lines, so shapes with many tokens and experts (enough 64 x 128
 // tiles to fill the CUs) go through the expert-GEMM pipeline instead.
 // grid = (ceil(T / (16 MT)), ceil(E / (16 NT))).
 // ---------------------------------------------------------------------------------------
