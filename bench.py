@@ -215,6 +215,20 @@ def build_if_missing():
     __graft_entry__._ensure_built()
 
 
+def segment_drops(dest_row, segments) -> dict:
+    """Drops per named token range ([EP-checks] "Top-2 does not insure against hot experts":
+    look at who loses when experts overflow).  dest_row is the [T, k] table of the layer (-1
+    for a dropped assignment); segments are (name, first token, end token)."""
+    import numpy as np
+
+    out = {}
+    for name, t0, t1 in segments:
+        rows = np.asarray(dest_row[t0:t1])
+        out[name] = {"tokens": int(t1 - t0), "dropped": int((rows < 0).sum()),
+                     "fully_dropped_tokens": int(np.all(rows < 0, axis=1).sum())}
+    return out
+
+
 def percentile(v, q):
     s = sorted(v)
     return s[min(len(s) - 1, max(0, math.ceil(q * len(s)) - 1))]
@@ -380,6 +394,8 @@ def main():
              "dropped_tokens": int(drops[0]), "dropped_per_slot": drops[1:w.k + 1].tolist(),
              "fully_dropped_tokens": int(drops[w.k + 1]), "kept_rows": N,
              "active_experts": E_active}
+    if w.segments:
+        stats["segments"] = segment_drops(lay.view("dest_row").cpu().numpy(), w.segments)
     if args.pad:
         R = moe.max_rows(s)
         stats["padded_rows"] = R

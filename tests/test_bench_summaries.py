@@ -86,3 +86,11 @@ def test_traffic_summary(bench, tmp_path):
     assert out["fetch_bytes_scaled"] == pytest.approx(200 * 1024 * 2)
     assert out["write_bytes_scaled"] == pytest.approx(50 * 1024 * 2)
     assert out["traffic_bytes"] == pytest.approx((200 + 50) * 1024 * 2)
+
+
+def test_segment_drops(bench):
+    # 5 tokens, k = 2; tokens 3 and 4 form the second segment, token 4 loses both slots
+    dest = [[0, 1], [2, -1], [3, 4], [-1, 5], [-1, -1]]
+    got = bench.segment_drops(dest, (("prefill", 0, 3), ("decode", 3, 5)))
+    assert got == {"prefill": {"tokens": 3, "dropped": 1, "fully_dropped_tokens": 0},
+                   "decode": {"tokens": 2, "dropped": 3, "fully_dropped_tokens": 1}}
