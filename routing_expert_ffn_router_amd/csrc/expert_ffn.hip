@@ -324,7 +324,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
       fa[i] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
           abuf + a_frag + i * 32 * P::kRowBytes + slot);
   };
-  // Multiply one stage.  The reads of k-step s+1 go out before the MFMAs of k-step s (two
+  // Multiply one stage.  The reads of k-step s+1 go out between the MFMAs of k-step s (two
   // register sets), so each k-step's MFMAs cover the next k-step's LDS latency.
   auto compute = [&](const lds_char* abuf, const lds_char* bbuf) {
     if (!band_live) return;
@@ -339,10 +339,21 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
 #pragma unroll
         for (int j = 0; j < P::NT; ++j)
           mma32_chunk(acc[i][j], fa[ks & 1][i], fb[ks & 1][j], T());
-      // order: [reads of step 0]; per step: reads of the next step, then its MFMAs
+      // order: [reads of step 0]; per step, its MFMAs with the next step's reads spread
+      // evenly between them (read r goes before MFMA floor(r * M / R)); measured about 1 %
+      // faster on the prefill layers than issuing the reads as one burst
       if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x100, P::MT + P::NT, 0);
-      if (ks + 1 < P::kKSteps) __builtin_amdgcn_sched_group_barrier(0x100, P::MT + P::NT, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, P::MT * P::NT, 0);
+      if (ks + 1 < P::kKSteps) {
+        constexpr int R = P::MT + P::NT, M = P::MT * P::NT;
+        unroll_steps<M>([&](auto MI) {
+          constexpr int m = decltype(MI)::value;
+          constexpr int r_lo = (m * R + M - 1) / M, r_hi = ((m + 1) * R + M - 1) / M;
+          if constexpr (r_hi > r_lo) __builtin_amdgcn_sched_group_barrier(0x100, r_hi - r_lo, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        });
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, P::MT * P::NT, 0);
+      }
     }
   };
   // Step kt (I = kt modulo the unroll): wait until stage kt of both rings has landed, make
