@@ -140,6 +140,7 @@ def summarize_counters(d):
         mfma_tflops   = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16 / duration."""
     import csv
     import glob
+    import re
     import statistics as st
 
     def rows(pattern):
@@ -165,7 +166,10 @@ def summarize_counters(d):
     def short(name):
         if "prefill_gemm_kernel" in name:
             # bf16 operands with an fp32 output: the router logits in dense mode
-            if ("IDF16b" in name and "fEEvPKT_" in name) or ("__bf16" in name and ", float>" in name):
+            # (mangled: the output type f, possibly followed by a back-reference, closes the
+            # template arguments; demangled: ", float" among them)
+            if ("IDF16b" in name and re.search(r"f(?:S\d*_)?EEvPKT_", name)) or (
+                    "__bf16" in name and re.search(r", float[,>]", name)):
                 return "prefill_gemm_kernel (router logits, dense)"
             return "prefill_gemm_kernel (" + (
                 "down" if "Lb0E" in name or "false" in name else "gate/up+SwiGLU") + ")"

@@ -16,9 +16,11 @@
 //   - Operands reach LDS by direct buffer -> LDS loads in 128-byte row pieces, in a ring of
 //     stages; fragments are read with a measured bank-conflict-free swizzle and fed to
 //     32x32x16 MFMAs (the bf16 form that runs at the full dense rate on gfx950).
-//   - Three tile shapes of the same template: prefill-sized experts (mean > 32 rows) use
+//   - Tile shapes of the same template: prefill-sized experts (mean > 32 rows) use
 //     256 x 256 tiles (128 flop per loaded byte) or, when that needs fewer row tiles or
-//     pads fewer rows, 320 x 256 tiles (142 flop per byte); decode-sized experts stream
+//     pads fewer rows, 320 x 256 tiles (142 flop per byte), an expert's short last tile
+//     128 x 256, or 128 x 512 (two n-tiles) behind two or more full 320-row tiles so that it
+//     keeps their pace through the shared weight panel; decode-sized experts stream
 //     weights in three stages with 64 x 256 tiles for gate/up (80 KB of weight reads in
 //     flight per CU) and 64 x 128 tiles for down (two blocks per CU).
 //   - SwiGLU: the gate and up rows of the same output columns are loaded side by side, so
@@ -145,6 +147,9 @@ using PrefillTallTile = PrefillTileT<128, 2, 320, 256, 2, 4, 1>;
 // An expert's last row tile when it holds at most 128 rows: 128 x 256, the weight ring
 // three deep (the same weight columns as the full tiles).
 using PrefillTailTile = PrefillTileT<128, 2, 128, 256, 2, 4, 1, 3>;
+// ... and twice as wide (two n-tiles) for the last tile of an expert with at least two full
+// 320-row tiles: 128 x 512, two 80 KB stages.
+using PrefillTailWideTile = PrefillTileT<128, 2, 128, 512, 2, 4, 1, 2>;
 // Decode: weight streaming.  64 x 256 tile, three 40 KB stages, so two stages (80 KB per
 // CU) of weight reads are in flight while one is multiplied.
 using DecodeDmaTile = PrefillTileT<128, 3, 64, 256, 2, 4>;
@@ -439,11 +444,17 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
 // index is remapped so each XCD walks a contiguous range of logical tiles, n fastest within
 // groups of group_n n-tiles.  An m-tile with at most PT::BM rows (an expert's last, partly
 // filled tile) runs the shorter tile PT with the same weight columns: fewer loads and MFMAs
-// instead of a full tile of mostly clamped rows.
+// instead of a full tile of mostly clamped rows.  When PW is twice as wide as P, the last
+// tile of an expert with at least two full tiles runs PW over n-tiles nt and nt + 1 in the
+// block of the even nt (the odd one exits): a short tile of single width runs about twice
+// as fast as the full tiles beside it and races ahead through the weight panel they share
+// in L2, so they miss; the double-width one keeps their pace.  Measured with the 320-row
+// tile: Mixtral-8x7B layer -2.8 %; experts with fewer full tiles keep PT, since with one
+// full tile (Mixtral-8x22B) the pairing's halved block count costs more than it saves.
 //
 // Dense mode (table == nullptr, used for the router logits): one operand A of dense_rows
 // rows and one B of N_out rows, m-tile mt covering rows mt * P::BM ...
-template <class T, bool SWIGLU, class P, class PT, class OutT>
+template <class T, bool SWIGLU, class P, class PT, class OutT, class PW>
 __global__ void __launch_bounds__(P::kThreads)
 prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
                     const T* __restrict__ B0, const T* __restrict__ B1,
@@ -455,6 +466,9 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
                     int stream_b) {
   static_assert(PT::BNW == P::BNW && PT::kThreads == P::kThreads && PT::BM <= P::BM,
                 "the shorter tile shares the n-tiling and the block size");
+  static_assert((PW::BNW == P::BNW || PW::BNW == 2 * P::BNW) && PW::BM == PT::BM &&
+                    PW::kThreads == P::kThreads,
+                "the wide tail tile spans one or two n-tiles of the full tile");
   extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
   const int bid = blockIdx.x;
   const int per_xcd = gridDim.x >> 3;
@@ -480,11 +494,21 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
     if (m_begin >= m_end) return;
   }
   lds_char* base = (lds_char*)smem_dyn;
-  if (PT::BM < P::BM && m_end - m_begin <= PT::BM)
+  if (PT::BM < P::BM && m_end - m_begin <= PT::BM) {
+    if constexpr (PW::BNW == 2 * P::BNW) {
+      if (table && m_begin - offsets[e] >= 2 * P::BM) {  // at least two full tiles before
+        if (nt & 1) return;
+        prefill_gemm_tile<T, SWIGLU, PW, OutT>(A, a_rows, B0, B1, b_expert_stride, C,
+                                               col_bias, Cacc, K, N_out, e, m_begin, m_end,
+                                               nt >> 1, half * k_steps, k_steps,
+                                               stream_b != 0, base);
+        return;
+      }
+    }
     prefill_gemm_tile<T, SWIGLU, PT, OutT>(A, a_rows, B0, B1, b_expert_stride, C, col_bias,
                                            Cacc, K, N_out, e, m_begin, m_end, nt,
                                            half * k_steps, k_steps, stream_b != 0, base);
-  else
+  } else
     prefill_gemm_tile<T, SWIGLU, P, OutT>(A, a_rows, B0, B1, b_expert_stride, C, col_bias, Cacc,
                                           K, N_out, e, m_begin, m_end, nt, half * k_steps,
                                           k_steps, stream_b != 0, base);
@@ -568,7 +592,8 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad
 
 namespace {
 
-template <class T, bool SW, class P = PrefillTile, class PT = PrefillTailTile, class OutT = T>
+template <class T, bool SW, class P = PrefillTile, class PT = PrefillTailTile, class OutT = T,
+          class PW = PT>
 hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const T* B1,
                           int64_t b_stride, OutT* C, int K, int N_out, const int32_t* offsets,
                           const int32_t* table, int64_t m_max, hipStream_t s,
@@ -582,11 +607,11 @@ hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const 
   const int n_groups = (n_tiles + group_n - 1) / group_n;
   const int64_t logical = m_max * group_n * n_groups;
   const int64_t grid = (logical * ksplit + 7) / 8 * 8;
-  const size_t lds = (size_t)(P::kLdsBytes > PT::kLdsBytes ? P::kLdsBytes : PT::kLdsBytes);
-  hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW, P, PT, OutT>,
+  const size_t lds = (size_t)std::max({P::kLdsBytes, PT::kLdsBytes, PW::kLdsBytes});
+  hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW, P, PT, OutT, PW>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  prefill_gemm_kernel<T, SW, P, PT, OutT><<<(unsigned)grid, P::kThreads, lds, s>>>(
+  prefill_gemm_kernel<T, SW, P, PT, OutT, PW><<<(unsigned)grid, P::kThreads, lds, s>>>(
       A, a_rows, B0, B1, b_stride, C, col_bias, c_acc, K, N_out, offsets, table, (int)m_max,
       n_tiles, group_n, (int)logical, ksplit, dense_rows, stream_b ? 1 : 0);
   return hipGetLastError();
@@ -612,13 +637,12 @@ hipError_t run_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
         xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s, 1,
         nullptr, nullptr, 0, p.stream_b, p.group_cap);
   if (p.tile == 2)
-    return launch_prefill<T, true, PrefillTallTile>(xp, rows, wg, wu, stride, h, (int)a.d,
-                                                    (int)a.F, a.offsets, a.sched, p.m_max, s, 1,
-                                                    nullptr, nullptr, 0, p.stream_b,
-                                                    p.group_cap);
-  return launch_prefill<T, true>(xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets,
-                                 a.sched, p.m_max, s, 1, nullptr, nullptr, 0, p.stream_b,
-                                 p.group_cap);
+    return launch_prefill<T, true, PrefillTallTile, PrefillTailTile, T, PrefillTailWideTile>(
+        xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s, 1,
+        nullptr, nullptr, 0, p.stream_b, p.group_cap);
+  return launch_prefill<T, true>(
+      xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s, 1,
+      nullptr, nullptr, 0, p.stream_b, p.group_cap);
 }
 
 template <class T>
@@ -642,13 +666,12 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   }
   const hipError_t e =
       p.tile == 2
-          ? launch_prefill<T, false, PrefillTallTile>(h, nullptr, (const T*)a.w_down, nullptr,
-                                                      stride, y, (int)a.F, (int)a.d, a.offsets,
-                                                      a.sched, p.m_max, s, ks, acc, nullptr, 0,
-                                                      p.stream_b, p.group_cap)
-          : launch_prefill<T, false>(h, nullptr, (const T*)a.w_down, nullptr, stride, y,
-                                     (int)a.F, (int)a.d, a.offsets, a.sched, p.m_max, s, ks,
-                                     acc, nullptr, 0, p.stream_b, p.group_cap);
+          ? launch_prefill<T, false, PrefillTallTile, PrefillTailTile, T, PrefillTailWideTile>(
+                h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F, (int)a.d,
+                a.offsets, a.sched, p.m_max, s, ks, acc, nullptr, 0, p.stream_b, p.group_cap)
+          : launch_prefill<T, false>(
+                h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F, (int)a.d,
+                a.offsets, a.sched, p.m_max, s, ks, acc, nullptr, 0, p.stream_b, p.group_cap);
   if (e != hipSuccess || ks == 1) return e;
   rows_from_f32_kernel<T><<<ew_blocks, 256, 0, s>>>(acc, a.offsets, (int)a.E, a.d, y);
   return hipGetLastError();

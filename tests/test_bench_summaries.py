@@ -10,8 +10,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GATE_UP = "void moe::prefill_gemm_kernel<__bf16, true, moe::PrefillTileT<128, 2, 320>>(x)"
 DOWN = "void moe::prefill_gemm_kernel<__bf16, false, moe::PrefillTileT<128, 2, 320>>(x)"
 # the same template with bf16 operands and an fp32 output: router logits in dense mode
-ROUTER = ("_ZN3moe19prefill_gemm_kernelIDF16bLb0ENS_12PrefillTileTILi128ELi3ELi64ELi256ELi2ELi4"
-          "ELi0ELi0EEES2_fEEvPKT_PKiS5_S5_lPT3_PKfPfiiS7_S7_iiiiiii")
+ROUTER = ("_ZN3moe19prefill_gemm_kernelIDF16bLb0ENS_12PrefillTileTILi128ELi3ELi64ELi128ELi2ELi4"
+          "ELi0ELi0EEES2_fS2_EEvPKT_PKiS5_S5_lPT3_PKfPfiiS7_S7_iiiiiii")
 COPY = "__amd_rocclr_copyBuffer"
 
 

@@ -35,6 +35,14 @@ SMALL = {
     # few, long down-GEMM tiles: the down GEMM splits its reduction in two halves
     "bf16_e8_split_down": W("bf16_e8_split_down", 700, 256, 8, 2, 2048, 1.25, "bf16", 1.1),
     "f32_e4_split_down": W("f32_e4_split_down", 600, 256, 4, 2, 1024, 1.0, "f32"),
+    # 320-row tiles where an expert's last tile (<= 128 rows) follows two or more full
+    # tiles, so it runs double width over two n-tiles: kept rows [1085, 615] with an odd
+    # n-tile count in the gate/up GEMM (F / 128 = 3) and a ragged one in the down GEMM
+    # (d = 384); fp32 with [1004, 746]; and [997, 868, 737, 698] with the down GEMM split
+    "bf16_e2_wide_tail": W("bf16_e2_wide_tail", 1700, 384, 2, 1, 384, None, "bf16", 0.6),
+    "f32_e2_wide_tail": W("f32_e2_wide_tail", 1750, 256, 2, 1, 384, None, "f32", 0.4),
+    "bf16_e4_wide_tail_split": W("bf16_e4_wide_tail_split", 1650, 256, 4, 2, 2048, None, "bf16",
+                                 0.3),
 }
 
 
@@ -244,7 +252,8 @@ def test_dispatch_invalid_and_duplicate_ids():
 # ------------------------------------------------------------------------------- S6-S7
 @pytest.mark.parametrize("name", ["tiny_f32", "bf16_e8_big_tiles", "bf16_e16_small_tiles",
                                   "bf16_e256_k8_decode", "f32_e4_big_tiles",
-                                  "bf16_e8_zipf_drops", "bf16_e3_k3"])
+                                  "bf16_e8_zipf_drops", "bf16_e3_k3", "bf16_e2_wide_tail",
+                                  "f32_e2_wide_tail", "bf16_e4_wide_tail_split"])
 def test_expert_ffn(name):
     w = SMALL[name]
     log(f"expert_ffn {w}")
