@@ -26,6 +26,9 @@
 //   - SwiGLU: the gate and up rows of the same output columns are loaded side by side, so
 //     the gate and up accumulators of one output element sit in the same lane and the
 //     epilogue computes silu(g) * u in registers.
+//   - Epilogue: the accumulators hold the transposed tile (weight fragment first), so each
+//     lane writes 4 consecutive outputs into LDS; the block then stores its tile from LDS
+//     with 16-byte stores over whole cache lines.
 //   - Block order: blocks are dealt round-robin to the 8 XCDs; the logical tile index is
 //     remapped so each XCD walks a contiguous range in which neighbouring tiles share the
 //     A rows (same m-tile) and the B rows (same n-group), keeping both in that XCD's L2.
@@ -46,7 +49,13 @@
 
 namespace moe {
 
-__device__ inline float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g) with the hardware reciprocal (about 1 ulp) instead of a correctly
+// rounded division: the SwiGLU epilogue evaluates it for every output of the gate/up GEMM,
+// and the division's ten instructions made that epilogue several percent of a tile.  For
+// g < -88 the reciprocal of +inf gives -0.0 where the exact value is below 1e-36.
+__device__ inline float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 
 // Tile table for one row-tile height BM: table[0] = number of m-tiles over all experts;
 // entry i (i < table[0]) is (expert, first row) at table[1 + 2i], table[2 + 2i].  Experts
@@ -197,7 +206,7 @@ __device__ inline void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <class T, bool SWIGLU, class P, class OutT>
+template <class T, bool SWIGLU, class P, class OutT, int kLdsAlloc>
 __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     const T* __restrict__ A, const int32_t* __restrict__ a_rows, const T* __restrict__ B0,
     const T* __restrict__ B1, int64_t b_expert_stride, OutT* __restrict__ C,
@@ -343,7 +352,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
       for (int i = 0; i < P::MT; ++i)
 #pragma unroll
         for (int j = 0; j < P::NT; ++j)
-          mma32_chunk(acc[i][j], fa[ks & 1][i], fb[ks & 1][j], T());
+          mma32_chunk(acc[i][j], fb[ks & 1][j], fa[ks & 1][i], T());
       // order: [reads of step 0]; per step, its MFMAs with the next step's reads spread
       // evenly between them (read r goes before MFMA floor(r * M / R)); measured about 1 %
       // faster on the prefill layers than issuing the reads as one burst
@@ -391,38 +400,106 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // drain the loads issued past the last stage before the block's LDS can be reassigned
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  if (!band_live) return;
-  // lane holds column (lane % 32) and rows 8 * (q / 4) + 4 * (lane / 32) + q % 4 of a tile
+  // Epilogue.  The weight fragment is the MFMA's first operand, so each accumulator tile
+  // is the transposed product: lane L holds activation row L % 32 of the 32 and, in
+  // acc[.][.][4a + b], output column 8a + 4 (L / 32) + b.  The block's outputs go through
+  // LDS in row-major order (4 consecutive columns per lane write) and leave it as 16-byte
+  // stores that cover whole cache lines; storing one element per lane per instruction
+  // straight from the accumulators took 7-17 % of a tile's time (measured per block).
+  // A split reduction adds its fp32 partial sums the same way, one float per lane, so the
+  // atomics of one instruction hit consecutive addresses.
+  __syncthreads();  // every wave's direct loads have landed and its fragment reads are done
   constexpr int NOUT = SWIGLU ? P::NT / 2 : P::NT;
+  const int h4 = 4 * frag_half;
+  auto staged = [&](auto st_tag, auto rd_tag, auto emit) {
+    using ST = decltype(st_tag);                       // staged element type
+    constexpr int RD = decltype(rd_tag)::value;        // bytes each lane reads back
+    constexpr int kRow = BN * (int)sizeof(ST);         // bytes of one staged row
+    constexpr int kChunks = kRow / 16;
+    static_assert(kChunks >= 16 && kChunks % 16 == 0, "swizzle spans 16 chunks");
+    constexpr int kTileRows = P::WM * 32;              // one row tile of every wave band
+    constexpr int IP0 = kLdsAlloc / (kTileRows * kRow);
+    constexpr int IP = IP0 < P::MT ? IP0 : P::MT;      // row tiles per pass
+    static_assert(IP >= 1, "one row tile of the output fits the block's LDS");
+    constexpr int kPer = kTileRows * IP * kRow / RD;   // lane reads per pass
 #pragma unroll
-  for (int i = 0; i < P::MT; ++i) {
+    for (int p0 = 0; p0 < P::MT; p0 += IP) {
+      if (p0 > 0) __syncthreads();  // the previous pass has been read back
+      if (band_live) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = m_begin + wm * P::MT * 32 + i * 32 + 8 * (q >> 2) + 4 * frag_half + (q & 3);
-      if (row >= m_end) continue;
-      const int col0 = nt * BN + wn * NOUT * 32 + frag_row;
-      OutT* crow = C + (int64_t)row * N_out + col0;
+        for (int ii = 0; ii < IP; ++ii) {
+          const int i = p0 + ii;
+          if (i >= P::MT) break;
+          const int srow = (wm * IP + ii) * 32 + frag_row;
+          lds_char* rowp = a0 + srow * kRow;
 #pragma unroll
-      for (int j = 0; j < NOUT; ++j) {
-        if (col0 + j * 32 >= N_out) continue;
-        float v;
-        if (SWIGLU)
-          v = silu_f32(acc[i][j][q]) * acc[i][j + NOUT][q];
-        else
-          v = acc[i][j][q];
-        if (!SWIGLU && Cacc)  // one half of a split reduction: add into the fp32 sums
-          unsafeAtomicAdd(Cacc + (int64_t)row * N_out + col0 + j * 32, v);
-        else if constexpr (std::is_same<OutT, float>::value)  // fp32 output (router logits)
-          crow[j * 32] = col_bias ? v + col_bias[col0 + j * 32] : v;
-        else
-          crow[j * 32] = Elt<T>::from_f32(v);
+          for (int j = 0; j < NOUT; ++j)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const int cb = (((wn * NOUT + j) * 32 + 8 * a + h4) * (int)sizeof(ST));
+              const int off = (((cb >> 4) ^ (srow & 15)) << 4) | (cb & 15);
+              float v[4];
+#pragma unroll
+              for (int b = 0; b < 4; ++b)
+                v[b] = SWIGLU ? silu_f32(acc[i][j][4 * a + b]) * acc[i][j + NOUT][4 * a + b]
+                              : acc[i][j][4 * a + b];
+              if constexpr (sizeof(ST) == 4) {
+                *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(rowp + off) =
+                    f32x4{v[0], v[1], v[2], v[3]};
+              } else {
+                typedef ST stx4 __attribute__((ext_vector_type(4)));
+                *reinterpret_cast<__attribute__((address_space(3))) stx4*>(rowp + off) =
+                    stx4{Elt<ST>::from_f32(v[0]), Elt<ST>::from_f32(v[1]),
+                         Elt<ST>::from_f32(v[2]), Elt<ST>::from_f32(v[3])};
+              }
+            }
+        }
+      }
+      __syncthreads();
+#pragma unroll 2
+      for (int it = 0; it < (kPer + P::kThreads - 1) / P::kThreads; ++it) {
+        const int q = it * P::kThreads + tid;
+        if (kPer % P::kThreads != 0 && q >= kPer) break;
+        const int srow = q / (kRow / RD), cbyte = (q % (kRow / RD)) * RD;
+        const int band = srow / (IP * 32), ii = (srow / 32) % IP;
+        const int row = m_begin + band * P::MT * 32 + (p0 + ii) * 32 + (srow & 31);
+        const int col = nt * BN + cbyte / (int)sizeof(ST);
+        if (p0 + ii >= P::MT || row >= m_end || col >= N_out) continue;
+        const int off = (((cbyte >> 4) ^ (srow & 15)) << 4) | (cbyte & 15);
+        emit(row, col, a0 + srow * kRow + off);
       }
     }
+  };
+  if (!SWIGLU && Cacc) {  // one half of a split reduction: add into the fp32 sums
+    staged(float(), IntC<4>{}, [&](int row, int col, const lds_char* src) {
+      unsafeAtomicAdd(Cacc + (int64_t)row * N_out + col,
+                      *reinterpret_cast<const __attribute__((address_space(3))) float*>(src));
+    });
+  } else if constexpr (std::is_same<OutT, float>::value) {  // fp32 output
+    staged(float(), IntC<16>{}, [&](int row, int col, const lds_char* src) {
+      f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(src);
+      float* dst = C + (int64_t)row * N_out + col;
+      if (col_bias)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) v[b] += col_bias[min(col + b, N_out - 1)];
+      if (N_out % 4 == 0) {
+        *reinterpret_cast<f32x4*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (col + b < N_out) dst[b] = v[b];
+      }
+    });
+  } else {  // bf16 output: N_out is a multiple of 128, so every chunk is whole and aligned
+    staged(OutT(), IntC<16>{}, [&](int row, int col, const lds_char* src) {
+      *reinterpret_cast<u32x4*>(C + (int64_t)row * N_out + col) =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(src);
+    });
   }
 }
 
 // Stage buffers of tile P in the block's LDS, then its body.
-template <class T, bool SWIGLU, class P, class OutT>
+template <class T, bool SWIGLU, class P, class OutT, int kLdsAlloc>
 __device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
     const T* __restrict__ A, const int32_t* __restrict__ a_rows, const T* __restrict__ B0,
     const T* __restrict__ B1, int64_t b_expert_stride, OutT* __restrict__ C,
@@ -431,7 +508,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
   constexpr int SA = P::kABytes, SB = P::kBBytes;
   lds_char* bb = base + P::kAStages * SA;
   // buffers past a ring's stage count are never used
-  prefill_gemm_body<T, SWIGLU, P, OutT>(
+  prefill_gemm_body<T, SWIGLU, P, OutT, kLdsAlloc>(
       A, a_rows, B0, B1, b_expert_stride, C, col_bias, Cacc, K, N_out, e, m_begin, m_end, nt,
       k_first, k_steps, stream_b, base, base + SA, base + (P::kAStages > 2 ? 2 * SA : 0), bb,
       bb + SB, bb + (P::kBStages > 2 ? 2 * SB : 0), bb + (P::kBStages > 3 ? 3 * SB : 0));
@@ -470,6 +547,8 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
                     PW::kThreads == P::kThreads,
                 "the wide tail tile spans one or two n-tiles of the full tile");
   extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
+  // dynamic LDS of the launch (launch_prefill allocates the largest of the three tiles)
+  constexpr int kLds = std::max({P::kLdsBytes, PT::kLdsBytes, PW::kLdsBytes});
   const int bid = blockIdx.x;
   const int per_xcd = gridDim.x >> 3;
   const int logical_all = (bid & 7) * per_xcd + (bid >> 3);
@@ -498,18 +577,18 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
     if constexpr (PW::BNW == 2 * P::BNW) {
       if (table && m_begin - offsets[e] >= 2 * P::BM) {  // at least two full tiles before
         if (nt & 1) return;
-        prefill_gemm_tile<T, SWIGLU, PW, OutT>(A, a_rows, B0, B1, b_expert_stride, C,
+        prefill_gemm_tile<T, SWIGLU, PW, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C,
                                                col_bias, Cacc, K, N_out, e, m_begin, m_end,
                                                nt >> 1, half * k_steps, k_steps,
                                                stream_b != 0, base);
         return;
       }
     }
-    prefill_gemm_tile<T, SWIGLU, PT, OutT>(A, a_rows, B0, B1, b_expert_stride, C, col_bias,
+    prefill_gemm_tile<T, SWIGLU, PT, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C, col_bias,
                                            Cacc, K, N_out, e, m_begin, m_end, nt,
                                            half * k_steps, k_steps, stream_b != 0, base);
   } else
-    prefill_gemm_tile<T, SWIGLU, P, OutT>(A, a_rows, B0, B1, b_expert_stride, C, col_bias, Cacc,
+    prefill_gemm_tile<T, SWIGLU, P, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C, col_bias, Cacc,
                                           K, N_out, e, m_begin, m_end, nt, half * k_steps,
                                           k_steps, stream_b != 0, base);
 }
