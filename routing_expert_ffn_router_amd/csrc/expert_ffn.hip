@@ -35,9 +35,9 @@
 //     The n-group width comes from the launch plan.
 //   - Weights that each tile reads alone (at most two row tiles per expert) are loaded with
 //     the non-temporal hint, so they do not displace the shared activation rows.
-//   - A down GEMM with few, long tiles splits its reduction in two halves that add fp32
-//     partial sums (deterministic with two addends), so the last round of tiles does not
-//     leave most CUs idle.
+//   - A down GEMM with few, long tiles splits its reduction into 2-4 pieces whose fp32
+//     partial sums a second launch adds in a fixed order (deterministic), so the last round
+//     of tiles does not leave most CUs idle.
 //   - Dense mode (no tile table, fp32 output with a column bias) serves the router logits
 //     of shapes with many tokens and experts.
 #include <algorithm>
@@ -278,7 +278,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   const int b_frag = (wn * kNG * 32 + frag_row) * P::kRowBytes;
   const int swz = P::swz(frag_row);
 
-  // stages k_first .. k_first + k_steps - 1 of the reduction (all of it, or one half)
+  // stages k_first .. k_first + k_steps - 1 of the reduction (all of it, or one piece)
   const int KT = k_steps;
   constexpr int SA = P::kAStages, SB = P::kBStages;
   constexpr int DA = SA - 1, DB = SB - 1;  // stages of each ring in flight ahead
@@ -406,8 +406,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // LDS in row-major order (4 consecutive columns per lane write) and leave it as 16-byte
   // stores that cover whole cache lines; storing one element per lane per instruction
   // straight from the accumulators took 7-17 % of a tile's time (measured per block).
-  // A split reduction adds its fp32 partial sums the same way, one float per lane, so the
-  // atomics of one instruction hit consecutive addresses.
+  // A piece of a split reduction stores its fp32 partial sums the same way.
   __syncthreads();  // every wave's direct loads have landed and its fragment reads are done
   constexpr int NOUT = SWIGLU ? P::NT / 2 : P::NT;
   const int h4 = 4 * frag_half;
@@ -470,10 +469,10 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
       }
     }
   };
-  if (!SWIGLU && Cacc) {  // one half of a split reduction: add into the fp32 sums
-    staged(float(), IntC<4>{}, [&](int row, int col, const lds_char* src) {
-      unsafeAtomicAdd(Cacc + (int64_t)row * N_out + col,
-                      *reinterpret_cast<const __attribute__((address_space(3))) float*>(src));
+  if (!SWIGLU && Cacc) {  // one piece of a split reduction: its fp32 partial sums
+    staged(float(), IntC<16>{}, [&](int row, int col, const lds_char* src) {
+      *reinterpret_cast<f32x4*>(Cacc + (int64_t)row * N_out + col) =
+          *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(src);
     });
   } else if constexpr (std::is_same<OutT, float>::value) {  // fp32 output
     staged(float(), IntC<16>{}, [&](int row, int col, const lds_char* src) {
@@ -514,10 +513,9 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
       bb + SB, bb + (P::kBStages > 2 ? 2 * SB : 0), bb + (P::kBStages > 3 ? 3 * SB : 0));
 }
 
-// One block per (m-tile, n-tile), or per (m-tile, n-tile, half of the reduction) when the
-// reduction is split in ksplit = 2 halves (then the halves add their fp32 partial sums into
-// Cacc, which must be zero before the launch: with exactly two addends on +0.0 the sum is
-// the same in either order).  Blocks are dealt round-robin to the 8 XCDs; the logical tile
+// One block per (m-tile, n-tile), or per (m-tile, n-tile, piece of the reduction) when the
+// reduction is split into ksplit pieces (then piece p stores its fp32 partial sums into
+// slot p of Cacc, acc_stride floats apart, for rows_from_slots_kernel to add).  Blocks are dealt round-robin to the 8 XCDs; the logical tile
 // index is remapped so each XCD walks a contiguous range of logical tiles, n fastest within
 // groups of group_n n-tiles.  An m-tile with at most PT::BM rows (an expert's last, partly
 // filled tile) runs the shorter tile PT with the same weight columns: fewer loads and MFMAs
@@ -540,7 +538,7 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
                     int N_out, const int32_t* __restrict__ offsets,
                     const int32_t* __restrict__ table, int m_tiles_max, int n_tiles,
                     int group_n, int grid_logical, int ksplit, int dense_rows,
-                    int stream_b) {
+                    int stream_b, int64_t acc_stride) {
   static_assert(PT::BNW == P::BNW && PT::kThreads == P::kThreads && PT::BM <= P::BM,
                 "the shorter tile shares the n-tiling and the block size");
   static_assert((PW::BNW == P::BNW || PW::BNW == 2 * P::BNW) && PW::BM == PT::BM &&
@@ -553,9 +551,13 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
   const int per_xcd = gridDim.x >> 3;
   const int logical_all = (bid & 7) * per_xcd + (bid >> 3);
   if (logical_all >= grid_logical * ksplit) return;
-  const int half = logical_all / grid_logical;
-  const int logical = logical_all - half * grid_logical;
-  const int k_steps = K * (int)sizeof(T) / P::kRowBytes / ksplit;
+  const int piece = logical_all / grid_logical;
+  const int logical = logical_all - piece * grid_logical;
+  // stages [k_first, k_first + k_steps) of the reduction: all of it, or piece `piece` of
+  // ksplit nearly equal pieces, whose fp32 partial sums go to slot `piece` of Cacc
+  const int KT = K * (int)sizeof(T) / P::kRowBytes;
+  const int k_first = piece * KT / ksplit, k_steps = (piece + 1) * KT / ksplit - k_first;
+  if (Cacc) Cacc += piece * acc_stride;
   const int per_group = m_tiles_max * group_n;
   const int grp = logical / per_group, rem = logical - grp * per_group;
   const int mt = rem / group_n, nt = grp * group_n + (rem - (rem / group_n) * group_n);
@@ -579,37 +581,38 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
         if (nt & 1) return;
         prefill_gemm_tile<T, SWIGLU, PW, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C,
                                                col_bias, Cacc, K, N_out, e, m_begin, m_end,
-                                               nt >> 1, half * k_steps, k_steps,
+                                               nt >> 1, k_first, k_steps,
                                                stream_b != 0, base);
         return;
       }
     }
     prefill_gemm_tile<T, SWIGLU, PT, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C, col_bias,
                                            Cacc, K, N_out, e, m_begin, m_end, nt,
-                                           half * k_steps, k_steps, stream_b != 0, base);
+                                           k_first, k_steps, stream_b != 0, base);
   } else
     prefill_gemm_tile<T, SWIGLU, P, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C, col_bias, Cacc,
-                                          K, N_out, e, m_begin, m_end, nt, half * k_steps,
+                                          K, N_out, e, m_begin, m_end, nt, k_first,
                                           k_steps, stream_b != 0, base);
 }
 
-// Rows [0, offsets[E]) of the fp32 partial sums of a split down GEMM: zeroed before it,
-// converted to the output type after it (d is a multiple of 4).
-__global__ void __launch_bounds__(256)
-zero_rows_f32_kernel(float* __restrict__ acc, const int32_t* __restrict__ offsets, int E,
-                     int64_t d) {
-  const int64_t n = (int64_t)offsets[E] * d / 4;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    reinterpret_cast<f32x4*>(acc)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
+// Rows [0, offsets[E]) of a split down GEMM: the sum of its `pieces` fp32 partial-sum slots
+// (slot stride `stride` floats), added in slot order so the result does not depend on which
+// piece finished first, converted to the output type (d is a multiple of 4).
 template <class T>
 __global__ void __launch_bounds__(256)
-rows_from_f32_kernel(const float* __restrict__ acc, const int32_t* __restrict__ offsets, int E,
-                     int64_t d, T* __restrict__ y) {
+rows_from_slots_kernel(const float* __restrict__ acc, int pieces, int64_t stride,
+                       const int32_t* __restrict__ offsets, int E, int64_t d,
+                       T* __restrict__ y) {
   const int64_t n = (int64_t)offsets[E] * d / 4;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * 256) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(acc)[i];
+    f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(acc) + i);
+    for (int p = 1; p < pieces; ++p) {
+      const f32x4 w =
+          __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(acc + p * stride) + i);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] += w[c];
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) y[4 * i + c] = Elt<T>::from_f32(v[c]);
   }
@@ -655,17 +658,22 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad
   const int64_t m_cap = E * ((C + p.bm - 1) / p.bm);
   p.m_max = m_cap < m_max ? m_cap : m_max;
   if (p.m_max < 0) p.m_max = 0;
-  // Down GEMM with few, long tiles: when the tile count (at most m_max x ceil(d / 256)) just
-  // exceeds a multiple of the 256 CUs, half the chip idles through the last round.  Split
-  // the reduction in two halves when that fills the rounds clearly better (in whole-tile
-  // time, rounds(2t) / 2 <= 0.85 rounds(t)), the reduction has an even number of at least
-  // 32 128-byte stages, and the tiles are prefill tiles.
+  // Down GEMM with few, long tiles: when the tile count t (at most m_max x ceil(d / 256))
+  // fills fewer than two rounds of the 256 CUs, much of the chip idles through the last
+  // one.  Split the reduction into S pieces, S aiming at about four rounds of pieces, at
+  // most 4 and at least 16 128-byte stages each, when that fills the rounds clearly better
+  // (in whole-tile time, rounds(S t) / S <= 0.85 rounds(t)) and the tiles are prefill
+  // tiles.  Each piece writes fp32 partial sums of its own, so S costs S x N x d x 4 bytes
+  // of stores and reads: measured on Mixtral-8x22B (t <= 384), three pieces -3.3 % on the
+  // layer against two -1.2 % and four -1.4 %.
   p.down_split = 1;
   const int64_t tiles = p.m_max * ((d + 255) / 256), stages = F * elt / 128, cus = 256;
   const auto rounds = [&](int64_t t) { return (t + cus - 1) / cus; };
-  if (!p.small && tiles > 0 && F * elt % 256 == 0 && stages >= 32 &&
-      100 * rounds(2 * tiles) <= 170 * rounds(tiles))
-    p.down_split = 2;
+  if (!p.small && tiles > 0 && tiles < 2 * cus) {
+    const int64_t split = std::min<int64_t>({(4 * cus + tiles - 1) / tiles, 4, stages / 16});
+    if (split >= 2 && 100 * rounds(split * tiles) <= 85 * split * rounds(tiles))
+      p.down_split = (int)split;
+  }
   return p;
 }
 
@@ -678,7 +686,7 @@ hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const 
                           const int32_t* table, int64_t m_max, hipStream_t s,
                           int ksplit = 1, float* c_acc = nullptr,
                           const float* col_bias = nullptr, int dense_rows = 0,
-                          bool stream_b = false, int group_cap = 8) {
+                          bool stream_b = false, int group_cap = 8, int64_t acc_stride = 0) {
   if (m_max <= 0) return hipSuccess;
   constexpr int BN = SW ? P::BNW / 2 : P::BNW;
   const int n_tiles = (N_out + BN - 1) / BN;
@@ -692,7 +700,7 @@ hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const 
   if (e != hipSuccess) return e;
   prefill_gemm_kernel<T, SW, P, PT, OutT, PW><<<(unsigned)grid, P::kThreads, lds, s>>>(
       A, a_rows, B0, B1, b_stride, C, col_bias, c_acc, K, N_out, offsets, table, (int)m_max,
-      n_tiles, group_n, (int)logical, ksplit, dense_rows, stream_b ? 1 : 0);
+      n_tiles, group_n, (int)logical, ksplit, dense_rows, stream_b ? 1 : 0, acc_stride);
   return hipGetLastError();
 }
 
@@ -733,26 +741,25 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
     return launch_prefill<T, false, DecodeDownTile, DecodeDownTile>(
         h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F, (int)a.d, a.offsets,
         a.sched, p.m_max, s, 1, nullptr, nullptr, 0, p.stream_b, p.group_cap);
-  // split reduction: zero the fp32 sums of rows [0, N), let both halves add into them,
-  // then convert the rows to the output type
+  // split reduction: each piece stores the fp32 partial sums of its rows into a slot of
+  // a.down_acc ([pieces, R, d]); a second launch adds the slots in order and converts
   const int ks = p.down_split;
   float* acc = ks > 1 ? a.down_acc : nullptr;
-  const unsigned ew_blocks = (unsigned)std::min<int64_t>((a.R * a.d / 4 + 255) / 256, 4096);
-  if (ks > 1) {
-    zero_rows_f32_kernel<<<ew_blocks, 256, 0, s>>>(acc, a.offsets, (int)a.E, a.d);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const int64_t slot = a.R * a.d;
   const hipError_t e =
       p.tile == 2
           ? launch_prefill<T, false, PrefillTallTile, PrefillTailTile, T, PrefillTailWideTile>(
                 h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F, (int)a.d,
-                a.offsets, a.sched, p.m_max, s, ks, acc, nullptr, 0, p.stream_b, p.group_cap)
+                a.offsets, a.sched, p.m_max, s, ks, acc, nullptr, 0, p.stream_b, p.group_cap,
+                slot)
           : launch_prefill<T, false>(
                 h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F, (int)a.d,
-                a.offsets, a.sched, p.m_max, s, ks, acc, nullptr, 0, p.stream_b, p.group_cap);
+                a.offsets, a.sched, p.m_max, s, ks, acc, nullptr, 0, p.stream_b, p.group_cap,
+                slot);
   if (e != hipSuccess || ks == 1) return e;
-  rows_from_f32_kernel<T><<<ew_blocks, 256, 0, s>>>(acc, a.offsets, (int)a.E, a.d, y);
+  const unsigned ew_blocks = (unsigned)std::min<int64_t>((a.R * a.d / 4 + 255) / 256, 4096);
+  rows_from_slots_kernel<T><<<ew_blocks, 256, 0, s>>>(acc, ks, slot, a.offsets, (int)a.E, a.d,
+                                                      y);
   return hipGetLastError();
 }
 

@@ -57,7 +57,7 @@ struct FfnPlan {
   int tile;        // 0 decode, 1 prefill 256 rows, 2 prefill 320 rows
   int bm;
   int64_t m_max;   // upper bound on m-tiles over all experts
-  int down_split;  // 1, or 2: the down GEMM splits its reduction in two halves
+  int down_split;  // 1, or the number of pieces the down GEMM splits its reduction into
   bool stream_b;   // weight loads carry the non-temporal hint (each line read by ~1 tile)
   int group_cap;   // n-tiles per launch-order group (each XCD walks groups of m x group)
 };
@@ -66,9 +66,9 @@ struct FfnPlan {
 FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad, int64_t d,
                  int64_t F, int64_t elt);
 inline int64_t ffn_table_ints(const FfnPlan& p) { return 1 + 2 * p.m_max; }
-// fp32 [R, d] partial sums of a split down GEMM (0 bytes when it does not split)
+// fp32 [down_split, R, d] partial sums of a split down GEMM (0 bytes when it does not split)
 inline int64_t ffn_down_acc_bytes(const FfnPlan& p, int64_t R, int64_t d) {
-  return p.down_split > 1 ? R * d * 4 : 0;
+  return p.down_split > 1 ? p.down_split * R * d * 4 : 0;
 }
 
 struct FfnArgs {
@@ -85,7 +85,7 @@ struct FfnArgs {
   void* h;               // [R, F]
   int32_t* sched;        // ffn_table_ints() ints
   void* y_perm;          // [R, d]
-  float* down_acc;       // [R, d] fp32, used when the plan splits the down GEMM
+  float* down_acc;       // [down_split, R, d] fp32, used when the plan splits the down GEMM
   bool table_ready;      // sched already holds this call's tile table (skip rebuilding it)
 };
 // S1 through the grouped-GEMM pipeline in dense mode (64 x 128 tiles, fp32 out + bias),

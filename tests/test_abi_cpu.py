@@ -66,24 +66,27 @@ def _down_acc_bytes(s):
 
 
 def test_down_split_region():
-    # The down GEMM splits its reduction when ceil(2t / 256) / 2 <= 0.85 ceil(t / 256) for
-    # t = m-tiles (upper bound) x ceil(d / 256), with an even number of >= 32 128-byte
-    # stages; then the workspace holds fp32 [R, d] partial sums (last region).
-    # Mixtral-8x22B-shaped, C = 640: t <= 16 x 24 = 384 (2 rounds), split 768 (3 half
-    # rounds = 1.5) -> splits.
+    # The down GEMM splits its reduction into S pieces when t = m-tiles (upper bound) x
+    # ceil(d / 256) is below two rounds of 256 CUs: S = min(ceil(1024 / t), 4, stages / 16)
+    # with stages = F * elt / 128, kept when S >= 2 and ceil(S t / 256) / S <= 0.85
+    # ceil(t / 256).  The workspace then ends with fp32 [S, R, d] partial sums.
+    # Mixtral-8x22B-shaped, C = 640: t <= 16 x 24 = 384, S = 3: 5 rounds of thirds (1.67)
+    # against 2 whole -> splits in three.
     s = moe.shape(2048, 6144, 8, 2, 16384, 640)
-    assert _down_acc_bytes(s) == 4096 * 6144 * 4
-    # Mixtral-8x7B-shaped: t <= 32 x 16 = 512 = 2 rounds exactly -> no split
+    assert _down_acc_bytes(s) == 3 * 4096 * 6144 * 4
+    # Mixtral-8x7B-shaped: t <= 32 x 16 = 512 = 2 rounds -> no split
     assert _down_acc_bytes(moe.shape(4096, 4096, 8, 2, 14336, 1280)) == 0
     # decode-sized experts stream weights: never split
     assert _down_acc_bytes(moe.shape(256, 7168, 256, 8, 2048, 0)) == 0
     # DeepSeek-V3 mixed batch: t = 256 x 28 = 28 rounds -> no split
     assert _down_acc_bytes(moe.shape(8192, 7168, 256, 8, 2048, 256)) == 0
-    # a short reduction (F * 2 / 128 = 6 stages) does not split; a long one does
+    # a short reduction (F * 2 / 128 = 6 stages) does not split; 32 stages allow two
+    # pieces, 64 stages four (t = 8 m-tiles x 1)
     assert _down_acc_bytes(moe.shape(700, 256, 8, 2, 384, 219)) == 0
-    assert _down_acc_bytes(moe.shape(700, 256, 8, 2, 2048, 219)) == 1400 * 256 * 4
-    # fp32: 4-byte elements, F = 1024 is 32 stages; F = 896 is 28 -> none
-    assert _down_acc_bytes(moe.shape(600, 256, 4, 2, 1024, 300, moe.MOE_F32)) == 1200 * 256 * 4
+    assert _down_acc_bytes(moe.shape(700, 256, 8, 2, 2048, 219)) == 2 * 1400 * 256 * 4
+    assert _down_acc_bytes(moe.shape(700, 256, 8, 2, 4096, 219)) == 4 * 1400 * 256 * 4
+    # fp32: 4-byte elements, F = 1024 is 32 stages (two pieces); F = 896 is 28 -> none
+    assert _down_acc_bytes(moe.shape(600, 256, 4, 2, 1024, 300, moe.MOE_F32)) == 2 * 1200 * 256 * 4
     assert _down_acc_bytes(moe.shape(600, 256, 4, 2, 896, 300, moe.MOE_F32)) == 0
 
 

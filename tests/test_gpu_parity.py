@@ -35,6 +35,8 @@ SMALL = {
     # few, long down-GEMM tiles: the down GEMM splits its reduction in two halves
     "bf16_e8_split_down": W("bf16_e8_split_down", 700, 256, 8, 2, 2048, 1.25, "bf16", 1.1),
     "f32_e4_split_down": W("f32_e4_split_down", 600, 256, 4, 2, 1024, 1.0, "f32"),
+    # a reduction of 64 stages over 8 m-tiles: the down GEMM splits it into four pieces
+    "bf16_e8_split4_down": W("bf16_e8_split4_down", 700, 256, 8, 2, 4096, 1.25, "bf16", 1.1),
     # 320-row tiles where an expert's last tile (<= 128 rows) follows two or more full
     # tiles, so it runs double width over two n-tiles: kept rows [1085, 615] with an odd
     # n-tile count in the gate/up GEMM (F / 128 = 3) and a ragged one in the down GEMM
@@ -253,7 +255,8 @@ def test_dispatch_invalid_and_duplicate_ids():
 @pytest.mark.parametrize("name", ["tiny_f32", "bf16_e8_big_tiles", "bf16_e16_small_tiles",
                                   "bf16_e256_k8_decode", "f32_e4_big_tiles",
                                   "bf16_e8_zipf_drops", "bf16_e3_k3", "bf16_e2_wide_tail",
-                                  "f32_e2_wide_tail", "bf16_e4_wide_tail_split"])
+                                  "f32_e2_wide_tail", "bf16_e4_wide_tail_split",
+                                  "bf16_e8_split4_down"])
 def test_expert_ffn(name):
     w = SMALL[name]
     log(f"expert_ffn {w}")
@@ -279,6 +282,37 @@ def test_expert_ffn(name):
     log(f"  N={N} rel err {err:.3e}")
     assert err <= (1e-5 if w.dtype == "f32" else OUT_TOL)
     assert np.all(np.isfinite(to_host(y[:N])))
+
+
+@pytest.mark.parametrize("name", ["bf16_e8_split_down", "f32_e4_split_down",
+                                  "bf16_e8_split4_down", "bf16_e4_wide_tail_split"])
+def test_split_down_deterministic(name):
+    # A split down GEMM adds its pieces' fp32 partial-sum slots in slot order, so two runs
+    # give the same bits; the second starts from a workspace of all-ones bytes (NaN floats
+    # in every slot), which must not reach any kept row.
+    w = SMALL[name]
+    log(f"split down determinism {w}")
+    h = host_inputs(w)
+    dt = torch_dtype(w)
+    s = shape_of(w)
+    assert moe.workspace_size(s) > moe.workspace_layout(s)["down_acc"], "shape must split"
+    L = oracle.router_logits(h["x"], h["w_router"], h["b_router"])
+    tab = oracle.dispatch(oracle.select_topk(L, w.k), w.E, s.capacity)
+    N, R = tab["n_kept"], moe.max_rows(s)
+    xp = np.zeros((R, w.d), np.float32)
+    xp[:N] = oracle.permute(h["x"], tab["src_token"], N)
+    args = (to_device(xp, dt), to_device(tab["expert_offsets"].astype(np.int32), torch.int32),
+            to_device(h["w_gate"], dt), to_device(h["w_up"], dt), to_device(h["w_down"], dt))
+    ws = torch.zeros(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
+    ys = []
+    for fill in (0, 255):
+        ws.fill_(fill)
+        y = torch.zeros((R, w.d), dtype=dt, device="cuda")
+        moe.expert_ffn(s, *args, ws, y)
+        torch.cuda.synchronize()
+        ys.append(to_host(y[:N]))
+    assert np.all(np.isfinite(ys[1]))
+    assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
 
 
 @pytest.mark.parametrize("name,pad", [("bf16_e8_big_tiles", False), ("bf16_e8_zipf_drops", False),
