@@ -32,7 +32,7 @@ SMALL = {
     "bf16_e1024_k64_max": W("bf16_e1024_k64_max", 96, 128, 1024, 64, 128, 1.0, "bf16", 0.02),
     # one expert: every token takes it, the gate is exactly 1
     "f32_e1_k1": W("f32_e1_k1", 300, 128, 1, 1, 256, None, "f32"),
-    # few, long down-GEMM tiles: the down GEMM splits its reduction in two halves
+    # few, long down-GEMM tiles (32 stages): the down GEMM splits its reduction in two pieces
     "bf16_e8_split_down": W("bf16_e8_split_down", 700, 256, 8, 2, 2048, 1.25, "bf16", 1.1),
     "f32_e4_split_down": W("f32_e4_split_down", 600, 256, 4, 2, 1024, 1.0, "f32"),
     # a reduction of 64 stages over 8 m-tiles: the down GEMM splits it into four pieces
