@@ -134,11 +134,14 @@ def test_router_logits(name):
 @pytest.mark.parametrize("T,d,E,dtype", [(2048, 256, 1024, "bf16"), (2047, 128, 1000, "f32"),
                                          (12300, 128, 100, "f32"), (6100, 256, 256, "bf16"),
                                          (600, 256, 1000, "bf16"), (1000, 128, 512, "bf16"),
-                                         (300, 128, 40, "bf16"), (8200, 128, 40, "f32")])
+                                         (300, 128, 40, "bf16"), (8200, 128, 40, "f32"),
+                                         (12300, 128, 102, "bf16")])
 def test_router_logits_tile_shapes(T, d, E, dtype):
     # sizes that select each router path: the expert-GEMM pipeline in dense mode (64 x 128
     # tiles, >= 192 of them; expert counts below one tile, at two tiles and ragged, ragged
-    # token tails), then the skinny kernel's 16 x 64 and 16 x 16 tiles
+    # token tails, and E = 102, whose rows do not start on 16-byte boundaries, so the
+    # epilogue stores element by element), then the skinny kernel's 16 x 64 and 16 x 16
+    # tiles
     log(f"router tiles T={T} d={d} E={E} {dtype}")
     rng = np.random.default_rng(T + E)
     x = rng.standard_normal((T, d)).astype(np.float32)
