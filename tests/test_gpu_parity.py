@@ -540,3 +540,38 @@ def test_layer_graph_replay_matches_eager(name, flags):
         assert torch.equal(lay.routed_counts, eager.routed_counts)
         assert torch.equal(lay.drops, eager.drops)
         assert torch.equal(lay.view("dest_row"), eager.view("dest_row"))
+
+
+# ------------------------------------------------------------------------------- streams
+def test_layers_on_two_streams_match_one_stream():
+    # Calls with distinct workspaces and outputs may run concurrently on different streams:
+    # two layers of different shapes (one with decode-sized experts, one whose down GEMM
+    # splits its reduction), enqueued alternately on two streams of default priority,
+    # reproduce their one-stream results bit for bit.
+    runs = []
+    for name in ("bf16_e256_k8_drops", "bf16_e8_split_down"):
+        w = SMALL[name]
+        d_in = device_inputs(w)
+        s = shape_of(w)
+        args = (d_in["x"], d_in["w_router"], d_in["b_router"], d_in["w_gate"], d_in["w_up"],
+                d_in["w_down"])
+        ref = moe.MoELayer(s)
+        ref(*args)
+        runs.append((moe.MoELayer(s), ref, args))
+    torch.cuda.synchronize()
+    streams = (torch.cuda.Stream(), torch.cuda.Stream())
+    for rep in range(3):
+        for lay, _, _ in runs:
+            lay.out.fill_(0)
+            lay.routed_counts.fill_(-1)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            for (lay, _, args), st in zip(runs, streams):
+                with torch.cuda.stream(st):
+                    lay(*args)
+        torch.cuda.synchronize()
+        for lay, ref, _ in runs:
+            assert torch.equal(lay.out, ref.out), f"rep {rep}"
+            assert torch.equal(lay.routed_counts, ref.routed_counts)
+            assert torch.equal(lay.drops, ref.drops)
+            assert torch.equal(lay.view("dest_row"), ref.view("dest_row"))
