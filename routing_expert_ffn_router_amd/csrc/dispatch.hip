@@ -68,7 +68,10 @@ scan_kernel(const int32_t* __restrict__ hist, int ntiles, int E, int C, int k, b
   const int chunk = (ntiles + q - 1) / q;
   const int t_begin = part * chunk, t_end = min(ntiles, t_begin + chunk);
   int sum = 0;
+  // unrolled so that several of the loads are in flight at once (the trip count is a
+  // runtime value; rolled, each load waited for the one before)
   if (live)
+#pragma unroll 8
     for (int t = t_begin; t < t_end; ++t) sum += hist[(int64_t)t * E + e];
   s_part[tid] = sum;
   __syncthreads();
@@ -79,6 +82,7 @@ scan_kernel(const int32_t* __restrict__ hist, int ntiles, int E, int C, int k, b
       if (p < part) run += v;
       total_e += v;
     }
+#pragma unroll 8
     for (int t = t_begin; t < t_end; ++t) {
       const int64_t i = (int64_t)t * E + e;
       const int h = hist[i];
