@@ -387,14 +387,13 @@ def main():
     routed = lay.routed_counts.cpu().numpy().astype(np.int64)
     kept = lay.tokens_per_expert.cpu().numpy().astype(np.int64)
     drops = lay.drops.cpu().numpy().astype(np.int64)
-    N = int(kept.sum())
-    E_active = int((kept > 0).sum())
-    srt = np.sort(routed)
-    mu = routed.sum() / w.E
+    rec = moe.expert_stats(w.T, w.k, routed, kept)  # the library's S9 record
+    N = rec["kept_rows"]
+    E_active = rec["active_experts"]
     stats = {"active_tokens": w.T, "top_k": w.k, "capacity": C,
-             "expert_p50": int(srt[max(0, math.ceil(0.5 * w.E) - 1)]),
-             "expert_p95": int(srt[max(0, math.ceil(0.95 * w.E) - 1)]),
-             "expert_max": int(srt[-1]), "expert_max_to_mean": round(float(srt[-1] / mu), 4),
+             "expert_p50": rec["expert_p50"], "expert_p95": rec["expert_p95"],
+             "expert_max": rec["expert_max"],
+             "expert_max_to_mean": round(rec["expert_max_to_mean"], 4),
              "dropped_tokens": int(drops[0]), "dropped_per_slot": drops[1:w.k + 1].tolist(),
              "fully_dropped_tokens": int(drops[w.k + 1]), "kept_rows": N,
              "active_experts": E_active}
@@ -410,7 +409,7 @@ def main():
     kbs = torch.empty_like(rbs)
     moe.slot_counts(s, lay.view("topk_idx"), lay.view("dest_row"), rbs, kbs)
     placement = np.arange(w.E) * args.ep // w.E
-    rec = moe.routing_record(rbs.cpu().numpy(), kbs.cpu().numpy(), placement,
+    rec = moe.routing_record(w.T, rbs.cpu().numpy(), kbs.cpu().numpy(), placement,
                              args.ranks_per_node)
     stats["routing"] = {
         "top_5_percent_expert_share": round(rec["top_5_percent_expert_share"], 4),

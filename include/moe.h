@@ -130,19 +130,111 @@ typedef enum {
 int64_t moe_capacity(int64_t T, int64_t k, int64_t E, double cf);
 
 /* Row slots R of x_perm, y_perm and src_token: min(T*k, E*C) with C = T when unlimited,
- * or E*C with MOE_FLAG_PAD_TO_CAPACITY.  Returns -1 for an invalid shape.  Host function. */
+ * or E*C with MOE_FLAG_PAD_TO_CAPACITY ([EP-serving] "Technical details": expert buffers
+ * sized by the capacity; [EP-checks] "Capacity factor changes quality, memory and tail
+ * latency": the capacity bounds what each expert's buffer must hold).  Returns -1 for an
+ * invalid shape.  Host function. */
 int64_t moe_max_rows(const moe_shape* shape);
 
 /* Bytes of device workspace that any call below needs for this shape (the same size
- * serves all of them); 0 for an invalid shape.  Host function. */
+ * serves all of them); 0 for an invalid shape.  [EP-checks] "Memory must be counted by
+ * phase": the dispatch and combine buffers and the MoE temporaries are a line of their own
+ * in the memory sheet, sized from the shape and capacity, not from the active parameters.
+ * Host function. */
 size_t moe_workspace_size(const moe_shape* shape);
 
 /* Byte offsets (host array of MOE_WS_COUNT) of each region in the workspace; a region of
- * size 0 still gets an offset.  Returns a moe_status.  Host function. */
+ * size 0 still gets an offset.  Regions are 256-byte aligned and laid out in the order of
+ * moe_ws_region, so a region's size is bounded by the next offset (the last one by
+ * moe_workspace_size).  [EP-checks] "Memory must be counted by phase" (which buffer each
+ * stage holds).  Returns a moe_status.  Host function. */
 int moe_workspace_layout(const moe_shape* shape, int64_t* offsets);
 
 /* Human-readable name of a moe_status value (static string).  Host function. */
 const char* moe_status_string(int status);
+
+/* Phases of moe_layer at which [EP-checks] "Memory must be counted by phase" asks for the
+ * memory held: before the MoE layer, after packing, after dispatch, after the expert
+ * compute.  At expert-parallel size 1 the dispatch exchange moves nothing, so the figures
+ * after packing and after dispatch are equal (a multi-GPU exchange would add its receive
+ * buffers at the second). */
+typedef enum {
+  MOE_PHASE_BEFORE_LAYER = 0,
+  MOE_PHASE_AFTER_PACK,     /* router tables, dispatch tables, x_perm when it is copied */
+  MOE_PHASE_AFTER_DISPATCH, /* equal to MOE_PHASE_AFTER_PACK on one GPU */
+  MOE_PHASE_AFTER_EXPERTS,  /* + the tile table, h, y_perm and any split-reduction slots */
+  MOE_PHASE_COUNT
+} moe_phase;
+
+/* Bytes of the workspace that moe_layer has written by the end of each moe_phase
+ * ([EP-checks] "Memory must be counted by phase"), as sums of the exact sizes of the
+ * regions each stage writes (moe_ws_region; row regions at their bound R = moe_max_rows,
+ * so these are upper bounds of what one call touches), assuming the optional outputs of
+ * moe_layer (routed_counts, tokens_per_expert, drops, status) are NULL and so kept in the
+ * workspace.  A gathered layer (see moe_layer) does not count x_perm.  The workspace itself
+ * is allocated once by the caller: these figures say how much of it each phase needs.
+ *   bytes  host array of MOE_PHASE_COUNT int64, out.
+ * Returns a moe_status.  Host function. */
+int moe_workspace_phases(const moe_shape* shape, int64_t* bytes);
+
+/* S9: the per-layer expert statistics record of [EP-checks] "Mean expert load proves
+ * almost nothing" (counts per expert after top-k, mean = sum / E, p50, p95, max, max over
+ * mean, the share held by the busiest 5 % of the experts, drops).  Readings: the record is
+ * over routed counts n_e (before capacity truncation, so a hot expert shows above the
+ * capacity); p50 and p95 are nearest ranks, the ceil(q E)-th smallest count with q E
+ * evaluated in IEEE double; the busiest 5 % are the ceil(0.05 E) largest counts. */
+typedef struct {
+  int64_t active_tokens;             /* T */
+  int64_t top_k;                     /* k */
+  int64_t experts;                   /* E */
+  int64_t routed;                    /* sum of n_e */
+  int64_t expert_p50;                /* nearest-rank median of n_e */
+  int64_t expert_p95;                /* nearest-rank 95th percentile of n_e */
+  int64_t expert_max;                /* max n_e */
+  double expert_mean;                /* sum n_e / E */
+  double expert_max_to_mean;         /* max / mean; NaN when nothing was routed */
+  int64_t top_5_percent_experts;     /* ceil(0.05 E) */
+  double top_5_percent_expert_share; /* their share of sum n_e; 0 when nothing was routed */
+  int64_t kept_rows;                 /* sum c_e (sum n_e without tokens_per_expert) */
+  int64_t active_experts;            /* experts with c_e > 0 */
+  int64_t dropped_tokens;            /* dropped assignments, sum (n_e - c_e) */
+} moe_expert_stats_t;
+
+/* Fill *out from host copies of the counts of one layer.
+ *   routed_counts      [E] int32 host, n_e >= 0
+ *   tokens_per_expert  [E] int32 host, nullable: c_e with 0 <= c_e <= n_e (NULL: no drops)
+ * Returns MOE_ERR_INVALID_ARG for T < 0, k < 1, E < 1, null pointers or counts outside
+ * those ranges.  Host function. */
+int moe_expert_stats(int64_t T, int64_t k, int64_t E, const int32_t* routed_counts,
+                     const int32_t* tokens_per_expert, moe_expert_stats_t* out);
+
+/* Per-slot record ([EP-checks] "Top-2 does not insure against hot experts": the second
+ * choice can pile onto the same hot experts, and which choices get dropped matters), from
+ * host copies of moe_slot_counts' tables.
+ *   routed_by_slot, kept_by_slot  [k, E] int32 host (kept <= routed entry by entry)
+ *   slot_max_to_mean    [k] double out: max_e routed_by_slot[j][e] / (T / E), the
+ *                       imbalance of the (j+1)-th choice alone (0 when T = 0)
+ *   drop_share_per_slot [k] double out: dropped assignments of slot j over all dropped
+ *                       ones (0 when nothing was dropped)
+ * Returns a moe_status.  Host function. */
+int moe_slot_stats(int64_t T, int64_t k, int64_t E, const int32_t* routed_by_slot,
+                   const int32_t* kept_by_slot, double* slot_max_to_mean,
+                   double* drop_share_per_slot);
+
+/* Load per rank and per node under a placement of the experts ([EP-checks] "Expert and GPU
+ * can be balanced differently": balanced experts do not make balanced GPUs).
+ *   routed_counts  [E] int32 host
+ *   placement      [E] int32 host: rank holding expert e, in [0, n_ranks)
+ *   ranks_per_node 0: no node figures; else ranks r * ranks_per_node ... form node r
+ *   rank_load      [n_ranks] int64 out: sum of n_e over the rank's experts
+ *   node_load      [ceil(n_ranks / ranks_per_node)] int64 out (nullable when
+ *                  ranks_per_node is 0)
+ *   max_to_mean    [2] double out: max over mean of the rank loads, then of the node loads
+ *                  (0 when nothing was routed or without nodes)
+ * Returns a moe_status.  Host function. */
+int moe_placement_load(int64_t E, const int32_t* routed_counts, const int32_t* placement,
+                       int64_t n_ranks, int64_t ranks_per_node, int64_t* rank_load,
+                       int64_t* node_load, double* max_to_mean);
 
 /*
  * moe_route -- S1 router logits and S2 top-k gating.
@@ -183,6 +275,9 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router,
  *   tokens_per_expert [E] int32 out: c_e = min(n_e, C)
  *   expert_offsets    [E+1] int32 out: exclusive scan of c_e
  *   src_token         [R] int32 out: token of each kept row, -1 for every other slot
+ *   src_slot          [R] int32 out, nullable: slot j of the assignment (t, j) each kept
+ *                     row holds, -1 for every other slot (dest_row inverted:
+ *                     dest_row[src_token[r], src_slot[r]] = r)
  *   dest_row          [T, k] int32 out: row of each assignment in x_perm, -1 if dropped
  *   drops             [k+2] int32 out (see above)
  *   x_perm            [R, d] dtype out: x_perm[r] = x[src_token[r]] for kept rows; nullable:
@@ -192,7 +287,8 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router,
 int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const void* x,
                  void* workspace, size_t workspace_bytes, int32_t* routed_counts,
                  int32_t* tokens_per_expert, int32_t* expert_offsets, int32_t* src_token,
-                 int32_t* dest_row, int32_t* drops, void* x_perm, hipStream_t stream);
+                 int32_t* src_slot, int32_t* dest_row, int32_t* drops, void* x_perm,
+                 hipStream_t stream);
 
 /*
  * moe_expert_ffn -- S6-S7: grouped SwiGLU FFN over the expert-contiguous rows.

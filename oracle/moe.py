@@ -257,6 +257,31 @@ def expert_ffn(x_perm: np.ndarray, expert_offsets: np.ndarray, w_gate, w_up, w_d
     return Y
 
 
+def expert_ffn_streamed(x: np.ndarray, src_token: np.ndarray, expert_offsets: np.ndarray,
+                        expert_weights: Callable[[int], tuple],
+                        progress: Optional[Callable[[int], None]] = None) -> np.ndarray:
+    """expert_ffn(permute(x, src_token, N), expert_offsets, ...) for layers whose weights are
+    too large to hold at once: Y[r] = FFN_e(x[src_token[r]]) for the rows r of each expert's
+    segment [off_e, off_{e+1}), with expert_weights(e) -> (Wg_e, Wu_e, Wd_e) called only for
+    experts that hold rows, one expert at a time.  Same steps as expert_ffn, in the same
+    expert order; progress(e), if given, is called after each expert."""
+    off = np.asarray(expert_offsets, dtype=np.int64)
+    src = np.asarray(src_token, dtype=np.int64)
+    E = off.shape[0] - 1
+    N = int(off[E])
+    Y = np.zeros((N, np.asarray(x).shape[1]), dtype=np.float64)
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            rows = src[a:b]
+            assert np.all(rows >= 0), "a kept row slot without a token"
+            wg, wu, wd = expert_weights(e)
+            Y[a:b] = swiglu_ffn(np.asarray(x)[rows], wg, wu, wd)
+        if progress is not None:
+            progress(e)
+    return Y
+
+
 # ------------------------------------------------------------------------------------------
 # S8  combine
 # ------------------------------------------------------------------------------------------

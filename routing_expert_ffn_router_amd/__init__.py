@@ -30,6 +30,8 @@ MOE_FLAG_PAD_TO_CAPACITY = 1
 MOE_FLAG_SLOT_MAJOR = 2
 MOE_FLAG_BIAS_SELECTION_ONLY = 4
 
+PHASES = ["before_layer", "after_pack", "after_dispatch", "after_experts"]
+
 WS_REGIONS = ["logits", "topk_idx", "topk_w", "routed", "kept", "offsets", "src_token",
               "dest_row", "drops", "status", "tile_hist", "tile_base", "sched", "x_perm", "h",
               "y_perm", "down_acc"]
@@ -46,6 +48,22 @@ class MoeShape(ctypes.Structure):
                 f"capacity={self.capacity}, dtype={'bf16' if self.dtype == 1 else 'f32'}, "
                 f"flags={self.flags}, n_groups={self.n_groups}, "
                 f"topk_groups={self.topk_groups})")
+
+
+class ExpertStats(ctypes.Structure):
+    """moe_expert_stats_t: the per-layer expert statistics record (see include/moe.h)."""
+    _fields_ = [("active_tokens", ctypes.c_int64), ("top_k", ctypes.c_int64),
+                ("experts", ctypes.c_int64), ("routed", ctypes.c_int64),
+                ("expert_p50", ctypes.c_int64), ("expert_p95", ctypes.c_int64),
+                ("expert_max", ctypes.c_int64), ("expert_mean", ctypes.c_double),
+                ("expert_max_to_mean", ctypes.c_double),
+                ("top_5_percent_experts", ctypes.c_int64),
+                ("top_5_percent_expert_share", ctypes.c_double),
+                ("kept_rows", ctypes.c_int64), ("active_experts", ctypes.c_int64),
+                ("dropped_tokens", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class MoeError(RuntimeError):
@@ -66,6 +84,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    if path == LIB_PATH:
+        from . import _build
+
+        if not _build.is_current():
+            raise RuntimeError(f"{path} was built from other sources than the ones in "
+                               "csrc/ and include/; run __graft_entry__.build() again")
     # torch ships its own HIP runtime with the same soname as the system one; importing
     # torch first makes libmoe.so bind to that copy, so tensors, streams and kernels all
     # live in one runtime (two copies in one process break launches on torch's streams).
@@ -78,9 +102,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_max_rows": (i64, [_S]),
         "moe_workspace_size": (sz, [_S]),
         "moe_workspace_layout": (i32, [_S, ctypes.POINTER(i64)]),
+        "moe_workspace_phases": (i32, [_S, ctypes.POINTER(i64)]),
+        "moe_expert_stats": (i32, [i64, i64, i64, _P, _P, ctypes.POINTER(ExpertStats)]),
+        "moe_slot_stats": (i32, [i64, i64, i64, _P, _P, _P, _P]),
+        "moe_placement_load": (i32, [i64, _P, _P, i64, i64, _P, _P, _P]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_route": (i32, [_S, _P, _P, _P, _P, i32, _P, _P, _P, _P]),
-        "moe_dispatch": (i32, [_S, _P, _P, _P, sz, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "moe_dispatch": (i32, [_S, _P, _P, _P, sz, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "moe_expert_ffn": (i32, [_S, _P, _P, _P, _P, _P, _P, sz, _P, _P]),
         "moe_expert_gate_up": (i32, [_S, _P, _P, _P, _P, _P, sz, _P, _P]),
         "moe_expert_gate_up_gathered": (i32, [_S, _P, _P, _P, _P, _P, _P, sz, _P, _P]),
@@ -135,6 +163,71 @@ def workspace_layout(s: MoeShape) -> dict:
     return {n: int(o) for n, o in zip(WS_REGIONS, offs)}
 
 
+def workspace_phases(s: MoeShape) -> dict:
+    """Workspace bytes moe_layer has written by the end of each phase (moe_workspace_phases)."""
+    out = (ctypes.c_int64 * len(PHASES))()
+    rc = load_library().moe_workspace_phases(ctypes.byref(s), out)
+    if rc != MOE_OK:
+        raise MoeError("moe_workspace_phases", rc)
+    return {n: int(v) for n, v in zip(PHASES, out)}
+
+
+def _host_i32(a):
+    """A C-contiguous int32 numpy copy of a host array (or of a CPU tensor)."""
+    import numpy as np
+
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+def expert_stats(T: int, k: int, routed_counts, tokens_per_expert=None) -> dict:
+    """The per-layer expert statistics record (moe_expert_stats) of host count arrays."""
+    n = _host_i32(routed_counts)
+    c = None if tokens_per_expert is None else _host_i32(tokens_per_expert)
+    if c is not None and c.shape != n.shape:
+        raise ValueError("routed_counts and tokens_per_expert differ in length")
+    rec = ExpertStats()
+    _check("moe_expert_stats", load_library().moe_expert_stats(
+        int(T), int(k), int(n.size), n.ctypes.data, None if c is None else c.ctypes.data,
+        ctypes.byref(rec)))
+    return rec.as_dict()
+
+
+def slot_stats(T: int, routed_by_slot, kept_by_slot) -> dict:
+    """moe_slot_stats of host [k, E] tables: each slot's max over mean and its share of the
+    drops."""
+    import numpy as np
+
+    r, c = _host_i32(routed_by_slot), _host_i32(kept_by_slot)
+    if r.ndim != 2 or r.shape != c.shape:
+        raise ValueError("routed_by_slot and kept_by_slot must be [k, E] arrays")
+    k, E = r.shape
+    mtm, share = np.zeros(k), np.zeros(k)
+    _check("moe_slot_stats", load_library().moe_slot_stats(
+        int(T), k, E, r.ctypes.data, c.ctypes.data, mtm.ctypes.data, share.ctypes.data))
+    return {"slot_max_to_mean": mtm.tolist(), "drop_share_per_slot": share.tolist()}
+
+
+def placement_load(routed_counts, placement, n_ranks: int, ranks_per_node: int = 0) -> dict:
+    """moe_placement_load: routed load per rank (and per node) under an expert placement."""
+    import numpy as np
+
+    n, pl = _host_i32(routed_counts), _host_i32(placement)
+    if n.shape != pl.shape:
+        raise ValueError("routed_counts and placement differ in length")
+    nodes = -(-n_ranks // ranks_per_node) if ranks_per_node > 0 else 0
+    rank_load = np.zeros(n_ranks, dtype=np.int64)
+    node_load = np.zeros(max(nodes, 1), dtype=np.int64)
+    mtm = np.zeros(2)
+    _check("moe_placement_load", load_library().moe_placement_load(
+        n.size, n.ctypes.data, pl.ctypes.data, int(n_ranks), int(ranks_per_node),
+        rank_load.ctypes.data, node_load.ctypes.data if nodes else None, mtm.ctypes.data))
+    out = {"rank_load": rank_load.tolist(), "rank_max_to_mean": float(mtm[0])}
+    if nodes:
+        out["node_load"] = node_load[:nodes].tolist()
+        out["node_max_to_mean"] = float(mtm[1])
+    return out
+
+
 def _ptr(t) -> Optional[int]:
     if t is None:
         return None
@@ -166,11 +259,12 @@ def route(s: MoeShape, x, w_router, b_router, logits, topk_idx, topk_w, status=N
 
 
 def dispatch(s: MoeShape, topk_idx, x, workspace, routed_counts, tokens_per_expert,
-             expert_offsets, src_token, dest_row, drops, x_perm, stream=None) -> None:
+             expert_offsets, src_token, dest_row, drops, x_perm, stream=None,
+             src_slot=None) -> None:
     _check("moe_dispatch", load_library().moe_dispatch(
         ctypes.byref(s), _ptr(topk_idx), _ptr(x), _ptr(workspace), _nbytes(workspace),
         _ptr(routed_counts), _ptr(tokens_per_expert), _ptr(expert_offsets), _ptr(src_token),
-        _ptr(dest_row), _ptr(drops), _ptr(x_perm), _stream(stream)))
+        _ptr(src_slot), _ptr(dest_row), _ptr(drops), _ptr(x_perm), _stream(stream)))
 
 
 def expert_ffn(s: MoeShape, x_perm, expert_offsets, w_gate, w_up, w_down, workspace, y_perm,
@@ -221,42 +315,25 @@ def slot_counts(s: MoeShape, topk_idx, dest_row, routed_by_slot, kept_by_slot,
         _ptr(kept_by_slot), _stream(stream)))
 
 
-def routing_record(routed_by_slot, kept_by_slot, placement=None,
+def routing_record(T: int, routed_by_slot, kept_by_slot, placement=None,
                    ranks_per_node: Optional[int] = None) -> dict:
-    """Host summary of moe_slot_counts' per-slot counts (arrays [k, E]): the share of the
-    busiest ceil(5 % of E) experts, each slot's max-to-mean, how the drops split over the
-    slots and, for an expert -> rank placement, the load per rank and per node."""
-    import math
-
+    """The observability record of moe_slot_counts' per-slot tables (host arrays [k, E]):
+    the share of the busiest ceil(5 % of E) experts (moe_expert_stats), each slot's max over
+    mean and share of the drops (moe_slot_stats) and, for an expert -> rank placement, the
+    load per rank and per node (moe_placement_load)."""
     import numpy as np
 
-    rbs = np.asarray(routed_by_slot, dtype=np.int64)
-    kbs = np.asarray(kept_by_slot, dtype=np.int64)
-    k, E = rbs.shape
+    rbs, kbs = _host_i32(routed_by_slot), _host_i32(kept_by_slot)
+    k = rbs.shape[0]
     n = rbs.sum(axis=0)
-    total = int(n.sum())
-    top = int(math.ceil(0.05 * E))
-    dropped = rbs.sum(axis=1) - kbs.sum(axis=1)
-    T = int(rbs[0].sum())
-    rec = {
-        "routed_by_slot": rbs.tolist(),
-        "kept_by_slot": kbs.tolist(),
-        "top_5_percent_experts": top,
-        "top_5_percent_expert_share": float(np.sort(n)[-top:].sum() / total) if total else 0.0,
-        "slot_max_to_mean": [float(r.max() * E / T) if T else 0.0 for r in rbs],
-        "drop_share_per_slot": [float(v / dropped.sum()) if dropped.sum() else 0.0
-                                for v in dropped],
-    }
+    st = expert_stats(T, k, n)
+    rec = {"routed_by_slot": rbs.tolist(), "kept_by_slot": kbs.tolist(),
+           "top_5_percent_experts": st["top_5_percent_experts"],
+           "top_5_percent_expert_share": st["top_5_percent_expert_share"]}
+    rec.update(slot_stats(T, rbs, kbs))
     if placement is not None:
-        pl = np.asarray(placement, dtype=np.int64)
-        rank_load = np.bincount(pl, weights=n, minlength=int(pl.max()) + 1).astype(np.int64)
-        rec["rank_load"] = rank_load.tolist()
-        rec["rank_max_to_mean"] = float(rank_load.max() / rank_load.mean()) if total else 0.0
-        if ranks_per_node:
-            nodes = np.arange(rank_load.size) // ranks_per_node
-            node_load = np.bincount(nodes, weights=rank_load).astype(np.int64)
-            rec["node_load"] = node_load.tolist()
-            rec["node_max_to_mean"] = float(node_load.max() / node_load.mean()) if total else 0.0
+        pl = np.asarray(placement)
+        rec.update(placement_load(n, pl, int(pl.max()) + 1, int(ranks_per_node or 0)))
     return rec
 
 

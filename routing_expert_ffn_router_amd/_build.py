@@ -5,6 +5,8 @@
 from __future__ import annotations
 
 import concurrent.futures as cf
+import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -14,8 +16,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+# hash of the sources and flags libmoe.so was built from, written next to the build objects
+STAMP = os.path.join(OBJ, "libmoe.sha256")
 
-SOURCES = ["route.hip", "dispatch.hip", "expert_ffn.hip", "combine.hip", "moe_abi.cpp"]
+SOURCES = ["route.hip", "dispatch.hip", "expert_ffn.hip", "combine.hip", "moe_abi.cpp",
+           "stats.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "hipcc")
 FLAGS = [
@@ -34,6 +39,32 @@ SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=unde
             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-shared-libasan",
             "-Xarch_host", "-fno-omit-frame-pointer"]
 LIB_SANITIZED = os.path.join(OBJ, "libmoe_sanitized.so")
+
+
+def source_hash() -> str:
+    """sha256 over the library's sources (csrc/, include/moe.h) and its compile flags."""
+    h = hashlib.sha256(" ".join(FLAGS).encode())
+    files = sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(ROOT, "include", "moe.h")]
+    for f in files:
+        if os.path.isfile(f):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def built_hash() -> str:
+    """The source hash recorded when libmoe.so was last built ("" if unknown)."""
+    try:
+        with open(STAMP) as fh:
+            return fh.read().strip()
+    except OSError:
+        return ""
+
+
+def is_current() -> bool:
+    """libmoe.so exists and was built from the sources as they are now."""
+    return os.path.exists(LIB) and built_hash() == source_hash()
 
 
 def _compile(src: str, sanitize: bool = False) -> str:
@@ -61,6 +92,9 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, lib)
+    if not sanitize:
+        with open(STAMP, "w") as fh:
+            fh.write(source_hash() + "\n")
     if verbose:
         print("built", lib)
     return lib

@@ -19,7 +19,7 @@
 //                  padded slots) and zeroed drop counters
 //   K5 rank        per assignment, its position = tile base + earlier waves of the tile
 //                  + rank inside the wave (wave ballots on the expert id bits); keep/drop,
-//                  dest_row, src_token and drop counters
+//                  dest_row, src_token (and src_slot) and drop counters
 //   K5c token_drop (slot-major only) tokens whose k assignments were all dropped
 //   K5b gather     x_perm[r] = x[src_token[r]] with 16-byte vector copies; empty slots
 //                  get src_token -1 (and, when padded, a zero row).  With packed rows and
@@ -107,7 +107,8 @@ __global__ void __launch_bounds__(kTileMax)
 rank_kernel(const int32_t* __restrict__ idx, int64_t total, int64_t T, int te, int k, int E,
             int C, int nbits, bool slot_major, const int32_t* __restrict__ tile_base,
             const int32_t* __restrict__ offsets, int32_t* __restrict__ dest_row,
-            int32_t* __restrict__ src_token, int32_t* __restrict__ drops, int64_t fill_R) {
+            int32_t* __restrict__ src_token, int32_t* __restrict__ src_slot,
+            int32_t* __restrict__ drops, int64_t fill_R) {
   extern __shared__ int32_t sm[];
   constexpr int kWaves = kTileMax / kWave;
   int32_t* s_cnt = sm;                          // [kWaves][E] per-wave expert counts
@@ -119,8 +120,10 @@ rank_kernel(const int32_t* __restrict__ idx, int64_t total, int64_t T, int te, i
   // no slot is written twice.
   if (fill_R > 0)
     for (int64_t r = offsets[E] + (int64_t)blockIdx.x * blockDim.x + tid; r < fill_R;
-         r += (int64_t)gridDim.x * blockDim.x)
+         r += (int64_t)gridDim.x * blockDim.x) {
       src_token[r] = -1;
+      if (src_slot) src_slot[r] = -1;
+    }
   for (int i = tid; i < kWaves * E; i += blockDim.x) s_cnt[i] = 0;
   s_tokdrop[tid] = 0;
   for (int i = tid; i < k + 2; i += blockDim.x) s_drop[i] = 0;
@@ -151,7 +154,10 @@ rank_kernel(const int32_t* __restrict__ idx, int64_t total, int64_t T, int te, i
     dropped = !keep;
     const int r = keep ? offsets[e] + pos : -1;
     dest_row[f] = r;
-    if (keep) src_token[r] = (int)(f / k);
+    if (keep) {
+      src_token[r] = (int)(f / k);
+      if (src_slot) src_slot[r] = (int)(f % k);
+    }
   } else if (active) {
     dest_row[f] = -1;
   }
@@ -195,6 +201,7 @@ token_drop_kernel(const int32_t* __restrict__ dest_row, int64_t T, int k,
 // and a zero row.
 __global__ void __launch_bounds__(256)
 gather_rows_kernel(const char* __restrict__ x, int32_t* __restrict__ src_token,
+                   int32_t* __restrict__ src_slot,
                    const int32_t* __restrict__ offsets, const int32_t* __restrict__ kept,
                    int E, int C, bool pad, int64_t R, int64_t row_bytes,
                    char* __restrict__ x_perm) {
@@ -204,7 +211,10 @@ gather_rows_kernel(const char* __restrict__ x, int32_t* __restrict__ src_token,
   for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < R; r += (int64_t)gridDim.x * 4) {
     if (pad) {
       if (r % C >= kept[r / C]) {
-        if (lane == 0) src_token[r] = -1;
+        if (lane == 0) {
+          src_token[r] = -1;
+          if (src_slot) src_slot[r] = -1;
+        }
         if (!x_perm) continue;
         char* dst = x_perm + r * row_bytes;
         const u32x4 z = {0u, 0u, 0u, 0u};
@@ -212,7 +222,10 @@ gather_rows_kernel(const char* __restrict__ x, int32_t* __restrict__ src_token,
         continue;
       }
     } else if (r >= N) {
-      if (lane == 0) src_token[r] = -1;
+      if (lane == 0) {
+        src_token[r] = -1;
+        if (src_slot) src_slot[r] = -1;
+      }
       continue;
     }
     if (!x_perm) continue;  // tables only
@@ -282,7 +295,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     const size_t lds = ((kTileMax / kWave) * a.E + kTileMax + a.k + 2) * sizeof(int32_t);
     rank_kernel<<<ntiles, kTileMax, lds, s>>>(a.topk_idx, total, a.T, te, (int)a.k, (int)a.E,
                                               (int)a.C, nbits, a.slot_major, a.tile_base,
-                                              a.offsets, a.dest_row, a.src_token, a.drops,
+                                              a.offsets, a.dest_row, a.src_token,
+                                              a.src_slot, a.drops,
                                               tail_in_rank ? a.R : 0);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.slot_major) {
@@ -295,7 +309,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     int64_t blocks = (a.R + 3) / 4;
     if (blocks > 4096) blocks = 4096;
     gather_rows_kernel<<<(unsigned)blocks, 256, 0, s>>>(
-        (const char*)a.x, a.src_token, a.offsets, a.kept, (int)a.E, (int)a.C, a.pad, a.R,
+        (const char*)a.x, a.src_token, a.src_slot, a.offsets, a.kept, (int)a.E, (int)a.C, a.pad, a.R,
         a.d * a.elt_bytes, (char*)a.x_perm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }

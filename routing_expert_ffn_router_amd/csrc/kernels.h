@@ -44,6 +44,7 @@ struct DispatchArgs {
   int32_t* kept;       // [E]
   int32_t* offsets;    // [E+1]
   int32_t* src_token;  // [R]
+  int32_t* src_slot;   // [R], nullable: slot of the assignment each kept row holds
   int32_t* dest_row;   // [T*k]
   int32_t* drops;      // [k+2]
   void* x_perm;        // [R, d]; null: tables only, no row copies

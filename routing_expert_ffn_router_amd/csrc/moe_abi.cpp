@@ -107,6 +107,15 @@ P* region(void* ws, const Layout& L, int r) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Rows of x addressed by 32-bit byte offsets in the gathered gate/up GEMM.
+bool gather_fits(const moe_shape* s) {
+  return s->T * s->d * elt_bytes(s->dtype) < ((int64_t)1 << 31);
+}
+
+// moe_layer lets the gate/up GEMM gather the token rows (x_perm is not written) with packed
+// rows whose x fits 32-bit offsets.
+bool layer_gathers(const moe_shape* s) { return !padded(s) && gather_fits(s); }
+
 int check_workspace(const moe_shape* s, const void* ws, size_t bytes, Layout* L) {
   *L = make_layout(s);
   if (!ws || (int64_t)bytes < L->total) return MOE_ERR_WORKSPACE;
@@ -163,6 +172,31 @@ int moe_workspace_layout(const moe_shape* s, int64_t* offsets) {
   return MOE_OK;
 }
 
+int moe_workspace_phases(const moe_shape* s, int64_t* bytes) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(s);
+  // regions moe_layer writes in each stage (with its optional outputs kept in the workspace)
+  static const int kPack[] = {MOE_WS_LOGITS,    MOE_WS_TOPK_IDX,  MOE_WS_TOPK_W,
+                              MOE_WS_STATUS,    MOE_WS_ROUTED,    MOE_WS_KEPT,
+                              MOE_WS_OFFSETS,   MOE_WS_SRC_TOKEN, MOE_WS_DEST_ROW,
+                              MOE_WS_DROPS,     MOE_WS_TILE_HIST, MOE_WS_TILE_BASE};
+  static const int kExperts[] = {MOE_WS_SCHED, MOE_WS_H, MOE_WS_Y_PERM, MOE_WS_DOWN_ACC};
+  int64_t pack = 0;
+  for (int r : kPack) pack += L.size[r];
+  if (!layer_gathers(s)) pack += L.size[MOE_WS_X_PERM];  // the copy the gathering GEMM skips
+  int64_t experts = pack;
+  // an empty layer writes its counters and status only: the expert GEMMs do not launch
+  if (s->T > 0)
+    for (int r : kExperts) experts += L.size[r];
+  bytes[MOE_PHASE_BEFORE_LAYER] = 0;
+  bytes[MOE_PHASE_AFTER_PACK] = pack;
+  bytes[MOE_PHASE_AFTER_DISPATCH] = pack;  // expert-parallel size 1: nothing is exchanged
+  bytes[MOE_PHASE_AFTER_EXPERTS] = experts;
+  return MOE_OK;
+}
+
 const char* moe_status_string(int st) {
   switch (st) {
     case MOE_OK: return "ok";
@@ -191,8 +225,8 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const flo
 
 int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, void* ws,
                  size_t ws_bytes, int32_t* routed_counts, int32_t* tokens_per_expert,
-                 int32_t* expert_offsets, int32_t* src_token, int32_t* dest_row, int32_t* drops,
-                 void* x_perm, hipStream_t st) {
+                 int32_t* expert_offsets, int32_t* src_token, int32_t* src_slot,
+                 int32_t* dest_row, int32_t* drops, void* x_perm, hipStream_t st) {
   int rc = check_shape(s);
   if (rc != MOE_OK) return rc;
   if (!routed_counts || !tokens_per_expert || !expert_offsets || !drops)
@@ -220,6 +254,7 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, voi
   a.kept = tokens_per_expert;
   a.offsets = expert_offsets;
   a.src_token = src_token;
+  a.src_slot = src_slot;
   a.dest_row = dest_row;
   a.drops = drops;
   a.x_perm = x_perm;
@@ -229,11 +264,6 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, voi
 }  // extern "C"
 
 namespace {
-
-// Rows of x addressed by 32-bit byte offsets in the gathered gate/up GEMM.
-bool gather_fits(const moe_shape* s) {
-  return s->T * s->d * elt_bytes(s->dtype) < ((int64_t)1 << 31);
-}
 
 // Shared body of the expert-FFN entry points; which = 1 (gate/up), 2 (down), 3 (both).  The
 // gate/up activations are x_perm, or, with src_rows, the rows src_rows[r] of x.
@@ -372,8 +402,8 @@ int moe_layer(const moe_shape* s, const void* x, const void* w_router, const flo
   rc = route_impl(s, x, w_router, b_router, logits, 0, idx, gates, stt, st);
   if (rc != MOE_OK) return rc;
   // packed rows: the gate/up GEMM gathers the token rows itself (x_perm is not written)
-  const bool gathered = !padded(s) && gather_fits(s);
-  rc = moe_dispatch(s, idx, x, ws, ws_bytes, routed, kept, offsets, src, dest, dr,
+  const bool gathered = layer_gathers(s);
+  rc = moe_dispatch(s, idx, x, ws, ws_bytes, routed, kept, offsets, src, nullptr, dest, dr,
                     gathered ? nullptr : x_perm, st);
   if (rc != MOE_OK) return rc;
   void* h = region<void>(ws, L, MOE_WS_H);

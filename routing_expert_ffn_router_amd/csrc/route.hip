@@ -4,6 +4,8 @@
 // dive": a router chooses the top-k experts of every token.  The layer specification fixes
 // the rest: fp32 logits, softmax top-k with ties to the lower expert index, and gates
 // renormalised over the selection.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -206,97 +208,105 @@ __device__ inline float group_sum_f32(float v, int G) {
 
 template <int V>
 __global__ void __launch_bounds__(256)
-topk_kernel(const float* __restrict__ logits, const float* __restrict__ sel_bias, int T_,
-            int E, int k, int G, int NG, int M, int32_t* __restrict__ topk_idx,
+topk_kernel(const float* __restrict__ logits, const float* __restrict__ sel_bias,
+            int64_t T_, int E, int k, int G, int NG, int M, int32_t* __restrict__ topk_idx,
             float* __restrict__ topk_w, int32_t* __restrict__ status) {
-  const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
-  const int tok = gtid / G, sub = gtid % G;
-  const bool active = tok < T_;
-  const float* row = logits + (int64_t)(active ? tok : 0) * E;
+  // Grid-stride over groups of G lanes in 64-bit indices (T * G may pass 2^31).  G divides
+  // the wave, so a wave's tokens lie in one pass and the loop condition is wave-uniform:
+  // every lane of a wave runs the same passes, as the group shuffles below require.
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t wave0 = (int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~(kWave - 1));
+       wave0 / G < T_; wave0 += stride) {
+    const int64_t gtid = wave0 + lane_id();
+    const int64_t tok = gtid / G;
+    const int sub = (int)(gtid % G);
+    const bool active = tok < T_;
+    const float* row = logits + (active ? tok : 0) * E;
 
-  uint64_t key[V];
-  float lg[V];  // the logits of this lane's experts (the gates use them)
-  int bad = 0;
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int e = sub + v * G;
-    key[v] = 0;
-    lg[v] = 0.f;
-    if (active && e < E) {
-      const float val = row[e];
-      lg[v] = val;
-      const float sv = sel_bias ? val + sel_bias[e] : val;
-      if (__builtin_isfinite(val) && __builtin_isfinite(sv))
-        key[v] = ((uint64_t)ordered_f32(sv) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-      else
-        bad = 1;
-    }
-  }
-  // group OR of the non-finite flag
-  for (int m = G >> 1; m > 0; m >>= 1) bad |= __shfl_xor(bad, m, kWave);
-  if (active && sub == 0 && bad && status) atomicAdd(status, 1);
-
-  if (NG > 1 && M < NG) {
-    const int gs = E / NG;
-    uint64_t gkey = 0;  // lane g: key of group g
-    for (int g = 0; g < NG; ++g) {
-      uint64_t b = 0;
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int e = sub + v * G;
-        if (e < E && e / gs == g && key[v] > b) b = key[v];
-      }
-      b = group_max_u64(b, G);
-      if (sub == g) gkey = b;
-    }
-    uint64_t chosen = 0;  // bit g: group g kept
-    for (int r = 0; r < M; ++r) {
-      const uint64_t b = group_max_u64(gkey, G);
-      if (b == 0) break;  // only tokens with non-finite logits get here
-      const int g = (int)(0xFFFFFFFFu - (uint32_t)b) / gs;
-      chosen |= 1ull << g;
-      if (sub == g) gkey = 0;
-    }
+    uint64_t key[V];
+    float lg[V];  // the logits of this lane's experts (the gates use them)
+    int bad = 0;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const int e = sub + v * G;
-      if (e < E && !((chosen >> (e / gs)) & 1ull)) key[v] = 0;
+      key[v] = 0;
+      lg[v] = 0.f;
+      if (active && e < E) {
+        const float val = row[e];
+        lg[v] = val;
+        const float sv = sel_bias ? val + sel_bias[e] : val;
+        if (__builtin_isfinite(val) && __builtin_isfinite(sv))
+          key[v] = ((uint64_t)ordered_f32(sv) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+        else
+          bad = 1;
+      }
     }
-  }
+    // group OR of the non-finite flag
+    for (int m = G >> 1; m > 0; m >>= 1) bad |= __shfl_xor(bad, m, kWave);
+    if (active && sub == 0 && bad && status) atomicAdd(status, 1);
 
-  // Slot 0 holds the best selection.  Round j's winner is expert e, held by lane e % G of
-  // the group as its entry e / G; that lane's logit reaches the group by one shuffle and
-  // lane j keeps slot j (k <= G).  The gates are exp(L_j - m) / sum with m the largest
-  // selected logit, computed by the k slot lanes together.
-  const int base = lane_id() & ~(G - 1);
-  int slot_e = 0;
-  float slot_l = -__builtin_huge_valf();
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+    if (NG > 1 && M < NG) {
+      const int gs = E / NG;
+      uint64_t gkey = 0;  // lane g: key of group g
+      for (int g = 0; g < NG; ++g) {
+        uint64_t b = 0;
 #pragma unroll
-    for (int v = 0; v < V; ++v) best = key[v] > best ? key[v] : best;
-    best = group_max_u64(best, G);
-    // the unique owner retires the winning key
+        for (int v = 0; v < V; ++v) {
+          const int e = sub + v * G;
+          if (e < E && e / gs == g && key[v] > b) b = key[v];
+        }
+        b = group_max_u64(b, G);
+        if (sub == g) gkey = b;
+      }
+      uint64_t chosen = 0;  // bit g: group g kept
+      for (int r = 0; r < M; ++r) {
+        const uint64_t b = group_max_u64(gkey, G);
+        if (b == 0) break;  // only tokens with non-finite logits get here
+        const int g = (int)(0xFFFFFFFFu - (uint32_t)b) / gs;
+        chosen |= 1ull << g;
+        if (sub == g) gkey = 0;
+      }
 #pragma unroll
-    for (int v = 0; v < V; ++v)
-      if (key[v] == best) key[v] = 0;
-    const int e = best ? (int)(0xFFFFFFFFu - (uint32_t)best) : 0;
-    float mine = 0.f;  // this lane's logit of expert e's column
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      if (v == e / G) mine = lg[v];
-    const float l = __shfl(mine, base + e % G, kWave);
-    if (sub == j) {
-      slot_e = e;
-      slot_l = l;
+      for (int v = 0; v < V; ++v) {
+        const int e = sub + v * G;
+        if (e < E && !((chosen >> (e / gs)) & 1ull)) key[v] = 0;
+      }
     }
-  }
-  const float m = group_max_f32(sub < k ? slot_l : -__builtin_huge_valf(), G);
-  const float ex = sub < k ? expf(slot_l - m) : 0.f;
-  const float inv = 1.0f / group_sum_f32(ex, G);
-  if (active && sub < k) {
-    topk_idx[(int64_t)tok * k + sub] = slot_e;
-    topk_w[(int64_t)tok * k + sub] = ex * inv;
+
+    // Slot 0 holds the best selection.  Round j's winner is expert e, held by lane e % G of
+    // the group as its entry e / G; that lane's logit reaches the group by one shuffle and
+    // lane j keeps slot j (k <= G).  The gates are exp(L_j - m) / sum with m the largest
+    // selected logit, computed by the k slot lanes together.
+    const int base = lane_id() & ~(G - 1);
+    int slot_e = 0;
+    float slot_l = -__builtin_huge_valf();
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int v = 0; v < V; ++v) best = key[v] > best ? key[v] : best;
+      best = group_max_u64(best, G);
+      // the unique owner retires the winning key
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (key[v] == best) key[v] = 0;
+      const int e = best ? (int)(0xFFFFFFFFu - (uint32_t)best) : 0;
+      float mine = 0.f;  // this lane's logit of expert e's column
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (v == e / G) mine = lg[v];
+      const float l = __shfl(mine, base + e % G, kWave);
+      if (sub == j) {
+        slot_e = e;
+        slot_l = l;
+      }
+    }
+    const float m = group_max_f32(sub < k ? slot_l : -__builtin_huge_valf(), G);
+    const float ex = sub < k ? expf(slot_l - m) : 0.f;
+    const float inv = 1.0f / group_sum_f32(ex, G);
+    if (active && sub < k) {
+      topk_idx[tok * k + sub] = slot_e;
+      topk_w[tok * k + sub] = ex * inv;
+    }
   }
 }
 
@@ -308,9 +318,10 @@ hipError_t launch_topk(const float* logits, const float* sel_bias, int64_t T, in
   while (G < E && G < 64) G <<= 1;
   const int V = (int)((E + G - 1) / G);
   const int64_t threads = T * G;
-  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  // at most 2^16 blocks; the kernel strides over the rest
+  const unsigned blocks = (unsigned)std::min<int64_t>((threads + 255) / 256, 1 << 16);
 #define MOE_TOPK(VV)                                                                     \
-  topk_kernel<VV><<<blocks, 256, 0, s>>>(logits, sel_bias, (int)T, (int)E, (int)k, G,    \
+  topk_kernel<VV><<<blocks, 256, 0, s>>>(logits, sel_bias, T, (int)E, (int)k, G,         \
                                          n_groups, topk_groups, idx, w, status)
   if (V <= 1)
     MOE_TOPK(1);

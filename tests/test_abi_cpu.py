@@ -133,7 +133,7 @@ def test_bad_shapes_rejected_everywhere(kw, err):
     assert lib.moe_workspace_size(s) == 0
     assert lib.moe_max_rows(s) == -1
     assert lib.moe_route(s, p, p, None, p, 0, p, p, None, None) == err
-    assert lib.moe_dispatch(s, p, p, p, 1 << 40, p, p, p, p, p, p, p, None) == err
+    assert lib.moe_dispatch(s, p, p, p, 1 << 40, p, p, p, p, None, p, p, p, None) == err
     assert lib.moe_expert_ffn(s, p, p, p, p, p, p, 1 << 40, p, None) == err
     assert lib.moe_combine(s, p, p, p, p, None) == err
     assert lib.moe_slot_counts(s, p, p, p, p, None) == err
@@ -185,10 +185,10 @@ def test_dispatch_tables_only_accepts_null_x_perm():
     s = ctypes.byref(_shape())
     p = FAKE
     # x_perm NULL: x is not needed either; the call fails only at the workspace check
-    assert lib.moe_dispatch(s, p, None, p, 16, p, p, p, p, p, p, None, None) == \
+    assert lib.moe_dispatch(s, p, None, p, 16, p, p, p, p, None, p, p, None, None) == \
         moe.MOE_ERR_WORKSPACE
     # x_perm given without x
-    assert lib.moe_dispatch(s, p, None, p, 1 << 40, p, p, p, p, p, p, p, None) == \
+    assert lib.moe_dispatch(s, p, None, p, 1 << 40, p, p, p, p, None, p, p, p, None) == \
         moe.MOE_ERR_INVALID_ARG
 
 
@@ -214,7 +214,7 @@ def test_routing_record_from_counts_matches_oracle():
         np.add.at(rbs[j], idx[:, j], 1)
         np.add.at(kbs[j], idx[:, j][tab["dest_row"][:, j] >= 0], 1)
     pl = np.arange(E) % 4
-    got = moe.routing_record(rbs, kbs, pl, ranks_per_node=2)
+    got = moe.routing_record(T, rbs, kbs, pl, ranks_per_node=2)
     want = oracle.routing_record(idx, tab["dest_row"], E, pl, ranks_per_node=2)
     for key, v in want.items():
         if isinstance(v, list) and v and isinstance(v[0], list):
@@ -235,8 +235,8 @@ def test_null_pointers_rejected():
     E = moe.MOE_ERR_INVALID_ARG
     assert lib.moe_route(s, None, p, None, p, 0, p, p, None, None) == E  # x
     assert lib.moe_route(s, p, p, None, None, 0, p, p, None, None) == E  # logits
-    assert lib.moe_dispatch(s, None, p, p, 1 << 40, p, p, p, p, p, p, p, None) == E
-    assert lib.moe_dispatch(s, p, p, p, 1 << 40, None, p, p, p, p, p, p, None) == E
+    assert lib.moe_dispatch(s, None, p, p, 1 << 40, p, p, p, p, None, p, p, p, None) == E
+    assert lib.moe_dispatch(s, p, p, p, 1 << 40, None, p, p, p, None, p, p, p, None) == E
     assert lib.moe_expert_ffn(s, p, p, None, p, p, p, 1 << 40, p, None) == E
     assert lib.moe_combine(s, p, None, p, p, None) == E
     assert lib.moe_layer(s, p, None, None, p, p, p, p, 1 << 40, p, None, None, None, None,
@@ -248,13 +248,13 @@ def test_misaligned_pointers_rejected():
     p, q = FAKE, FAKE + 8
     A = moe.MOE_ERR_ALIGNMENT
     assert lib.moe_route(s, q, p, None, p, 0, p, p, None, None) == A
-    assert lib.moe_dispatch(s, p, p, p, 1 << 40, p, p, p, p, p, p, q, None) == A
+    assert lib.moe_dispatch(s, p, p, p, 1 << 40, p, p, p, p, None, p, p, q, None) == A
     assert lib.moe_expert_ffn(s, p, p, p, q, p, p, 1 << 40, p, None) == A
     assert lib.moe_combine(s, q, p, p, p, None) == A
     assert lib.moe_layer(s, p, p, None, p, p, p, p, 1 << 40, q, None, None, None, None,
                          None) == A
     # the workspace must be 256-byte aligned
-    assert lib.moe_dispatch(s, p, p, p + 16, 1 << 40, p, p, p, p, p, p, p, None) == A
+    assert lib.moe_dispatch(s, p, p, p + 16, 1 << 40, p, p, p, p, None, p, p, p, None) == A
 
 
 def test_workspace_checked():
@@ -263,8 +263,8 @@ def test_workspace_checked():
     p = FAKE
     need = moe.workspace_size(sh)
     W = moe.MOE_ERR_WORKSPACE
-    assert lib.moe_dispatch(s, p, p, None, need, p, p, p, p, p, p, p, None) == W
-    assert lib.moe_dispatch(s, p, p, p, need - 1, p, p, p, p, p, p, p, None) == W
+    assert lib.moe_dispatch(s, p, p, None, need, p, p, p, p, None, p, p, p, None) == W
+    assert lib.moe_dispatch(s, p, p, p, need - 1, p, p, p, p, None, p, p, p, None) == W
     assert lib.moe_expert_ffn(s, p, p, p, p, p, p, need - 256, p, None) == W
     assert lib.moe_layer(s, p, p, None, p, p, p, p, 16, p, None, None, None, None, None) == W
 
@@ -282,3 +282,126 @@ def test_library_has_no_oracle_or_torch_dependency():
     out = subprocess.run(["ldd", moe.LIB_PATH], capture_output=True, text=True).stdout
     assert "torch" not in out and "python" not in out.lower()
     assert "amdhip64" in out
+
+
+# ---------------------------------------------------------------- S9 record (host C code)
+def _stats_cases():
+    rng = np.random.default_rng(11)
+    cases = []
+    for E in (1, 2, 4, 8, 20, 40, 100, 256, 1000, 1024):
+        for k in (1, 2, 8):
+            if k > E:
+                continue
+            T = int(rng.integers(1, 3000))
+            idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]) if E <= 40 else \
+                rng.integers(0, E, (T, k))
+            n = np.bincount(idx.ravel(), minlength=E)
+            cases.append((T, k, n))
+    return cases
+
+
+@pytest.mark.parametrize("T,k,n", _stats_cases())
+def test_expert_stats_matches_oracle(T, k, n):
+    C = max(1, int(np.median(n)))
+    c = np.minimum(n, C)
+    got = moe.expert_stats(T, k, n, c)
+    want = oracle.expert_stats(n, T, k, tokens_per_expert=c, dropped=int((n - c).sum()))
+    for key in ("active_tokens", "top_k", "expert_p50", "expert_p95", "expert_max",
+                "dropped_tokens"):
+        assert got[key] == want[key], key
+    assert got["expert_mean"] == pytest.approx(want["expert_mean"], rel=1e-15)
+    assert got["expert_max_to_mean"] == pytest.approx(want["expert_max_to_mean"], rel=1e-15)
+    assert got["routed"] == n.sum() and got["experts"] == n.size
+    # conservation: kept rows plus dropped assignments are the routed ones
+    assert got["kept_rows"] + got["dropped_tokens"] == got["routed"]
+    assert got["active_experts"] == int((c > 0).sum())
+    # the top-5 % share agrees with the oracle's routing record of the same counts
+    top = int(np.ceil(0.05 * n.size))
+    assert got["top_5_percent_experts"] == top
+    assert got["top_5_percent_expert_share"] == pytest.approx(
+        np.sort(n)[::-1][:top].sum() / n.sum(), rel=1e-15)
+
+
+def test_expert_stats_page_example():
+    # [EP-checks] "Mean expert load proves almost nothing": its printed record fixes max
+    # and max/mean of the four counts (1003 / 882.25 -> 1.14); its p50 / p95 fit no standard
+    # percentile rule and are not pins
+    import json
+    import os
+
+    rec = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                      "expert_stats_record.json")))
+    n = np.array(rec["tokens_per_expert"])
+    st = moe.expert_stats(int(n.sum()) // 2, rec["top_k"], n)
+    assert st["expert_max"] == rec["expert_max"]
+    assert round(st["expert_max_to_mean"], 2) == rec["expert_max_to_mean"]
+    assert st["dropped_tokens"] == rec["dropped_tokens"] == 0
+    # nearest rank on 1..100: the median is 50 and the 95th percentile 95
+    st = moe.expert_stats(5050, 1, np.arange(1, 101))
+    assert (st["expert_p50"], st["expert_p95"], st["expert_max"]) == (50, 95, 100)
+
+
+def test_expert_stats_degenerate_and_invalid():
+    st = moe.expert_stats(0, 2, np.zeros(8, np.int32))
+    assert st["routed"] == 0 and st["top_5_percent_expert_share"] == 0.0
+    assert np.isnan(st["expert_max_to_mean"])
+    with pytest.raises(moe.MoeError):
+        moe.expert_stats(10, 2, np.array([3, -1]))
+    with pytest.raises(moe.MoeError):
+        moe.expert_stats(10, 2, np.array([3, 1]), np.array([4, 1]))  # kept > routed
+    with pytest.raises(moe.MoeError):
+        moe.placement_load(np.array([3, 1]), np.array([0, 2]), n_ranks=2)  # rank 2 of 2
+
+
+# ---------------------------------------------------------------- memory by phase
+PHASE_SHAPES = [
+    _shape(),                                                  # packed: the GEMM gathers
+    _shape(flags=moe.MOE_FLAG_PAD_TO_CAPACITY),                # padded: x_perm is copied
+    moe.shape(2048, 6144, 8, 2, 16384, 640),                   # down GEMM split in three
+    moe.shape(256, 7168, 256, 8, 2048, 0),                     # decode-sized
+    moe.shape(1 << 20, 2048, 8, 1, 128, 0, moe.MOE_BF16),      # x past 2^31 bytes: copied
+    _shape(T=0),
+]
+
+
+@pytest.mark.parametrize("sh", PHASE_SHAPES)
+def test_workspace_phases_follow_the_layout(sh):
+    # [EP-checks] "Memory must be counted by phase": the bytes each phase has written are
+    # the sizes of the regions its stages write, read off moe_workspace_layout
+    ph = moe.workspace_phases(sh)
+    lay = moe.workspace_layout(sh)
+    total = moe.workspace_size(sh)
+    names = moe.WS_REGIONS
+    ends = [lay[names[i + 1]] if i + 1 < len(names) else total for i in range(len(names))]
+    R = moe.max_rows(sh)
+    b = 2 if sh.dtype == moe.MOE_BF16 else 4
+    size = {
+        "logits": sh.T * sh.E * 4, "topk_idx": sh.T * sh.k * 4, "topk_w": sh.T * sh.k * 4,
+        "routed": sh.E * 4, "kept": sh.E * 4, "offsets": (sh.E + 1) * 4, "src_token": R * 4,
+        "dest_row": sh.T * sh.k * 4, "drops": (sh.k + 2) * 4, "status": 4,
+        "x_perm": R * sh.d * b, "h": R * sh.F * b, "y_perm": R * sh.d * b,
+    }
+    # region sizes bounded by the layout: each region ends before the next one starts
+    for i, n in enumerate(names):
+        room = ends[i] - lay[n]
+        if n in size:
+            assert size[n] <= room < size[n] + 256, n
+    internal = {n: ends[i] - lay[n] for i, n in enumerate(names)
+                if n in ("tile_hist", "tile_base", "sched", "down_acc")}
+    pack = sum(size[n] for n in ("logits", "topk_idx", "topk_w", "status", "routed", "kept",
+                                 "offsets", "src_token", "dest_row", "drops"))
+    pack_internal = internal["tile_hist"] + internal["tile_base"]
+    if not moe.gathered_layer(sh):
+        pack += size["x_perm"]
+    assert ph["before_layer"] == 0
+    assert pack <= ph["after_pack"] <= pack + pack_internal
+    assert ph["after_dispatch"] == ph["after_pack"]
+    if sh.T == 0:
+        assert ph["after_experts"] == ph["after_pack"]
+        return
+    exp = size["h"] + size["y_perm"]
+    grown = ph["after_experts"] - ph["after_pack"]
+    assert exp <= grown <= exp + internal["sched"] + internal["down_acc"]
+    assert ph["after_experts"] <= total
+    if sh.E == 8 and sh.T == 2048:  # the split down GEMM's fp32 slots are counted
+        assert grown >= exp + 3 * R * sh.d * 4

@@ -28,6 +28,7 @@ big = [-(1 << 62), -1, 0, 1, 2, 3, 8, 64, 65, 128, 1000, 1024, 1025, (1 << 20) +
        (1 << 31) - 1, 1 << 31, 1 << 40, (1 << 62) + 5]
 small = [-5, 0, 1, 2, 3, 4, 8, 63, 64, 65, 1 << 30]
 offs = (ctypes.c_int64 * len(moe.WS_REGIONS))()
+phases = (ctypes.c_int64 * len(moe.PHASES))()
 P, W = 1 << 40, 1 << 40  # never dereferenced: every call below fails validation first
 n = 0
 for T, d, E, k in itertools.product(big[:12] + big[14:], [128, 256, 100, 1 << 20, 1 << 21, -128],
@@ -38,8 +39,9 @@ for T, d, E, k in itertools.product(big[:12] + big[14:], [128, 256, 100, 1 << 20
         s = moe.shape(T, d, E, k, F, cap, dt, fl, ng, mg)
         b = ctypes.byref(s)
         lib.moe_workspace_size(b); lib.moe_max_rows(b); lib.moe_workspace_layout(b, offs)
+        lib.moe_workspace_phases(b, phases)
         assert lib.moe_route(b, P, P, None, None, 0, P, P, None, None) != 0 or T == 0
-        lib.moe_dispatch(b, P, P, None, W, P, P, P, P, P, P, P, None)
+        lib.moe_dispatch(b, P, P, None, W, P, P, P, P, None, P, P, P, None)
         lib.moe_expert_ffn(b, P, P, P, P, P, None, W, P, None)
         lib.moe_expert_gate_up(b, P, P, P, P, None, W, P, None)
         lib.moe_expert_gate_up_gathered(b, P, P, P, P, P, None, W, P, None)
@@ -54,6 +56,28 @@ for T, k, E in itertools.product(big, small, small):
 for st in range(-10, 3):
     lib.moe_status_string(st)
 lib.moe_workspace_size(None); lib.moe_max_rows(None); lib.moe_workspace_layout(None, offs)
+lib.moe_workspace_phases(None, phases)
+# the host records run for real on host arrays: counts of every size, invalid ones included
+import numpy as np
+rng = np.random.default_rng(0)
+for E in (1, 2, 7, 20, 256, 1024):
+    for k in (1, 2, 8):
+        n = rng.integers(0, 50, E).astype(np.int32)
+        c = np.minimum(n, rng.integers(0, 50, E)).astype(np.int32)
+        moe.expert_stats(int(n.sum()) // k, k, n, c)
+        moe.expert_stats(0, k, np.zeros(E, np.int32))
+        rbs = rng.integers(0, 9, (k, E)).astype(np.int32)
+        moe.slot_stats(37, rbs, np.minimum(rbs, 3))
+        for ranks in (1, 3, 8):
+            moe.placement_load(n, rng.integers(0, ranks, E), ranks, 2)
+            moe.placement_load(n, rng.integers(0, ranks, E), ranks, 0)
+        bad = n.copy(); bad[-1] = -1
+        assert lib.moe_expert_stats(5, k, E, bad.ctypes.data, None, ctypes.byref(moe.ExpertStats())) != 0
+        more = n + 1  # kept above routed (a named array: it must outlive the call)
+        assert lib.moe_expert_stats(5, k, E, n.ctypes.data, more.ctypes.data, ctypes.byref(moe.ExpertStats())) != 0
+        pl = np.full(E, 9, np.int32)
+        out = np.zeros(16, np.int64); mtm = np.zeros(2)
+        assert lib.moe_placement_load(E, n.ctypes.data, pl.ctypes.data, 4, 2, out.ctypes.data, out.ctypes.data, mtm.ctypes.data) != 0
 print("ok", n)
 """
 

@@ -140,9 +140,11 @@ def _run_dispatch(s, idx_np, x_np, dt):
     R = moe.max_rows(s)
     ws = torch.empty(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
     g = dict(routed=_i32(E), kept=_i32(E), offsets=_i32(E + 1), src=_i32(R), dest=_i32(T, k),
-             drops=_i32(k + 2), x_perm=torch.full((R, d), 7.0, dtype=dt, device="cuda"))
+             drops=_i32(k + 2), x_perm=torch.full((R, d), 7.0, dtype=dt, device="cuda"),
+             slot=torch.full((R,), 7777, dtype=torch.int32, device="cuda"))
     moe.dispatch(s, to_device(idx_np, torch.int32), to_device(x_np, dt), ws, g["routed"],
-                 g["kept"], g["offsets"], g["src"], g["dest"], g["drops"], g["x_perm"])
+                 g["kept"], g["offsets"], g["src"], g["dest"], g["drops"], g["x_perm"],
+                 src_slot=g["slot"])
     torch.cuda.synchronize()
     return R, g
 
@@ -169,6 +171,7 @@ def test_dispatch_variants_bit_exact(T, E, k, C, d, dtype, bias, flags):
     assert np.array_equal(g["offsets"].cpu().numpy(), ref["expert_offsets"])
     assert np.array_equal(g["dest"].cpu().numpy(), ref["dest_row"])
     assert np.array_equal(g["src"].cpu().numpy(), ref["src_token"][:R])
+    assert np.array_equal(g["slot"].cpu().numpy(), ref["src_slot"][:R])
     drops = g["drops"].cpu().numpy()
     assert drops[0] == ref["drops_total"]
     assert np.array_equal(drops[1:k + 1], ref["drops_per_slot"])
@@ -300,9 +303,10 @@ def test_slot_counts(T, E, k, C, flags):
     rec = oracle.routing_record(idx, ref["dest_row"], E)
     assert rbs.cpu().numpy().tolist() == rec["routed_by_slot"]
     assert kbs.cpu().numpy().tolist() == rec["kept_by_slot"]
-    host = moe.routing_record(rbs.cpu().numpy(), kbs.cpu().numpy())
+    host = moe.routing_record(T, rbs.cpu().numpy(), kbs.cpu().numpy())
     assert host["top_5_percent_expert_share"] == pytest.approx(rec["top_5_percent_expert_share"])
     assert host["drop_share_per_slot"] == pytest.approx(rec["drop_share_per_slot"])
+    assert host["slot_max_to_mean"] == pytest.approx(rec["slot_max_to_mean"])
 
 
 def test_slot_counts_skip_invalid_ids():

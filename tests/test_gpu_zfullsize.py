@@ -1,12 +1,12 @@
 """GPU parity at the full layer sizes, in the launch configuration bench.py times.
 
-The oracle cannot run these layers whole in a test, so:
   - dispatch tables are compared bit for bit over all T*k assignments, with the oracle's
     own routing (from its float64 logits of the seeded inputs) fed to moe_dispatch;
   - moe_layer is checked on every token's logits (tolerance), on every token's selection
-    (exact up to near-ties of the oracle's logits), and on the outputs of sampled tokens,
-    which the oracle computes one token at a time with the expert weights regenerated
-    slice by slice from the seeded generator.
+    (exact up to near-ties of the oracle's float64 logits), on every routing table (bit for
+    bit, the oracle routing from the GPU's fp32 logits) and on every output row, which the
+    oracle computes with each expert's weights regenerated from the seeded generator one
+    expert at a time.
 """
 import numpy as np
 import pytest
@@ -14,8 +14,8 @@ import pytest
 import moe_inputs as mi
 import oracle
 import routing_expert_ffn_router_amd as moe
-from _util import (OUT_TOL, device_inputs, log, logits_tol, near_tie_ok, rel_err, shape_of,
-                   to_device, to_host)
+from _fullsize import check_layer_every_token
+from _util import log, shape_of, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -67,85 +67,20 @@ def test_fullsize_dispatch_bit_exact(name):
     assert drops[0] == ref["drops_total"]
     assert np.array_equal(drops[1:w.k + 1], ref["drops_per_slot"])
     assert drops[w.k + 1] == ref["fully_dropped_tokens"]
-    # sampled rows of the permuted copy, bit for bit
+    # every row of the permuted copy, bit for bit: x_perm[r] = x[src_token[r]] with the
+    # oracle's src_token (the gather itself done by torch indexing of the seeded x)
     N = ref["n_kept"]
+    src = torch.from_numpy(ref["src_token"][:N]).cuda()
+    assert torch.equal(g["xp"][:N].view(torch.int16), xd[src].view(torch.int16))
+    # and the sampled rows against the host copy of x
     rows = np.unique(np.linspace(0, N - 1, 64).astype(np.int64))
     got = to_host(g["xp"][torch.from_numpy(rows).cuda()])
     assert np.array_equal(got, x[ref["src_token"][rows]])
     log(f"  N={N} drops={ref['drops_total']} ok")
 
 
-def _sample_tokens(w, agree):
-    T = w.T
-    cand = [0, 1, T // 3, T // 2, T - 2, T - 1]
-    for seg in w.segments:
-        cand += [seg[1], (seg[1] + seg[2]) // 2, seg[2] - 1]
-    out = []
-    for t in cand:
-        # nearest token at or after t whose routing agrees on both sides
-        for u in list(range(t, T)) + list(range(0, t)):
-            if agree[u]:
-                if u not in out:
-                    out.append(u)
-                break
-    return sorted(out)[: (6 if w.E > 8 else 8)]
-
-
 @pytest.mark.parametrize("name", FULL)
-def test_fullsize_layer_sampled(name):
+def test_fullsize_layer_every_token(name):
     w = mi.WORKLOADS[name]
-    log(f"full-size layer {name}")
-    s = shape_of(w)
-    dev = device_inputs(w)
-    lay = moe.MoELayer(s)
-    lay(dev["x"], dev["w_router"], dev["b_router"], dev["w_gate"], dev["w_up"], dev["w_down"])
-    torch.cuda.synchronize()
-    del dev
-    torch.cuda.empty_cache()
-    assert lay.status.item() == 0
-    x, L = _host_routing(w)
-    tol = logits_tol(L)
-    L_gpu = lay.view("logits").cpu().numpy()
-    dl = float(np.max(np.abs(L_gpu - L)))
-    log(f"  max|dL| {dl:.3e} (tol {tol:.3e})")
-    assert dl <= tol
-    idx = oracle.select_topk(L, w.k)
-    gates = oracle.gate_weights(L, idx)
-    ref = oracle.dispatch(idx, w.E, s.capacity)
-    idx_gpu = lay.view("topk_idx").cpu().numpy()
-    # routing from the GPU's own fp32 logits is bit-exact: selection, gates, every table
-    idx_own = oracle.select_topk(L_gpu, w.k)
-    assert np.array_equal(idx_gpu, idx_own)
-    assert np.max(np.abs(lay.view("topk_w").cpu().numpy() - oracle.gate_weights(L_gpu, idx_own))) <= 1e-6
-    own = oracle.dispatch(idx_own, w.E, s.capacity)
-    assert np.array_equal(lay.view("dest_row").cpu().numpy(), own["dest_row"])
-    assert np.array_equal(lay.view("offsets").cpu().numpy(), own["expert_offsets"])
-    assert np.array_equal(lay.tokens_per_expert.cpu().numpy(), own["tokens_per_expert"])
-    assert np.array_equal(lay.drops.cpu().numpy()[1:w.k + 1], own["drops_per_slot"])
-    bad, unexplained = near_tie_ok(L, idx_gpu, idx, tol)
-    log(f"  selection differs on {len(bad)} tokens (all near-ties: {not unexplained})")
-    assert not unexplained
-    dest_gpu = lay.view("dest_row").cpu().numpy()
-    agree = np.all(idx_gpu == idx, axis=1) & np.all((dest_gpu >= 0) == (ref["dest_row"] >= 0),
-                                                    axis=1)
-    if len(bad) == 0:
-        assert np.array_equal(lay.routed_counts.cpu().numpy(), ref["routed_counts"])
-        assert np.array_equal(dest_gpu, ref["dest_row"])
-        assert int(lay.drops[0]) == ref["drops_total"]
-    else:
-        assert agree.mean() >= 0.99
-    toks = _sample_tokens(w, agree)
-    kept = ref["dest_row"][toks] >= 0
-    d, F = w.d, w.F
-
-    def weights(e):
-        return (mi.host_tensor_f32(w, "w_gate", e, 1)[0], mi.host_tensor_f32(w, "w_up", e, 1)[0],
-                mi.host_tensor_f32(w, "w_down", e, 1)[0])
-
-    want = oracle.token_outputs(x[toks], idx[toks], kept, gates[toks], weights)
-    got = to_host(lay.out[torch.tensor(toks, device="cuda")])
-    err = rel_err(got, want)
-    log(f"  sampled tokens {toks}: rel err {err:.3e}")
-    assert err <= OUT_TOL
-    del lay
-    torch.cuda.empty_cache()
+    log(f"full-size layer {name}: every token")
+    check_layer_every_token(w, shape_of(w), torch)

@@ -299,3 +299,38 @@ def test_stats_page_example():
 def test_stats_nearest_rank():
     st = oracle.expert_stats(np.arange(1, 101), T=5050, k=1)
     assert st["expert_p50"] == 50 and st["expert_p95"] == 95 and st["expert_max"] == 100
+
+
+def test_streamed_expert_ffn_dense_special_case():
+    # E = 1: every row is the same dense SwiGLU FFN of its token (torch F.linear), whatever
+    # order src_token gathers the tokens in
+    T, d, F = 11, 12, 20
+    x = rng.standard_normal((T, d))
+    Wg, Wu, Wd = (rng.standard_normal(s) for s in ((F, d), (F, d), (d, F)))
+    src = rng.permutation(T)
+    calls = []
+    Y = oracle.expert_ffn_streamed(x, src, np.array([0, T]), lambda e: (calls.append(e) or
+                                                                         (Wg, Wu, Wd)))
+    xt = torch.from_numpy(x[src])
+    F_ = torch.nn.functional
+    want = F_.linear(F_.silu(F_.linear(xt, torch.from_numpy(Wg))) *
+                     F_.linear(xt, torch.from_numpy(Wu)), torch.from_numpy(Wd)).numpy()
+    assert calls == [0]
+    assert np.max(np.abs(Y - want)) < 1e-12 * np.max(np.abs(want))
+
+
+def test_streamed_layer_equals_batched_layer():
+    # the streamed path (weights fetched per expert, rows gathered through src_token) and
+    # the batched layer agree on a layer with drops; experts without rows are never fetched
+    w = mi.WORKLOADS["tiny_f32"]
+    x = mi.host_tensor_f32(w, "x")
+    Wr = mi.host_tensor_f32(w, "w_router")
+    Wg, Wu, Wd = (mi.host_tensor_f32(w, n) for n in ("w_gate", "w_up", "w_down"))
+    C = oracle.capacity(w.T, w.k, w.E, 0.5)
+    res = oracle.moe_layer(x, Wr, None, Wg, Wu, Wd, k=w.k, C=C)
+    fetched = []
+    Y = oracle.expert_ffn_streamed(x, res["src_token"], res["expert_offsets"],
+                                   lambda e: (fetched.append(e) or (Wg[e], Wu[e], Wd[e])))
+    out = oracle.combine(Y, res["dest_row"], res["topk_w"])
+    assert fetched == [e for e in range(w.E) if res["tokens_per_expert"][e] > 0]
+    assert np.max(np.abs(out - res["out"])) < 1e-12 * np.max(np.abs(res["out"]))
