@@ -54,6 +54,14 @@ def parse():
                    help="the router bias shifts the selection only, not the gates")
     p.add_argument("--groups", default=None, metavar="G:M",
                    help="group-limited top-k: G expert groups, M kept per token")
+    p.add_argument("--capacity-factor", type=float, default=None,
+                   help="override the workload's capacity factor (<= 0: no limit)")
+    p.add_argument("--cf-sweep", default=None, metavar="CF,CF,...",
+                   help="also time the layer at each capacity factor ('none': no limit)")
+    p.add_argument("--other-steps", type=int, default=10,
+                   help="timed steps of each other workload in the default run")
+    p.add_argument("--no-other-workloads", action="store_true",
+                   help="time the headline workload only")
     p.add_argument("--ep", type=int, default=8,
                    help="ranks of the expert placement in the routing record (contiguous)")
     p.add_argument("--ranks-per-node", type=int, default=8)
@@ -240,7 +248,8 @@ def percentile(v, q):
 
 def cpu_baseline(w, ntok: int) -> dict:
     """The oracle, as it stands, on the first `ntok` tokens of the workload (capacity
-    recomputed for ntok tokens with the same factor), full router and expert weights."""
+    recomputed for ntok tokens with the same factor), full router and expert weights.  Its
+    steps run one by one (the same calls its moe_layer makes) so each stage is timed."""
     import numpy as np
     import threadpoolctl
 
@@ -252,15 +261,34 @@ def cpu_baseline(w, ntok: int) -> dict:
     b = mi.router_bias(w)
     wg, wu, wd = (mi.host_tensor_f32(w, n) for n in ("w_gate", "w_up", "w_down"))
     C = oracle.capacity(ntok, w.k, w.E, w.capacity_factor)
+    stages = {}
     t0 = time.perf_counter()
-    res = oracle.moe_layer(x, wr, b, wg, wu, wd, w.k, C)
-    dt = time.perf_counter() - t0
-    assert np.all(np.isfinite(res["out"]))
+
+    def lap(name):
+        nonlocal t0
+        t = time.perf_counter()
+        stages[name] = round(t - t0, 4)
+        t0 = t
+
+    L = oracle.router_logits(x, wr, b)
+    lap("router_s")
+    idx = oracle.select_topk(L, w.k)
+    gates = oracle.gate_weights(L, idx)
+    lap("topk_s")
+    tab = oracle.dispatch(idx, w.E, C)
+    xp = oracle.permute(x, tab["src_token"], tab["n_kept"])
+    lap("dispatch_s")
+    Y = oracle.expert_ffn(xp, tab["expert_offsets"], wg, wu, wd)
+    lap("expert_ffn_s")
+    out = oracle.combine(Y, tab["dest_row"], gates)
+    lap("combine_s")
+    dt = sum(stages.values())
+    assert np.all(np.isfinite(out))
     threads = 0
     for info in threadpoolctl.threadpool_info():
         threads = max(threads, int(info.get("num_threads", 0)))
     return {"value": ntok / dt, "unit": "tokens/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds": round(dt, 3), "stage_seconds": stages,
             "sample": f"first {ntok} of {w.T} tokens of {w.name}, all {w.E} experts, "
                       f"capacity {C} (same factor), float64 numpy oracle",
             "cpu_model": _cpu_model()}
@@ -274,6 +302,291 @@ def _cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def gate_up_roofline(w, N, E_active, t_ms) -> dict:
+    """Roofline of the gate/up grouped GEMM (the dominant kernel): algorithmic flops 4 N d F
+    against the dtype's MFMA peak, or, below the ridge, algorithmic bytes
+    b (2 E_active F d + N d + N F) against HBM, over its event-timed duration."""
+    t = t_ms * 1e-3
+    flops = 4.0 * N * w.d * w.F
+    nbytes = w.elt_bytes * (2.0 * E_active * w.F * w.d + N * w.d + N * w.F)
+    peak = (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS) * 1e12
+    if nbytes == 0 or t <= 0:
+        return {"bound": "mfma", "achieved": 0.0, "peak": peak / 1e12, "unit": "TFLOP/s",
+                "frac": 0.0}
+    if flops / nbytes >= peak / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(flops / t / 1e12, 2), "peak": peak / 1e12,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(nbytes / t / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    return roof
+
+
+def layer_roofline_frac(w, N, E_active, ms) -> float:
+    """t_roof / t_step with t_roof = max(F_alg / P, B_alg / BW) over the whole layer:
+    F_alg = 2 T d E + 6 d F N, B_alg = b (2 T d + E d + 3 d F E_active)."""
+    peak = (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS) * 1e12
+    F_alg = 2.0 * w.T * w.d * w.E + 6.0 * w.d * w.F * N
+    B_alg = w.elt_bytes * (2.0 * w.T * w.d + w.E * w.d + 3.0 * w.d * w.F * E_active)
+    return round(max(F_alg / peak, B_alg / (PEAK_HBM_GBS * 1e9)) / (ms * 1e-3), 4)
+
+
+def device_inputs(w):
+    import torch
+
+    import moe_inputs as mi
+
+    dev = {n: mi.device_tensor(w, n) for n in ("x", "w_router", "w_gate", "w_up", "w_down")}
+    b_np = mi.router_bias(w)
+    bias = None if b_np is None else torch.from_numpy(b_np).cuda()
+    return (dev["x"], dev["w_router"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])
+
+
+def time_steps(run_step, K, stream):
+    """Exactly K steps between synchronisations, an event after each: (ms/step, per-step ms,
+    wall seconds)."""
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(K):
+        run_step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]
+    return ev[0].elapsed_time(ev[K]) / K, step_ms, wall
+
+
+def staged_ms(lay, args_l, passes, stream) -> dict:
+    """Mean ms of each stage of the layer run as its ABI calls with events between them.
+
+    Each stage is its own ABI call from Python, and a short stage (the router, the
+    dispatch) can finish on the GPU before the host has enqueued the next one.  The staged
+    layers are therefore enqueued back to back with one synchronisation at the end: the host
+    enqueues a layer's short stages while the GPU runs the previous layer's GEMMs, so the
+    events time GPU work, not host gaps.  The first layer, which has no predecessor to hide
+    behind, is not counted."""
+    import torch
+
+    runs = []
+    for _ in range(passes + 1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        marks = []
+        for name in lay.stages(*args_l):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            marks.append((name, e))
+        runs.append((e0, marks))
+    torch.cuda.synchronize()
+    times = {}
+    for e0, marks in runs[1:]:
+        prev = e0
+        for name, e in marks:
+            times.setdefault(name, []).append(prev.elapsed_time(e))
+            prev = e
+    return {n: statistics.mean(v) for n, v in times.items()}
+
+
+SENTINEL = 0xA5
+
+
+def written_extent(region_bytes) -> int:
+    """Bytes from the start of a region to its last byte that no longer holds the sentinel
+    (every region is written from its start: rows 0 .. N-1, tables, counters)."""
+    import torch
+
+    n = region_bytes.numel()
+    if n == 0:
+        return 0
+    chunk = 1 << 16
+    full = n // chunk * chunk
+    last = -1
+    if full:
+        hit = (region_bytes[:full].view(-1, chunk) != SENTINEL).any(dim=1)
+        nz = torch.nonzero(hit)
+        if nz.numel():
+            c = int(nz[-1])
+            inner = torch.nonzero(region_bytes[c * chunk:(c + 1) * chunk] != SENTINEL)
+            last = c * chunk + int(inner[-1])
+    tail = torch.nonzero(region_bytes[full:] != SENTINEL)
+    if tail.numel():
+        last = full + int(tail[-1])
+    return last + 1
+
+
+def memory_by_phase(lay, args_l, moe) -> dict:
+    """[EP-checks] "Memory must be counted by phase": the workspace bytes the layer has
+    written by the end of each phase, measured (the workspace is filled with a sentinel
+    byte, the layer runs stage by stage, and after each phase every region's written extent
+    is read back) beside the library's bound (moe_workspace_phases), plus torch's allocated
+    and peak figures.  The library allocates nothing, so torch's figures are flat across
+    the phases: inputs, weights, outputs and the one workspace, allocated beforehand."""
+    import torch
+
+    s, ws = lay.shape, lay.workspace
+    lay_off = moe.workspace_layout(s)
+    names = moe.WS_REGIONS
+    ends = [lay_off[names[i + 1]] if i + 1 < len(names) else ws.numel()
+            for i in range(len(names))]
+    ws.fill_(SENTINEL)
+    torch.cuda.synchronize()
+
+    def touched():
+        per = {n: written_extent(ws[lay_off[n]:ends[i]]) for i, n in enumerate(names)}
+        return sum(per.values()), per
+
+    phase_of = {"dispatch": "after_pack", "down": "after_experts"}
+    measured = {"before_layer": 0}
+    alloc = {"before_layer": torch.cuda.memory_allocated()}
+    per_region = {}
+    for name in lay.stages(*args_l):
+        if name in phase_of:
+            torch.cuda.synchronize()
+            total, per_region = touched()
+            measured[phase_of[name]] = total
+            alloc[phase_of[name]] = torch.cuda.memory_allocated()
+    measured["after_dispatch"] = measured["after_pack"]  # expert-parallel size 1
+    alloc["after_dispatch"] = alloc["after_pack"]
+    bound = moe.workspace_phases(s)
+    order = moe.PHASES
+    return {
+        "workspace_bytes": int(ws.numel()),
+        "written_bytes_measured": {p: int(measured[p]) for p in order},
+        "written_bytes_bound": {p: int(bound[p]) for p in order},
+        "written_by_region_after_experts": {n: v for n, v in per_region.items() if v},
+        "torch_allocated_bytes": {p: int(alloc[p]) for p in order},
+        "torch_peak_allocated_bytes": int(torch.cuda.max_memory_allocated()),
+        "torch_peak_reserved_bytes": int(torch.cuda.max_memory_reserved()),
+    }
+
+
+def routing_summary(moe, w, s, lay, ep, ranks_per_node) -> dict:
+    """The layer's S9 record (moe_expert_stats over the routed and kept counts), drops, and
+    the per-slot and placement record of moe_slot_counts' tables under a contiguous
+    placement of the experts over `ep` ranks."""
+    import numpy as np
+    import torch
+
+    routed = lay.routed_counts.cpu().numpy()
+    kept = lay.tokens_per_expert.cpu().numpy()
+    drops = lay.drops.cpu().numpy().astype(np.int64)
+    rec = moe.expert_stats(w.T, w.k, routed, kept)
+    stats = {"active_tokens": w.T, "top_k": w.k, "capacity": int(s.capacity),
+             "expert_p50": rec["expert_p50"], "expert_p95": rec["expert_p95"],
+             "expert_max": rec["expert_max"],
+             "expert_max_to_mean": round(rec["expert_max_to_mean"], 4),
+             "top_5_percent_expert_share": round(rec["top_5_percent_expert_share"], 4),
+             "dropped_tokens": int(drops[0]), "dropped_per_slot": drops[1:w.k + 1].tolist(),
+             "fully_dropped_tokens": int(drops[w.k + 1]), "kept_rows": rec["kept_rows"],
+             "active_experts": rec["active_experts"]}
+    if w.segments:
+        stats["segments"] = segment_drops(lay.view("dest_row").cpu().numpy(), w.segments)
+    rbs = torch.empty((w.k, w.E), dtype=torch.int32, device="cuda")
+    kbs = torch.empty_like(rbs)
+    moe.slot_counts(s, lay.view("topk_idx"), lay.view("dest_row"), rbs, kbs)
+    placement = np.arange(w.E) * ep // w.E
+    rr = moe.routing_record(w.T, rbs.cpu().numpy(), kbs.cpu().numpy(), placement,
+                            ranks_per_node)
+    stats["routing"] = {
+        "slot_max_to_mean": [round(v, 3) for v in rr["slot_max_to_mean"]],
+        "drop_share_per_slot": [round(v, 4) for v in rr["drop_share_per_slot"]],
+        "ep_ranks": ep, "rank_load": rr["rank_load"],
+        "rank_max_to_mean": round(rr["rank_max_to_mean"], 4),
+        "node_load": rr["node_load"], "node_max_to_mean": round(rr["node_max_to_mean"], 4)}
+    return stats
+
+
+def measure(moe, w, s, args_l, K, W, graph=False, passes=5, ep=8, ranks_per_node=8,
+            phases=True) -> dict:
+    """Time K moe_layer steps of shape s after W warm-up steps, then the staged pass, the
+    routing record, the rooflines and (phases) the memory record."""
+    import torch
+
+    lay = moe.MoELayer(s)
+    stream = torch.cuda.current_stream()
+    for _ in range(W):
+        lay(*args_l)
+    torch.cuda.synchronize()
+    run_step = lambda: lay(*args_l)  # noqa: E731
+    if graph:  # the same launches, replayed from a captured HIP graph
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            lay(*args_l)
+        run_step = g.replay
+        for _ in range(W):
+            run_step()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+    ms, step_ms, wall = time_steps(run_step, K, stream)
+    st = staged_ms(lay, args_l, max(K, passes), stream)
+    stats = routing_summary(moe, w, s, lay, ep, ranks_per_node)
+    N, E_active = stats["kept_rows"], stats["active_experts"]
+    roof = gate_up_roofline(w, N, E_active, st["gate_up"])
+    roof["traffic"] = traffic_for(w.name)
+    roof["kernel"] = "prefill_gemm_kernel (gate/up + SwiGLU), incl. its tile-table launch"
+    roof["kernel_ms"] = round(st["gate_up"], 4)
+    out = {
+        "ms_per_step": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+        "wall_ms_per_step": round(wall * 1e3 / K, 4),
+        "step_ms_p50_p95_p99": [round(percentile(step_ms, q), 4) for q in (0.5, 0.95, 0.99)],
+        "roofline": roof,
+        "down_roofline_frac": gate_up_roofline(w, N, E_active, 2.0 * st["down"])["frac"],
+        "layer_roofline_frac": layer_roofline_frac(w, N, E_active, ms),
+        "stage_ms": {"router_ms": round(st["router"], 4), "pack_ms": round(st["dispatch"], 4),
+                     "expert_compute_ms": round(st["gate_up"] + st["down"], 4),
+                     "gate_up_ms": round(st["gate_up"], 4), "down_ms": round(st["down"], 4),
+                     "unpack_ms": round(st["combine"], 4)},
+        "expert_stats": stats,
+    }
+    if phases:
+        out["memory_by_phase"] = memory_by_phase(lay, args_l, moe)
+    del lay
+    return out
+
+
+def cf_sweep(moe, w, args_l, factors, K, W, dtype) -> list:
+    """[EP-checks] "Capacity factor changes quality, memory and tail latency": the same
+    inputs at each capacity factor: drop rate per layer and per slot, step time p50 / p95 /
+    p99, max over mean, and the workspace the capacity implies."""
+    import torch
+
+    rows = []
+    for cf in factors:
+        C = moe.capacity(w.T, w.k, w.E, cf)
+        s = moe.shape(w.T, w.d, w.E, w.k, w.F, C, dtype)
+        lay = moe.MoELayer(s)
+        for _ in range(W):
+            lay(*args_l)
+        ms, step_ms, _ = time_steps(lambda: lay(*args_l), K, torch.cuda.current_stream())
+        drops = lay.drops.cpu().numpy()
+        rec = moe.expert_stats(w.T, w.k, lay.routed_counts.cpu().numpy(),
+                               lay.tokens_per_expert.cpu().numpy())
+        kept = lay.tokens_per_expert.cpu().numpy()
+        rows.append({
+            "capacity_factor": cf, "capacity": C,
+            "drop_rate": round(float(drops[0]) / (w.T * w.k), 5),
+            "drop_rate_per_slot": [round(float(v) / w.T, 5) for v in drops[1:w.k + 1]],
+            "fully_dropped_tokens": int(drops[w.k + 1]),
+            "ms_per_step": round(ms, 4),
+            "step_ms_p50_p95_p99": [round(percentile(step_ms, q), 4) for q in (0.5, 0.95, 0.99)],
+            "expert_max_to_mean": round(rec["expert_max_to_mean"], 4),
+            "kept_max_to_mean": round(float(kept.max()) / (float(kept.sum()) / w.E), 4),
+            "workspace_bytes": moe.workspace_size(s),
+            "max_rows": moe.max_rows(s),
+        })
+        del lay
+    return rows
+
+
+OTHER_WORKLOADS = ["tiny_f32", "mixtral_8x22b_zipf", "dsv3_decode", "dsv3_mixed"]
+SWEEP_WORKLOAD, SWEEP_FACTORS = "mixtral_8x22b_zipf", (1.0, 1.25, 1.5, 2.0, None)
 
 
 def main():
@@ -293,7 +606,6 @@ def main():
               "it does not run on several GPUs.", file=sys.stderr)
         sys.exit(2)
     build_if_missing()
-    import numpy as np
     import torch
 
     import moe_inputs as mi
@@ -301,80 +613,23 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = mi.WORKLOADS[args.workload]
-    C = moe.capacity(w.T, w.k, w.E, w.capacity_factor)
+    cf = w.capacity_factor if args.capacity_factor is None else (
+        None if args.capacity_factor <= 0 else args.capacity_factor)
+    C = moe.capacity(w.T, w.k, w.E, cf)
     dtype = moe.MOE_BF16 if w.dtype == "bf16" else moe.MOE_F32
     flags = ((moe.MOE_FLAG_PAD_TO_CAPACITY if args.pad else 0) |
              (moe.MOE_FLAG_SLOT_MAJOR if args.slot_major else 0) |
              (moe.MOE_FLAG_BIAS_SELECTION_ONLY if args.bias_selection_only else 0))
     G, M = (int(v) for v in args.groups.split(":")) if args.groups else (0, 0)
     s = moe.shape(w.T, w.d, w.E, w.k, w.F, C, dtype, flags=flags, n_groups=G, topk_groups=M)
-    b_elt = w.elt_bytes
     print(f"# workload {w.name}: {s}", file=sys.stderr, flush=True)
 
-    dev = {n: mi.device_tensor(w, n) for n in ("x", "w_router", "w_gate", "w_up", "w_down")}
-    b_np = mi.router_bias(w)
-    bias = None if b_np is None else torch.from_numpy(b_np).cuda()
-    args_l = (dev["x"], dev["w_router"], bias, dev["w_gate"], dev["w_up"], dev["w_down"])
-    lay = moe.MoELayer(s)
-    stream = torch.cuda.current_stream()
-
-    for _ in range(args.warmup):
-        lay(*args_l)
-    torch.cuda.synchronize()
-    run_step = lambda: lay(*args_l)  # noqa: E731
-    if args.graph:  # the same launches, replayed from a captured HIP graph
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            lay(*args_l)
-        run_step = graph.replay
-        for _ in range(args.warmup):
-            run_step()
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-
-    # ---- timed region: exactly K moe_layer calls ------------------------------------------
-    K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(K):
-        run_step()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]
-    total_ms = ev[0].elapsed_time(ev[K])
-    ms_per_step = total_ms / K
-    print(f"# timed {K} steps: {ms_per_step:.4f} ms/step (wall {wall * 1e3 / K:.4f})",
-          file=sys.stderr, flush=True)
-
-    # ---- staged pass: the same launches with events between the ABI calls ------------------
-    # Each stage is its own ABI call from Python, and a short stage (the router, the
-    # dispatch) can finish on the GPU before the host has enqueued the next one.  The
-    # staged layers are therefore enqueued back to back with one synchronisation at the
-    # end: the host enqueues a layer's short stages while the GPU runs the previous layer's
-    # GEMMs, so the events time GPU work, not host gaps.  The first layer, which has no
-    # predecessor to hide behind, is not counted.
-    stage_times = {}
-    passes = []
-    for i in range(max(K, 5) + 1):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        marks = []
-        for name in lay.stages(*args_l):
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(stream)
-            marks.append((name, e))
-        passes.append((e0, marks))
-    torch.cuda.synchronize()
-    for e0, marks in passes[1:]:
-        prev = e0
-        for name, e in marks:
-            stage_times.setdefault(name, []).append(prev.elapsed_time(e))
-            prev = e
-    stage_ms = {n: statistics.mean(v) for n, v in stage_times.items()}
-
+    torch.cuda.reset_peak_memory_stats()
+    args_l = device_inputs(w)
+    m = measure(moe, w, s, args_l, args.steps, args.warmup, graph=args.graph, ep=args.ep,
+                ranks_per_node=args.ranks_per_node)
+    print(f"# timed {args.steps} steps: {m['ms_per_step']:.4f} ms/step "
+          f"(wall {m['wall_ms_per_step']:.4f})", file=sys.stderr, flush=True)
     if args.copy_calibration:  # a plain device copy of known size, for counter scaling
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -382,99 +637,70 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    # ---- routing statistics of the last call ------------------------------------------------
-    routed = lay.routed_counts.cpu().numpy().astype(np.int64)
-    kept = lay.tokens_per_expert.cpu().numpy().astype(np.int64)
-    drops = lay.drops.cpu().numpy().astype(np.int64)
-    rec = moe.expert_stats(w.T, w.k, routed, kept)  # the library's S9 record
-    N = rec["kept_rows"]
-    E_active = rec["active_experts"]
-    stats = {"active_tokens": w.T, "top_k": w.k, "capacity": C,
-             "expert_p50": rec["expert_p50"], "expert_p95": rec["expert_p95"],
-             "expert_max": rec["expert_max"],
-             "expert_max_to_mean": round(rec["expert_max_to_mean"], 4),
-             "dropped_tokens": int(drops[0]), "dropped_per_slot": drops[1:w.k + 1].tolist(),
-             "fully_dropped_tokens": int(drops[w.k + 1]), "kept_rows": N,
-             "active_experts": E_active}
-    if w.segments:
-        stats["segments"] = segment_drops(lay.view("dest_row").cpu().numpy(), w.segments)
-    if args.pad:
-        R = moe.max_rows(s)
-        stats["padded_rows"] = R
-        stats["pad_fraction"] = round(1.0 - N / R, 4)
-    # per-slot counts on the device, summarised on the host, under a contiguous placement of
-    # the experts over --ep ranks
-    rbs = torch.empty((w.k, w.E), dtype=torch.int32, device="cuda")
-    kbs = torch.empty_like(rbs)
-    moe.slot_counts(s, lay.view("topk_idx"), lay.view("dest_row"), rbs, kbs)
-    placement = np.arange(w.E) * args.ep // w.E
-    rec = moe.routing_record(w.T, rbs.cpu().numpy(), kbs.cpu().numpy(), placement,
-                             args.ranks_per_node)
-    stats["routing"] = {
-        "top_5_percent_expert_share": round(rec["top_5_percent_expert_share"], 4),
-        "slot_max_to_mean": [round(v, 3) for v in rec["slot_max_to_mean"]],
-        "drop_share_per_slot": [round(v, 4) for v in rec["drop_share_per_slot"]],
-        "ep_ranks": args.ep, "rank_load": rec["rank_load"],
-        "rank_max_to_mean": round(rec["rank_max_to_mean"], 4),
-        "node_load": rec["node_load"], "node_max_to_mean": round(rec["node_max_to_mean"], 4)}
-
-    # ---- roofline of the dominant kernel (gate/up grouped GEMM) ------------------------------
-    t_gu = stage_ms["gate_up"] * 1e-3
-    flops_gu = 4.0 * N * w.d * w.F
-    bytes_gu = b_elt * (2.0 * E_active * w.F * w.d + N * w.d + N * w.F)
-    peak_flops = (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS) * 1e12
-    ridge = peak_flops / (PEAK_HBM_GBS * 1e9)
-    if flops_gu / bytes_gu >= ridge:
-        roof = {"bound": "mfma", "achieved": round(flops_gu / t_gu / 1e12, 2),
-                "peak": peak_flops / 1e12, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(bytes_gu / t_gu / 1e9, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = traffic_for(w.name)
-    roof["kernel"] = "prefill_gemm_kernel (gate/up + SwiGLU), incl. its tile-table launch"
-    roof["kernel_ms"] = round(stage_ms["gate_up"], 4)
-
-    # whole-layer roofline: algorithmic work of the layer against both peaks
-    F_alg = 2.0 * w.T * w.d * w.E + 6.0 * w.d * w.F * N
-    B_alg = b_elt * (2.0 * w.T * w.d + w.E * w.d + 3.0 * w.d * w.F * E_active)
-    t_roof = max(F_alg / peak_flops, B_alg / (PEAK_HBM_GBS * 1e9))
-    layer_frac = t_roof / (ms_per_step * 1e-3)
+    sweep = None
+    if args.cf_sweep:
+        factors = [None if v in ("none", "0") else float(v) for v in args.cf_sweep.split(",")]
+        sweep = cf_sweep(moe, w, args_l, factors, args.steps, args.warmup, dtype)
+    del args_l
+    torch.cuda.empty_cache()
 
     result = {
         "metric": METRIC,
-        "value": round(w.T / (ms_per_step * 1e-3), 1),
+        "value": m["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded Philox inputs, random-init weights)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F,
-                   "capacity_factor": w.capacity_factor, "capacity": C,
+                   "capacity_factor": cf, "capacity": C,
                    "router_bias_zipf_s": w.zipf_s,
                    "dispatch": "pad_to_capacity" if args.pad else "packed",
                    "drop_order": "slot_major" if args.slot_major else "token_major",
                    "bias": "selection_only" if args.bias_selection_only else "logits",
                    "groups": [G, M] if G > 1 else None,
                    "launch": "hip_graph_replay" if args.graph else "stream"},
-        "roofline": roof,
-        "layer_roofline_frac": round(layer_frac, 4),
-        "step_ms_p50_p95_p99": [round(percentile(step_ms, q), 4) for q in (0.5, 0.95, 0.99)],
-        "stage_ms": {"router_ms": round(stage_ms["router"], 4),
-                     "pack_ms": round(stage_ms["dispatch"], 4),
-                     "expert_compute_ms": round(stage_ms["gate_up"] + stage_ms["down"], 4),
-                     "gate_up_ms": round(stage_ms["gate_up"], 4),
-                     "down_ms": round(stage_ms["down"], 4),
-                     "unpack_ms": round(stage_ms["combine"], 4)},
-        "expert_stats": stats,
+        "roofline": m["roofline"],
+        "layer_roofline_frac": m["layer_roofline_frac"],
+        "down_roofline_frac": m["down_roofline_frac"],
+        "step_ms_p50_p95_p99": m["step_ms_p50_p95_p99"],
+        "stage_ms": m["stage_ms"],
+        "expert_stats": m["expert_stats"],
+        "memory_by_phase": m["memory_by_phase"],
         "cpu_baseline": None,
     }
+    if sweep is not None:
+        result["cf_sweep"] = sweep
+    default_run = not (flags or G > 1 or args.graph or args.capacity_factor is not None or
+                       args.cf_sweep or args.workload != DEFAULT_WORKLOAD)
+    if default_run and not args.no_other_workloads:
+        # every other workload, timed the same way (fewer steps), and the capacity-factor
+        # sweep of the skewed Mixtral-8x22B layer; reported beside the headline, not in it
+        others = {}
+        for name in OTHER_WORKLOADS:
+            wo = mi.WORKLOADS[name]
+            so = moe.shape(wo.T, wo.d, wo.E, wo.k, wo.F,
+                           moe.capacity(wo.T, wo.k, wo.E, wo.capacity_factor),
+                           moe.MOE_BF16 if wo.dtype == "bf16" else moe.MOE_F32)
+            print(f"# workload {name}", file=sys.stderr, flush=True)
+            al = device_inputs(wo)
+            mo = measure(moe, wo, so, al, args.other_steps, args.warmup, phases=True)
+            mo["config"] = {"T": wo.T, "d": wo.d, "E": wo.E, "k": wo.k, "F": wo.F,
+                            "capacity_factor": wo.capacity_factor, "capacity": int(so.capacity),
+                            "router_bias_zipf_s": wo.zipf_s, "dtype": wo.dtype}
+            if name == SWEEP_WORKLOAD:
+                print(f"# capacity-factor sweep on {name}", file=sys.stderr, flush=True)
+                result["cf_sweep"] = {"workload": name, "rows": cf_sweep(
+                    moe, wo, al, SWEEP_FACTORS, args.other_steps, args.warmup, moe.MOE_BF16)}
+            others[name] = mo
+            del al
+            torch.cuda.empty_cache()
+        result["workloads"] = others
     if not args.no_cpu_baseline and not (flags or G > 1):
         ntok = args.cpu_tokens or CPU_SAMPLE_TOKENS.get(w.name, 256)
         print(f"# cpu baseline: oracle on {ntok} tokens", file=sys.stderr, flush=True)

@@ -264,7 +264,9 @@ def expert_ffn_streamed(x: np.ndarray, src_token: np.ndarray, expert_offsets: np
     too large to hold at once: Y[r] = FFN_e(x[src_token[r]]) for the rows r of each expert's
     segment [off_e, off_{e+1}), with expert_weights(e) -> (Wg_e, Wu_e, Wd_e) called only for
     experts that hold rows, one expert at a time.  Same steps as expert_ffn, in the same
-    expert order; progress(e), if given, is called after each expert."""
+    expert order; progress(e), if given, is called after each expert.  An empty slot of the
+    padded layout (src_token -1) is a zero row, whose FFN is exactly zero (silu(0) * 0 = 0),
+    so its Y row stays zero."""
     off = np.asarray(expert_offsets, dtype=np.int64)
     src = np.asarray(src_token, dtype=np.int64)
     E = off.shape[0] - 1
@@ -272,11 +274,11 @@ def expert_ffn_streamed(x: np.ndarray, src_token: np.ndarray, expert_offsets: np
     Y = np.zeros((N, np.asarray(x).shape[1]), dtype=np.float64)
     for e in range(E):
         a, b = int(off[e]), int(off[e + 1])
-        if b > a:
-            rows = src[a:b]
-            assert np.all(rows >= 0), "a kept row slot without a token"
+        rows = src[a:b]
+        has = np.nonzero(rows >= 0)[0]
+        if has.size:
             wg, wu, wd = expert_weights(e)
-            Y[a:b] = swiglu_ffn(np.asarray(x)[rows], wg, wu, wd)
+            Y[a + has] = swiglu_ffn(np.asarray(x)[rows[has]], wg, wu, wd)
         if progress is not None:
             progress(e)
     return Y

@@ -19,8 +19,8 @@ LIB = os.path.join(PKG, "libmoe.so")
 # hash of the sources and flags libmoe.so was built from, written next to the build objects
 STAMP = os.path.join(OBJ, "libmoe.sha256")
 
-SOURCES = ["route.hip", "dispatch.hip", "expert_ffn.hip", "combine.hip", "moe_abi.cpp",
-           "stats.cpp"]
+SOURCES = ["route.hip", "dispatch.hip", "expert_ffn.hip", "combine.hip",
+           "moe_abi.cpp", "stats.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "hipcc")
 FLAGS = [
@@ -42,9 +42,12 @@ LIB_SANITIZED = os.path.join(OBJ, "libmoe_sanitized.so")
 
 
 def source_hash() -> str:
-    """sha256 over the library's sources (csrc/, include/moe.h) and its compile flags."""
-    h = hashlib.sha256(" ".join(FLAGS).encode())
-    files = sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(ROOT, "include", "moe.h")]
+    """sha256 over the library's compiled sources, the headers they include and the compile
+    flags."""
+    # flags with the repository's location taken out, so a copy elsewhere hashes the same
+    h = hashlib.sha256(" ".join(f.replace(ROOT, "") for f in FLAGS).encode())
+    files = ([os.path.join(CSRC, f) for f in SOURCES] +
+             sorted(glob.glob(os.path.join(CSRC, "*.h"))) + [os.path.join(ROOT, "include", "moe.h")])
     for f in files:
         if os.path.isfile(f):
             h.update(os.path.basename(f).encode())

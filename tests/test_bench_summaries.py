@@ -94,3 +94,39 @@ def test_segment_drops(bench):
     got = bench.segment_drops(dest, (("prefill", 0, 3), ("decode", 3, 5)))
     assert got == {"prefill": {"tokens": 3, "dropped": 1, "fully_dropped_tokens": 0},
                    "decode": {"tokens": 2, "dropped": 3, "fully_dropped_tokens": 1}}
+
+
+def test_written_extent(bench):
+    import torch
+
+    buf = torch.full((200_000,), bench.SENTINEL, dtype=torch.uint8)
+    assert bench.written_extent(buf) == 0
+    buf[123_456] = 0
+    assert bench.written_extent(buf) == 123_457
+    buf[199_999] = 1  # past the last whole 64 KiB chunk
+    assert bench.written_extent(buf) == 200_000
+    small = torch.full((10,), bench.SENTINEL, dtype=torch.uint8)
+    small[3] = 7
+    assert bench.written_extent(small) == 4
+    assert bench.written_extent(small[:0]) == 0
+
+
+def test_rooflines(bench):
+    import moe_inputs as mi
+
+    # Mixtral-8x7B gate/up: 4 N d F flops over the event time, against 2500 TFLOP/s
+    w = mi.WORKLOADS["mixtral_8x7b_prefill"]
+    r = bench.gate_up_roofline(w, 8192, 8, 1.6204)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert r["achieved"] == pytest.approx(4 * 8192 * 4096 * 14336 / 1.6204e-3 / 1e12, rel=1e-4)
+    assert r["frac"] == pytest.approx(r["achieved"] / 2500.0, abs=1e-4)
+    # DeepSeek-V3 decode: 8 rows per expert, far below the ridge: bytes against 8 TB/s
+    w = mi.WORKLOADS["dsv3_decode"]
+    r = bench.gate_up_roofline(w, 2048, 256, 2.0)
+    want = 2 * (2 * 256 * 2048 * 7168 + 2048 * 7168 + 2048 * 2048) / 2e-3 / 1e9
+    assert r["bound"] == "hbm" and r["achieved"] == pytest.approx(want, rel=1e-4)
+    # layer: max(F_alg / P, B_alg / BW) over the step time
+    w = mi.WORKLOADS["mixtral_8x7b_prefill"]
+    F_alg = 2 * 4096 * 4096 * 8 + 6 * 4096 * 14336 * 8192
+    assert bench.layer_roofline_frac(w, 8192, 8, 2.0) == pytest.approx(
+        F_alg / 2.5e15 / 2e-3, abs=1e-4)

@@ -334,3 +334,18 @@ def test_streamed_layer_equals_batched_layer():
     out = oracle.combine(Y, res["dest_row"], res["topk_w"])
     assert fetched == [e for e in range(w.E) if res["tokens_per_expert"][e] > 0]
     assert np.max(np.abs(out - res["out"])) < 1e-12 * np.max(np.abs(res["out"]))
+
+
+def test_streamed_layer_padded_equals_batched():
+    # padded layout: the empty slots of each expert's C rows are zero rows (FFN exactly 0);
+    # the streamed path skips them and equals the batched padded layer
+    w = mi.WORKLOADS["tiny_f32"]
+    x = mi.host_tensor_f32(w, "x")
+    Wr = mi.host_tensor_f32(w, "w_router")
+    Wg, Wu, Wd = (mi.host_tensor_f32(w, n) for n in ("w_gate", "w_up", "w_down"))
+    res = oracle.moe_layer(x, Wr, None, Wg, Wu, Wd, k=w.k, C=24, pad_to_capacity=True)
+    assert np.any(res["src_token"] < 0)
+    Y = oracle.expert_ffn_streamed(x, res["src_token"], res["expert_offsets"],
+                                   lambda e: (Wg[e], Wu[e], Wd[e]))
+    assert np.array_equal(Y[res["src_token"] < 0], np.zeros_like(Y[res["src_token"] < 0]))
+    assert np.max(np.abs(Y - res["y_perm"])) < 1e-12 * np.max(np.abs(res["y_perm"]))
