@@ -48,7 +48,8 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = -2, /* outside the limits above or unknown dtype */
   MOE_ERR_ALIGNMENT = -3,   /* a tensor pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = -4,   /* workspace null or smaller than moe_workspace_size() */
-  MOE_ERR_HIP = -5          /* a kernel launch failed */
+  MOE_ERR_HIP = -5,         /* a kernel launch failed */
+  MOE_ERR_SCRATCH = -6      /* the shape needs more than the static dispatch scratch */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -289,6 +290,26 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, const void* x,
                  int32_t* tokens_per_expert, int32_t* expert_offsets, int32_t* src_token,
                  int32_t* src_slot, int32_t* dest_row, int32_t* drops, void* x_perm,
                  hipStream_t stream);
+
+/*
+ * moe_dispatch_no_workspace -- moe_dispatch for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same operation, arguments and results as moe_dispatch, without the workspace.  The
+ * dispatch's scratch tables (per-tile expert histogram and its per-expert scan, int32
+ * [ntiles, E] each, 256-byte aligned, ntiles = ceil(T*k / (floor(512 / k) * k))) live in a
+ * static array of MOE_DISPATCH_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  Calls on one GPU share that array: calls that overlap on one
+ * GPU (concurrent streams, or threads) race and must not be made.  Shapes whose two tables
+ * need more than the array holds return MOE_ERR_SCRATCH before anything is enqueued.  The
+ * first call on a device looks up that device's copy of the array (no allocation); a
+ * failed lookup returns MOE_ERR_HIP.  Nothing here allocates or frees memory.
+ */
+#define MOE_DISPATCH_SCRATCH_BYTES (8u << 20)
+int moe_dispatch_no_workspace(const moe_shape* shape, const int32_t* topk_idx, const void* x,
+                              int32_t* routed_counts, int32_t* tokens_per_expert,
+                              int32_t* expert_offsets, int32_t* src_token, int32_t* src_slot,
+                              int32_t* dest_row, int32_t* drops, void* x_perm,
+                              hipStream_t stream);
 
 /*
  * moe_expert_ffn -- S6-S7: grouped SwiGLU FFN over the expert-contiguous rows.

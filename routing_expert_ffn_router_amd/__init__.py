@@ -22,6 +22,8 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_ALIGNMENT = -3
 MOE_ERR_WORKSPACE = -4
 MOE_ERR_HIP = -5
+MOE_ERR_SCRATCH = -6
+DISPATCH_SCRATCH_BYTES = 8 << 20  # MOE_DISPATCH_SCRATCH_BYTES
 
 MOE_F32 = 0
 MOE_BF16 = 1
@@ -109,6 +111,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_route": (i32, [_S, _P, _P, _P, _P, i32, _P, _P, _P, _P]),
         "moe_dispatch": (i32, [_S, _P, _P, _P, sz, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "moe_dispatch_no_workspace": (i32, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "moe_expert_ffn": (i32, [_S, _P, _P, _P, _P, _P, _P, sz, _P, _P]),
         "moe_expert_gate_up": (i32, [_S, _P, _P, _P, _P, _P, sz, _P, _P]),
         "moe_expert_gate_up_gathered": (i32, [_S, _P, _P, _P, _P, _P, _P, sz, _P, _P]),
@@ -265,6 +268,17 @@ def dispatch(s: MoeShape, topk_idx, x, workspace, routed_counts, tokens_per_expe
         ctypes.byref(s), _ptr(topk_idx), _ptr(x), _ptr(workspace), _nbytes(workspace),
         _ptr(routed_counts), _ptr(tokens_per_expert), _ptr(expert_offsets), _ptr(src_token),
         _ptr(src_slot), _ptr(dest_row), _ptr(drops), _ptr(x_perm), _stream(stream)))
+
+
+def dispatch_no_workspace(s: MoeShape, topk_idx, x, routed_counts, tokens_per_expert,
+                          expert_offsets, src_token, dest_row, drops, x_perm, stream=None,
+                          src_slot=None) -> None:
+    """moe_dispatch without a workspace: its scratch tables live in the library's static
+    per-GPU array (calls that overlap on one GPU race)."""
+    _check("moe_dispatch_no_workspace", load_library().moe_dispatch_no_workspace(
+        ctypes.byref(s), _ptr(topk_idx), _ptr(x), _ptr(routed_counts), _ptr(tokens_per_expert),
+        _ptr(expert_offsets), _ptr(src_token), _ptr(src_slot), _ptr(dest_row), _ptr(drops),
+        _ptr(x_perm), _stream(stream)))
 
 
 def expert_ffn(s: MoeShape, x_perm, expert_offsets, w_gate, w_up, w_down, workspace, y_perm,

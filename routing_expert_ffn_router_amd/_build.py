@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 # hash of the sources and flags libmoe.so was built from, written next to the build objects
 STAMP = os.path.join(OBJ, "libmoe.sha256")
 
-SOURCES = ["route.hip", "dispatch.hip", "expert_ffn.hip", "combine.hip",
+SOURCES = ["route.hip", "dispatch.hip", "expert_ffn.hip", "combine.hip", "noalloc.hip",
            "moe_abi.cpp", "stats.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "hipcc")

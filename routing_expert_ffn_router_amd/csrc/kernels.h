@@ -50,6 +50,9 @@ struct DispatchArgs {
   void* x_perm;        // [R, d]; null: tables only, no row copies
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+// The static scratch of moe_dispatch_no_workspace on the current device: its address
+// (looked up once per device) and size in bytes.
+hipError_t dispatch_scratch(void** ptr, size_t* bytes);
 
 // S6-S7.  The grouped GEMMs run over a device-side tile table (expert, first row) of
 // row-tile height bm with at most m_max entries.

@@ -123,6 +123,53 @@ int check_workspace(const moe_shape* s, const void* ws, size_t bytes, Layout* L)
   return MOE_OK;
 }
 
+// Argument checks of the dispatch (everything but the scratch tables).
+int check_dispatch_args(const moe_shape* s, const int32_t* topk_idx, const void* x,
+                        const int32_t* routed_counts, const int32_t* tokens_per_expert,
+                        const int32_t* expert_offsets, const int32_t* src_token,
+                        const int32_t* dest_row, const int32_t* drops, const void* x_perm) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!routed_counts || !tokens_per_expert || !expert_offsets || !drops)
+    return MOE_ERR_INVALID_ARG;
+  if (s->T > 0 && (!topk_idx || !src_token || !dest_row || (x_perm && !x)))
+    return MOE_ERR_INVALID_ARG;
+  if (s->T > 0 && x_perm && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+// The dispatch launches, with the scratch tables tile_hist / tile_base ([ntiles, E] int32
+// each) from the workspace or from the static array.
+int dispatch_launch(const moe_shape* s, const int32_t* topk_idx, const void* x,
+                    int32_t* tile_hist, int32_t* tile_base, int32_t* routed_counts,
+                    int32_t* tokens_per_expert, int32_t* expert_offsets, int32_t* src_token,
+                    int32_t* src_slot, int32_t* dest_row, int32_t* drops, void* x_perm,
+                    hipStream_t st) {
+  moe::DispatchArgs a;
+  a.topk_idx = topk_idx;
+  a.x = x;
+  a.T = s->T;
+  a.d = s->d;
+  a.E = s->E;
+  a.k = s->k;
+  a.C = eff_capacity(s);
+  a.R = max_rows(s);
+  a.elt_bytes = elt_bytes(s->dtype);
+  a.slot_major = (s->flags & MOE_FLAG_SLOT_MAJOR) != 0;
+  a.pad = padded(s);
+  a.tile_hist = tile_hist;
+  a.tile_base = tile_base;
+  a.routed = routed_counts;
+  a.kept = tokens_per_expert;
+  a.offsets = expert_offsets;
+  a.src_token = src_token;
+  a.src_slot = src_slot;
+  a.dest_row = dest_row;
+  a.drops = drops;
+  a.x_perm = x_perm;
+  return hip_status(moe::launch_dispatch(a, st));
+}
+
 int route_impl(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
                float* logits, int logits_given, int32_t* idx, float* gates, int32_t* status,
                hipStream_t st) {
@@ -205,6 +252,7 @@ const char* moe_status_string(int st) {
     case MOE_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH: return "shape needs more than the static dispatch scratch";
     default: return "unknown status";
   }
 }
@@ -227,38 +275,36 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, voi
                  size_t ws_bytes, int32_t* routed_counts, int32_t* tokens_per_expert,
                  int32_t* expert_offsets, int32_t* src_token, int32_t* src_slot,
                  int32_t* dest_row, int32_t* drops, void* x_perm, hipStream_t st) {
-  int rc = check_shape(s);
+  int rc = check_dispatch_args(s, topk_idx, x, routed_counts, tokens_per_expert,
+                               expert_offsets, src_token, dest_row, drops, x_perm);
   if (rc != MOE_OK) return rc;
-  if (!routed_counts || !tokens_per_expert || !expert_offsets || !drops)
-    return MOE_ERR_INVALID_ARG;
-  if (s->T > 0 && (!topk_idx || !src_token || !dest_row || (x_perm && !x)))
-    return MOE_ERR_INVALID_ARG;
-  if (s->T > 0 && x_perm && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_ALIGNMENT;
   Layout L;
   if ((rc = check_workspace(s, ws, ws_bytes, &L)) != MOE_OK) return rc;
-  moe::DispatchArgs a;
-  a.topk_idx = topk_idx;
-  a.x = x;
-  a.T = s->T;
-  a.d = s->d;
-  a.E = s->E;
-  a.k = s->k;
-  a.C = eff_capacity(s);
-  a.R = max_rows(s);
-  a.elt_bytes = elt_bytes(s->dtype);
-  a.slot_major = (s->flags & MOE_FLAG_SLOT_MAJOR) != 0;
-  a.pad = padded(s);
-  a.tile_hist = region<int32_t>(ws, L, MOE_WS_TILE_HIST);
-  a.tile_base = region<int32_t>(ws, L, MOE_WS_TILE_BASE);
-  a.routed = routed_counts;
-  a.kept = tokens_per_expert;
-  a.offsets = expert_offsets;
-  a.src_token = src_token;
-  a.src_slot = src_slot;
-  a.dest_row = dest_row;
-  a.drops = drops;
-  a.x_perm = x_perm;
-  return hip_status(moe::launch_dispatch(a, st));
+  return dispatch_launch(s, topk_idx, x, region<int32_t>(ws, L, MOE_WS_TILE_HIST),
+                         region<int32_t>(ws, L, MOE_WS_TILE_BASE), routed_counts,
+                         tokens_per_expert, expert_offsets, src_token, src_slot, dest_row,
+                         drops, x_perm, st);
+}
+
+int moe_dispatch_no_workspace(const moe_shape* s, const int32_t* topk_idx, const void* x,
+                              int32_t* routed_counts, int32_t* tokens_per_expert,
+                              int32_t* expert_offsets, int32_t* src_token, int32_t* src_slot,
+                              int32_t* dest_row, int32_t* drops, void* x_perm,
+                              hipStream_t st) {
+  int rc = check_dispatch_args(s, topk_idx, x, routed_counts, tokens_per_expert,
+                               expert_offsets, src_token, dest_row, drops, x_perm);
+  if (rc != MOE_OK) return rc;
+  // the two scratch tables, each 256-byte aligned, in the static array
+  const int64_t table = align_up(moe::dispatch_ntiles(s->T, s->k) * s->E * 4);
+  if (2 * table > (int64_t)MOE_DISPATCH_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* scratch = nullptr;
+  size_t bytes = 0;
+  if (moe::dispatch_scratch(&scratch, &bytes) != hipSuccess) return MOE_ERR_HIP;
+  if ((int64_t)bytes < 2 * table) return MOE_ERR_SCRATCH;
+  int32_t* hist = static_cast<int32_t*>(scratch);
+  int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + table);
+  return dispatch_launch(s, topk_idx, x, hist, base, routed_counts, tokens_per_expert,
+                         expert_offsets, src_token, src_slot, dest_row, drops, x_perm, st);
 }
 
 }  // extern "C"

@@ -405,3 +405,19 @@ def test_workspace_phases_follow_the_layout(sh):
     assert ph["after_experts"] <= total
     if sh.E == 8 and sh.T == 2048:  # the split down GEMM's fp32 slots are counted
         assert grown >= exp + 3 * R * sh.d * 4
+
+
+def test_no_workspace_dispatch_checks_before_any_launch():
+    # argument checks as moe_dispatch; a shape whose two scratch tables exceed the static
+    # array is refused with MOE_ERR_SCRATCH before the first HIP call
+    p = FAKE
+    f = lib.moe_dispatch_no_workspace
+    big = _shape(T=1 << 21, E=1024, k=1, capacity=0)  # 2 x 4096 x 1024 x 4 B = 32 MiB
+    assert f(ctypes.byref(big), p, None, p, p, p, p, None, p, p, None, None) == \
+        moe.MOE_ERR_SCRATCH
+    s = ctypes.byref(_shape())
+    assert f(s, None, p, p, p, p, p, None, p, p, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(s, p, p, p, p, p, p, None, p, p, p + 8, None) == moe.MOE_ERR_ALIGNMENT
+    assert f(ctypes.byref(_shape(k=9)), p, p, p, p, p, p, None, p, p, None, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert moe.status_string(moe.MOE_ERR_SCRATCH).startswith("shape needs more")
