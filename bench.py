@@ -74,6 +74,9 @@ def parse():
                         "(GRBM_COUNT), MFMA busy share (SQ_VALU_MFMA_BUSY_CYCLES over "
                         "GRBM_GUI_ACTIVE) and bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16), "
                         "for whichever of these counters the run holds")
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                   help="per kernel and grid of a rocprofv3 --kernel-trace run: dispatches and "
+                        "mean / median / min / max duration")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                         "script into profiles/traffic_<workload>.json and exit")
@@ -145,10 +148,12 @@ def summarize_counters(d):
     SQ_INSTS_VALU_MFMA_MOPS_BF16 counts bf16 MFMA work in units of 512 flops:
         clock_ghz     = GRBM_COUNT / XCDs / duration
         mfma_busy_pct = 100 * SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs * SIMDs)
-        mfma_tflops   = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16 / duration."""
+        mfma_tflops   = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16 / duration
+    and, where the run holds them, the LDS bank-conflict share of the LDS cycles
+    (SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE) and the L2 hit rate (TCC_HIT over
+    TCC_HIT + TCC_MISS)."""
     import csv
     import glob
-    import re
     import statistics as st
 
     def rows(pattern):
@@ -171,18 +176,6 @@ def summarize_counters(d):
         e = disp.setdefault(did, {"name": r["Kernel_Name"], "ns": span[did]})
         e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
 
-    def short(name):
-        if "prefill_gemm_kernel" in name:
-            # bf16 operands with an fp32 output: the router logits in dense mode
-            # (mangled: the output type f, possibly followed by a back-reference, closes the
-            # template arguments; demangled: ", float" among them)
-            if ("IDF16b" in name and re.search(r"f(?:S\d*_)?EEvPKT_", name)) or (
-                    "__bf16" in name and re.search(r", float[,>]", name)):
-                return "prefill_gemm_kernel (router logits, dense)"
-            return "prefill_gemm_kernel (" + (
-                "down" if "Lb0E" in name or "false" in name else "gate/up+SwiGLU") + ")"
-        return name.split("(")[0].split("<")[0].replace("void ", "")
-
     per = {}
     for e in disp.values():
         ns = e["ns"]
@@ -192,21 +185,75 @@ def summarize_counters(d):
         if "SQ_VALU_MFMA_BUSY_CYCLES" in e and e.get("GRBM_GUI_ACTIVE"):
             f["mfma_busy_pct"] = (100.0 * e["SQ_VALU_MFMA_BUSY_CYCLES"] /
                                   (e["GRBM_GUI_ACTIVE"] / n_xcc * n_simd))
+        if "SQ_LDS_BANK_CONFLICT" in e and e.get("SQ_LDS_IDX_ACTIVE"):
+            f["lds_bank_conflict_pct"] = (100.0 * e["SQ_LDS_BANK_CONFLICT"] /
+                                          e["SQ_LDS_IDX_ACTIVE"])
+        hit, miss = e.get("TCC_HIT_sum", e.get("TCC_HIT")), e.get("TCC_MISS_sum",
+                                                                   e.get("TCC_MISS"))
+        if hit is not None and miss is not None and hit + miss > 0:
+            f["l2_hit_pct"] = 100.0 * hit / (hit + miss)
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in e:
             f["mfma_tflops"] = 512.0 * e["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / ns / 1e3
             f["mfma_gflop_per_dispatch"] = 512.0 * e["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / 1e9
-        per.setdefault(short(e["name"]), []).append(f)
+        per.setdefault(_short_kernel(e["name"]), []).append(f)
     out = []
     for name, v in sorted(per.items(), key=lambda kv: -sum(f["ns"] for f in kv[1])):
         k = {"kernel": name, "dispatches": len(v),
              "median_us": round(st.median(f["ns"] for f in v) / 1e3, 1)}
         for key, nd in (("clock_ghz", 3), ("mfma_busy_pct", 1), ("mfma_tflops", 1),
-                        ("mfma_gflop_per_dispatch", 2)):
+                        ("mfma_gflop_per_dispatch", 2), ("lds_bank_conflict_pct", 2),
+                        ("l2_hit_pct", 1)):
             vals = [f[key] for f in v if key in f]
             if vals:
                 k[key] = round(st.median(vals), nd)
         out.append(k)
     return {"xcds": n_xcc, "simds": n_simd, "kernels": out}
+
+
+def _short_kernel(name):
+    """Readable name of a kernel of this library (the grouped GEMM by its role)."""
+    import re
+
+    if "prefill_gemm_kernel" in name:
+        # bf16 operands with an fp32 output: the router logits in dense mode (mangled: the
+        # output type f, possibly followed by a back-reference, closes the template
+        # arguments; demangled: ", float" among them)
+        if ("IDF16b" in name and re.search(r"f(?:S\d*_)?EEvPKT_", name)) or (
+                "__bf16" in name and re.search(r", float[,>]", name)):
+            return "prefill_gemm_kernel (router logits, dense)"
+        return "prefill_gemm_kernel (" + (
+            "down" if "Lb0E" in name or "false" in name else "gate/up+SwiGLU") + ")"
+    return name.split("(")[0].split("<")[0].replace("void ", "")
+
+
+def summarize_trace(d):
+    """Per (kernel, grid) of a rocprofv3 --kernel-trace run: dispatches and their mean,
+    median, min and max duration.  The grid tells apart layers that launch the same kernel
+    (the Mixtral-8x7B and -8x22B GEMMs share one template instance)."""
+    import csv
+    import glob
+    import statistics as st
+
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    if not rows:
+        raise SystemExit(f"no kernel trace in {d}")
+    per = {}
+    for r in rows:
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
+        wg = int(r.get("Workgroup_Size_X") or r.get("Workgroup_Size") or 1)
+        key = (_short_kernel(r["Kernel_Name"]), grid // max(wg, 1), wg)
+        per.setdefault(key, []).append(ns)
+    out = []
+    for (name, blocks, wg), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        out.append({"kernel": name, "blocks": blocks, "block_threads": wg,
+                    "dispatches": len(v), "mean_us": round(st.mean(v) / 1e3, 1),
+                    "median_us": round(st.median(v) / 1e3, 1),
+                    "min_us": round(min(v) / 1e3, 1), "max_us": round(max(v) / 1e3, 1),
+                    "total_ms": round(sum(v) / 1e6, 3)})
+    return out
 
 
 def traffic_for(workload):
@@ -593,6 +640,9 @@ def main():
     args = parse()
     if args.summarize_counters:
         print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        return
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
         return
     if args.summarize_traffic:
         t = summarize_traffic(*args.summarize_traffic, args.workload)

@@ -130,3 +130,21 @@ def test_rooflines(bench):
     F_alg = 2 * 4096 * 4096 * 8 + 6 * 4096 * 14336 * 8192
     assert bench.layer_roofline_frac(w, 8192, 8, 2.0) == pytest.approx(
         F_alg / 2.5e15 / 2e-3, abs=1e-4)
+
+
+def test_trace_summary_splits_by_grid(bench, tmp_path):
+    # the same GEMM kernel launched with two grids (two layers) is summarised per grid
+    def row(i, name, grid, ns):
+        return {"Dispatch_Id": str(i), "Kernel_Name": name, "Start_Timestamp": "0",
+                "End_Timestamp": str(ns), "Grid_Size_X": str(grid * 512),
+                "Workgroup_Size_X": "512"}
+    _write(tmp_path / "x_kernel_trace.csv",
+           [row(1, GATE_UP, 3136, 1_600_000), row(2, GATE_UP, 3136, 1_700_000),
+            row(3, GATE_UP, 1536, 1_100_000), row(4, DOWN, 448, 800_000)])
+    out = bench.summarize_trace(str(tmp_path))
+    by = {(r["kernel"], r["blocks"]): r for r in out}
+    a = by[("prefill_gemm_kernel (gate/up+SwiGLU)", 3136)]
+    assert a["dispatches"] == 2 and a["mean_us"] == 1650.0 and a["min_us"] == 1600.0
+    assert by[("prefill_gemm_kernel (gate/up+SwiGLU)", 1536)]["mean_us"] == 1100.0
+    assert by[("prefill_gemm_kernel (down)", 448)]["total_ms"] == 0.8
+    assert out[0]["blocks"] == 3136  # ordered by total time
