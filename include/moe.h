@@ -119,7 +119,7 @@ typedef enum {
   MOE_WS_X_PERM,      /* [R, d] */
   MOE_WS_H,           /* [R, F] */
   MOE_WS_Y_PERM,      /* [R, d] */
-  MOE_WS_DOWN_ACC,    /* internal: float [S, R, d] when the down GEMM splits its reduction */
+  MOE_WS_DOWN_ACC,    /* internal: fp32 partial sums of the down GEMM's split tail tiles */
   MOE_WS_COUNT
 } moe_ws_region;
 
@@ -357,11 +357,13 @@ int moe_expert_gate_up_gathered(const moe_shape* shape, const void* x,
  * moe_expert_down -- S7 alone: y_perm[r] = h[r] w_down[e]^T for the rows of each expert
  * (same sources as moe_expert_ffn).  One grouped GEMM launch after a one-block tile-table
  * launch.  For shapes whose down GEMM has few, long tiles (at most m-tiles x ceil(d / 256)
- * of them, fewer than two rounds of the 256 CUs), the GEMM splits its reduction axis into
- * S = 2 to 4 pieces, each storing fp32 partial sums into its own slot of the workspace
- * region MOE_WS_DOWN_ACC, and one more launch adds the slots in slot order and converts
- * the sums to y_perm, so the result does not depend on which piece finished first.  Such
- * shapes get a non-empty MOE_WS_DOWN_ACC (S x R x d floats) from moe_workspace_size.
+ * of them, fewer than two rounds of the 256 CUs), the tiles that fall into the last,
+ * partial round (counted on the device) split their reduction axis into up to 8 pieces,
+ * each storing its tile of fp32 partial sums into a slot of the workspace region
+ * MOE_WS_DOWN_ACC; one more launch adds each tile's slots in piece order and converts the
+ * sums to y_perm, so the result does not depend on which piece finished first.  Such shapes
+ * get a non-empty MOE_WS_DOWN_ACC (at most 256 slots of BM x 256 floats, BM the row-tile
+ * height) from moe_workspace_size.
  *   h      [R, F] dtype in
  *   y_perm [R, d] dtype out (rows >= expert_offsets[E] not written)
  */

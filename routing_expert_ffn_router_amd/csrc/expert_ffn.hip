@@ -469,9 +469,9 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
       }
     }
   };
-  if (!SWIGLU && Cacc) {  // one piece of a split reduction: its fp32 partial sums
+  if (!SWIGLU && Cacc) {  // one piece of a split reduction: its tile of fp32 partial sums
     staged(float(), IntC<16>{}, [&](int row, int col, const lds_char* src) {
-      *reinterpret_cast<f32x4*>(Cacc + (int64_t)row * N_out + col) =
+      *reinterpret_cast<f32x4*>(Cacc + (int64_t)(row - m_begin) * BN + (col - nt * BN)) =
           *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(src);
     });
   } else if constexpr (std::is_same<OutT, float>::value) {  // fp32 output
@@ -513,11 +513,50 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
       bb + SB, bb + (P::kBStages > 2 ? 2 * SB : 0), bb + (P::kBStages > 3 ? 3 * SB : 0));
 }
 
-// One block per (m-tile, n-tile), or per (m-tile, n-tile, piece of the reduction) when the
-// reduction is split into ksplit pieces (then piece p stores its fp32 partial sums into
-// slot p of Cacc, acc_stride floats apart, for rows_from_slots_kernel to add).  Blocks are dealt round-robin to the 8 XCDs; the logical tile
-// index is remapped so each XCD walks a contiguous range of logical tiles, n fastest within
-// groups of group_n n-tiles.  An m-tile with at most PT::BM rows (an expert's last, partly
+// Down GEMM with few, long tiles: the tail split.  The t = m-tiles x n-tiles tiles (m-tiles
+// counted on the device) are numbered densely, n fastest within groups of group_n n-tiles.
+// The first floor(t / cus) * cus tiles run whole; the tail of t mod cus tiles, which would
+// leave most CUs idle through a last partial round, is split along the reduction into
+// S = min(s_max, cus / tail) pieces, each storing its tile of fp32 partial sums in a slot of
+// its own for tail_sum_kernel to add in piece order (deterministic).  S < 2: nothing splits.
+struct TailSplit {
+  int tiles, whole, tail, pieces;
+};
+__device__ inline TailSplit tail_split_of(int m_tiles, int n_tiles, int s_max) {
+  TailSplit p;
+  p.tiles = m_tiles * n_tiles;
+  p.whole = p.tiles / kSplitCUs * kSplitCUs;
+  p.tail = p.tiles - p.whole;
+  p.pieces = p.tail ? min(s_max, kSplitCUs / p.tail) : 1;
+  if (p.pieces < 2) {
+    p.whole = p.tiles;
+    p.tail = 0;
+    p.pieces = 1;
+  }
+  return p;
+}
+// (m-tile, n-tile) of dense tile number i: groups of m_tiles x group_n tiles, n fastest
+// within a group; the last group holds the n_tiles mod group_n remaining n-tiles.
+__device__ inline void dense_tile(int i, int m_tiles, int n_tiles, int group_n, int* mt,
+                                  int* nt) {
+  const int per_group = m_tiles * group_n, full = n_tiles / group_n;
+  if (i < full * per_group) {
+    const int grp = i / per_group, rem = i - grp * per_group;
+    *mt = rem / group_n;
+    *nt = grp * group_n + rem % group_n;
+  } else {
+    const int rem = i - full * per_group, gw = n_tiles - full * group_n;
+    *mt = rem / gw;
+    *nt = full * group_n + rem % gw;
+  }
+}
+
+// One block per (m-tile, n-tile), or, with the tail split, per whole tile or per piece of a
+// tail tile.  Blocks are dealt round-robin to the 8 XCDs; the logical tile index is
+// remapped so each XCD walks a contiguous range of logical tiles, n fastest within
+// groups of group_n n-tiles (with the tail split: XCD x runs its share of the whole tiles
+// first, so the first round holds whole tiles only, then its share of the pieces).
+// An m-tile with at most PT::BM rows (an expert's last, partly
 // filled tile) runs the shorter tile PT with the same weight columns: fewer loads and MFMAs
 // instead of a full tile of mostly clamped rows.  When PW is twice as wide as P, the last
 // tile of an expert with at least two full tiles runs PW over n-tiles nt and nt + 1 in the
@@ -537,8 +576,8 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
                     const float* __restrict__ col_bias, float* __restrict__ Cacc, int K,
                     int N_out, const int32_t* __restrict__ offsets,
                     const int32_t* __restrict__ table, int m_tiles_max, int n_tiles,
-                    int group_n, int grid_logical, int ksplit, int dense_rows,
-                    int stream_b, int64_t acc_stride) {
+                    int group_n, int grid_logical, int tail_split, int dense_rows,
+                    int stream_b) {
   static_assert(PT::BNW == P::BNW && PT::kThreads == P::kThreads && PT::BM <= P::BM,
                 "the shorter tile shares the n-tiling and the block size");
   static_assert((PW::BNW == P::BNW || PW::BNW == 2 * P::BNW) && PW::BM == PT::BM &&
@@ -547,21 +586,40 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
   extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
   // dynamic LDS of the launch (launch_prefill allocates the largest of the three tiles)
   constexpr int kLds = std::max({P::kLdsBytes, PT::kLdsBytes, PW::kLdsBytes});
-  const int bid = blockIdx.x;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   const int per_xcd = gridDim.x >> 3;
-  const int logical_all = (bid & 7) * per_xcd + (bid >> 3);
-  if (logical_all >= grid_logical * ksplit) return;
-  const int piece = logical_all / grid_logical;
-  const int logical = logical_all - piece * grid_logical;
-  // stages [k_first, k_first + k_steps) of the reduction: all of it, or piece `piece` of
-  // ksplit nearly equal pieces, whose fp32 partial sums go to slot `piece` of Cacc
+  // stages [k_first, k_first + k_steps) of the reduction: all of it, or one piece of a tail
+  // tile, whose fp32 partial sums go to its slot of Cacc
   const int KT = K * (int)sizeof(T) / P::kRowBytes;
-  const int k_first = piece * KT / ksplit, k_steps = (piece + 1) * KT / ksplit - k_first;
-  if (Cacc) Cacc += piece * acc_stride;
-  const int per_group = m_tiles_max * group_n;
-  const int grp = logical / per_group, rem = logical - grp * per_group;
-  const int mt = rem / group_n, nt = grp * group_n + (rem - (rem / group_n) * group_n);
-  if (nt >= n_tiles) return;
+  int mt, nt, k_first = 0, k_steps = KT;
+  float* acc = nullptr;
+  if (tail_split > 0) {  // tile-table mode only (launch_prefill refuses other uses)
+    const int m_tiles = table[0];
+    const TailSplit ts = tail_split_of(m_tiles, n_tiles, tail_split);
+    const int w8 = (ts.whole + 7) / 8, q8 = (ts.tail * ts.pieces + 7) / 8;
+    int tile;
+    if (j < w8) {
+      tile = xcd * w8 + j;
+      if (tile >= ts.whole) return;
+    } else {
+      const int q = xcd * q8 + (j - w8);
+      if (j - w8 >= q8 || q >= ts.tail * ts.pieces) return;
+      const int piece = q / ts.tail;
+      tile = ts.whole + (q - piece * ts.tail);
+      k_first = piece * KT / ts.pieces;
+      k_steps = (piece + 1) * KT / ts.pieces - k_first;
+      acc = Cacc + ((int64_t)(tile - ts.whole) * ts.pieces + piece) * (P::BM * P::BNW);
+    }
+    dense_tile(tile, m_tiles, n_tiles, group_n, &mt, &nt);
+  } else {
+    const int logical = xcd * per_xcd + j;
+    if (logical >= grid_logical) return;
+    const int per_group = m_tiles_max * group_n;
+    const int grp = logical / per_group, rem = logical - grp * per_group;
+    mt = rem / group_n;
+    nt = grp * group_n + (rem - (rem / group_n) * group_n);
+    if (nt >= n_tiles) return;
+  }
   int e, m_begin, m_end;
   if (table) {
     if (mt >= table[0]) return;
@@ -577,44 +635,58 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
   lds_char* base = (lds_char*)smem_dyn;
   if (PT::BM < P::BM && m_end - m_begin <= PT::BM) {
     if constexpr (PW::BNW == 2 * P::BNW) {
-      if (table && m_begin - offsets[e] >= 2 * P::BM) {  // at least two full tiles before
+      // at least two full tiles before (not with the tail split, whose pieces each hold
+      // the partial sums of one n-tile)
+      if (table && tail_split == 0 && m_begin - offsets[e] >= 2 * P::BM) {
         if (nt & 1) return;
         prefill_gemm_tile<T, SWIGLU, PW, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C,
-                                               col_bias, Cacc, K, N_out, e, m_begin, m_end,
+                                               col_bias, acc, K, N_out, e, m_begin, m_end,
                                                nt >> 1, k_first, k_steps,
                                                stream_b != 0, base);
         return;
       }
     }
     prefill_gemm_tile<T, SWIGLU, PT, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C, col_bias,
-                                           Cacc, K, N_out, e, m_begin, m_end, nt,
+                                           acc, K, N_out, e, m_begin, m_end, nt,
                                            k_first, k_steps, stream_b != 0, base);
   } else
-    prefill_gemm_tile<T, SWIGLU, P, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C, col_bias, Cacc,
+    prefill_gemm_tile<T, SWIGLU, P, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C, col_bias, acc,
                                           K, N_out, e, m_begin, m_end, nt, k_first,
                                           k_steps, stream_b != 0, base);
 }
 
-// Rows [0, offsets[E]) of a split down GEMM: the sum of its `pieces` fp32 partial-sum slots
-// (slot stride `stride` floats), added in slot order so the result does not depend on which
-// piece finished first, converted to the output type (d is a multiple of 4).
-template <class T>
+// The tail tiles of a tail-split down GEMM: tile i (dense number whole + i) is the sum of
+// its S slots of fp32 partial sums ([BM, BN] each, slot i * S + p), added in piece order so
+// the result does not depend on which piece finished first, converted to the output type
+// and stored into the tile's valid rows and columns.  grid = (kSplitCUs, any): blockIdx.x
+// is the tail tile (surplus blocks exit), blockIdx.y strides over its float4 groups.
+template <class T, int BM, int BN>
 __global__ void __launch_bounds__(256)
-rows_from_slots_kernel(const float* __restrict__ acc, int pieces, int64_t stride,
-                       const int32_t* __restrict__ offsets, int E, int64_t d,
-                       T* __restrict__ y) {
-  const int64_t n = (int64_t)offsets[E] * d / 4;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * 256) {
-    f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(acc) + i);
-    for (int p = 1; p < pieces; ++p) {
-      const f32x4 w =
-          __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(acc + p * stride) + i);
+tail_sum_kernel(const float* __restrict__ acc, const int32_t* __restrict__ offsets,
+                const int32_t* __restrict__ table, int n_tiles, int group_n, int s_max,
+                int N_out, T* __restrict__ y) {
+  const int m_tiles = table[0];
+  const TailSplit ts = tail_split_of(m_tiles, n_tiles, s_max);
+  const int i = blockIdx.x;
+  if (i >= ts.tail) return;
+  int mt, nt;
+  dense_tile(ts.whole + i, m_tiles, n_tiles, group_n, &mt, &nt);
+  const int e = table[1 + 2 * mt], m_begin = table[2 + 2 * mt];
+  const int rows = min(offsets[e + 1] - m_begin, BM), cols = min(BN, N_out - nt * BN);
+  const float* src = acc + (int64_t)i * ts.pieces * (BM * BN);
+  for (int f = blockIdx.y * 256 + threadIdx.x; f < rows * (BN / 4); f += gridDim.y * 256) {
+    const int r = f / (BN / 4), c = (f % (BN / 4)) * 4;
+    if (c >= cols) continue;
+    f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + r * BN + c));
+    for (int p = 1; p < ts.pieces; ++p) {
+      const f32x4 w = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(src + (int64_t)p * (BM * BN) + r * BN + c));
 #pragma unroll
-      for (int c = 0; c < 4; ++c) v[c] += w[c];
+      for (int q = 0; q < 4; ++q) v[q] += w[q];
     }
+    T* dst = y + (int64_t)(m_begin + r) * N_out + nt * BN + c;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) y[4 * i + c] = Elt<T>::from_f32(v[c]);
+    for (int q = 0; q < 4; ++q) dst[q] = Elt<T>::from_f32(v[q]);
   }
 }
 
@@ -658,50 +730,66 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad
   const int64_t m_cap = E * ((C + p.bm - 1) / p.bm);
   p.m_max = m_cap < m_max ? m_cap : m_max;
   if (p.m_max < 0) p.m_max = 0;
-  // Down GEMM with few, long tiles: when the tile count t (at most m_max x ceil(d / 256))
-  // fills fewer than two rounds of the 256 CUs, much of the chip idles through the last
-  // one.  Split the reduction into S pieces, S aiming at about four rounds of pieces, at
-  // most 4 and at least 16 128-byte stages each, when that fills the rounds clearly better
-  // (in whole-tile time, rounds(S t) / S <= 0.85 rounds(t)) and the tiles are prefill
-  // tiles.  Each piece writes fp32 partial sums of its own, so S costs S x N x d x 4 bytes
-  // of stores and reads: measured on Mixtral-8x22B (t <= 384), three pieces -3.3 % on the
-  // layer against two -1.2 % and four -1.4 %.
+  // Down GEMM with few, long tiles: when the tile count (at most m_max x ceil(d / 256))
+  // is below two rounds of the 256 CUs, the last, partial round would leave most of the
+  // chip idle for a whole tile time.  The GEMM then runs the tail split (tail_split_of):
+  // the tiles of the last partial round, counted on the device, are split along the
+  // reduction into up to down_split pieces (at most 8, at least 16 128-byte stages each)
+  // whose fp32 partial sums another launch adds in piece order.  Only those tiles pay for
+  // partial sums (at most 256 pieces of BM x 256 floats); the whole tiles store their
+  // outputs directly.  This replaced a split of every tile into three pieces on the
+  // Mixtral-8x22B layer (288 tiles: 256 whole, 32 in eight pieces).
   p.down_split = 1;
-  const int64_t tiles = p.m_max * ((d + 255) / 256), stages = F * elt / 128, cus = 256;
-  const auto rounds = [&](int64_t t) { return (t + cus - 1) / cus; };
-  if (!p.small && tiles > 0 && tiles < 2 * cus) {
-    const int64_t split = std::min<int64_t>({(4 * cus + tiles - 1) / tiles, 4, stages / 16});
-    if (split >= 2 && 100 * rounds(split * tiles) <= 85 * split * rounds(tiles))
+  p.down_pieces_max = 0;
+  const int64_t tiles = p.m_max * ((d + 255) / 256), stages = F * elt / 128;
+  if (!p.small && tiles > 0 && tiles < 2 * kSplitCUs) {
+    const int64_t split = std::min<int64_t>(8, stages / 16);
+    if (split >= 2) {
       p.down_split = (int)split;
+      p.down_pieces_max = std::min<int64_t>(kSplitCUs, tiles * split);
+    }
   }
   return p;
 }
 
 namespace {
 
+// tail_split > 0 (tile-table mode, no SwiGLU): the tail split with at most tail_split pieces
+// per tail tile, partial sums in c_acc, then tail_sum_kernel.
 template <class T, bool SW, class P = PrefillTile, class PT = PrefillTailTile, class OutT = T,
           class PW = PT>
 hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const T* B1,
                           int64_t b_stride, OutT* C, int K, int N_out, const int32_t* offsets,
-                          const int32_t* table, int64_t m_max, hipStream_t s,
-                          int ksplit = 1, float* c_acc = nullptr,
-                          const float* col_bias = nullptr, int dense_rows = 0,
-                          bool stream_b = false, int group_cap = 8, int64_t acc_stride = 0) {
+                          const int32_t* table, int64_t m_max, hipStream_t s, int tail_split,
+                          float* c_acc, const float* col_bias, int dense_rows, bool stream_b,
+                          int group_cap) {
   if (m_max <= 0) return hipSuccess;
+  // the tail split runs over a tile table, without SwiGLU, into a partial-sum buffer
+  if (tail_split > 0 && (SW || !table || !c_acc || !std::is_same<OutT, T>::value))
+    return hipErrorInvalidValue;
   constexpr int BN = SW ? P::BNW / 2 : P::BNW;
   const int n_tiles = (N_out + BN - 1) / BN;
   const int group_n = n_tiles < group_cap ? n_tiles : group_cap;
   const int n_groups = (n_tiles + group_n - 1) / group_n;
   const int64_t logical = m_max * group_n * n_groups;
-  const int64_t grid = (logical * ksplit + 7) / 8 * 8;
+  // with the tail split, each XCD's share of the whole tiles (at most m_max x n_tiles of
+  // them) and of the pieces (at most kSplitCUs)
+  const int64_t grid = tail_split > 0 ? 8 * ((m_max * n_tiles + 7) / 8 + kSplitCUs / 8)
+                                      : (logical + 7) / 8 * 8;
   const size_t lds = (size_t)std::max({P::kLdsBytes, PT::kLdsBytes, PW::kLdsBytes});
   hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW, P, PT, OutT, PW>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   prefill_gemm_kernel<T, SW, P, PT, OutT, PW><<<(unsigned)grid, P::kThreads, lds, s>>>(
       A, a_rows, B0, B1, b_stride, C, col_bias, c_acc, K, N_out, offsets, table, (int)m_max,
-      n_tiles, group_n, (int)logical, ksplit, dense_rows, stream_b ? 1 : 0, acc_stride);
-  return hipGetLastError();
+      n_tiles, group_n, (int)logical, tail_split, dense_rows, stream_b ? 1 : 0);
+  if ((e = hipGetLastError()) != hipSuccess || tail_split == 0) return e;
+  if constexpr (!SW && std::is_same<OutT, T>::value) {
+    tail_sum_kernel<T, P::BM, P::BNW><<<dim3(kSplitCUs, 8), 256, 0, s>>>(
+        c_acc, offsets, table, n_tiles, group_n, tail_split, N_out, C);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_table(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
@@ -719,17 +807,18 @@ hipError_t run_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   const int64_t stride = a.F * a.d;
   const T* wg = (const T*)a.w_gate;
   const T* wu = (const T*)a.w_up;
+  // no tail split (0), no partial sums, no column bias, tile-table mode (0 dense rows)
   if (p.small)
     return launch_prefill<T, true, DecodeDmaTile, DecodeDmaTile>(
-        xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s, 1,
+        xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s, 0,
         nullptr, nullptr, 0, p.stream_b, p.group_cap);
   if (p.tile == 2)
     return launch_prefill<T, true, PrefillTallTile, PrefillTailTile, T, PrefillTailWideTile>(
-        xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s, 1,
+        xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s, 0,
         nullptr, nullptr, 0, p.stream_b, p.group_cap);
-  return launch_prefill<T, true>(
-      xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s, 1,
-      nullptr, nullptr, 0, p.stream_b, p.group_cap);
+  return launch_prefill<T, true>(xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets,
+                                 a.sched, p.m_max, s, 0, nullptr, nullptr, 0, p.stream_b,
+                                 p.group_cap);
 }
 
 template <class T>
@@ -740,27 +829,17 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
   if (p.small)
     return launch_prefill<T, false, DecodeDownTile, DecodeDownTile>(
         h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F, (int)a.d, a.offsets,
-        a.sched, p.m_max, s, 1, nullptr, nullptr, 0, p.stream_b, p.group_cap);
-  // split reduction: each piece stores the fp32 partial sums of its rows into a slot of
-  // a.down_acc ([pieces, R, d]); a second launch adds the slots in order and converts
-  const int ks = p.down_split;
-  float* acc = ks > 1 ? a.down_acc : nullptr;
-  const int64_t slot = a.R * a.d;
-  const hipError_t e =
-      p.tile == 2
-          ? launch_prefill<T, false, PrefillTallTile, PrefillTailTile, T, PrefillTailWideTile>(
-                h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F, (int)a.d,
-                a.offsets, a.sched, p.m_max, s, ks, acc, nullptr, 0, p.stream_b, p.group_cap,
-                slot)
-          : launch_prefill<T, false>(
-                h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F, (int)a.d,
-                a.offsets, a.sched, p.m_max, s, ks, acc, nullptr, 0, p.stream_b, p.group_cap,
-                slot);
-  if (e != hipSuccess || ks == 1) return e;
-  const unsigned ew_blocks = (unsigned)std::min<int64_t>((a.R * a.d / 4 + 255) / 256, 4096);
-  rows_from_slots_kernel<T><<<ew_blocks, 256, 0, s>>>(acc, ks, slot, a.offsets, (int)a.E, a.d,
-                                                      y);
-  return hipGetLastError();
+        a.sched, p.m_max, s, 0, nullptr, nullptr, 0, p.stream_b, p.group_cap);
+  // tail split: the tiles of the last partial round run in pieces (see ffn_plan)
+  const int ts = p.down_split > 1 ? p.down_split : 0;
+  float* acc = ts ? a.down_acc : nullptr;
+  if (p.tile == 2)
+    return launch_prefill<T, false, PrefillTallTile, PrefillTailTile, T, PrefillTailWideTile>(
+        h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F, (int)a.d, a.offsets,
+        a.sched, p.m_max, s, ts, acc, nullptr, 0, p.stream_b, p.group_cap);
+  return launch_prefill<T, false>(h, nullptr, (const T*)a.w_down, nullptr, stride, y, (int)a.F,
+                                  (int)a.d, a.offsets, a.sched, p.m_max, s, ts, acc, nullptr, 0,
+                                  p.stream_b, p.group_cap);
 }
 
 }  // namespace
@@ -777,13 +856,14 @@ bool router_gemm_suits(int64_t T, int64_t E) {
 hipError_t launch_router_gemm(int dtype, const void* x, const void* w, const float* b,
                               float* logits, int64_t T, int64_t d, int64_t E, hipStream_t s) {
   const int64_t m_tiles = (T + RouterTile::BM - 1) / RouterTile::BM;
+  // dense mode: no tile table, no tail split, the bias in the epilogue, n-groups of 8
   if (dtype == 1)
     return launch_prefill<bf16, false, RouterTile, RouterTile, float>(
         (const bf16*)x, nullptr, (const bf16*)w, nullptr, 0, logits, (int)d, (int)E, nullptr,
-        nullptr, m_tiles, s, 1, nullptr, b, (int)T);
+        nullptr, m_tiles, s, 0, nullptr, b, (int)T, false, 8);
   return launch_prefill<float, false, RouterTile, RouterTile, float>(
       (const float*)x, nullptr, (const float*)w, nullptr, 0, logits, (int)d, (int)E, nullptr,
-      nullptr, m_tiles, s, 1, nullptr, b, (int)T);
+      nullptr, m_tiles, s, 0, nullptr, b, (int)T, false, 8);
 }
 
 hipError_t launch_expert_ffn(const FfnArgs& a, int which, hipStream_t s) {

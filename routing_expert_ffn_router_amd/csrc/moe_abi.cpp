@@ -88,7 +88,7 @@ Layout make_layout(const moe_shape* s) {
   L.size[MOE_WS_X_PERM] = R * s->d * b;
   L.size[MOE_WS_H] = R * s->F * b;
   L.size[MOE_WS_Y_PERM] = R * s->d * b;
-  L.size[MOE_WS_DOWN_ACC] = moe::ffn_down_acc_bytes(plan, R, s->d);
+  L.size[MOE_WS_DOWN_ACC] = moe::ffn_down_acc_bytes(plan);
   int64_t o = 0;
   for (int i = 0; i < MOE_WS_COUNT; ++i) {
     L.off[i] = o;

@@ -66,14 +66,15 @@ def _down_acc_bytes(s):
 
 
 def test_down_split_region():
-    # The down GEMM splits its reduction into S pieces when t = m-tiles (upper bound) x
-    # ceil(d / 256) is below two rounds of 256 CUs: S = min(ceil(1024 / t), 4, stages / 16)
-    # with stages = F * elt / 128, kept when S >= 2 and ceil(S t / 256) / S <= 0.85
-    # ceil(t / 256).  The workspace then ends with fp32 [S, R, d] partial sums.
-    # Mixtral-8x22B-shaped, C = 640: t <= 16 x 24 = 384, S = 3: 5 rounds of thirds (1.67)
-    # against 2 whole -> splits in three.
+    # Tail split of the down GEMM: when t = m-tiles (upper bound) x ceil(d / 256) is below
+    # two rounds of 256 CUs, the tiles of the last partial round (counted on the device)
+    # split their reduction into up to S = min(8, stages / 16) pieces, stages = F * elt /
+    # 128, S >= 2.  The workspace then ends with min(256, t * S) slots of BM x 256 fp32
+    # partial sums (BM = 320 or 256, the plan's row tile).
+    # Mixtral-8x22B-shaped, C = 640, 320-row tiles: t <= 16 x 24 = 384, 256 stages -> S = 8,
+    # 256 slots
     s = moe.shape(2048, 6144, 8, 2, 16384, 640)
-    assert _down_acc_bytes(s) == 3 * 4096 * 6144 * 4
+    assert _down_acc_bytes(s) == 256 * 320 * 256 * 4
     # Mixtral-8x7B-shaped: t <= 32 x 16 = 512 = 2 rounds -> no split
     assert _down_acc_bytes(moe.shape(4096, 4096, 8, 2, 14336, 1280)) == 0
     # decode-sized experts stream weights: never split
@@ -81,12 +82,14 @@ def test_down_split_region():
     # DeepSeek-V3 mixed batch: t = 256 x 28 = 28 rounds -> no split
     assert _down_acc_bytes(moe.shape(8192, 7168, 256, 8, 2048, 256)) == 0
     # a short reduction (F * 2 / 128 = 6 stages) does not split; 32 stages allow two
-    # pieces, 64 stages four (t = 8 m-tiles x 1)
+    # pieces, 64 stages four (t <= 8 m-tiles of 256 rows x 1)
     assert _down_acc_bytes(moe.shape(700, 256, 8, 2, 384, 219)) == 0
-    assert _down_acc_bytes(moe.shape(700, 256, 8, 2, 2048, 219)) == 2 * 1400 * 256 * 4
-    assert _down_acc_bytes(moe.shape(700, 256, 8, 2, 4096, 219)) == 4 * 1400 * 256 * 4
-    # fp32: 4-byte elements, F = 1024 is 32 stages (two pieces); F = 896 is 28 -> none
-    assert _down_acc_bytes(moe.shape(600, 256, 4, 2, 1024, 300, moe.MOE_F32)) == 2 * 1200 * 256 * 4
+    assert _down_acc_bytes(moe.shape(700, 256, 8, 2, 2048, 219)) == 8 * 2 * 256 * 256 * 4
+    assert _down_acc_bytes(moe.shape(700, 256, 8, 2, 4096, 219)) == 8 * 4 * 256 * 256 * 4
+    # fp32: 4-byte elements, F = 1024 is 32 stages (two pieces of t <= 4 tiles of 320 rows);
+    # F = 896 is 28 -> none
+    assert _down_acc_bytes(moe.shape(600, 256, 4, 2, 1024, 300, moe.MOE_F32)) == \
+        4 * 2 * 320 * 256 * 4
     assert _down_acc_bytes(moe.shape(600, 256, 4, 2, 896, 300, moe.MOE_F32)) == 0
 
 
@@ -404,7 +407,7 @@ def test_workspace_phases_follow_the_layout(sh):
     assert exp <= grown <= exp + internal["sched"] + internal["down_acc"]
     assert ph["after_experts"] <= total
     if sh.E == 8 and sh.T == 2048:  # the split down GEMM's fp32 slots are counted
-        assert grown >= exp + 3 * R * sh.d * 4
+        assert grown >= exp + 256 * 320 * 256 * 4
 
 
 def test_no_workspace_dispatch_checks_before_any_launch():
