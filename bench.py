@@ -223,6 +223,10 @@ def _short_kernel(name):
             return "prefill_gemm_kernel (router logits, dense)"
         return "prefill_gemm_kernel (" + (
             "down" if "Lb0E" in name or "false" in name else "gate/up+SwiGLU") + ")"
+    m = re.match(r"_ZN(\d+)moe(\d+)", name)  # mangled moe::<name><template args>
+    if m:
+        start = m.end()
+        return "moe::" + name[start:start + int(m.group(2))]
     return name.split("(")[0].split("<")[0].replace("void ", "")
 
 
