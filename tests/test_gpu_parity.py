@@ -576,3 +576,27 @@ def test_layers_on_two_streams_match_one_stream():
             assert torch.equal(lay.routed_counts, ref.routed_counts)
             assert torch.equal(lay.drops, ref.drops)
             assert torch.equal(lay.view("dest_row"), ref.view("dest_row"))
+
+
+def test_route_given_logits_past_2_31_lanes():
+    # The top-k kernel gives each token a group of G lanes (G = 64 for E >= 64): with
+    # T = 2^25 + 1000 tokens, T * G passes 2^31, which 32-bit lane indices would wrap.
+    # Tokens at both ends (and across the 2^31 boundary) must get the oracle's selection.
+    T, E, k = (1 << 25) + 1000, 64, 1
+    g = torch.Generator(device="cuda").manual_seed(11)
+    logits = torch.randn((T, E), generator=g, device="cuda", dtype=torch.float32)
+    s = moe.shape(T, 128, E, k, 128, 0, moe.MOE_F32)
+    idx = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    status = _i32(1)
+    moe.route(s, None, None, None, logits, idx, w, status, logits_given=True)
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    assert int((idx < 0).sum()) == 0  # every token written
+    for t0 in (0, (1 << 25) - 500, T - 600):
+        rows = slice(t0, t0 + 600)
+        L = logits[rows].cpu().numpy()
+        assert np.array_equal(idx[rows].cpu().numpy(), oracle.select_topk(L, k))
+        assert np.all(w[rows].cpu().numpy() == 1.0)  # k = 1: the gate is exactly 1
+    del logits
+    torch.cuda.empty_cache()
