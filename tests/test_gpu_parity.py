@@ -600,3 +600,43 @@ def test_route_given_logits_past_2_31_lanes():
         assert np.all(w[rows].cpu().numpy() == 1.0)  # k = 1: the gate is exactly 1
     del logits
     torch.cuda.empty_cache()
+
+
+def test_down_tail_split_whole_and_pieces():
+    # A down GEMM with whole tiles and a split tail at a size the oracle runs in seconds:
+    # T = 4096, k = 1, E = 8, no capacity limit plans 320-row tiles with at most 20 m-tiles
+    # x 16 n-tiles (d = 4096) < two rounds, so the tail split is on (F = 2048: 32 stages,
+    # two pieces).  The expert offsets are chosen so the table holds 20 m-tiles: 7 experts
+    # of 330 rows (a full tile and a 10-row tail each) and one of 1786 (five full tiles and
+    # a 186-row one): 320 tiles, 256 whole and 64 in two pieces each.  Outputs against the
+    # oracle, and two runs bit for bit (the second from a NaN-filled workspace).
+    T, d, E, k, F = 4096, 4096, 8, 1, 2048
+    s = moe.shape(T, d, E, k, F, 0, moe.MOE_BF16)
+    lay = moe.workspace_layout(s)
+    assert moe.workspace_size(s) - lay["down_acc"] >= 128 * 320 * 256 * 4
+    counts = np.array([330] * 7 + [T - 7 * 330])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    tiles = sum(-(-int(c) // 320) for c in counts)
+    assert tiles == 20 and tiles * (d // 256) == 320
+    rng = np.random.default_rng(77)
+    bf = lambda a: mi.bf16_bits_to_f32(mi.bf16_rne_np(a.astype(np.float32)))  # noqa: E731
+    xp = bf(rng.standard_normal((T, d)))
+    wg = bf(rng.standard_normal((E, F, d)) / np.sqrt(d))
+    wu = bf(rng.standard_normal((E, F, d)) / np.sqrt(d))
+    wd = bf(rng.standard_normal((E, d, F)) / np.sqrt(d))
+    args = (to_device(xp, torch.bfloat16), to_device(offsets, torch.int32),
+            to_device(wg, torch.bfloat16), to_device(wu, torch.bfloat16),
+            to_device(wd, torch.bfloat16))
+    ws = torch.empty(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
+    ys = []
+    for fill in (0, 255):
+        ws.fill_(fill)
+        y = torch.zeros((T, d), dtype=torch.bfloat16, device="cuda")
+        moe.expert_ffn(s, *args, ws, y)
+        torch.cuda.synchronize()
+        ys.append(y)
+    assert torch.equal(ys[0], ys[1])
+    ref = oracle.expert_ffn(xp, offsets, wg, wu, wd)
+    err = rel_err(to_host(ys[0]), ref)
+    log(f"  down tail split (256 whole + 64 x 2 pieces): rel err {err:.3e}")
+    assert err <= OUT_TOL
