@@ -636,6 +636,48 @@ def cf_sweep(moe, w, args_l, factors, K, W, dtype) -> list:
     return rows
 
 
+def vendor_reference(w, N, reps=10) -> dict:
+    """Reference points on the same box, outside the layer: hipBLASLt (through torch.matmul,
+    plain 2-D products of contiguous bf16 operands) on the dense equivalents of the two
+    grouped GEMMs (all N kept rows against one expert-sized weight, an easier shape than
+    the grouped one), and a 1 GiB device-to-device copy as the attainable HBM rate."""
+    import torch
+
+    out = {}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    g = torch.Generator(device="cuda").manual_seed(5)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    for name, (m, kk, n) in (("gate_up", (N, w.d, 2 * w.F)), ("down", (N, w.F, w.d))):
+        a = torch.randn((m, kk), generator=g, device="cuda").to(dt)
+        b = (torch.randn((kk, n), generator=g, device="cuda") / math.sqrt(kk)).to(dt)
+        ms = timed(lambda: torch.matmul(a, b))
+        tf = 2.0 * m * kk * n / (ms * 1e-3) / 1e12
+        out[f"dense_{name}"] = {"shape_mkn": [m, kk, n], "ms": round(ms, 4),
+                                "tflops": round(tf, 1), "frac": round(tf / peak, 4)}
+        del a, b
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src))
+    out["copy_1gib"] = {"ms": round(ms, 4), "gbs": round(2.0 * (1 << 30) / (ms * 1e-3) / 1e9, 1),
+                        "frac_of_8tbs": round(2.0 * (1 << 30) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 OTHER_WORKLOADS = ["tiny_f32", "mixtral_8x22b_zipf", "dsv3_decode", "dsv3_mixed"]
 SWEEP_WORKLOAD, SWEEP_FACTORS = "mixtral_8x22b_zipf", (1.0, 1.25, 1.5, 2.0, None)
 
@@ -732,6 +774,10 @@ def main():
         result["cf_sweep"] = sweep
     default_run = not (flags or G > 1 or args.graph or args.capacity_factor is not None or
                        args.cf_sweep or args.workload != DEFAULT_WORKLOAD)
+    if default_run:
+        print("# vendor reference: hipBLASLt dense GEMMs, device copy", file=sys.stderr,
+              flush=True)
+        result["vendor_reference"] = vendor_reference(w, m["expert_stats"]["kept_rows"])
     if default_run and not args.no_other_workloads:
         # every other workload, timed the same way (fewer steps), and the capacity-factor
         # sweep of the skewed Mixtral-8x22B layer; reported beside the headline, not in it
