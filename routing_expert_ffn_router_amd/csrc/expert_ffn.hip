@@ -35,9 +35,9 @@
 //     The n-group width comes from the launch plan.
 //   - Weights that each tile reads alone (at most two row tiles per expert) are loaded with
 //     the non-temporal hint, so they do not displace the shared activation rows.
-//   - A down GEMM with few, long tiles splits its reduction into 2-4 pieces whose fp32
-//     partial sums a second launch adds in a fixed order (deterministic), so the last round
-//     of tiles does not leave most CUs idle.
+//   - A down GEMM with few, long tiles runs the tiles of its last, partial round in up to 8
+//     pieces along the reduction, whose fp32 partial sums a second launch adds in a fixed
+//     order (deterministic), so that round does not leave most CUs idle (tail split).
 //   - Dense mode (no tile table, fp32 output with a column bias) serves the router logits
 //     of shapes with many tokens and experts.
 #include <algorithm>
