@@ -13,7 +13,11 @@ it yields the per-stage timing record (router / pack / expert compute / unpack, 
 airouter.kz, "Expert parallelism in MoE needs measurements before launch", section
 "All-to-all must be profiled separately from compute") and the duration of the dominant
 kernel, from which the roofline fraction is computed.  The CPU oracle, timed on a bounded
-sample of the same workload, is reported as a baseline.
+sample of the same workload, is reported as a baseline.  The default run also times the other
+workloads, sweeps the capacity factor of the skewed Mixtral-8x22B layer, and reports reference
+points measured on the same GPU outside the timed region: hipBLASLt on the dense equivalents
+of the two GEMMs, a device copy, and the bf16 MFMA rate and clock the chip sustains
+(--mfma-ceiling).
 """
 from __future__ import annotations
 
@@ -67,6 +71,10 @@ def parse():
     p.add_argument("--ranks-per-node", type=int, default=8)
     p.add_argument("--graph", action="store_true",
                    help="time replays of a HIP graph that captured one moe_layer call")
+    p.add_argument("--mfma-ceiling", nargs="?", const="both", default=None,
+                   choices=["both", "random", "zero"],
+                   help="only measure the sustained bf16 MFMA rate and clock (libmoe_calib.so) "
+                        "on random and/or all-zero operands")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a device copy of known size (for rocprofv3 --pmc scaling)")
     p.add_argument("--summarize-counters", metavar="PMC_DIR",
@@ -227,6 +235,8 @@ def _short_kernel(name):
     if m:
         start = m.end()
         return "moe::" + name[start:start + int(m.group(2))]
+    if "mfma_rate_kernel" in name:  # the calibration loop (libmoe_calib.so)
+        return "mfma_rate_kernel (calibration)"
     return name.split("(")[0].split("<")[0].replace("void ", "")
 
 
@@ -678,6 +688,46 @@ def vendor_reference(w, N, reps=10) -> dict:
     return out
 
 
+def mfma_ceiling(moe, iters=300_000, reps=5, operands=("random", "zero")) -> dict:
+    """The bf16 MFMA rate this GPU sustains with every SIMD of every CU issuing nothing but
+    independent 32x32x16 MFMAs on register operands (libmoe_calib.so), and the shader clock
+    it holds meanwhile (cycle counter over the constant-rate wall clock), for random operands
+    (the data statistics of the layer) and for all-zero operands.  The published peak assumes
+    the full clock; under this load the power limit sets the clock, so the random-operand
+    rate is the ceiling an MFMA-bound kernel can approach."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus * 8, dtype=torch.float32, device="cuda")
+    cyc = torch.zeros(2 * cus, dtype=torch.int64, device="cuda")
+    khz = moe.calib_wall_clock_khz()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    flops = cus * 8 * iters * 4 * 32768
+    out = {"cus": cus, "iters": iters, "flops_per_launch": flops}
+    for label, rnd in (("random_bf16", True), ("zero_operands", False)):
+        if ("random" if rnd else "zero") not in operands:
+            continue
+        for r in range(2):  # warm-up: the clock settles under the load
+            moe.calib_mfma(cus, iters, 977 + r, rnd, sink, cyc)
+        torch.cuda.synchronize()
+        ms, ghz = [], []
+        for r in range(reps):
+            ev[0].record()
+            moe.calib_mfma(cus, iters, 1000 + r, rnd, sink, cyc)
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]))
+            c = cyc.view(cus, 2).sum(dim=0).tolist()
+            ghz.append(c[0] / c[1] * khz * 1e3 / 1e9 if c[1] > 0 else float("nan"))
+        assert bool(torch.isfinite(sink).all()), "calibration accumulators not finite"
+        t = statistics.median(ms)
+        tf = flops / (t * 1e-3) / 1e12
+        out[label] = {"ms": round(t, 3), "tflops": round(tf, 1),
+                      "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "clock_ghz": round(statistics.median(ghz), 3)}
+    return out
+
+
 OTHER_WORKLOADS = ["tiny_f32", "mixtral_8x22b_zipf", "dsv3_decode", "dsv3_mixed"]
 SWEEP_WORKLOAD, SWEEP_FACTORS = "mixtral_8x22b_zipf", (1.0, 1.25, 1.5, 2.0, None)
 
@@ -708,6 +758,11 @@ def main():
     import routing_expert_ffn_router_amd as moe
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.mfma_ceiling:  # the calibration alone (for a counter run of it)
+        ops = {"both": ("random", "zero"), "random": ("random",), "zero": ("zero",)}
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(moe, operands=ops[args.mfma_ceiling])}),
+              flush=True)
+        return
     w = mi.WORKLOADS[args.workload]
     cf = w.capacity_factor if args.capacity_factor is None else (
         None if args.capacity_factor <= 0 else args.capacity_factor)
@@ -801,6 +856,18 @@ def main():
             del al
             torch.cuda.empty_cache()
         result["workloads"] = others
+    if default_run:
+        print("# bf16 MFMA ceiling: register-operand MFMA loop on every SIMD", file=sys.stderr,
+              flush=True)
+        ceil = mfma_ceiling(moe)
+        result["mfma_ceiling"] = ceil
+        # the MFMA-bound GEMMs against the rate the chip sustains under the power limit
+        top = ceil["random_bf16"]["tflops"]
+        for roof in [result["roofline"]] + [v["roofline"] for v in
+                                            result.get("workloads", {}).values()]:
+            if roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and roof["peak"] == \
+                    PEAK_BF16_TFLOPS:
+                roof["frac_of_mfma_ceiling"] = round(roof["achieved"] / top, 4)
     if not args.no_cpu_baseline and not (flags or G > 1):
         ntok = args.cpu_tokens or CPU_SAMPLE_TOKENS.get(w.name, 256)
         print(f"# cpu baseline: oracle on {ntok} tokens", file=sys.stderr, flush=True)

@@ -435,3 +435,38 @@ class MoELayer:
         yield "down"
         combine(s, v("y_perm"), v("dest_row"), v("topk_w"), self.out, stream=stream)
         yield "combine"
+
+
+# ------------------------------------------------------------------------------ calibration
+CALIB_PATH = os.path.join(_PKG, "libmoe_calib.so")
+_calib = None
+
+
+def load_calib() -> ctypes.CDLL:
+    """Load libmoe_calib.so (include/moe_calib.h): the MFMA-rate calibration that the
+    measurement harness reports beside the published peak.  Not part of the layer."""
+    global _calib
+    if _calib is None:
+        load_library()  # the staleness check covers both libraries; binds torch's runtime
+        lib = ctypes.CDLL(CALIB_PATH)
+        lib.moe_calib_mfma.restype = ctypes.c_int
+        lib.moe_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_int,
+                                       _P, _P, _P]
+        lib.moe_calib_wall_clock_khz.restype = ctypes.c_int
+        lib.moe_calib_wall_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int)]
+        _calib = lib
+    return _calib
+
+
+def calib_mfma(blocks: int, iters: int, seed: int, random_operands: bool, sink, cycles,
+               stream=None) -> None:
+    """Enqueue moe_calib_mfma: sink float32[blocks * 8], cycles int64[2 * blocks] on the GPU."""
+    _check("moe_calib_mfma", load_calib().moe_calib_mfma(
+        int(blocks), int(iters), int(seed) & 0xFFFFFFFF, int(bool(random_operands)),
+        _ptr(sink), _ptr(cycles), _stream(stream)))
+
+
+def calib_wall_clock_khz() -> int:
+    khz = ctypes.c_int(0)
+    _check("moe_calib_wall_clock_khz", load_calib().moe_calib_wall_clock_khz(ctypes.byref(khz)))
+    return int(khz.value)

@@ -21,6 +21,9 @@ STAMP = os.path.join(OBJ, "libmoe.sha256")
 
 SOURCES = ["route.hip", "dispatch.hip", "expert_ffn.hip", "combine.hip", "noalloc.hip",
            "moe_abi.cpp", "stats.cpp"]
+# the MFMA-rate calibration for the measurement harness, in a library of its own
+CALIB_SOURCES = ["calib.hip"]
+CALIB_LIB = os.path.join(PKG, "libmoe_calib.so")
 
 HIPCC = os.environ.get("HIPCC", "hipcc")
 FLAGS = [
@@ -46,8 +49,9 @@ def source_hash() -> str:
     flags."""
     # flags with the repository's location taken out, so a copy elsewhere hashes the same
     h = hashlib.sha256(" ".join(f.replace(ROOT, "") for f in FLAGS).encode())
-    files = ([os.path.join(CSRC, f) for f in SOURCES] +
-             sorted(glob.glob(os.path.join(CSRC, "*.h"))) + [os.path.join(ROOT, "include", "moe.h")])
+    files = ([os.path.join(CSRC, f) for f in SOURCES + CALIB_SOURCES] +
+             sorted(glob.glob(os.path.join(CSRC, "*.h"))) +
+             [os.path.join(ROOT, "include", h) for h in ("moe.h", "moe_calib.h")])
     for f in files:
         if os.path.isfile(f):
             h.update(os.path.basename(f).encode())
@@ -66,8 +70,8 @@ def built_hash() -> str:
 
 
 def is_current() -> bool:
-    """libmoe.so exists and was built from the sources as they are now."""
-    return os.path.exists(LIB) and built_hash() == source_hash()
+    """libmoe.so and libmoe_calib.so exist and were built from the sources as they are now."""
+    return os.path.exists(LIB) and os.path.exists(CALIB_LIB) and built_hash() == source_hash()
 
 
 def _compile(src: str, sanitize: bool = False) -> str:
@@ -82,20 +86,26 @@ def _compile(src: str, sanitize: bool = False) -> str:
     return obj
 
 
-def build(verbose: bool = False, sanitize: bool = False) -> str:
-    """Compile and link libmoe.so (or, with sanitize, the host-sanitized copy in _build/)."""
-    os.makedirs(os.path.join(OBJ, "sanitized") if sanitize else OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
-    lib = LIB_SANITIZED if sanitize else LIB
+def _link(lib: str, objs: list, extra: list) -> None:
     tmp = lib + ".tmp"
-    extra = SANITIZE if sanitize else []
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile and link libmoe.so and libmoe_calib.so (or, with sanitize, the host-sanitized
+    copy of libmoe.so in _build/)."""
+    os.makedirs(os.path.join(OBJ, "sanitized") if sanitize else OBJ, exist_ok=True)
+    srcs = SOURCES if sanitize else SOURCES + CALIB_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda src: _compile(src, sanitize), srcs))
+    lib = LIB_SANITIZED if sanitize else LIB
+    _link(lib, objs[:len(SOURCES)], SANITIZE if sanitize else [])
     if not sanitize:
+        _link(CALIB_LIB, objs[len(SOURCES):], [])
         with open(STAMP, "w") as fh:
             fh.write(source_hash() + "\n")
     if verbose:

@@ -19,6 +19,24 @@ def test_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_calib_library_exports_its_header():
+    # the MFMA-rate calibration of the measurement harness lives in libmoe_calib.so
+    import os
+
+    calib = moe.load_calib()
+    names = moe.header_functions(os.path.join(os.path.dirname(moe.HEADER_PATH),
+                                              "moe_calib.h"))
+    assert names == ["moe_calib_mfma", "moe_calib_wall_clock_khz"]
+    for n in names:
+        assert hasattr(calib, n), n
+    # invalid arguments are refused before any HIP call
+    sink = ctypes.c_void_p(16)
+    for blocks, iters, operands in [(0, 1, 1), (1, 0, 1), (1, 1, 2), (-1, 5, 0)]:
+        assert calib.moe_calib_mfma(blocks, iters, 0, operands, sink, sink, None) == -1
+    assert calib.moe_calib_mfma(1, 1, 0, 1, None, sink, None) == -1
+    assert calib.moe_calib_wall_clock_khz(None) == -1
+
+
 def test_header_cites_the_pages():
     text = " ".join(open(moe.HEADER_PATH).read().replace("*", " ").split())
     for section in ("Deep dive", "Technical details", "Capacity factor changes quality",

@@ -148,3 +148,13 @@ def test_trace_summary_splits_by_grid(bench, tmp_path):
     assert by[("prefill_gemm_kernel (gate/up+SwiGLU)", 1536)]["mean_us"] == 1100.0
     assert by[("prefill_gemm_kernel (down)", 448)]["total_ms"] == 0.8
     assert out[0]["blocks"] == 3136  # ordered by total time
+
+
+def test_kernel_names(bench):
+    assert bench._short_kernel(GATE_UP) == "prefill_gemm_kernel (gate/up+SwiGLU)"
+    assert bench._short_kernel(DOWN) == "prefill_gemm_kernel (down)"
+    assert bench._short_kernel(ROUTER) == "prefill_gemm_kernel (router logits, dense)"
+    assert bench._short_kernel("_ZN3moe14combine_kernelIDF16bEEvPKT_") == "moe::combine_kernel"
+    assert (bench._short_kernel("_ZN12_GLOBAL__N_116mfma_rate_kernelEijiPfPy")
+            == "mfma_rate_kernel (calibration)")
+    assert bench._short_kernel(COPY) == COPY
