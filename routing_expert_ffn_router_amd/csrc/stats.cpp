@@ -1,7 +1,8 @@
 // Host-side records of one layer's routing: the per-layer expert statistics, the per-slot
-// record, the load of a placement of the experts over ranks and nodes, and the workspace
-// bytes the layer has written by the end of each phase.  Plain C++ over host arrays that
-// the caller copied back from the device; nothing here touches the GPU.
+// record and the load of a placement of the experts over ranks and nodes.  Plain C++ over
+// host arrays that the caller copied back from the device; nothing here touches the GPU.
+// (The memory record by phase, moe_workspace_phases, sits with the workspace layout in
+// moe_abi.cpp.)
 //
 // [EP-checks] airouter.kz, "Expert parallelism in MoE needs measurements before launch":
 //   "Mean expert load proves almost nothing" -- the per-layer record (counts per expert,
@@ -9,9 +10,7 @@
 //   "Top-2 does not insure against hot experts" -- look at each choice separately, and at
 //     which choices get dropped;
 //   "Expert and GPU can be balanced differently" -- load per rank and per node under a
-//     placement of the experts;
-//   "Memory must be counted by phase" -- peaks before the layer, after packing, after
-//     dispatch and after the expert compute.
+//     placement of the experts.
 #include <math.h>
 #include <stdint.h>
 
