@@ -112,8 +112,13 @@ typedef __attribute__((address_space(3))) char lds_char;
 // DSEL_: which waves issue the direct loads: 0 = all eight; 1 = waves 4-7, one per SIMD
 // (waves are placed on the SIMDs round-robin), so each SIMD keeps one wave that never
 // waits on the address unit (measured about 2.5% faster on the prefill tiles).
+// M16_: each 32x32 tile of a wave is computed as 2 x 2 tiles of v_mfma_f32_16x16x32_bf16
+// (64-byte k-steps) instead of v_mfma_f32_32x32x16_bf16 (32-byte k-steps).  Same results;
+// on random data the 16x16 form holds a higher clock under the power limit (measured by
+// the calibration loop: 1.94 against 1.75 GHz), but its fragments need twice the registers
+// per k-step, which the 320-row tile does not have.
 template <int ROWB, int STAGES, int BM_, int BNW_, int WM_, int WN_, int DSEL_ = 0,
-          int BSTAGES_ = 0>
+          int BSTAGES_ = 0, int M16_ = 0>
 struct PrefillTileT {
   static constexpr int BM = BM_, BNW = BNW_, kWaves = 8, kThreads = 512;
   static constexpr int WM = WM_, WN = WN_;
@@ -123,7 +128,11 @@ struct PrefillTileT {
   static constexpr int kWaveCols = NT * 32;                    // weight rows per wave
   static constexpr int kRowBytes = ROWB;
   static constexpr int kChunks = ROWB / 16;                  // 16-byte chunks per row
-  static constexpr int kKSteps = ROWB / 32;                  // 32-byte MFMA k-steps
+  static constexpr bool kM16 = M16_ != 0;
+  static constexpr int kSub = kM16 ? 2 : 1;          // MFMA tiles per 32 rows (and columns)
+  static constexpr int kFragRows = 32 / kSub;        // rows of one MFMA operand fragment
+  static constexpr int kStepChunks = 64 / kFragRows;  // 16-byte chunks of one k-step
+  static constexpr int kKSteps = ROWB / 16 / kStepChunks;  // MFMA k-steps per stage
   // separate rings: activation rows (kAStages) and weight rows (kBStages)
   static constexpr int kAStages = STAGES, kBStages = BSTAGES_ ? BSTAGES_ : STAGES;
   static constexpr int kABytes = BM * kRowBytes, kBBytes = BNW * kRowBytes;
@@ -149,8 +158,8 @@ struct PrefillTileT {
     return ROWB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
   }
 };
-// Prefill: 256 x 256 tile, two 64 KB stages of 128-byte row pieces.
-using PrefillTile = PrefillTileT<128, 2, 256, 256, 2, 4, 1, 3>;
+// Prefill: 256 x 256 tile, two 64 KB stages of 128-byte row pieces, 16x16 MFMA tiles.
+using PrefillTile = PrefillTileT<128, 2, 256, 256, 2, 4, 1, 3, 1>;
 // Prefill with tall experts: 320 x 256 tile, two 72 KB stages (142 flop per loaded byte).
 using PrefillTallTile = PrefillTileT<128, 2, 320, 256, 2, 4, 1>;
 // An expert's last row tile when it holds at most 128 rows: 128 x 256, the weight ring
@@ -260,17 +269,28 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   }
   const int dma_lds = dslot * 1024;
 
-  f32x16 acc[P::MT][P::NT];
+  // accumulators of the wave's 32x32 tiles: one f32x16 each, or (M16) 2 x 2 f32x4 of the
+  // 16x16 tiles [activation half][output-column half]
+  using AccT = typename std::conditional<P::kM16, f32x4[2][2], f32x16>::type;
+  AccT acc[P::MT][P::NT];
 #pragma unroll
   for (int i = 0; i < P::MT; ++i)
 #pragma unroll
-    for (int j = 0; j < P::NT; ++j)
+    for (int j = 0; j < P::NT; ++j) {
+      if constexpr (P::kM16) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        for (int h = 0; h < 4; ++h) acc[i][j][h / 2][h % 2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+      }
+    }
 
   // a wave whose 128-row band lies past the expert's rows skips its MFMAs
   const bool band_live = m_begin + wm * P::MT * 32 < m_end;
-  const int frag_row = lane & 31, frag_half = lane >> 5;
+  // lane l supplies row l % FR of an operand fragment and its k-chunk l / FR of the k-step
+  constexpr int FR = P::kFragRows, SUB = P::kSub;
+  const int frag_row = lane & (FR - 1), frag_k = lane / FR;
   const int a_frag = (wm * P::MT * 32 + frag_row) * P::kRowBytes;
   // weight rows of this wave: NT tiles of 32; with SwiGLU NT/2 gate tiles (from the gate
   // half of the stage) and the NT/2 up tiles of the same output columns
@@ -325,24 +345,30 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
 #pragma unroll
     for (int i = nA; i < nA + nB; ++i) dma(i, kt, buf);
   };
-  // Fragments of one 32-byte k-step: MT activation tiles + NT weight tiles.
+  // Fragments of one k-step: SUB per 32 rows of the MT activation tiles and the NT weight
+  // tiles (fragment SUB * t + h holds rows t * 32 + FR * h ..).
   auto load_frags = [&](const lds_char* abuf, const lds_char* bbuf, int ks, u32x4* fa,
                         u32x4* fb) {
-    const int slot = ((ks * 2 + frag_half) ^ swz) << 4;
+    const int slot = ((ks * P::kStepChunks + frag_k) ^ swz) << 4;
 #pragma unroll
     for (int j = 0; j < P::NT; ++j)
-      fb[j] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          bbuf + b_frag + ((j < kNG ? 0 : kBRows - kNG * 32) + j * 32) * P::kRowBytes + slot);
+#pragma unroll
+      for (int h = 0; h < SUB; ++h)
+        fb[SUB * j + h] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            bbuf + b_frag + ((j < kNG ? 0 : kBRows - kNG * 32) + j * 32 + FR * h) *
+                                P::kRowBytes + slot);
 #pragma unroll
     for (int i = 0; i < P::MT; ++i)
-      fa[i] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          abuf + a_frag + i * 32 * P::kRowBytes + slot);
+#pragma unroll
+      for (int h = 0; h < SUB; ++h)
+        fa[SUB * i + h] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            abuf + a_frag + (i * 32 + FR * h) * P::kRowBytes + slot);
   };
   // Multiply one stage.  The reads of k-step s+1 go out between the MFMAs of k-step s (two
   // register sets), so each k-step's MFMAs cover the next k-step's LDS latency.
   auto compute = [&](const lds_char* abuf, const lds_char* bbuf) {
     if (!band_live) return;
-    u32x4 fa[2][P::MT], fb[2][P::NT];
+    u32x4 fa[2][SUB * P::MT], fb[2][SUB * P::NT];
     load_frags(abuf, bbuf, 0, fa[0], fb[0]);
 #pragma unroll
     for (int ks = 0; ks < P::kKSteps; ++ks) {
@@ -351,14 +377,23 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
 #pragma unroll
       for (int i = 0; i < P::MT; ++i)
 #pragma unroll
-        for (int j = 0; j < P::NT; ++j)
-          mma32_chunk(acc[i][j], fb[ks & 1][j], fa[ks & 1][i], T());
+        for (int hi = 0; hi < SUB; ++hi)
+#pragma unroll
+          for (int j = 0; j < P::NT; ++j)
+#pragma unroll
+            for (int hj = 0; hj < SUB; ++hj) {
+              if constexpr (P::kM16)
+                mma_chunk(acc[i][j][hi][hj], fb[ks & 1][2 * j + hj], fa[ks & 1][2 * i + hi],
+                          T());
+              else
+                mma32_chunk(acc[i][j], fb[ks & 1][j], fa[ks & 1][i], T());
+            }
       // order: [reads of step 0]; per step, its MFMAs with the next step's reads spread
       // evenly between them (read r goes before MFMA floor(r * M / R)); measured about 1 %
       // faster on the prefill layers than issuing the reads as one burst
-      if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x100, P::MT + P::NT, 0);
+      if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x100, SUB * (P::MT + P::NT), 0);
       if (ks + 1 < P::kKSteps) {
-        constexpr int R = P::MT + P::NT, M = P::MT * P::NT;
+        constexpr int R = SUB * (P::MT + P::NT), M = SUB * SUB * P::MT * P::NT;
         unroll_steps<M>([&](auto MI) {
           constexpr int m = decltype(MI)::value;
           constexpr int r_lo = (m * R + M - 1) / M, r_hi = ((m + 1) * R + M - 1) / M;
@@ -366,7 +401,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         });
       } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, P::MT * P::NT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, SUB * SUB * P::MT * P::NT, 0);
       }
     }
   };
@@ -402,14 +437,21 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
 
   // Epilogue.  The weight fragment is the MFMA's first operand, so each accumulator tile
   // is the transposed product: lane L holds activation row L % 32 of the 32 and, in
-  // acc[.][.][4a + b], output column 8a + 4 (L / 32) + b.  The block's outputs go through
+  // acc[.][.][4a + b], output column 8a + 4 (L / 32) + b; with 16x16 tiles, activation row
+  // 16 hi + L % 16 and, in acc[.][.][hi][a][b], output column 16a + 4 (L / 16) + b.  The block's outputs go through
   // LDS in row-major order (4 consecutive columns per lane write) and leave it as 16-byte
   // stores that cover whole cache lines; storing one element per lane per instruction
   // straight from the accumulators took 7-17 % of a tile's time (measured per block).
   // A piece of a split reduction stores its fp32 partial sums the same way.
   __syncthreads();  // every wave's direct loads have landed and its fragment reads are done
   constexpr int NOUT = SWIGLU ? P::NT / 2 : P::NT;
-  const int h4 = 4 * frag_half;
+  const int q4 = 4 * frag_k;
+  auto acc_at = [&](int i, int j, int hi, int a, int b) -> float {
+    if constexpr (P::kM16)
+      return acc[i][j][hi][a][b];
+    else
+      return acc[i][j][4 * a + b];
+  };
   auto staged = [&](auto st_tag, auto rd_tag, auto emit) {
     using ST = decltype(st_tag);                       // staged element type
     constexpr int RD = decltype(rd_tag)::value;        // bytes each lane reads back
@@ -429,19 +471,21 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
         for (int ii = 0; ii < IP; ++ii) {
           const int i = p0 + ii;
           if (i >= P::MT) break;
-          const int srow = (wm * IP + ii) * 32 + frag_row;
+#pragma unroll
+          for (int hi = 0; hi < SUB; ++hi) {
+          const int srow = (wm * IP + ii) * 32 + FR * hi + frag_row;
           lds_char* rowp = a0 + srow * kRow;
 #pragma unroll
           for (int j = 0; j < NOUT; ++j)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-              const int cb = (((wn * NOUT + j) * 32 + 8 * a + h4) * (int)sizeof(ST));
+            for (int a = 0; a < 4 / SUB; ++a) {
+              const int cb = (((wn * NOUT + j) * 32 + 8 * SUB * a + q4) * (int)sizeof(ST));
               const int off = (((cb >> 4) ^ (srow & 15)) << 4) | (cb & 15);
               float v[4];
 #pragma unroll
               for (int b = 0; b < 4; ++b)
-                v[b] = SWIGLU ? silu_f32(acc[i][j][4 * a + b]) * acc[i][j + NOUT][4 * a + b]
-                              : acc[i][j][4 * a + b];
+                v[b] = SWIGLU ? silu_f32(acc_at(i, j, hi, a, b)) * acc_at(i, j + NOUT, hi, a, b)
+                              : acc_at(i, j, hi, a, b);
               if constexpr (sizeof(ST) == 4) {
                 *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(rowp + off) =
                     f32x4{v[0], v[1], v[2], v[3]};
@@ -452,6 +496,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
                          Elt<ST>::from_f32(v[2]), Elt<ST>::from_f32(v[3])};
               }
             }
+          }
         }
       }
       __syncthreads();
