@@ -235,8 +235,11 @@ def _short_kernel(name):
     if m:
         start = m.end()
         return "moe::" + name[start:start + int(m.group(2))]
+    if name.startswith("Cijk_"):  # hipBLASLt's GEMM in the vendor reference
+        return "hipBLASLt GEMM (vendor reference)"
     if "mfma_rate_kernel" in name:  # the calibration loop (libmoe_calib.so)
-        return "mfma_rate_kernel (calibration)"
+        one = "ILi1E" in name or "<1>" in name
+        return "mfma_rate_kernel (calibration, " + ("16x16x32)" if one else "32x32x16)")
     return name.split("(")[0].split("<")[0].replace("void ", "")
 
 
@@ -692,7 +695,8 @@ def mfma_ceiling(moe, iters=300_000, reps=5, operands=("random", "zero")) -> dic
     """The bf16 MFMA rate this GPU sustains with every SIMD of every CU issuing nothing but
     independent 32x32x16 MFMAs on register operands (libmoe_calib.so), and the shader clock
     it holds meanwhile (cycle counter over the constant-rate wall clock), for random operands
-    (the data statistics of the layer) and for all-zero operands.  The published peak assumes
+    (the data statistics of the layer) and for all-zero operands; and, for comparison, the
+    16x16x32 form on random operands.  The published peak assumes
     the full clock; under this load the power limit sets the clock, so the random-operand
     rate is the ceiling an MFMA-bound kernel can approach."""
     import torch
@@ -702,18 +706,20 @@ def mfma_ceiling(moe, iters=300_000, reps=5, operands=("random", "zero")) -> dic
     cyc = torch.zeros(2 * cus, dtype=torch.int64, device="cuda")
     khz = moe.calib_wall_clock_khz()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    flops = cus * 8 * iters * 4 * 32768
-    out = {"cus": cus, "iters": iters, "flops_per_launch": flops}
-    for label, rnd in (("random_bf16", True), ("zero_operands", False)):
+    out = {"cus": cus, "iters": iters}
+    # 32x32x16 on random and on zero operands; 16x16x32 on random operands for comparison
+    for label, rnd, shape in (("random_bf16", True, 0), ("zero_operands", False, 0),
+                              ("random_bf16_16x16x32", True, 1)):
         if ("random" if rnd else "zero") not in operands:
             continue
+        flops = cus * 8 * iters * 4 * (32768 if shape == 0 else 16384)
         for r in range(2):  # warm-up: the clock settles under the load
-            moe.calib_mfma(cus, iters, 977 + r, rnd, sink, cyc)
+            moe.calib_mfma(cus, iters, 977 + r, rnd, sink, cyc, shape=shape)
         torch.cuda.synchronize()
         ms, ghz = [], []
         for r in range(reps):
             ev[0].record()
-            moe.calib_mfma(cus, iters, 1000 + r, rnd, sink, cyc)
+            moe.calib_mfma(cus, iters, 1000 + r, rnd, sink, cyc, shape=shape)
             ev[1].record()
             torch.cuda.synchronize()
             ms.append(ev[0].elapsed_time(ev[1]))
@@ -722,7 +728,7 @@ def mfma_ceiling(moe, iters=300_000, reps=5, operands=("random", "zero")) -> dic
         assert bool(torch.isfinite(sink).all()), "calibration accumulators not finite"
         t = statistics.median(ms)
         tf = flops / (t * 1e-3) / 1e12
-        out[label] = {"ms": round(t, 3), "tflops": round(tf, 1),
+        out[label] = {"flops_per_launch": flops, "ms": round(t, 3), "tflops": round(tf, 1),
                       "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                       "clock_ghz": round(statistics.median(ghz), 3)}
     return out
@@ -827,8 +833,11 @@ def main():
     }
     if sweep is not None:
         result["cf_sweep"] = sweep
+    # (a counter run with --copy-calibration keeps to the layer and the calibration copies:
+    # the vendor reference's own device copy would be taken for one of them)
     default_run = not (flags or G > 1 or args.graph or args.capacity_factor is not None or
-                       args.cf_sweep or args.workload != DEFAULT_WORKLOAD)
+                       args.cf_sweep or args.workload != DEFAULT_WORKLOAD or
+                       args.copy_calibration)
     if default_run:
         print("# vendor reference: hipBLASLt dense GEMMs, device copy", file=sys.stderr,
               flush=True)

@@ -155,6 +155,9 @@ def test_kernel_names(bench):
     assert bench._short_kernel(DOWN) == "prefill_gemm_kernel (down)"
     assert bench._short_kernel(ROUTER) == "prefill_gemm_kernel (router logits, dense)"
     assert bench._short_kernel("_ZN3moe14combine_kernelIDF16bEEvPKT_") == "moe::combine_kernel"
-    assert (bench._short_kernel("_ZN12_GLOBAL__N_116mfma_rate_kernelEijiPfPy")
-            == "mfma_rate_kernel (calibration)")
+    assert (bench._short_kernel("_ZN12_GLOBAL__N_116mfma_rate_kernelILi0EEEvijiPfPy")
+            == "mfma_rate_kernel (calibration, 32x32x16)")
+    assert (bench._short_kernel("void (anonymous namespace)::mfma_rate_kernel<1>(int)")
+            == "mfma_rate_kernel (calibration, 16x16x32)")
     assert bench._short_kernel(COPY) == COPY
+    assert bench._short_kernel("Cijk_Ailk_Bljk_BBS_BH_UserArgs") == "hipBLASLt GEMM (vendor reference)"
