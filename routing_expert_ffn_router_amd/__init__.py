@@ -451,7 +451,7 @@ def load_calib() -> ctypes.CDLL:
         lib = ctypes.CDLL(CALIB_PATH)
         lib.moe_calib_mfma.restype = ctypes.c_int
         lib.moe_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_int,
-                                       _P, _P, _P]
+                                       ctypes.c_int, _P, _P, _P]
         lib.moe_calib_wall_clock_khz.restype = ctypes.c_int
         lib.moe_calib_wall_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int)]
         _calib = lib
@@ -459,10 +459,11 @@ def load_calib() -> ctypes.CDLL:
 
 
 def calib_mfma(blocks: int, iters: int, seed: int, random_operands: bool, sink, cycles,
-               stream=None) -> None:
-    """Enqueue moe_calib_mfma: sink float32[blocks * 8], cycles int64[2 * blocks] on the GPU."""
+               shape: int = 0, stream=None) -> None:
+    """Enqueue moe_calib_mfma (shape 0: 32x32x16, 1: 16x16x32): sink float32[blocks * 8],
+    cycles int64[2 * blocks] on the GPU."""
     _check("moe_calib_mfma", load_calib().moe_calib_mfma(
-        int(blocks), int(iters), int(seed) & 0xFFFFFFFF, int(bool(random_operands)),
+        int(blocks), int(iters), int(seed) & 0xFFFFFFFF, int(bool(random_operands)), int(shape),
         _ptr(sink), _ptr(cycles), _stream(stream)))
 
 

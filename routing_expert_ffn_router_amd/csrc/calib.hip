@@ -1,6 +1,6 @@
 // Calibration of the bf16 MFMA roofline on this GPU: the rate the chip sustains when every
-// SIMD issues nothing but independent v_mfma_f32_32x32x16_bf16 on register operands, and the
-// shader clock it holds meanwhile.  The published dense peak (2.5 PFLOP/s) assumes the full
+// SIMD issues nothing but independent bf16 MFMAs (32x32x16, or 16x16x32 for comparison) on
+// register operands, and the shader clock it holds meanwhile.  The published dense peak (2.5 PFLOP/s) assumes the full
 // 2.4 GHz clock; under load the clock is set by the power limit, and the data the multipliers
 // see moves it: random operands draw more power than zeros.  The GEMM kernels are measured
 // against the published peak; this gives the ceiling beside it.
@@ -13,7 +13,6 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;       // two per SIMD, as in the GEMM kernels
@@ -38,9 +37,14 @@ __device__ inline uint32_t random_bf16_pair(uint32_t h) {
   return lo | (hi << 16);
 }
 
+// SHAPE 0: v_mfma_f32_32x32x16_bf16 (32768 flops, 16 accumulators per lane);
+// SHAPE 1: v_mfma_f32_16x16x32_bf16 (16384 flops, 4 accumulators per lane).
+template <int SHAPE>
 __global__ __launch_bounds__(kWaves * 64) void mfma_rate_kernel(int iters, uint32_t seed,
                                                                 int operands, float* sink,
                                                                 unsigned long long* cycles) {
+  typedef float accv __attribute__((ext_vector_type(SHAPE == 0 ? 16 : 4)));
+  constexpr int kAcc = SHAPE == 0 ? 16 : 4;
   __shared__ float pad[kLdsPad / sizeof(float)];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   u32x4 a[kChains], b[kChains];
@@ -53,24 +57,30 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rate_kernel(int iters, uint3
       a[j][q] = operands ? random_bf16_pair(hash32(ctr ^ seed)) : 0u;
       b[j][q] = operands ? random_bf16_pair(hash32((ctr + 1) ^ seed)) : 0u;
     }
-  f32x16 acc[kChains];
+  accv acc[kChains];
 #pragma unroll
-  for (int j = 0; j < kChains; ++j) acc[j] = f32x16{};
+  for (int j = 0; j < kChains; ++j) acc[j] = accv{};
   __syncthreads();
   const unsigned long long c0 = clock64(), w0 = wall_clock64();
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
-    for (int j = 0; j < kChains; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[j]),
-                                                       __builtin_bit_cast(bf16x8, b[j]),
-                                                       acc[j], 0, 0, 0);
+    for (int j = 0; j < kChains; ++j) {
+      if constexpr (SHAPE == 0)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[j]),
+                                                         __builtin_bit_cast(bf16x8, b[j]),
+                                                         acc[j], 0, 0, 0);
+      else
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[j]),
+                                                         __builtin_bit_cast(bf16x8, b[j]),
+                                                         acc[j], 0, 0, 0);
+    }
   }
   const unsigned long long c1 = clock64(), w1 = wall_clock64();
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < kChains; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s += acc[j][i];
+    for (int i = 0; i < kAcc; ++i) s += acc[j][i];
   // the LDS pad is touched only so the compiler keeps its allocation
   if (iters < 0) pad[threadIdx.x] = s;
   __syncthreads();
@@ -87,12 +97,17 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rate_kernel(int iters, uint3
 
 extern "C" {
 
-int moe_calib_mfma(int blocks, int iters, uint32_t seed, int operands, float* sink,
+int moe_calib_mfma(int blocks, int iters, uint32_t seed, int operands, int shape, float* sink,
                    unsigned long long* cycles, hipStream_t stream) {
-  if (blocks <= 0 || iters <= 0 || (operands != 0 && operands != 1) || !sink || !cycles)
+  if (blocks <= 0 || iters <= 0 || (operands != 0 && operands != 1) ||
+      (shape != 0 && shape != 1) || !sink || !cycles)
     return -1;
-  hipLaunchKernelGGL(mfma_rate_kernel, dim3(blocks), dim3(kWaves * 64), 0, stream, iters, seed,
-                     operands, sink, cycles);
+  if (shape == 0)
+    hipLaunchKernelGGL(mfma_rate_kernel<0>, dim3(blocks), dim3(kWaves * 64), 0, stream, iters,
+                       seed, operands, sink, cycles);
+  else
+    hipLaunchKernelGGL(mfma_rate_kernel<1>, dim3(blocks), dim3(kWaves * 64), 0, stream, iters,
+                       seed, operands, sink, cycles);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -31,9 +31,11 @@ def test_calib_library_exports_its_header():
         assert hasattr(calib, n), n
     # invalid arguments are refused before any HIP call
     sink = ctypes.c_void_p(16)
-    for blocks, iters, operands in [(0, 1, 1), (1, 0, 1), (1, 1, 2), (-1, 5, 0)]:
-        assert calib.moe_calib_mfma(blocks, iters, 0, operands, sink, sink, None) == -1
-    assert calib.moe_calib_mfma(1, 1, 0, 1, None, sink, None) == -1
+    for blocks, iters, operands, shape in [(0, 1, 1, 0), (1, 0, 1, 0), (1, 1, 2, 0),
+                                           (-1, 5, 0, 1), (1, 1, 1, 2), (1, 1, 0, -1)]:
+        assert calib.moe_calib_mfma(blocks, iters, 0, operands, shape, sink, sink, None) == -1
+    assert calib.moe_calib_mfma(1, 1, 0, 1, 0, None, sink, None) == -1
+    assert calib.moe_calib_mfma(1, 1, 0, 1, 1, sink, None, None) == -1
     assert calib.moe_calib_wall_clock_khz(None) == -1
 
 

@@ -1,10 +1,11 @@
 """GPU check of the MFMA-rate calibration (libmoe_calib.so): the loop really computes the
-32x32x16 bf16 products it counts, on the operands it claims, so its flop count is honest.
+bf16 products it counts, on the operands it claims, so its flop count is honest.
 
-Each wave accumulates, for 4 chains, iters times the 32x32 product C = A B^T of its register
-operands (lane l holds row l % 32 of A and of B at k = 8 (l / 32) .. 8 (l / 32) + 7).  The sum
-of all elements of C is sum_k (sum_m A[m, k]) (sum_n B[n, k]), which the host computes from
-the same hash; a wave's sink value is iters times the sum over its 4 chains."""
+Each wave accumulates, for 4 chains, iters times the product C = A B^T of its register
+operands: 32x32 with k = 16 (lane l holds row l % 32 of A and of B at k = 8 (l / 32) ..
+8 (l / 32) + 7), or 16x16 with k = 32 (row l % 16, k = 8 (l / 16) .. 8 (l / 16) + 7).  The
+sum of all elements of C is sum_k (sum_m A[m, k]) (sum_n B[n, k]), which the host computes
+from the same hash; a wave's sink value is iters times the sum over its 4 chains."""
 import numpy as np
 import pytest
 
@@ -36,17 +37,17 @@ def bf16_value(half):
     return sign * (1.0 + mant / 128.0) * np.exp2(exp.astype(np.float64) - 127)
 
 
-def expected_sink(blocks, iters, seed):
+def expected_sink(blocks, iters, seed, shape=0):
     """Each wave's exact sink value, and a bound on its fp32 rounding error."""
     want = np.zeros(blocks * WAVES)
     bound = np.zeros(blocks * WAVES)
     lane = np.arange(64, dtype=np.uint64)
-    kbase = (8 * (lane // 32)).astype(np.int64)
+    kbase = (8 * (lane // (32 if shape == 0 else 16))).astype(np.int64)
     for blk in range(blocks):
         for wave in range(WAVES):
             total = absum = 0.0
             for j in range(CHAINS):
-                col = {n: np.zeros(16) for n in ("a", "b", "|a|", "|b|")}
+                col = {n: np.zeros(32) for n in ("a", "b", "|a|", "|b|")}
                 for q in range(4):
                     ctr = ((blk * WAVES + wave) * 64 + lane) * (2 * CHAINS * 4) + (j * 4 + q) * 2
                     for name, h in (("a", hash32(ctr ^ seed)), ("b", hash32((ctr + 1) ^ seed))):
@@ -57,7 +58,7 @@ def expected_sink(blocks, iters, seed):
                 total += float(np.dot(col["a"], col["b"]))
                 absum += float(np.dot(col["|a|"], col["|b|"]))
             want[blk * WAVES + wave] = iters * total
-            # 16-term MFMA sums, iters accumulations, 16 + 64 terms per wave: well under 64 u
+            # 16- or 32-term MFMA sums, iters accumulations, 16 + 64 terms per wave: < 64 u
             bound[blk * WAVES + wave] = 64 * 2.0 ** -24 * iters * absum
     return want, bound
 
@@ -70,21 +71,22 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def test_calib_mfma_computes_the_counted_products():
+@pytest.mark.parametrize("shape", [0, 1])
+def test_calib_mfma_computes_the_counted_products(shape):
     blocks, iters, seed = 4, 3, 12345
     sink = torch.full((blocks * WAVES,), float("nan"), device="cuda")
     cyc = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
-    moe.calib_mfma(blocks, iters, seed, True, sink, cyc)
+    moe.calib_mfma(blocks, iters, seed, True, sink, cyc, shape=shape)
     torch.cuda.synchronize()
     got = sink.cpu().numpy().astype(np.float64)
-    want, bound = expected_sink(blocks, iters, seed)
+    want, bound = expected_sink(blocks, iters, seed, shape)
     assert np.all(np.abs(got - want) <= bound), (got[:4], want[:4], bound[:4])
     assert np.all(np.abs(want) > bound)  # the check has teeth
     c = cyc.view(blocks, 2).cpu().numpy()
     assert np.all(c > 0)
     # repeated with the same seed: the same values bit for bit
     sink2 = torch.empty_like(sink)
-    moe.calib_mfma(blocks, iters, seed, True, sink2, cyc)
+    moe.calib_mfma(blocks, iters, seed, True, sink2, cyc, shape=shape)
     torch.cuda.synchronize()
     assert torch.equal(sink, sink2)
 
