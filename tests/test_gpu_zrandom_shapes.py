@@ -1,6 +1,6 @@
 """GPU parity on seeded random layer shapes: the whole layer through moe_layer against the
 oracle, across token counts, expert counts, k, capacity, widths, dtypes and the routing
-variants together.
+variants together, and on wider layers with long reductions.
 
 The shapes are drawn once from a fixed seed (the list is the same on every run), sized so
 that the float64 oracle finishes each in a few seconds.  As in the variant tests, the logits
@@ -55,11 +55,47 @@ def _random_cases(n=40, seed=20261203):
     return cases
 
 
+def _long_k_cases(n=16, seed=20261204):
+    """Wider layers with long reductions (d and F up to 4096, so 16-64 k-stages per GEMM
+    tile): the prefill tiles' full pipelines, and the tail split of down GEMMs with few
+    tiles and F >= 2048.  The weights stay small enough for the float64 oracle."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        E = int(rng.choice([2, 3, 4, 8, 16, 64]))
+        k = int(rng.integers(1, min(E, 4) + 1))
+        d = int(rng.choice([1024, 2048, 4096]))
+        F = int(rng.choice([512, 1024, 2048, 4096]))
+        if E * d * F > 6.8e7:  # float64 weight copies in the oracle
+            continue
+        t_max = int(min(4096, 4e9 / (k * d * F)))
+        if t_max < 16:
+            continue
+        T = int(rng.integers(16, t_max + 1))
+        dtype = "f32" if rng.random() < 0.1 else "bf16"
+        cf = None if rng.random() < 0.3 else float(rng.choice([1.0, 1.25, 2.0]))
+        zipf = float(rng.choice([0.0, 0.0, 1.1]))
+        flags = SLOT if rng.random() < 0.2 else 0
+        cases.append((mi.Workload(f"longk{len(cases)}", T, d, E, k, F, cf, dtype, zipf),
+                      flags, 0, 0))
+    return cases
+
+
 CASES = _random_cases()
+LONG_K = _long_k_cases()
 
 
 @pytest.mark.parametrize("w,flags,G,M", CASES, ids=[c[0].name for c in CASES])
 def test_random_layer(w, flags, G, M):
+    _check_layer(w, flags, G, M)
+
+
+@pytest.mark.parametrize("w,flags,G,M", LONG_K, ids=[c[0].name for c in LONG_K])
+def test_random_layer_long_k(w, flags, G, M):
+    _check_layer(w, flags, G, M)
+
+
+def _check_layer(w, flags, G, M):
     log(f"random layer {w} flags={flags} groups={G}/{M}")
     h = host_inputs(w)
     C = moe.capacity(w.T, w.k, w.E, w.capacity_factor)
