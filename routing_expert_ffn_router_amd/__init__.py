@@ -410,10 +410,12 @@ class MoELayer:
         return workspace_view(self.workspace, self.shape, region)
 
     def stages(self, x, w_router, b_router, w_gate, w_up, w_down, stream=None):
-        """The same layer as __call__, as the five ABI calls moe_layer makes internally
-        (route, dispatch, gate/up GEMM, down GEMM, combine; the dispatch builds the tables
-        only and the gate/up GEMM gathers the rows when moe_layer does so), yielding after
-        each one so a caller can record events between stages."""
+        """The same layer as __call__, as five public ABI calls (route, dispatch, gate/up
+        GEMM, down GEMM, combine; the dispatch builds the tables only and the gate/up GEMM
+        gathers the rows when moe_layer does so), yielding after each one so a caller can
+        record events between stages.  The same kernels run, except that moe_layer's
+        dispatch also writes the GEMMs' tile table, which moe_expert_gate_up builds with a
+        launch of its own here."""
         s, ws = self.shape, self.workspace
         v = self.view
         route(s, x, w_router, b_router, v("logits"), v("topk_idx"), v("topk_w"), self.status,

@@ -5,25 +5,21 @@
 // GPU it is a gather: every token reads its k expert rows through dest_row (the inverse of
 // the dispatch permutation), so no two threads write the same output and no atomics are
 // needed.  Slots are summed in order 0..k-1 in fp32, which makes the result deterministic.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-// One wave per (token, 64-chunk column segment): lane l of segment s sums chunk
-// s * 64 + l of the token's k expert rows.  Splitting each row over several waves keeps
-// enough loads in flight when T is small (a decode step of 256 tokens x 14 segments).
+// Token t, column segment seg: lane l sums 16-byte chunk seg * 64 + l of the token's
+// expert rows.
 template <class T, int G>
-__global__ void __launch_bounds__(256)
-combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ dest,
-               const float* __restrict__ w, T* __restrict__ out, int64_t T_, int d, int k,
-               int segs) {
+__device__ inline void combine_item(const T* __restrict__ y, const int32_t* __restrict__ dest,
+                                    const float* __restrict__ w, T* __restrict__ out, int d,
+                                    int k, int64_t t, int seg) {
   constexpr int P = Elt<T>::kPerChunk;
-  const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t t = gw / segs;
-  if (t >= T_) return;
-  const int c = (int)(gw % segs) * kWave + lane;  // 16-byte chunk of the row
+  const int c = seg * kWave + lane_id();  // 16-byte chunk of the row
   if (c >= d / P) return;
   const int32_t* dt = dest + t * k;
   const float* wt = w + t * k;
@@ -63,13 +59,30 @@ combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ dest,
   __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + t * d + (int64_t)c * P));
 }
 
+// One wave per (token, 64-chunk column segment): lane l of segment s sums chunk
+// s * 64 + l of the token's k expert rows.  Splitting each row over several waves keeps
+// enough loads in flight when T is small (a decode step of 256 tokens x 14 segments).
+// The grid is capped (launch_combine) and the waves stride over the T * segs work items,
+// so any T * d fits the launch limits.
+template <class T, int G>
+__global__ void __launch_bounds__(256)
+combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ dest,
+               const float* __restrict__ w, T* __restrict__ out, int64_t T_, int d, int k,
+               int segs) {
+  const int wave = threadIdx.x / kWave;
+  const int64_t items = T_ * segs;
+  for (int64_t gw = (int64_t)blockIdx.x * 4 + wave; gw < items; gw += (int64_t)gridDim.x * 4)
+    combine_item<T, G>(y, dest, w, out, d, k, gw / segs, (int)(gw % segs));
+}
+
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* dest_row,
                           const float* topk_w, void* out, int64_t T, int64_t d, int64_t k,
                           hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int per_chunk = dtype == 1 ? 8 : 4;
   const int segs = (int)((d / per_chunk + kWave - 1) / kWave);
-  const unsigned blocks = (unsigned)((T * segs + 3) / 4);
+  // at most 2^20 blocks (4 waves each); the waves stride over the rest
+  const unsigned blocks = (unsigned)std::min<int64_t>((T * segs + 3) / 4, 1 << 20);
   // slot groups of 8 when k is large enough to fill them, else 4
   if (dtype == 1 && k > 4)
     combine_kernel<bf16, 8><<<blocks, 256, 0, s>>>((const bf16*)y_perm, dest_row, topk_w,

@@ -24,6 +24,11 @@
 //   K5b gather     x_perm[r] = x[src_token[r]] with 16-byte vector copies; empty slots
 //                  get src_token -1 (and, when padded, a zero row).  With packed rows and
 //                  no copy requested, K5 marks the empty slots and K5b is not launched.
+//   K345 fused     for at most 8192 assignments over at most 256 experts: K3-K5 (and the
+//                  grouped GEMMs' tile table) in one block, one launch instead of three or
+//                  four (the decode-sized and small prefill layers are launch-bound here).
+// On request the scan (or the fused kernel) also writes the grouped GEMMs' tile table from
+// the offsets it has just computed, which saves that table its own launch.
 #include "common.h"
 #include "kernels.h"
 
@@ -54,11 +59,27 @@ tile_hist_kernel(const int32_t* __restrict__ idx, int64_t total, int64_t T, int 
 // the largest with q * E <= 1024), so the
 // per-expert scans over many tiles run q-wide; partial sums meet in LDS.  The threads with
 // part 0 (tid = e) then hold the kept counts in expert order for the offsets scan.
+// Tile table of row-tile height bm for the grouped GEMMs (table[0] = tile count, capped at
+// m_max; entry i = (expert, first row) at table[1 + 2i], table[2 + 2i]): expert e's rows
+// are rows[e] from row0[e] on.  Every thread of the block calls it (it holds barriers); the
+// threads with e < E bring their expert's values.
+__device__ inline void write_tile_table(int e, int E, int row0, int rows, int bm, int m_max,
+                                        int* smem, int32_t* __restrict__ table) {
+  const int tiles = e < E ? rows / bm + (rows % bm != 0) : 0;
+  int total;
+  const int pre = block_exclusive_scan(tiles, smem, &total);
+  if (threadIdx.x == 0) table[0] = total < m_max ? total : m_max;
+  for (int i = 0; i < tiles && pre + i < m_max; ++i) {
+    table[1 + 2 * (pre + i)] = e;
+    table[2 + 2 * (pre + i)] = row0 + i * bm;
+  }
+}
+
 __global__ void __launch_bounds__(1024)
 scan_kernel(const int32_t* __restrict__ hist, int ntiles, int E, int C, int k, bool pad,
             int32_t* __restrict__ tile_base, int32_t* __restrict__ routed,
             int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
-            int32_t* __restrict__ drops) {
+            int32_t* __restrict__ drops, int32_t* __restrict__ table, int bm, int m_max) {
   __shared__ int smem[17];
   __shared__ int s_part[1024];
   int q = 1;
@@ -101,6 +122,10 @@ scan_kernel(const int32_t* __restrict__ hist, int ntiles, int E, int C, int k, b
   if (live && part == 0) offsets[e] = pad ? e * C : ex;
   if (tid == 0) offsets[E] = pad ? E * C : total;
   for (int i = tid; i < k + 2; i += blockDim.x) drops[i] = 0;
+  // padded experts own C rows each, which the GEMMs compute whole
+  if (table)
+    write_tile_table(live && part == 0 ? e : E, E, pad ? e * C : ex, pad ? C : c, bm, m_max,
+                     smem, table);
 }
 
 __global__ void __launch_bounds__(kTileMax)
@@ -174,6 +199,128 @@ rank_kernel(const int32_t* __restrict__ idx, int64_t total, int64_t T, int te, i
   __syncthreads();
   for (int i = tid; i < k + 2; i += blockDim.x)
     if (s_drop[i]) atomicAdd(&drops[i], s_drop[i]);
+}
+
+// K3-K5 in one block of 1024 threads, for total <= kFusedPer * 1024 assignments and
+// E <= kFusedDispatchMaxE experts (dispatch_fused).  Thread tid holds the experts of visit positions c * 1024 + tid
+// (c < kFusedPer) in registers.  Pass 1 counts every expert in LDS; the block then scans
+// the kept counts into offsets (and the tile table, when asked for); pass 2 walks the
+// 1024-position chunks in visit order, ranking each assignment after the running count of
+// its expert, the earlier waves of its chunk (per-wave counts in LDS) and the earlier lanes
+// of its wave (ballots on the expert-id bits), the same positions the tiled kernels give.
+// Drop counters and the per-token drop count live in LDS and are stored once at the end.
+// Invalid expert ids (outside [0, E)) are ignored by the counts and dropped, as there.
+constexpr int kFusedPer = (int)(kFusedDispatchEntries / 1024);
+constexpr int kFusedWaves = 1024 / kWave;
+
+__global__ void __launch_bounds__(1024)
+dispatch_fused_kernel(const int32_t* __restrict__ idx, int total, int T, int k, int E, int C,
+                      int nbits, bool slot_major, bool pad, int32_t* __restrict__ routed,
+                      int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
+                      int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token,
+                      int32_t* __restrict__ src_slot, int32_t* __restrict__ drops,
+                      int64_t fill_R, int32_t* __restrict__ table, int bm, int m_max) {
+  extern __shared__ int32_t fsm[];
+  int32_t* s_run = fsm;                      // [E] routed counts, then running positions
+  int32_t* s_off = s_run + E;                // [E] first row of each expert
+  int32_t* s_wc = s_off + E;                 // [kFusedWaves][E] per-wave counts of a chunk
+  int32_t* s_tok = s_wc + kFusedWaves * E;   // [T] dropped assignments per token
+  int32_t* s_drop = s_tok + T;               // [k + 2] drop counters
+  __shared__ int smem[17];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  for (int i = tid; i < E; i += 1024) s_run[i] = 0;
+  for (int i = tid; i < kFusedWaves * E; i += 1024) s_wc[i] = 0;
+  for (int i = tid; i < T; i += 1024) s_tok[i] = 0;
+  for (int i = tid; i < k + 2; i += 1024) s_drop[i] = 0;
+  __syncthreads();
+  // ev[c]: expert of visit position c * 1024 + tid; -1 an invalid id, -2 past the end
+  int ev[kFusedPer];
+#pragma unroll
+  for (int c = 0; c < kFusedPer; ++c) {
+    const int p = c * 1024 + tid;
+    int e = -2;
+    if (p < total) {
+      e = idx[visit_entry(p, T, k, slot_major)];
+      if (e < 0 || e >= E) e = -1;
+    }
+    ev[c] = e;
+  }
+#pragma unroll
+  for (int c = 0; c < kFusedPer; ++c)
+    if (ev[c] >= 0) atomicAdd(&s_run[ev[c]], 1);
+  __syncthreads();
+  // counts, capacity and offsets (E <= 256 threads hold one expert each)
+  const int n_e = tid < E ? s_run[tid] : 0;
+  const int c_e = n_e < C ? n_e : C;
+  int n_kept;
+  const int ex = block_exclusive_scan(c_e, smem, &n_kept);
+  const int row0 = pad ? (tid < E ? tid * C : 0) : ex;
+  if (tid < E) {
+    routed[tid] = n_e;
+    kept[tid] = c_e;
+    offsets[tid] = row0;
+    s_off[tid] = row0;
+    s_run[tid] = 0;  // every thread has read its count (the scan holds barriers)
+  }
+  if (tid == 0) offsets[E] = pad ? E * C : n_kept;
+  if (table) write_tile_table(tid < E ? tid : E, E, row0, pad ? C : c_e, bm, m_max, smem, table);
+  // packed rows without a copy: the row slots past the kept rows are empty
+  for (int64_t r = n_kept + tid; r < fill_R; r += 1024) {
+    src_token[r] = -1;
+    if (src_slot) src_slot[r] = -1;
+  }
+  __syncthreads();
+
+  for (int c = 0; c < kFusedPer && c * 1024 < total; ++c) {
+    const int p = c * 1024 + tid;
+    const int e = ev[c];
+    const bool valid = e >= 0, active = e != -2;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    const int rank = __popcll(same & ((1ull << lane) - 1ull));
+    if (valid && rank == 0) s_wc[wave * E + e] = __popcll(same);
+    __syncthreads();
+    const int f = active ? (int)visit_entry(p, T, k, slot_major) : 0;  // entry t * k + j
+    bool dropped = active;
+    if (valid) {
+      int pos = s_run[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += s_wc[w * E + e];
+      const bool keep = pos < C;
+      dropped = !keep;
+      const int r = keep ? s_off[e] + pos : -1;
+      dest_row[f] = r;
+      if (keep) {
+        src_token[r] = f / k;
+        if (src_slot) src_slot[r] = f % k;
+      }
+    } else if (active) {
+      dest_row[f] = -1;
+    }
+    if (dropped) {
+      atomicAdd(&s_drop[0], 1);
+      atomicAdd(&s_drop[1 + f % k], 1);
+      atomicAdd(&s_tok[f / k], 1);
+    }
+    __syncthreads();
+    // advance the running counts past this chunk and clear its wave counts
+    for (int i = tid; i < E; i += 1024) {
+      int add = 0;
+      for (int w = 0; w < kFusedWaves; ++w) add += s_wc[w * E + i];
+      s_run[i] += add;
+    }
+    __syncthreads();
+    for (int i = tid; i < kFusedWaves * E; i += 1024) s_wc[i] = 0;
+    __syncthreads();
+  }
+  // tokens whose k assignments were all dropped
+  for (int t = tid; t < T; t += 1024)
+    if (s_tok[t] == k) atomicAdd(&s_drop[k + 1], 1);
+  __syncthreads();
+  for (int i = tid; i < k + 2; i += 1024) drops[i] = s_drop[i];
 }
 
 // Tokens whose k assignments were all dropped, for the slot-major order (there a token's
@@ -277,20 +424,33 @@ hipError_t launch_slot_counts(const int32_t* idx, const int32_t* dest_row, int64
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int64_t total = a.T * a.k;
   const int te = (int)dispatch_tile_entries(a.k);
-  const int ntiles = (int)dispatch_ntiles(a.T, a.k);
+  int ntiles = (int)dispatch_ntiles(a.T, a.k);
   int nbits = 0;
   while ((1ll << nbits) < a.E) ++nbits;
   hipError_t err;
   // packed rows without a copy: the rank kernel marks the empty row slots itself
   const bool tail_in_rank = !a.x_perm && !a.pad && ntiles > 0;
+  const int bm = a.table ? a.table_bm : 0, m_max = a.table ? (int)a.table_m_max : 0;
+  if (dispatch_fused(a.T, a.k, a.E)) {
+    const size_t lds = ((2 + kFusedWaves) * a.E + a.T + a.k + 2) * sizeof(int32_t);
+    dispatch_fused_kernel<<<1, 1024, lds, s>>>(
+        a.topk_idx, (int)total, (int)a.T, (int)a.k, (int)a.E, (int)a.C, nbits, a.slot_major,
+        a.pad, a.routed, a.kept, a.offsets, a.dest_row, a.src_token, a.src_slot, a.drops,
+        tail_in_rank ? a.R : 0, a.table, bm, m_max);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    ntiles = 0;  // the tiled kernels below are not needed
+  }
   if (ntiles > 0) {
     tile_hist_kernel<<<ntiles, kTileMax, a.E * sizeof(int32_t), s>>>(
         a.topk_idx, total, a.T, te, (int)a.k, (int)a.E, a.slot_major, a.tile_hist);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  scan_kernel<<<1, 1024, 0, s>>>(a.tile_hist, ntiles, (int)a.E, (int)a.C, (int)a.k, a.pad,
-                                 a.tile_base, a.routed, a.kept, a.offsets, a.drops);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (total == 0 || ntiles > 0) {
+    scan_kernel<<<1, 1024, 0, s>>>(a.tile_hist, ntiles, (int)a.E, (int)a.C, (int)a.k, a.pad,
+                                   a.tile_base, a.routed, a.kept, a.offsets, a.drops, a.table,
+                                   bm, m_max);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   if (ntiles > 0) {
     const size_t lds = ((kTileMax / kWave) * a.E + kTileMax + a.k + 2) * sizeof(int32_t);
     rank_kernel<<<ntiles, kTileMax, lds, s>>>(a.topk_idx, total, a.T, te, (int)a.k, (int)a.E,

@@ -797,6 +797,14 @@ FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad
   return p;
 }
 
+// Upper bound on the blocks of either grouped-GEMM launch of plan p (launch_prefill): at
+// most m_max x (n-tiles rounded up to whole groups, < 2 x n-tiles) logical tiles of at least
+// 128 columns, rounded up to a multiple of 8, plus the tail split's pieces.
+int64_t ffn_max_blocks(const FfnPlan& p, int64_t d, int64_t F) {
+  const int64_t n128 = ((d > F ? d : F) + 127) / 128;
+  return p.m_max * 2 * n128 + 8 + kSplitCUs;
+}
+
 namespace {
 
 // tail_split > 0 (tile-table mode, no SwiGLU): the tail split with at most tail_split pieces
@@ -892,10 +900,12 @@ hipError_t run_down(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
 // Router logits L = x w^T (+ b) through the same pipeline in dense mode: 64-token x
 // 128-expert tiles, fp32 output with the bias added in the epilogue.  Used when there are
 // enough tiles to spread over the CUs.
+// (At most 2^22 tiles, so the launch stays within 2^31 threads; larger shapes take the
+// router kernel, whose blocks stride over the token tiles.)
 bool router_gemm_suits(int64_t T, int64_t E) {
   const int64_t tiles = ((T + RouterTile::BM - 1) / RouterTile::BM) *
                         ((E + RouterTile::BNW - 1) / RouterTile::BNW);
-  return E >= 64 && tiles >= 192;
+  return E >= 64 && tiles >= 192 && tiles <= ((int64_t)1 << 22);
 }
 
 hipError_t launch_router_gemm(int dtype, const void* x, const void* w, const float* b,

@@ -19,10 +19,11 @@ inline int64_t dispatch_ntiles(int64_t T, int64_t k) {
 
 hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
 
-// S1
+// S1.  status_zero (nullable): an int32 the launch also sets to 0 before the logits are
+// complete (the top-k status counter), without a launch of its own where it can.
 hipError_t launch_router_logits(int dtype, const void* x, const void* w, const float* b,
                                 float* logits, int64_t T, int64_t d, int64_t E,
-                                hipStream_t s);
+                                int32_t* status_zero, hipStream_t s);
 // S2
 // sel_bias (nullable): selection-only bias.  n_groups > 1: group-limited selection keeping
 // topk_groups groups (n_groups <= min(E, 64), dividing E).
@@ -48,8 +49,20 @@ struct DispatchArgs {
   int32_t* dest_row;   // [T*k]
   int32_t* drops;      // [k+2]
   void* x_perm;        // [R, d]; null: tables only, no row copies
+  // nullable: also write the grouped GEMMs' tile table of row height table_bm (at most
+  // table_m_max entries, launch_expert_ffn's layout) from the offsets
+  int32_t* table = nullptr;
+  int table_bm = 0;
+  int64_t table_m_max = 0;
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+// The dispatch of T * k assignments over E experts runs in one block (no per-tile scratch
+// tables) when it holds at most 8192 assignments over at most 256 experts.
+constexpr int64_t kFusedDispatchEntries = 8192;
+constexpr int64_t kFusedDispatchMaxE = 256;
+inline bool dispatch_fused(int64_t T, int64_t k, int64_t E) {
+  return T * k > 0 && T * k <= kFusedDispatchEntries && E <= kFusedDispatchMaxE;
+}
 // The static scratch of moe_dispatch_no_workspace on the current device: its address
 // (looked up once per device) and size in bytes.
 hipError_t dispatch_scratch(void** ptr, size_t* bytes);
@@ -71,6 +84,8 @@ struct FfnPlan {
 FfnPlan ffn_plan(int64_t T, int64_t E, int64_t k, int64_t C, int64_t R, bool pad, int64_t d,
                  int64_t F, int64_t elt);
 inline int64_t ffn_table_ints(const FfnPlan& p) { return 1 + 2 * p.m_max; }
+// Upper bound on the blocks of one grouped-GEMM launch of plan p (512 threads each).
+int64_t ffn_max_blocks(const FfnPlan& p, int64_t d, int64_t F);
 // CUs the tail split of the down GEMM fills (MI355X: 256).
 constexpr int kSplitCUs = 256;
 // fp32 partial sums of the down GEMM's split tail tiles: down_pieces_max slots of

@@ -30,6 +30,12 @@ constexpr int64_t kMaxGroups = 64;
 bool padded(const moe_shape* s) { return (s->flags & MOE_FLAG_PAD_TO_CAPACITY) != 0; }
 bool grouped(const moe_shape* s) { return s->n_groups > 1 && s->topk_groups < s->n_groups; }
 
+int64_t max_rows(const moe_shape* s) {
+  const int64_t a = s->T * s->k, b = s->E * eff_capacity(s);
+  if (padded(s)) return b;
+  return a < b ? a : b;
+}
+
 int check_shape(const moe_shape* s) {
   if (!s) return MOE_ERR_INVALID_ARG;
   if (s->T < 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->F <= 0) return MOE_ERR_INVALID_ARG;
@@ -51,13 +57,12 @@ int check_shape(const moe_shape* s) {
     if (s->topk_groups < 1 || s->topk_groups > s->n_groups) return MOE_ERR_INVALID_ARG;
     if (s->k > (int64_t)s->topk_groups * (s->E / s->n_groups)) return MOE_ERR_INVALID_ARG;
   }
+  // every grouped-GEMM launch within 2^32 threads (512 per block)
+  const int64_t R = max_rows(s);
+  const moe::FfnPlan plan = moe::ffn_plan(s->T, s->E, s->k, eff_capacity(s), R, padded(s),
+                                          s->d, s->F, elt_bytes(s->dtype));
+  if (moe::ffn_max_blocks(plan, s->d, s->F) >= ((int64_t)1 << 23)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
-}
-
-int64_t max_rows(const moe_shape* s) {
-  const int64_t a = s->T * s->k, b = s->E * eff_capacity(s);
-  if (padded(s)) return b;
-  return a < b ? a : b;
 }
 
 struct Layout {
@@ -140,11 +145,13 @@ int check_dispatch_args(const moe_shape* s, const int32_t* topk_idx, const void*
 
 // The dispatch launches, with the scratch tables tile_hist / tile_base ([ntiles, E] int32
 // each) from the workspace or from the static array.
+// With table set, the dispatch also writes the grouped GEMMs' tile table of the layer's
+// plan there (moe_layer).
 int dispatch_launch(const moe_shape* s, const int32_t* topk_idx, const void* x,
                     int32_t* tile_hist, int32_t* tile_base, int32_t* routed_counts,
                     int32_t* tokens_per_expert, int32_t* expert_offsets, int32_t* src_token,
                     int32_t* src_slot, int32_t* dest_row, int32_t* drops, void* x_perm,
-                    hipStream_t st) {
+                    hipStream_t st, int32_t* table = nullptr) {
   moe::DispatchArgs a;
   a.topk_idx = topk_idx;
   a.x = x;
@@ -167,6 +174,13 @@ int dispatch_launch(const moe_shape* s, const int32_t* topk_idx, const void* x,
   a.dest_row = dest_row;
   a.drops = drops;
   a.x_perm = x_perm;
+  if (table) {
+    const moe::FfnPlan plan = moe::ffn_plan(s->T, s->E, s->k, a.C, a.R, a.pad, s->d, s->F,
+                                            a.elt_bytes);
+    a.table = table;
+    a.table_bm = plan.bm;
+    a.table_m_max = plan.m_max;
+  }
   return hip_status(moe::launch_dispatch(a, st));
 }
 
@@ -174,13 +188,16 @@ int route_impl(const moe_shape* s, const void* x, const void* w_router, const fl
                float* logits, int logits_given, int32_t* idx, float* gates, int32_t* status,
                hipStream_t st) {
   hipError_t e;
-  if (status && (e = moe::launch_zero_i32(status, 1, st)) != hipSuccess) return MOE_ERR_HIP;
-  if (s->T == 0) return MOE_OK;
+  // the status counter starts at zero: cleared by the router launch when there is one
+  if (logits_given || s->T == 0) {
+    if (status && (e = moe::launch_zero_i32(status, 1, st)) != hipSuccess) return MOE_ERR_HIP;
+    if (s->T == 0) return MOE_OK;
+  }
   // with a selection-only bias the logits stay unbiased and the bias goes to the top-k
   const bool sel_only = (s->flags & MOE_FLAG_BIAS_SELECTION_ONLY) != 0;
   if (!logits_given) {
     e = moe::launch_router_logits(s->dtype, x, w_router, sel_only ? nullptr : b_router, logits,
-                                  s->T, s->d, s->E, st);
+                                  s->T, s->d, s->E, status, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   const int ng = grouped(s) ? s->n_groups : 1, mg = grouped(s) ? s->topk_groups : 1;
@@ -224,14 +241,18 @@ int moe_workspace_phases(const moe_shape* s, int64_t* bytes) {
   if (rc != MOE_OK) return rc;
   if (!bytes) return MOE_ERR_INVALID_ARG;
   const Layout L = make_layout(s);
-  // regions moe_layer writes in each stage (with its optional outputs kept in the workspace)
-  static const int kPack[] = {MOE_WS_LOGITS,    MOE_WS_TOPK_IDX,  MOE_WS_TOPK_W,
-                              MOE_WS_STATUS,    MOE_WS_ROUTED,    MOE_WS_KEPT,
+  // regions moe_layer writes in each stage (with its optional outputs kept in the workspace);
+  // its dispatch also writes the grouped GEMMs' tile table, and the per-tile scratch tables
+  // only where it runs tiled (not in one block)
+  static const int kPack[] = {MOE_WS_LOGITS,    MOE_WS_TOPK_IDX, MOE_WS_TOPK_W,
+                              MOE_WS_STATUS,    MOE_WS_ROUTED,   MOE_WS_KEPT,
                               MOE_WS_OFFSETS,   MOE_WS_SRC_TOKEN, MOE_WS_DEST_ROW,
-                              MOE_WS_DROPS,     MOE_WS_TILE_HIST, MOE_WS_TILE_BASE};
-  static const int kExperts[] = {MOE_WS_SCHED, MOE_WS_H, MOE_WS_Y_PERM, MOE_WS_DOWN_ACC};
+                              MOE_WS_DROPS,     MOE_WS_SCHED};
+  static const int kExperts[] = {MOE_WS_H, MOE_WS_Y_PERM, MOE_WS_DOWN_ACC};
   int64_t pack = 0;
   for (int r : kPack) pack += L.size[r];
+  if (!moe::dispatch_fused(s->T, s->k, s->E))
+    pack += L.size[MOE_WS_TILE_HIST] + L.size[MOE_WS_TILE_BASE];
   if (!layer_gathers(s)) pack += L.size[MOE_WS_X_PERM];  // the copy the gathering GEMM skips
   int64_t experts = pack;
   // an empty layer writes its counters and status only: the expert GEMMs do not launch
@@ -314,7 +335,7 @@ namespace {
 // Shared body of the expert-FFN entry points; which = 1 (gate/up), 2 (down), 3 (both).  The
 // gate/up activations are x_perm, or, with src_rows, the rows src_rows[r] of x.
 // With table_ready the workspace already holds the tile table of these offsets (moe_layer's
-// down GEMM reuses the gate/up GEMM's).
+// dispatch wrote it).
 int expert_ffn_impl(const moe_shape* s, int which, const void* x_perm, const void* x,
                     const int32_t* src_rows, void* h, const int32_t* expert_offsets,
                     const void* w_gate, const void* w_up, const void* w_down, void* ws,
@@ -449,15 +470,19 @@ int moe_layer(const moe_shape* s, const void* x, const void* w_router, const flo
   if (rc != MOE_OK) return rc;
   // packed rows: the gate/up GEMM gathers the token rows itself (x_perm is not written)
   const bool gathered = layer_gathers(s);
-  rc = moe_dispatch(s, idx, x, ws, ws_bytes, routed, kept, offsets, src, nullptr, dest, dr,
-                    gathered ? nullptr : x_perm, st);
+  void* x_copy = gathered ? nullptr : x_perm;
+  rc = check_dispatch_args(s, idx, x, routed, kept, offsets, src, dest, dr, x_copy);
+  if (rc != MOE_OK) return rc;
+  // the dispatch also writes the grouped GEMMs' tile table from the offsets it computes
+  rc = dispatch_launch(s, idx, x, region<int32_t>(ws, L, MOE_WS_TILE_HIST),
+                       region<int32_t>(ws, L, MOE_WS_TILE_BASE), routed, kept, offsets, src,
+                       nullptr, dest, dr, x_copy, st, region<int32_t>(ws, L, MOE_WS_SCHED));
   if (rc != MOE_OK) return rc;
   void* h = region<void>(ws, L, MOE_WS_H);
-  rc = gathered ? moe_expert_gate_up_gathered(s, x, src, offsets, w_gate, w_up, ws, ws_bytes,
-                                              h, st)
-                : moe_expert_gate_up(s, x_perm, offsets, w_gate, w_up, ws, ws_bytes, h, st);
+  rc = expert_ffn_impl(s, 1, gathered ? nullptr : x_perm, gathered ? x : nullptr,
+                       gathered ? src : nullptr, h, offsets, w_gate, w_up, nullptr, ws,
+                       ws_bytes, nullptr, st, /*table_ready=*/true);
   if (rc != MOE_OK) return rc;
-  // the down GEMM reuses the tile table the gate/up GEMM just built from the same offsets
   rc = expert_ffn_impl(s, 2, nullptr, nullptr, nullptr, h, offsets, nullptr, nullptr, w_down,
                        ws, ws_bytes, y_perm, st, /*table_ready=*/true);
   if (rc != MOE_OK) return rc;

@@ -42,17 +42,17 @@ hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
 // assignment (lane group g takes chunks 2g and 2g + 1), so the products pair up.  Each load
 // touches half of 16 cache lines, so shapes with many tokens and experts (enough 64 x 128
 // tiles to fill the CUs) go through the expert-GEMM pipeline instead.
-// grid = (ceil(T / (16 MT)), ceil(E / (16 NT))).
+// grid = (min(ceil(T / (16 MT)), 2^16), ceil(E / (16 NT))): the blocks of a column of the
+// grid stride over the token tiles.  With status_zero set, the first thread of block (0, 0)
+// also clears that word (the top-k kernel after this one counts into it), which saves the
+// layer a launch.
 // ---------------------------------------------------------------------------------------
 template <class T, int MT, int NT, int kRouterWaves>
-__global__ void __launch_bounds__(kRouterWaves* kWave)
-router_logits_kernel(const T* __restrict__ x, const T* __restrict__ w,
-                     const float* __restrict__ bias, float* __restrict__ logits, int T_,
-                     int d, int E) {
-  extern __shared__ float part[];  // [W][MT][NT][4][kWave]
+__device__ __attribute__((always_inline)) inline void router_logits_tile(const T* __restrict__ x, const T* __restrict__ w,
+                                          const float* __restrict__ bias,
+                                          float* __restrict__ logits, int T_, int d, int E,
+                                          int t0, int e0, float* part) {
   const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int t0 = blockIdx.x * MT * 16;
-  const int e0 = blockIdx.y * NT * 16;
   const int r = lane & 15, g = lane >> 4;
   const char* xa[MT];
 #pragma unroll
@@ -125,41 +125,63 @@ router_logits_kernel(const T* __restrict__ x, const T* __restrict__ w,
   }
 }
 
+template <class T, int MT, int NT, int kRouterWaves>
+__global__ void __launch_bounds__(kRouterWaves* kWave)
+router_logits_kernel(const T* __restrict__ x, const T* __restrict__ w,
+                     const float* __restrict__ bias, float* __restrict__ logits, int T_,
+                     int d, int E, int32_t* __restrict__ status_zero) {
+  extern __shared__ float part[];  // [W][MT][NT][4][kWave]
+  if (status_zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status_zero = 0;
+  const int tiles = (T_ + MT * 16 - 1) / (MT * 16);
+  for (int tb = blockIdx.x; tb < tiles; tb += gridDim.x) {
+    router_logits_tile<T, MT, NT, kRouterWaves>(x, w, bias, logits, T_, d, E, tb * MT * 16,
+                                                blockIdx.y * NT * 16, part);
+    __syncthreads();  // the partial tiles have been read before the next tile writes them
+  }
+}
+
 template <class T, int MT, int NT, int W>
 hipError_t launch_router_tile(const T* x, const T* w, const float* b, float* logits,
-                              int64_t T_, int64_t d, int64_t E, hipStream_t s) {
+                              int64_t T_, int64_t d, int64_t E, int32_t* status_zero,
+                              hipStream_t s) {
   const size_t lds = (size_t)W * MT * NT * 4 * kWave * sizeof(float);
   hipError_t e = hipFuncSetAttribute((const void*)router_logits_kernel<T, MT, NT, W>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((T_ + 16 * MT - 1) / (16 * MT)),
+  const dim3 grid((unsigned)std::min<int64_t>((T_ + 16 * MT - 1) / (16 * MT), 1 << 16),
                   (unsigned)((E + 16 * NT - 1) / (16 * NT)));
   router_logits_kernel<T, MT, NT, W><<<grid, W * kWave, lds, s>>>(x, w, b, logits, (int)T_,
-                                                                  (int)d, (int)E);
+                                                                  (int)d, (int)E, status_zero);
   return hipGetLastError();
 }
 
 template <class T>
 hipError_t launch_router_typed(const T* x, const T* w, const float* b, float* logits,
-                               int64_t T_, int64_t d, int64_t E, hipStream_t s) {
+                               int64_t T_, int64_t d, int64_t E, int32_t* status_zero,
+                               hipStream_t s) {
   // 16 x 64 tiles when that still gives at least 512 blocks (two per CU), else 16 x 16
   // (larger shapes take the GEMM pipeline, see launch_router_logits).
   const int64_t t16 = (T_ + 15) / 16;
   if (E > 16 && t16 * ((E + 63) / 64) >= 512)
-    return launch_router_tile<T, 1, 4, 8>(x, w, b, logits, T_, d, E, s);
-  return launch_router_tile<T, 1, 1, 8>(x, w, b, logits, T_, d, E, s);
+    return launch_router_tile<T, 1, 4, 8>(x, w, b, logits, T_, d, E, status_zero, s);
+  return launch_router_tile<T, 1, 1, 8>(x, w, b, logits, T_, d, E, status_zero, s);
 }
 
 hipError_t launch_router_logits(int dtype, const void* x, const void* w, const float* b,
                                 float* logits, int64_t T, int64_t d, int64_t E,
-                                hipStream_t s) {
-  if (T == 0) return hipSuccess;
+                                int32_t* status_zero, hipStream_t s) {
+  if (T == 0) return status_zero ? launch_zero_i32(status_zero, 1, s) : hipSuccess;
   // many tokens and experts: full-line direct loads into LDS and 32x32 MFMA tiles (the
   // expert-GEMM pipeline); the kernel below reads half cache lines per load
-  if (router_gemm_suits(T, E)) return launch_router_gemm(dtype, x, w, b, logits, T, d, E, s);
+  if (router_gemm_suits(T, E)) {
+    hipError_t e = status_zero ? launch_zero_i32(status_zero, 1, s) : hipSuccess;
+    return e != hipSuccess ? e : launch_router_gemm(dtype, x, w, b, logits, T, d, E, s);
+  }
   if (dtype == 1)
-    return launch_router_typed<bf16>((const bf16*)x, (const bf16*)w, b, logits, T, d, E, s);
-  return launch_router_typed<float>((const float*)x, (const float*)w, b, logits, T, d, E, s);
+    return launch_router_typed<bf16>((const bf16*)x, (const bf16*)w, b, logits, T, d, E,
+                                     status_zero, s);
+  return launch_router_typed<float>((const float*)x, (const float*)w, b, logits, T, d, E,
+                                    status_zero, s);
 }
 
 // ---------------------------------------------------------------------------------------

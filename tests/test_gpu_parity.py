@@ -173,6 +173,11 @@ DISPATCH_CASES = [
     (100, 1, 1, 40, 128, "f32", 0.0),
     (4096, 8, 2, 1280, 384, "bf16", 0.0),
     (1, 8, 8, 0, 128, "bf16", 0.0),
+    # around the one-block dispatch's limits (8192 assignments, 256 experts): just past the
+    # assignments (tiled), at both limits (one block), past the experts (tiled)
+    (4097, 8, 2, 1100, 128, "bf16", 0.3),
+    (1024, 256, 8, 40, 128, "bf16", 0.05),
+    (30, 257, 4, 0, 128, "f32", 0.0),
 ]
 
 
@@ -576,6 +581,35 @@ def test_layers_on_two_streams_match_one_stream():
             assert torch.equal(lay.routed_counts, ref.routed_counts)
             assert torch.equal(lay.drops, ref.drops)
             assert torch.equal(lay.view("dest_row"), ref.view("dest_row"))
+
+
+def test_router_logits_past_grid_cap():
+    # The router kernel's grid holds at most 2^16 token tiles of 16 tokens; the blocks
+    # stride over the rest.  T = 2^20 + 77 tokens: blocks 0-5 also take tiles past 2^16.
+    # The launch also clears the status word (pre-filled here), and one token with an
+    # infinite input value is counted into it.
+    T, d, E, k = (1 << 20) + 77, 128, 8, 2
+    g = torch.Generator(device="cuda").manual_seed(12)
+    x = torch.randn((T, d), generator=g, device="cuda").to(torch.bfloat16)
+    x[T - 3, 5] = float("inf")
+    wr = (torch.randn((E, d), generator=g, device="cuda") / d ** 0.5).to(torch.bfloat16)
+    s = moe.shape(T, d, E, k, 128, 0, moe.MOE_BF16)
+    L = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx, w = _i32(0, T, k), torch.empty((T, k), device="cuda")
+    status = torch.full((1,), 77, dtype=torch.int32, device="cuda")
+    moe.route(s, x, wr, None, L, idx, w, status)
+    torch.cuda.synchronize()
+    assert status.item() == 1
+    wr_h = wr.float().cpu().numpy()
+    for t0 in (0, (1 << 20) - 40, T - 90):
+        rows = slice(t0, t0 + 80)
+        xr = x[rows].float().cpu().numpy()
+        ref = oracle.router_logits(xr, wr_h, None)
+        got = L[rows].cpu().numpy()
+        fin = np.all(np.isfinite(ref), axis=1)
+        assert np.max(np.abs(got[fin] - ref[fin])) <= logits_tol(ref[fin])
+        assert np.array_equal(idx[rows].cpu().numpy()[fin], oracle.select_topk(got[fin], k))
+    assert not np.all(np.isfinite(L[T - 3].cpu().numpy()))
 
 
 def test_route_given_logits_past_2_31_lanes():
