@@ -116,7 +116,8 @@ typedef __attribute__((address_space(3))) char lds_char;
 // (64-byte k-steps) instead of v_mfma_f32_32x32x16_bf16 (32-byte k-steps).  Same results;
 // on random data the 16x16 form holds a higher clock under the power limit (measured by
 // the calibration loop: 1.94 against 1.75 GHz), but its fragments need twice the registers
-// per k-step, which the 320-row tile does not have.
+// per k-step, which the 320-row tile does not have.  M16_ = 2: the 16x16 form for bf16
+// only (ForElt); fp32 gains nothing from it and would run short of registers.
 template <int ROWB, int STAGES, int BM_, int BNW_, int WM_, int WN_, int DSEL_ = 0,
           int BSTAGES_ = 0, int M16_ = 0>
 struct PrefillTileT {
@@ -129,6 +130,9 @@ struct PrefillTileT {
   static constexpr int kRowBytes = ROWB;
   static constexpr int kChunks = ROWB / 16;                  // 16-byte chunks per row
   static constexpr bool kM16 = M16_ != 0;
+  // 16x16 form with more than four 32-row tiles per wave: the lean fragment schedule
+  // (compute_lean), whose fragments fit the registers the 320-row tile leaves
+  static constexpr bool kLean = kM16 && BM_ / WM_ / 32 > 4;
   static constexpr int kSub = kM16 ? 2 : 1;          // MFMA tiles per 32 rows (and columns)
   static constexpr int kFragRows = 32 / kSub;        // rows of one MFMA operand fragment
   static constexpr int kStepChunks = 64 / kFragRows;  // 16-byte chunks of one k-step
@@ -158,16 +162,26 @@ struct PrefillTileT {
     return ROWB == 64 ? ((r >> 2) & 3) : ((r >> 1) & 7);
   }
 };
+// The tile P as it runs on element type T (M16_ = 2 resolved to the 16x16 form for bf16).
+template <class P, class T>
+struct ForElt {
+  using type = P;
+};
+template <int R, int S, int BM, int BNW, int WM, int WN, int D, int BS, class T>
+struct ForElt<PrefillTileT<R, S, BM, BNW, WM, WN, D, BS, 2>, T> {
+  using type = PrefillTileT<R, S, BM, BNW, WM, WN, D, BS, sizeof(T) == 2 ? 1 : 0>;
+};
+
 // Prefill: 256 x 256 tile, two 64 KB stages of 128-byte row pieces, 16x16 MFMA tiles.
 using PrefillTile = PrefillTileT<128, 2, 256, 256, 2, 4, 1, 3, 1>;
 // Prefill with tall experts: 320 x 256 tile, two 72 KB stages (142 flop per loaded byte).
-using PrefillTallTile = PrefillTileT<128, 2, 320, 256, 2, 4, 1>;
+using PrefillTallTile = PrefillTileT<128, 2, 320, 256, 2, 4, 1, 0, 2>;
 // An expert's last row tile when it holds at most 128 rows: 128 x 256, the weight ring
 // three deep (the same weight columns as the full tiles).
-using PrefillTailTile = PrefillTileT<128, 2, 128, 256, 2, 4, 1, 3>;
+using PrefillTailTile = PrefillTileT<128, 2, 128, 256, 2, 4, 1, 3, 2>;
 // ... and twice as wide (two n-tiles) for the last tile of an expert with at least two full
 // 320-row tiles: 128 x 512, two 80 KB stages.
-using PrefillTailWideTile = PrefillTileT<128, 2, 128, 512, 2, 4, 1, 2>;
+using PrefillTailWideTile = PrefillTileT<128, 2, 128, 512, 2, 4, 1, 2, 2>;
 // Decode: weight streaming.  64 x 256 tile, three 40 KB stages, so two stages (80 KB per
 // CU) of weight reads are in flight while one is multiplied.
 using DecodeDmaTile = PrefillTileT<128, 3, 64, 256, 2, 4>;
@@ -405,6 +419,67 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
       }
     }
   };
+  // The 16x16 form with many activation tiles per wave (P::kLean): the double-buffered
+  // schedule above would hold 2 x (2 MT + 2 NT) fragments and spill the 320-row tile.  Here
+  // the weight fragments of a k-step are double-buffered across k-steps, while the
+  // activation fragments stream through a ring of three items (an item = the two 16-row
+  // fragments of one 32-row tile), each loaded two items (16 MFMAs of this wave) before its
+  // MFMAs: 2 NT + 3 SUB fragments instead of 2 (2 MT + 2 NT).  Same products in the same
+  // order per accumulator as compute().
+  auto compute_lean = [&](const lds_char* abuf, const lds_char* bbuf) {
+    if constexpr (P::kLean) {
+    if (!band_live) return;
+    constexpr int KS = P::kKSteps, NI = KS * P::MT, RING = 3;
+    u32x4 fb[2][SUB * P::NT], fa[RING][SUB];
+    auto ld_b = [&](int ks, u32x4* dst) {
+      const int slot = ((ks * P::kStepChunks + frag_k) ^ swz) << 4;
+#pragma unroll
+      for (int j = 0; j < P::NT; ++j)
+#pragma unroll
+        for (int h = 0; h < SUB; ++h)
+          dst[SUB * j + h] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+              bbuf + b_frag + ((j < kNG ? 0 : kBRows - kNG * 32) + j * 32 + FR * h) *
+                                  P::kRowBytes + slot);
+    };
+    auto ld_a = [&](int ks, int i, u32x4* dst) {
+      const int slot = ((ks * P::kStepChunks + frag_k) ^ swz) << 4;
+#pragma unroll
+      for (int h = 0; h < SUB; ++h)
+        dst[h] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            abuf + a_frag + (i * 32 + FR * h) * P::kRowBytes + slot);
+    };
+    ld_b(0, fb[0]);
+    unroll_steps<RING - 1>([&](auto N) {
+      constexpr int n = decltype(N)::value;
+      ld_a(n / P::MT, n % P::MT, fa[n]);
+    });
+    __builtin_amdgcn_sched_group_barrier(0x100, SUB * P::NT + (RING - 1) * SUB, 0);
+    unroll_steps<NI>([&](auto N) {
+      constexpr int n = decltype(N)::value, ks = n / P::MT, i = n % P::MT;
+      constexpr int nl = n + RING - 1;  // the item whose fragments are loaded now
+      constexpr bool load_a = nl < NI;
+      constexpr bool load_b = i == 1 && ks + 1 < KS;  // the next k-step's weight fragments
+      if constexpr (load_a) ld_a(nl / P::MT, nl % P::MT, fa[nl % RING]);
+      if constexpr (load_b) ld_b(ks + 1, fb[(ks + 1) & 1]);
+#pragma unroll
+      for (int hi = 0; hi < SUB; ++hi)
+#pragma unroll
+        for (int j = 0; j < P::NT; ++j)
+#pragma unroll
+          for (int hj = 0; hj < SUB; ++hj)
+            mma_chunk(acc[i][j][hi][hj], fb[ks & 1][SUB * j + hj], fa[n % RING][hi], T());
+      // this item's loads first, then its MFMAs, the loads spread between them
+      constexpr int R = (load_a ? SUB : 0) + (load_b ? SUB * P::NT : 0);
+      constexpr int M = SUB * SUB * P::NT;
+      unroll_steps<M>([&](auto MI) {
+        constexpr int m = decltype(MI)::value;
+        constexpr int r_lo = (m * R + M - 1) / M, r_hi = ((m + 1) * R + M - 1) / M;
+        if constexpr (r_hi > r_lo) __builtin_amdgcn_sched_group_barrier(0x100, r_hi - r_lo, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      });
+    });
+    }
+  };
   // Step kt (I = kt modulo the unroll): wait until stage kt of both rings has landed, make
   // every wave's loads visible, issue activation stage kt + DA and weight stage kt + DB into
   // the buffers step kt-1 finished reading, then multiply.  The loads of a step go out
@@ -418,7 +493,10 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     wait_vm_barrier<kWait>();
     dma_a(kt + DA, ring_a(IntC<decltype(I)::value + DA>{}));
     dma_b(kt + DB, ring_b(IntC<decltype(I)::value + DB>{}));
-    compute(ring_a(I), ring_b(I));
+    if constexpr (P::kLean)
+      compute_lean(ring_a(I), ring_b(I));
+    else
+      compute(ring_a(I), ring_b(I));
   };
 
   // prologue: the loads of steps -max(DA, DB) .. -1, issued as those steps would
@@ -552,7 +630,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_tile(
   constexpr int SA = P::kABytes, SB = P::kBBytes;
   lds_char* bb = base + P::kAStages * SA;
   // buffers past a ring's stage count are never used
-  prefill_gemm_body<T, SWIGLU, P, OutT, kLdsAlloc>(
+  prefill_gemm_body<T, SWIGLU, typename ForElt<P, T>::type, OutT, kLdsAlloc>(
       A, a_rows, B0, B1, b_expert_stride, C, col_bias, Cacc, K, N_out, e, m_begin, m_end, nt,
       k_first, k_steps, stream_b, base, base + SA, base + (P::kAStages > 2 ? 2 * SA : 0), bb,
       bb + SB, bb + (P::kBStages > 2 ? 2 * SB : 0), bb + (P::kBStages > 3 ? 3 * SB : 0));
