@@ -112,7 +112,7 @@ __device__ __attribute__((always_inline)) inline void router_logits_tile(const T
 #pragma unroll
       for (int i = 0; i < 4; ++i) part[wave * kTile + ((m * NT + n) * 4 + i) * kWave + lane] = acc[m][n][i];
   __syncthreads();
-  // thread -> (m, n, i, lane) of the tile; sum the 8 partial tiles in wave order
+  // thread -> (m, n, i, lane) of the tile; sum the W partial tiles in wave order
   for (int o = threadIdx.x; o < kTile; o += blockDim.x) {
     const int mn = o / (4 * kWave), i = (o / kWave) % 4, l = o % kWave;
     const int m = mn / NT, n = mn % NT;
@@ -160,10 +160,14 @@ hipError_t launch_router_typed(const T* x, const T* w, const float* b, float* lo
                                int64_t T_, int64_t d, int64_t E, int32_t* status_zero,
                                hipStream_t s) {
   // 16 x 64 tiles when that still gives at least 512 blocks (two per CU), else 16 x 16
-  // (larger shapes take the GEMM pipeline, see launch_router_logits).
+  // (larger shapes take the GEMM pipeline, see launch_router_logits).  With at most 512
+  // blocks of 16 x 16 (a decode step, or E = 8 with up to 8192 tokens) each CU holds one or
+  // two blocks, whose loads are all the CU has in flight: 16 waves split the reduction then.
   const int64_t t16 = (T_ + 15) / 16;
   if (E > 16 && t16 * ((E + 63) / 64) >= 512)
     return launch_router_tile<T, 1, 4, 8>(x, w, b, logits, T_, d, E, status_zero, s);
+  if (t16 * ((E + 15) / 16) <= 512)
+    return launch_router_tile<T, 1, 1, 16>(x, w, b, logits, T_, d, E, status_zero, s);
   return launch_router_tile<T, 1, 1, 8>(x, w, b, logits, T_, d, E, status_zero, s);
 }
 
