@@ -121,13 +121,28 @@ def _pmc_rows(d):
     return rows
 
 
+# The two counter runs a traffic summary is made from (repository root R on the GPU machine),
+# then the summary itself.
+TRAFFIC_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc {c} --kernel-trace "
+    "--output-format csv -d $R/gpurun_out/prof/{t}_{w} -o run -- python3 $R/bench.py "
+    "--no-cpu-baseline --steps 5 --warmup 2 --no-other-workloads --workload {w} "
+    "--copy-calibration",
+    "cd $R && python3 bench.py --workload {w} --summarize-traffic gpurun_out/prof/fetch_{w} "
+    "gpurun_out/prof/write_{w}",
+]
+
+
 def summarize_traffic(fetch_dir, write_dir, workload):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant kernel, scaled by what the
     same counters read for the calibration copy of COPY_BYTES."""
     import statistics as st
 
     out = {"workload": workload, "kernel_source_sha": kernel_source_sha(),
-           "copy_bytes": COPY_BYTES}
+           "copy_bytes": COPY_BYTES,
+           "commands": [TRAFFIC_COMMANDS[0].format(c=c, t=t, w=workload)
+                        for c, t in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))] +
+                       [TRAFFIC_COMMANDS[1].format(w=workload)]}
     for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = [r for r in _pmc_rows(d) if r["Counter_Name"] == counter]
         copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]

@@ -24,7 +24,7 @@
 //   K5b gather     x_perm[r] = x[src_token[r]] with 16-byte vector copies; empty slots
 //                  get src_token -1 (and, when padded, a zero row).  With packed rows and
 //                  no copy requested, K5 marks the empty slots and K5b is not launched.
-//   K345 fused     for at most 8192 assignments over at most 256 experts: K3-K5 (and the
+//   K345 fused     for at most 2048 assignments over at most 256 experts: K3-K5 (and the
 //                  grouped GEMMs' tile table) in one block, one launch instead of three or
 //                  four (the decode-sized and small prefill layers are launch-bound here).
 // On request the scan (or the fused kernel) also writes the grouped GEMMs' tile table from

@@ -173,11 +173,15 @@ DISPATCH_CASES = [
     (100, 1, 1, 40, 128, "f32", 0.0),
     (4096, 8, 2, 1280, 384, "bf16", 0.0),
     (1, 8, 8, 0, 128, "bf16", 0.0),
-    # around the one-block dispatch's limits (8192 assignments, 256 experts): just past the
-    # assignments (tiled), at both limits (one block), past the experts (tiled)
+    # around the one-block dispatch's limits (2048 assignments, 256 experts): at the
+    # assignments (one block), just past them (tiled), at both limits (one block), past
+    # the experts (tiled); and tiled shapes whose scan also writes the tile table
+    (1024, 8, 2, 280, 128, "bf16", 0.3),
+    (1025, 8, 2, 280, 128, "bf16", 0.3),
+    (256, 256, 8, 12, 128, "bf16", 0.05),
+    (30, 257, 4, 0, 128, "f32", 0.0),
     (4097, 8, 2, 1100, 128, "bf16", 0.3),
     (1024, 256, 8, 40, 128, "bf16", 0.05),
-    (30, 257, 4, 0, 128, "f32", 0.0),
 ]
 
 

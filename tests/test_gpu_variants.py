@@ -132,7 +132,9 @@ DISPATCH_CASES = [  # T, E, k, C, d, dtype, bias s, flags
     (3, 3, 2, 1, 128, "f32", 0.0, PAD | SLOT),
     (37, 256, 8, 0, 128, "bf16", 0.0, PAD),  # no limit: C = T slots per expert
     (100, 1, 1, 40, 128, "f32", 0.0, PAD),
-    # just past the one-block dispatch's 8192 assignments (tiled), and at them (one block)
+    # just past the one-block dispatch's 2048 assignments (tiled), and at them (one block)
+    (1030, 8, 2, 300, 128, "bf16", 0.3, SLOT),
+    (256, 256, 8, 12, 128, "bf16", 0.05, PAD | SLOT),
     (4100, 8, 2, 1100, 128, "bf16", 0.3, SLOT),
     (1024, 256, 8, 40, 128, "bf16", 0.05, PAD | SLOT),
 ]
