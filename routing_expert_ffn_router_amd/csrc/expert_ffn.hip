@@ -300,8 +300,12 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
       }
     }
 
-  // a wave whose 128-row band lies past the expert's rows skips its MFMAs
+  // a wave whose band of MT x 32 rows lies past the expert's rows skips its MFMAs; in a
+  // band that ends inside the expert's last rows, the 32-row tiles past them (mt_live and
+  // on) skip theirs (the band's waves run the partial copy of the multiply, see step)
   const bool band_live = m_begin + wm * P::MT * 32 < m_end;
+  const int mt_live = __builtin_amdgcn_readfirstlane(
+      band_live ? min(P::MT, (m_end - m_begin - wm * P::MT * 32 + 31) / 32) : 0);
   // lane l supplies row l % FR of an operand fragment and its k-chunk l / FR of the k-step
   constexpr int FR = P::kFragRows, SUB = P::kSub;
   const int frag_row = lane & (FR - 1), frag_k = lane / FR;
@@ -380,7 +384,9 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   };
   // Multiply one stage.  The reads of k-step s+1 go out between the MFMAs of k-step s (two
   // register sets), so each k-step's MFMAs cover the next k-step's LDS latency.
-  auto compute = [&](const lds_char* abuf, const lds_char* bbuf) {
+  // live: the 32-row tiles of the band that hold rows (compile-time; step picks the copy)
+  auto compute = [&](const lds_char* abuf, const lds_char* bbuf, auto live) {
+    constexpr int LIVE = decltype(live)::value;
     if (!band_live) return;
     u32x4 fa[2][SUB * P::MT], fb[2][SUB * P::NT];
     load_frags(abuf, bbuf, 0, fa[0], fb[0]);
@@ -389,7 +395,8 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
       if (ks + 1 < P::kKSteps)
         load_frags(abuf, bbuf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < P::MT; ++i)
+      for (int i = 0; i < P::MT; ++i) {
+        if (i >= LIVE) continue;
 #pragma unroll
         for (int hi = 0; hi < SUB; ++hi)
 #pragma unroll
@@ -402,6 +409,7 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
               else
                 mma32_chunk(acc[i][j], fb[ks & 1][j], fa[ks & 1][i], T());
             }
+      }
       // order: [reads of step 0]; per step, its MFMAs with the next step's reads spread
       // evenly between them (read r goes before MFMA floor(r * M / R)); measured about 1 %
       // faster on the prefill layers than issuing the reads as one burst
@@ -426,8 +434,9 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // fragments of one 32-row tile), each loaded two items (16 MFMAs of this wave) before its
   // MFMAs: 2 NT + 3 SUB fragments instead of 2 (2 MT + 2 NT).  Same products in the same
   // order per accumulator as compute().
-  auto compute_lean = [&](const lds_char* abuf, const lds_char* bbuf) {
+  auto compute_lean = [&](const lds_char* abuf, const lds_char* bbuf, auto live) {
     if constexpr (P::kLean) {
+    constexpr int LIVE = decltype(live)::value;
     if (!band_live) return;
     constexpr int KS = P::kKSteps, NI = KS * P::MT, RING = 3;
     u32x4 fb[2][SUB * P::NT], fa[RING][SUB];
@@ -461,13 +470,15 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
       constexpr bool load_b = i == 1 && ks + 1 < KS;  // the next k-step's weight fragments
       if constexpr (load_a) ld_a(nl / P::MT, nl % P::MT, fa[nl % RING]);
       if constexpr (load_b) ld_b(ks + 1, fb[(ks + 1) & 1]);
+      if constexpr (i < LIVE) {
 #pragma unroll
-      for (int hi = 0; hi < SUB; ++hi)
+        for (int hi = 0; hi < SUB; ++hi)
 #pragma unroll
-        for (int j = 0; j < P::NT; ++j)
+          for (int j = 0; j < P::NT; ++j)
 #pragma unroll
-          for (int hj = 0; hj < SUB; ++hj)
-            mma_chunk(acc[i][j][hi][hj], fb[ks & 1][SUB * j + hj], fa[n % RING][hi], T());
+            for (int hj = 0; hj < SUB; ++hj)
+              mma_chunk(acc[i][j][hi][hj], fb[ks & 1][SUB * j + hj], fa[n % RING][hi], T());
+      }
       // this item's loads first, then its MFMAs, the loads spread between them
       constexpr int R = (load_a ? SUB : 0) + (load_b ? SUB * P::NT : 0);
       constexpr int M = SUB * SUB * P::NT;
@@ -488,15 +499,15 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // its MFMAs end the step; it takes precedence over its partner wave (measured 0.3-0.6 %
   // faster on the prefill layers, the reverse order 0.8 % slower).
   if (P::kDmaSel == 1 && issuer) __builtin_amdgcn_s_setprio(3);
-  auto step = [&](int kt, auto I) {
+  auto step = [&](int kt, auto I, auto live) {
     if (kt >= KT) return;
     wait_vm_barrier<kWait>();
     dma_a(kt + DA, ring_a(IntC<decltype(I)::value + DA>{}));
     dma_b(kt + DB, ring_b(IntC<decltype(I)::value + DB>{}));
     if constexpr (P::kLean)
-      compute_lean(ring_a(I), ring_b(I));
+      compute_lean(ring_a(I), ring_b(I), live);
     else
-      compute(ring_a(I), ring_b(I));
+      compute(ring_a(I), ring_b(I), live);
   };
 
   // prologue: the loads of steps -max(DA, DB) .. -1, issued as those steps would
@@ -507,9 +518,22 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     if constexpr (v + DB >= 0) dma_b(v + DB, ring_b(IntC<v + DB>{}));
   });
   constexpr int L = SA == SB ? SA : SB % SA == 0 ? SB : SA * SB;  // the rings repeat
-  for (int kt = 0; kt < KT; kt += L) unroll_steps<L>([&](auto I) {
-    step(kt + decltype(I)::value, I);
-  });
+  // one copy of the k-loop per count of live 32-row tiles, so that no multiply tests tiles
+  // inside its MFMA stream (the wave's count is the same for every step)
+  auto k_loop = [&](auto live) {
+    for (int kt = 0; kt < KT; kt += L) unroll_steps<L>([&](auto I) {
+      step(kt + decltype(I)::value, I, live);
+    });
+  };
+  // (bf16 only: the fp32 tiles keep one copy, which fits their registers)
+  if (sizeof(T) != 2 || mt_live == P::MT || mt_live == 0) {
+    k_loop(IntC<P::MT>{});
+  } else {
+    unroll_steps<P::MT - 1>([&](auto V) {
+      constexpr int v = decltype(V)::value + 1;
+      if (mt_live == v) k_loop(IntC<v>{});
+    });
+  }
   // drain the loads issued past the last stage before the block's LDS can be reassigned
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
