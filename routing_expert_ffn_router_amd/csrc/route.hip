@@ -5,6 +5,7 @@
 // the rest: fp32 logits, softmax top-k with ties to the lower expert index, and gates
 // renormalised over the selection.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -209,6 +210,9 @@ hipError_t launch_router_logits(int dtype, const void* x, const void* w, const f
 // g's key on lane g (NG <= G); M rounds of a max-reduction over those pick the groups, and
 // the keys of experts outside them are cleared before the k rounds.
 // ---------------------------------------------------------------------------------------
+template <int N>
+using IntC32 = std::integral_constant<int, N>;
+
 __device__ inline uint32_t ordered_f32(float v) {
   if (v == 0.0f) v = 0.0f;  // -0.0 == +0.0
   const uint32_t u = __float_as_uint(v);
@@ -336,10 +340,129 @@ topk_kernel(const float* __restrict__ logits, const float* __restrict__ sel_bias
   }
 }
 
+// The same selection for groups of at most 16 lanes (E <= 256 experts, k <= 16 slots,
+// no group-limited selection): a group lies inside one 16-lane row of the wave, so its
+// reductions are DPP moves (quad_perm [1,0,3,2] and [2,3,0,1], then row_half_mirror and
+// row_mirror, which pair every lane with one lane of each larger block) instead of LDS
+// permutes.  The k rounds only keep the winning expert on slot lane j; afterwards each slot
+// lane reads its expert's logit back from the row the group has just read.  Same keys,
+// same selection; the gates' sums run in another order (within the gate tolerance).
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+template <int CTRL>
+__device__ inline float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+// op over the G lanes of a group (G a power of two <= 16, groups aligned to G lanes)
+template <int G, class V, class Dpp, class Op>
+__device__ inline V row_group_reduce(V v, Dpp dpp, Op op) {
+  if constexpr (G > 1) v = op(v, dpp(v, IntC32<0xB1>{}));
+  if constexpr (G > 2) v = op(v, dpp(v, IntC32<0x4E>{}));
+  if constexpr (G > 4) v = op(v, dpp(v, IntC32<0x141>{}));
+  if constexpr (G > 8) v = op(v, dpp(v, IntC32<0x140>{}));
+  return v;
+}
+
+template <int G, int V>
+__global__ void __launch_bounds__(256)
+topk_row_kernel(const float* __restrict__ logits, const float* __restrict__ sel_bias,
+                int64_t T_, int E, int k, int32_t* __restrict__ topk_idx,
+                float* __restrict__ topk_w, int32_t* __restrict__ status) {
+  auto d64 = [](uint64_t v, auto c) { return dpp_u64<decltype(c)::value>(v); };
+  auto d32 = [](uint32_t v, auto c) { return dpp_u32<decltype(c)::value>(v); };
+  auto df = [](float v, auto c) { return dpp_f32<decltype(c)::value>(v); };
+  // grid-stride over the groups; G divides the wave, so the loop condition is wave-uniform
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t wave0 = (int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~(kWave - 1));
+       wave0 / G < T_; wave0 += stride) {
+    const int64_t gtid = wave0 + lane_id();
+    const int64_t tok = gtid / G;
+    const int sub = (int)(gtid % G);
+    const bool active = tok < T_;
+    const float* row = logits + (active ? tok : 0) * E;
+    uint64_t key[V];
+    uint32_t bad = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = sub + v * G;
+      key[v] = 0;
+      if (active && e < E) {
+        const float val = row[e];
+        const float sv = sel_bias ? val + sel_bias[e] : val;
+        if (__builtin_isfinite(val) && __builtin_isfinite(sv))
+          key[v] = ((uint64_t)ordered_f32(sv) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+        else
+          bad = 1;
+      }
+    }
+    bad = row_group_reduce<G>(bad, d32, [](uint32_t a, uint32_t b) { return a | b; });
+    if (active && sub == 0 && bad && status) atomicAdd(status, 1);
+    int slot_e = 0;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int v = 0; v < V; ++v) best = key[v] > best ? key[v] : best;
+      best = row_group_reduce<G>(best, d64,
+                                 [](uint64_t a, uint64_t b) { return a > b ? a : b; });
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (key[v] == best) key[v] = 0;  // the unique owner retires the winning key
+      if (sub == j) slot_e = best ? (int)(0xFFFFFFFFu - (uint32_t)best) : 0;
+    }
+    const float slot_l = active && sub < k ? row[slot_e] : -__builtin_huge_valf();
+    const float m = row_group_reduce<G>(slot_l, df, [](float a, float b) { return fmaxf(a, b); });
+    const float ex = sub < k ? expf(slot_l - m) : 0.f;
+    const float inv =
+        1.0f / row_group_reduce<G>(ex, df, [](float a, float b) { return a + b; });
+    if (active && sub < k) {
+      topk_idx[tok * k + sub] = slot_e;
+      topk_w[tok * k + sub] = ex * inv;
+    }
+  }
+}
+
 hipError_t launch_topk(const float* logits, const float* sel_bias, int64_t T, int64_t E,
                        int64_t k, int n_groups, int topk_groups, int32_t* idx, float* w,
                        int32_t* status, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  // groups inside a 16-lane row: DPP reductions
+  if (!(n_groups > 1 && topk_groups < n_groups) && E <= 256 && k <= 16) {
+    int G = 1;
+    while (G < E && G < 16) G <<= 1;
+    G = G < (int)k ? (int)k : G;  // k <= 16 slot lanes
+    while (G & (G - 1)) ++G;      // (a power of two)
+    const int V = (int)((E + G - 1) / G);
+    const unsigned blocks = (unsigned)std::min<int64_t>((T * G + 255) / 256, 1 << 16);
+#define MOE_TOPK_ROW(GG, VV)                                                             \
+  topk_row_kernel<GG, VV><<<blocks, 256, 0, s>>>(logits, sel_bias, T, (int)E, (int)k,    \
+                                                 idx, w, status)
+    if (G == 1)
+      MOE_TOPK_ROW(1, 1);
+    else if (G == 2)
+      MOE_TOPK_ROW(2, 1);
+    else if (G == 4)
+      MOE_TOPK_ROW(4, 1);
+    else if (G == 8)
+      MOE_TOPK_ROW(8, 1);
+    else if (V <= 1)
+      MOE_TOPK_ROW(16, 1);
+    else if (V <= 2)
+      MOE_TOPK_ROW(16, 2);
+    else if (V <= 4)
+      MOE_TOPK_ROW(16, 4);
+    else if (V <= 8)
+      MOE_TOPK_ROW(16, 8);
+    else
+      MOE_TOPK_ROW(16, 16);
+#undef MOE_TOPK_ROW
+    return hipGetLastError();
+  }
   int G = 1;
   while (G < E && G < 64) G <<= 1;
   const int V = (int)((E + G - 1) / G);
