@@ -27,8 +27,9 @@
  *   - Errors: arguments are validated before anything is enqueued and a negative
  *     moe_status is returned on failure (nothing is launched).  A failed launch returns
  *     MOE_ERR_HIP.  T = 0 is valid.
- *   - Limits: 1 <= E <= 1024, 1 <= k <= min(E, 64), d and F multiples of 128,
- *     T * k < 2^31.
+ *   - Limits: 1 <= E <= 1024, 1 <= k <= min(E, 64), d and F multiples of 128 and at most
+ *     2^20, T * k < 2^31, and a grouped-GEMM grid (rows and columns of the shape's tiles)
+ *     within 2^32 threads; moe_workspace_size() returns 0 for a shape outside them.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -403,7 +404,8 @@ int moe_slot_counts(const moe_shape* shape, const int32_t* topk_idx, const int32
  * separately from compute": every expert is local and no all-to-all runs.  With packed
  * rows (no MOE_FLAG_PAD_TO_CAPACITY) and T * d * sizeof(dtype) < 2^31 the gate/up GEMM
  * gathers the token rows itself (moe_expert_gate_up_gathered) and the x_perm region is
- * left unwritten.  The down GEMM reuses the tile table the gate/up GEMM built.
+ * left unwritten.  The dispatch also writes the grouped GEMMs' tile table from the offsets
+ * it computes, and both GEMMs read it from the workspace.
  *   out               [T, d] dtype out
  *   routed_counts, tokens_per_expert [E] int32 out, nullable (then kept in the workspace)
  *   drops             [k+2] int32 out, nullable

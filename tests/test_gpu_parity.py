@@ -66,9 +66,12 @@ ROUTE_CASES = [(1000, 8, 2, "normal"), (37, 8, 1, "ties"), (513, 256, 8, "normal
                (50, 1, 1, "normal"), (0, 8, 2, "normal"), (70, 64, 64, "ties"),
                (200, 1024, 64, "normal"),
                # the 16-lane row groups (E <= 256, k <= 16) at their edges: k = 16 slots,
-               # E just past 16 and at 256, k past the lanes E alone would need, E = 2
+               # E just past 16 and at 256, k past the lanes E alone would need, E = 2,
+               # more tokens than the blocks' first pass; and the 64-lane groups just
+               # outside them
                (333, 17, 16, "normal"), (100, 256, 16, "ties"), (77, 5, 5, "ties"),
-               (90, 16, 9, "normal"), (91, 2, 2, "ties"), (65, 257, 8, "normal")]
+               (90, 16, 9, "normal"), (91, 2, 2, "ties"), (2100, 256, 8, "normal"),
+               (65, 257, 8, "normal")]
 
 
 @pytest.mark.parametrize("T,E,k,kind", ROUTE_CASES)
