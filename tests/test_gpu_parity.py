@@ -45,6 +45,11 @@ SMALL = {
     "f32_e2_wide_tail": W("f32_e2_wide_tail", 1750, 256, 2, 1, 384, None, "f32", 0.4),
     "bf16_e4_wide_tail_split": W("bf16_e4_wide_tail_split", 1650, 256, 4, 2, 2048, None, "bf16",
                                  0.3),
+    # 320-row tiles whose second 160-row band ends inside the expert's last rows with 1, 2,
+    # 3, 4 and 5 live 32-row tiles (kept rows [568, 432, 313, 275, 205, 230, 187, 190]): the
+    # band runs the k-loop copy that skips its empty tiles' MFMAs
+    "bf16_e8_partial_bands": W("bf16_e8_partial_bands", 2400, 256, 8, 1, 384, None, "bf16",
+                               0.4),
 }
 
 
@@ -277,7 +282,7 @@ def test_dispatch_invalid_and_duplicate_ids():
                                   "bf16_e256_k8_decode", "f32_e4_big_tiles",
                                   "bf16_e8_zipf_drops", "bf16_e3_k3", "bf16_e2_wide_tail",
                                   "f32_e2_wide_tail", "bf16_e4_wide_tail_split",
-                                  "bf16_e8_split4_down"])
+                                  "bf16_e8_split4_down", "bf16_e8_partial_bands"])
 def test_expert_ffn(name):
     w = SMALL[name]
     log(f"expert_ffn {w}")
