@@ -66,8 +66,9 @@ __device__ inline void mma_chunk(f32x4& acc, const u32x4& a, const u32x4& b, flo
 //   bf16: one v_mfma_f32_32x32x16_bf16.  On gfx950 both this instruction and the 16x16x32
 //         form sustain the full dense bf16 rate per clock (2.48 PFLOP/s over the chip on
 //         zero operands); on random data the 16x16x32 form holds a higher clock under the
-//         power limit (1.94 against 1.75 GHz in a register-only loop), but a 32x32 tile
-//         needs half its fragment registers, which the largest GEMM tile depends on.
+//         power limit (1.94 against 1.75 GHz in a register-only loop), so the prefill tiles
+//         use that form and this one serves the HBM-bound decode tiles, where the 32x32
+//         tile's fragments take half the registers.
 //   fp32: four v_mfma_f32_32x32x2_f32, element i of the chunk in the i-th one.
 // ---------------------------------------------------------------------------------------
 typedef float f32x16 __attribute__((ext_vector_type(16)));

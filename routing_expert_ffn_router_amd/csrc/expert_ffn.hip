@@ -15,7 +15,9 @@
 //     upper bound on the tile count and surplus blocks exit at once.
 //   - Operands reach LDS by direct buffer -> LDS loads in 128-byte row pieces, in a ring of
 //     stages; fragments are read with a measured bank-conflict-free swizzle and fed to
-//     32x32x16 MFMAs (the bf16 form that runs at the full dense rate on gfx950).
+//     16x16x32 MFMAs in the bf16 prefill tiles (on random data they hold a higher clock under
+//     the power limit than the 32x32x16 form) and 32x32x16 MFMAs in the decode tiles and
+//     in fp32.
 //   - Tile shapes of the same template: prefill-sized experts (mean > 32 rows) use
 //     256 x 256 tiles (128 flop per loaded byte) or, when that needs fewer row tiles or
 //     pads fewer rows, 320 x 256 tiles (142 flop per byte), an expert's short last tile
@@ -23,6 +25,8 @@
 //     keeps their pace through the shared weight panel; decode-sized experts stream
 //     weights in three stages with 64 x 256 tiles for gate/up (80 KB of weight reads in
 //     flight per CU) and 64 x 128 tiles for down (two blocks per CU).
+//   - A wave band that ends inside an expert's last rows skips the MFMAs of its empty
+//     32-row tiles (a copy of the k-loop per live-tile count).
 //   - SwiGLU: the gate and up rows of the same output columns are loaded side by side, so
 //     the gate and up accumulators of one output element sit in the same lane and the
 //     epilogue computes silu(g) * u in registers.
@@ -116,8 +120,9 @@ typedef __attribute__((address_space(3))) char lds_char;
 // (64-byte k-steps) instead of v_mfma_f32_32x32x16_bf16 (32-byte k-steps).  Same results;
 // on random data the 16x16 form holds a higher clock under the power limit (measured by
 // the calibration loop: 1.94 against 1.75 GHz), but its fragments need twice the registers
-// per k-step, which the 320-row tile does not have.  M16_ = 2: the 16x16 form for bf16
-// only (ForElt); fp32 gains nothing from it and would run short of registers.
+// per k-step: the 320-row tile runs the lean fragment schedule (kLean).  M16_ = 2: the
+// 16x16 form for bf16 only (ForElt); fp32 gains nothing from it and would run short of
+// registers.
 template <int ROWB, int STAGES, int BM_, int BNW_, int WM_, int WN_, int DSEL_ = 0,
           int BSTAGES_ = 0, int M16_ = 0>
 struct PrefillTileT {
