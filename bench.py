@@ -885,13 +885,15 @@ def main():
               flush=True)
         ceil = mfma_ceiling(moe)
         result["mfma_ceiling"] = ceil
-        # the MFMA-bound GEMMs against the rate the chip sustains under the power limit
-        top = ceil["random_bf16"]["tflops"]
+        # the MFMA-bound GEMMs against the rate the chip sustains under the power limit with
+        # the MFMA form they issue (16x16x32 in every bf16 prefill tile)
+        top = ceil["random_bf16_16x16x32"]["tflops"]
         for roof in [result["roofline"]] + [v["roofline"] for v in
                                             result.get("workloads", {}).values()]:
             if roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and roof["peak"] == \
                     PEAK_BF16_TFLOPS:
                 roof["frac_of_mfma_ceiling"] = round(roof["achieved"] / top, 4)
+                roof["mfma_ceiling_form"] = "16x16x32"
     if not args.no_cpu_baseline and not (flags or G > 1):
         ntok = args.cpu_tokens or CPU_SAMPLE_TOKENS.get(w.name, 256)
         print(f"# cpu baseline: oracle on {ntok} tokens", file=sys.stderr, flush=True)
