@@ -54,11 +54,6 @@ tile_hist_kernel(const int32_t* __restrict__ idx, int64_t total, int64_t T, int 
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(int64_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
-// One block of 1024 threads.  Thread tid = part * E + e scans part `part` of expert e's
-// tile counts (q parts per expert, q the smallest power of two >= the tile count, at most
-// the largest with q * E <= 1024), so the
-// per-expert scans over many tiles run q-wide; partial sums meet in LDS.  The threads with
-// part 0 (tid = e) then hold the kept counts in expert order for the offsets scan.
 // Tile table of row-tile height bm for the grouped GEMMs (table[0] = tile count, capped at
 // m_max; entry i = (expert, first row) at table[1 + 2i], table[2 + 2i]): expert e's rows
 // are rows[e] from row0[e] on.  Every thread of the block calls it (it holds barriers); the
@@ -75,6 +70,12 @@ __device__ inline void write_tile_table(int e, int E, int row0, int rows, int bm
   }
 }
 
+// One block of 1024 threads.  Thread tid = part * E + e scans part `part` of expert e's
+// tile counts (q parts per expert, q the smallest power of two >= the tile count, at most
+// the largest with q * E <= 1024), so the
+// per-expert scans over many tiles run q-wide; partial sums meet in LDS.  The threads with
+// part 0 (tid = e) then hold the kept counts in expert order for the offsets scan.  With
+// `table` set the block also writes the grouped GEMMs' tile table (write_tile_table).
 __global__ void __launch_bounds__(1024)
 scan_kernel(const int32_t* __restrict__ hist, int ntiles, int E, int C, int k, bool pad,
             int32_t* __restrict__ tile_base, int32_t* __restrict__ routed,
@@ -202,12 +203,13 @@ rank_kernel(const int32_t* __restrict__ idx, int64_t total, int64_t T, int te, i
 }
 
 // K3-K5 in one block of 1024 threads, for total <= kFusedPer * 1024 assignments and
-// E <= kFusedDispatchMaxE experts (dispatch_fused).  Thread tid holds the experts of visit positions c * 1024 + tid
-// (c < kFusedPer) in registers.  Pass 1 counts every expert in LDS; the block then scans
-// the kept counts into offsets (and the tile table, when asked for); pass 2 walks the
-// 1024-position chunks in visit order, ranking each assignment after the running count of
-// its expert, the earlier waves of its chunk (per-wave counts in LDS) and the earlier lanes
-// of its wave (ballots on the expert-id bits), the same positions the tiled kernels give.
+// E <= kFusedDispatchMaxE experts (dispatch_fused).  Thread tid holds the experts of visit
+// positions c * 1024 + tid (c < kFusedPer) in registers.  Pass 1 counts every expert in
+// LDS; the block then scans the kept counts into offsets (and the tile table, when asked
+// for); pass 2 walks the 1024-position chunks in visit order, ranking each assignment after
+// the running count of its expert, the earlier waves of its chunk (per-wave counts in LDS)
+// and the earlier lanes of its wave (ballots on the expert-id bits), the same positions the
+// tiled kernels give.
 // Drop counters and the per-token drop count live in LDS and are stored once at the end.
 // Invalid expert ids (outside [0, E)) are ignored by the counts and dropped, as there.
 constexpr int kFusedPer = (int)(kFusedDispatchEntries / 1024);

@@ -49,10 +49,9 @@ hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
 // layer a launch.
 // ---------------------------------------------------------------------------------------
 template <class T, int MT, int NT, int kRouterWaves>
-__device__ __attribute__((always_inline)) inline void router_logits_tile(const T* __restrict__ x, const T* __restrict__ w,
-                                          const float* __restrict__ bias,
-                                          float* __restrict__ logits, int T_, int d, int E,
-                                          int t0, int e0, float* part) {
+__device__ __attribute__((always_inline)) inline void router_logits_tile(
+    const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ logits, int T_, int d, int E, int t0, int e0, float* part) {
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
   const char* xa[MT];
