@@ -347,9 +347,16 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // With stream_b the weight loads carry the non-temporal hint: the plan sets it when each
   // weight line is read by about one tile, and then it keeps the streamed weights from
   // displacing the activation rows the other tiles reuse.
+  // With two stages in each ring every step waits for all of a wave's loads (kWait = 0),
+  // so the number of loads may vary: an activation load whose rows all lie past the
+  // expert's last row is skipped (its LDS rows feed only outputs that are never stored).
+  // A step is bound by the loads' issue and latency, so the partial tiles get cheaper.
+  constexpr bool kSkipDeadRows = SA == 2 && SB == 2 && sizeof(T) == 2;  // (bf16: fp32 keeps its registers)
+  const int m_rows = m_end - m_begin;
   auto dma = [&](int i, int kt, lds_char* buf) {
     const uint32_t koff = (uint32_t)(k_first + min(kt, KT - 1)) * P::kRowBytes;
     const int blk = (i < nA ? i : i - nA) * P::kDmaWaves;
+    if (kSkipDeadRows && i < nA && (blk + dslot) * P::kRowsPerLoad >= m_rows) return;
     const auto rsrc = buffer_rsrc(base[P::template kind_of<SWIGLU>(i)]);
     if (i >= nA && stream_b)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, buf + dma_lds + blk * 1024, 16, voff[i],
