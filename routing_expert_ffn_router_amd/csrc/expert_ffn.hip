@@ -351,7 +351,8 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // so the number of loads may vary: an activation load whose rows all lie past the
   // expert's last row is skipped (its LDS rows feed only outputs that are never stored).
   // A step is bound by the loads' issue and latency, so the partial tiles get cheaper.
-  constexpr bool kSkipDeadRows = SA == 2 && SB == 2 && sizeof(T) == 2;  // (bf16: fp32 keeps its registers)
+  // (bf16 only: the test would cost the fp32 instances registers)
+  constexpr bool kSkipDeadRows = SA == 2 && SB == 2 && sizeof(T) == 2;
   const int m_rows = m_end - m_begin;
   auto dma = [&](int i, int kt, lds_char* buf) {
     const uint32_t koff = (uint32_t)(k_first + min(kt, KT - 1)) * P::kRowBytes;
@@ -724,10 +725,14 @@ __device__ inline void dense_tile(int i, int m_tiles, int n_tiles, int group_n, 
 // in L2, so they miss; the double-width one keeps their pace.  Measured with the 320-row
 // tile: Mixtral-8x7B layer -2.8 %; experts with fewer full tiles keep PT, since with one
 // full tile (Mixtral-8x22B) the pairing's halved block count costs more than it saves.
+// When PM is shorter than P and taller than PT, an m-tile of PT::BM + 1 ... PM::BM rows (an
+// expert's last tile) runs PM: the 320-row gate/up GEMM gives such tiles the 256-row tile,
+// whose deeper weight ring hides more of the load latency that bounds a partly filled
+// tall tile (Mixtral-8x22B gate/up -2 %; its down GEMM gained nothing and keeps P).
 //
 // Dense mode (table == nullptr, used for the router logits): one operand A of dense_rows
 // rows and one B of N_out rows, m-tile mt covering rows mt * P::BM ...
-template <class T, bool SWIGLU, class P, class PT, class OutT, class PW>
+template <class T, bool SWIGLU, class P, class PT, class OutT, class PW, class PM>
 __global__ void __launch_bounds__(P::kThreads)
 prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
                     const T* __restrict__ B0, const T* __restrict__ B1,
@@ -742,9 +747,12 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
   static_assert((PW::BNW == P::BNW || PW::BNW == 2 * P::BNW) && PW::BM == PT::BM &&
                     PW::kThreads == P::kThreads,
                 "the wide tail tile spans one or two n-tiles of the full tile");
+  static_assert(PM::BNW == P::BNW && PM::kThreads == P::kThreads && PM::BM <= P::BM,
+                "the medium tile shares the n-tiling and the block size");
   extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
   // dynamic LDS of the launch (launch_prefill allocates the largest of the three tiles)
-  constexpr int kLds = std::max({P::kLdsBytes, PT::kLdsBytes, PW::kLdsBytes});
+  constexpr int kLds =
+      std::max({P::kLdsBytes, PT::kLdsBytes, PW::kLdsBytes, PM::kLdsBytes});
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   const int per_xcd = gridDim.x >> 3;
   // stages [k_first, k_first + k_steps) of the reduction: all of it, or one piece of a tail
@@ -792,6 +800,14 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
     if (m_begin >= m_end) return;
   }
   lds_char* base = (lds_char*)smem_dyn;
+  if constexpr (PM::BM < P::BM && PM::BM > PT::BM) {
+    if (table && m_end - m_begin > PT::BM && m_end - m_begin <= PM::BM) {
+      prefill_gemm_tile<T, SWIGLU, PM, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C,
+                                                   col_bias, acc, K, N_out, e, m_begin, m_end,
+                                                   nt, k_first, k_steps, stream_b != 0, base);
+      return;
+    }
+  }
   if (PT::BM < P::BM && m_end - m_begin <= PT::BM) {
     if constexpr (PW::BNW == 2 * P::BNW) {
       // at least two full tiles before (not with the tail split, whose pieces each hold
@@ -924,7 +940,7 @@ namespace {
 // tail_split > 0 (tile-table mode, no SwiGLU): the tail split with at most tail_split pieces
 // per tail tile, partial sums in c_acc, then tail_sum_kernel.
 template <class T, bool SW, class P = PrefillTile, class PT = PrefillTailTile, class OutT = T,
-          class PW = PT>
+          class PW = PT, class PM = P>
 hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const T* B1,
                           int64_t b_stride, OutT* C, int K, int N_out, const int32_t* offsets,
                           const int32_t* table, int64_t m_max, hipStream_t s, int tail_split,
@@ -943,11 +959,12 @@ hipError_t launch_prefill(const T* A, const int32_t* a_rows, const T* B0, const 
   // them) and of the pieces (at most kSplitCUs)
   const int64_t grid = tail_split > 0 ? 8 * ((m_max * n_tiles + 7) / 8 + kSplitCUs / 8)
                                       : (logical + 7) / 8 * 8;
-  const size_t lds = (size_t)std::max({P::kLdsBytes, PT::kLdsBytes, PW::kLdsBytes});
-  hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW, P, PT, OutT, PW>,
+  const size_t lds =
+      (size_t)std::max({P::kLdsBytes, PT::kLdsBytes, PW::kLdsBytes, PM::kLdsBytes});
+  hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<T, SW, P, PT, OutT, PW, PM>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  prefill_gemm_kernel<T, SW, P, PT, OutT, PW><<<(unsigned)grid, P::kThreads, lds, s>>>(
+  prefill_gemm_kernel<T, SW, P, PT, OutT, PW, PM><<<(unsigned)grid, P::kThreads, lds, s>>>(
       A, a_rows, B0, B1, b_stride, C, col_bias, c_acc, K, N_out, offsets, table, (int)m_max,
       n_tiles, group_n, (int)logical, tail_split, dense_rows, stream_b ? 1 : 0);
   if ((e = hipGetLastError()) != hipSuccess || tail_split == 0) return e;
@@ -980,7 +997,8 @@ hipError_t run_gate_up(const FfnArgs& a, const FfnPlan& p, hipStream_t s) {
         xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s, 0,
         nullptr, nullptr, 0, p.stream_b, p.group_cap);
   if (p.tile == 2)
-    return launch_prefill<T, true, PrefillTallTile, PrefillTailTile, T, PrefillTailWideTile>(
+    return launch_prefill<T, true, PrefillTallTile, PrefillTailTile, T, PrefillTailWideTile,
+                          PrefillTile>(
         xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets, a.sched, p.m_max, s, 0,
         nullptr, nullptr, 0, p.stream_b, p.group_cap);
   return launch_prefill<T, true>(xp, rows, wg, wu, stride, h, (int)a.d, (int)a.F, a.offsets,
