@@ -239,9 +239,9 @@ def _short_kernel(name):
 
     if "prefill_gemm_kernel" in name:
         # bf16 operands with an fp32 output: the router logits in dense mode (mangled: the
-        # output type f, possibly followed by a back-reference, closes the template
-        # arguments; demangled: ", float" among them)
-        if ("IDF16b" in name and re.search(r"f(?:S\d*_)?EEvPKT_", name)) or (
+        # output type f, possibly followed by back-references to the tile types, closes the
+        # template arguments; demangled: ", float" among them)
+        if ("IDF16b" in name and re.search(r"f(?:S\d*_)*EEvPKT_", name)) or (
                 "__bf16" in name and re.search(r", float[,>]", name)):
             return "prefill_gemm_kernel (router logits, dense)"
         return "prefill_gemm_kernel (" + (

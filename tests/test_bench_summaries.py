@@ -12,6 +12,13 @@ DOWN = "void moe::prefill_gemm_kernel<__bf16, false, moe::PrefillTileT<128, 2, 3
 # the same template with bf16 operands and an fp32 output: router logits in dense mode
 ROUTER = ("_ZN3moe19prefill_gemm_kernelIDF16bLb0ENS_12PrefillTileTILi128ELi3ELi64ELi128ELi2ELi4"
           "ELi0ELi0EEES2_fS2_EEvPKT_PKiS5_S5_lPT3_PKfPfiiS7_S7_iiiiiii")
+# ... with one more tile type after the output type (two back-references), and a down GEMM
+# whose output type is bf16 followed by back-references
+ROUTER_PM = ("_ZN3moe19prefill_gemm_kernelIDF16bLb0ENS_12PrefillTileTILi128ELi3ELi64ELi128ELi2ELi4"
+             "ELi0ELi0ELi0EEES2_fS2_S2_EEvPKT_PKiS5_S5_lPT3_PKfPfiiS7_S7_iiiiiii")
+DOWN_PM = ("_ZN3moe19prefill_gemm_kernelIDF16bLb0ENS_12PrefillTileTILi128ELi2ELi256ELi256ELi2ELi4"
+           "ELi1ELi3ELi1EEENS1_ILi128ELi2ELi128ELi256ELi2ELi4ELi1ELi3ELi2EEEDF16bS3_S2_EEvPKT_PKiS6_"
+           "S6_lPT3_PKfPfiiS8_S8_iiiiiii")
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -154,6 +161,8 @@ def test_kernel_names(bench):
     assert bench._short_kernel(GATE_UP) == "prefill_gemm_kernel (gate/up+SwiGLU)"
     assert bench._short_kernel(DOWN) == "prefill_gemm_kernel (down)"
     assert bench._short_kernel(ROUTER) == "prefill_gemm_kernel (router logits, dense)"
+    assert bench._short_kernel(ROUTER_PM) == "prefill_gemm_kernel (router logits, dense)"
+    assert bench._short_kernel(DOWN_PM) == "prefill_gemm_kernel (down)"
     assert bench._short_kernel("_ZN3moe14combine_kernelIDF16bEEvPKT_") == "moe::combine_kernel"
     assert (bench._short_kernel("_ZN12_GLOBAL__N_116mfma_rate_kernelILi0EEEvijiPfPy")
             == "mfma_rate_kernel (calibration, 32x32x16)")
