@@ -121,15 +121,15 @@ def _pmc_rows(d):
     return rows
 
 
-# The two counter runs a traffic summary is made from (repository root R on the GPU machine),
-# then the summary itself.
+# The two counter runs a traffic summary is made from (R: the repository root, OUT: the folder,
+# relative to R, that receives the profiler's output), then the summary itself.
 TRAFFIC_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 150 rocprofv3 --pmc {c} --kernel-trace "
-    "--output-format csv -d $R/gpurun_out/prof/{t}_{w} -o run -- python3 $R/bench.py "
+    "--output-format csv -d $R/$OUT/prof/{t}_{w} -o run -- python3 $R/bench.py "
     "--no-cpu-baseline --steps 5 --warmup 2 --no-other-workloads --workload {w} "
     "--copy-calibration",
-    "cd $R && python3 bench.py --workload {w} --summarize-traffic gpurun_out/prof/fetch_{w} "
-    "gpurun_out/prof/write_{w}",
+    "cd $R && python3 bench.py --workload {w} --summarize-traffic $OUT/prof/fetch_{w} "
+    "$OUT/prof/write_{w}",
 ]
 
 
@@ -665,7 +665,7 @@ def cf_sweep(moe, w, args_l, factors, K, W, dtype) -> list:
 
 
 def vendor_reference(w, N, reps=10) -> dict:
-    """Reference points on the same box, outside the layer: hipBLASLt (through torch.matmul,
+    """Reference points on the same GPU, outside the layer: hipBLASLt (through torch.matmul,
     plain 2-D products of contiguous bf16 operands) on the dense equivalents of the two
     grouped GEMMs (all N kept rows against one expert-sized weight, an easier shape than
     the grouped one), and a 1 GiB device-to-device copy as the attainable HBM rate."""
