@@ -1,8 +1,9 @@
 // Calibration of the bf16 MFMA roofline on this GPU: the rate the chip sustains when every
 // SIMD issues nothing but independent bf16 MFMAs (32x32x16, or 16x16x32 for comparison) on
-// register operands, and the shader clock it holds meanwhile.  The published dense peak (2.5 PFLOP/s) assumes the full
-// 2.4 GHz clock; under load the clock is set by the power limit, and the data the multipliers
-// see moves it: random operands draw more power than zeros.  The GEMM kernels are measured
+// register operands, and the shader clock it holds meanwhile.  The published dense peak
+// (2.5 PFLOP/s) assumes the full 2.4 GHz clock; under load the clock is set by the power
+// limit, and the data the multipliers see moves it: random operands draw more power than
+// zeros.  The GEMM kernels are measured
 // against the published peak; this gives the ceiling beside it.
 #include <stdint.h>
 

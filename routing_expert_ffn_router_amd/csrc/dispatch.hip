@@ -471,8 +471,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     int64_t blocks = (a.R + 3) / 4;
     if (blocks > 4096) blocks = 4096;
     gather_rows_kernel<<<(unsigned)blocks, 256, 0, s>>>(
-        (const char*)a.x, a.src_token, a.src_slot, a.offsets, a.kept, (int)a.E, (int)a.C, a.pad, a.R,
-        a.d * a.elt_bytes, (char*)a.x_perm);
+        (const char*)a.x, a.src_token, a.src_slot, a.offsets, a.kept, (int)a.E, (int)a.C, a.pad,
+        a.R, a.d * a.elt_bytes, (char*)a.x_perm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;

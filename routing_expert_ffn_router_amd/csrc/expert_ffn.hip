@@ -238,9 +238,9 @@ template <class T, bool SWIGLU, class P, class OutT, int kLdsAlloc>
 __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
     const T* __restrict__ A, const int32_t* __restrict__ a_rows, const T* __restrict__ B0,
     const T* __restrict__ B1, int64_t b_expert_stride, OutT* __restrict__ C,
-    const float* __restrict__ col_bias, float* __restrict__ Cacc, int K, int N_out, int e, int m_begin, int m_end, int nt,
-    int k_first, int k_steps, bool stream_b, lds_char* __restrict__ a0,
-    lds_char* __restrict__ a1,
+    const float* __restrict__ col_bias, float* __restrict__ Cacc, int K, int N_out, int e,
+    int m_begin, int m_end, int nt, int k_first, int k_steps, bool stream_b,
+    lds_char* __restrict__ a0, lds_char* __restrict__ a1,
     lds_char* __restrict__ a2, lds_char* __restrict__ b0, lds_char* __restrict__ b1,
     lds_char* __restrict__ b2, lds_char* __restrict__ b3) {
   constexpr int BN = SWIGLU ? P::BNW / 2 : P::BNW;
@@ -255,11 +255,11 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // up rows of the same output columns after them.  Each load fills one block of
   // kRowsPerLoad rows; load i of issuing wave `dslot` fills block i * kDmaWaves + dslot of
   // the concatenated rows (activations, then weights), so the operand a load reads
-  // (kind_of(i)) is the same for every issuing wave and known at compile time.  Each operand is addressed
-  // through a buffer resource based at the tile's first row: a lane's source is a 32-bit
-  // offset (row within the tile, clamped to the valid rows, times the row pitch, plus its
-  // swizzled chunk) and the stage's k offset is a scalar.  Clamped rows are loaded but
-  // their results never stored.
+  // (kind_of(i)) is the same for every issuing wave and known at compile time.  Each
+  // operand is addressed through a buffer resource based at the tile's first row: a lane's
+  // source is a 32-bit offset (row within the tile, clamped to the valid rows, times the row
+  // pitch, plus its swizzled chunk) and the stage's k offset is a scalar.  Clamped rows are
+  // loaded but their results never stored.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const bool issuer = P::kDmaSel == 0 || wave_u >= 4;
   const int dslot = P::kDmaSel == 0 ? wave_u : wave_u - 4;
@@ -553,10 +553,11 @@ __device__ __attribute__((always_inline)) inline void prefill_gemm_body(
   // Epilogue.  The weight fragment is the MFMA's first operand, so each accumulator tile
   // is the transposed product: lane L holds activation row L % 32 of the 32 and, in
   // acc[.][.][4a + b], output column 8a + 4 (L / 32) + b; with 16x16 tiles, activation row
-  // 16 hi + L % 16 and, in acc[.][.][hi][a][b], output column 16a + 4 (L / 16) + b.  The block's outputs go through
-  // LDS in row-major order (4 consecutive columns per lane write) and leave it as 16-byte
-  // stores that cover whole cache lines; storing one element per lane per instruction
-  // straight from the accumulators took 7-17 % of a tile's time (measured per block).
+  // 16 hi + L % 16 and, in acc[.][.][hi][a][b], output column 16a + 4 (L / 16) + b.  The
+  // block's outputs go through LDS in row-major order (4 consecutive columns per lane
+  // write) and leave it as 16-byte stores that cover whole cache lines; storing one element
+  // per lane per instruction straight from the accumulators took 7-17 % of a tile's time
+  // (measured per block).
   // A piece of a split reduction stores its fp32 partial sums the same way.
   __syncthreads();  // every wave's direct loads have landed and its fragment reads are done
   constexpr int NOUT = SWIGLU ? P::NT / 2 : P::NT;
@@ -825,9 +826,9 @@ prefill_gemm_kernel(const T* __restrict__ A, const int32_t* __restrict__ a_rows,
                                            acc, K, N_out, e, m_begin, m_end, nt,
                                            k_first, k_steps, stream_b != 0, base);
   } else
-    prefill_gemm_tile<T, SWIGLU, P, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C, col_bias, acc,
-                                          K, N_out, e, m_begin, m_end, nt, k_first,
-                                          k_steps, stream_b != 0, base);
+    prefill_gemm_tile<T, SWIGLU, P, OutT, kLds>(A, a_rows, B0, B1, b_expert_stride, C,
+                                                col_bias, acc, K, N_out, e, m_begin, m_end,
+                                                nt, k_first, k_steps, stream_b != 0, base);
 }
 
 // The tail tiles of a tail-split down GEMM: tile i (dense number whole + i) is the sum of

@@ -110,7 +110,8 @@ __device__ __attribute__((always_inline)) inline void router_logits_tile(
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part[wave * kTile + ((m * NT + n) * 4 + i) * kWave + lane] = acc[m][n][i];
+      for (int i = 0; i < 4; ++i)
+        part[wave * kTile + ((m * NT + n) * 4 + i) * kWave + lane] = acc[m][n][i];
   __syncthreads();
   // thread -> (m, n, i, lane) of the tile; sum the W partial tiles in wave order
   for (int o = threadIdx.x; o < kTile; o += blockDim.x) {
