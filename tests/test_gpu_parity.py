@@ -690,3 +690,51 @@ def test_down_tail_split_whole_and_pieces():
     err = rel_err(to_host(ys[0]), ref)
     log(f"  down tail split (256 whole + 64 x 2 pieces): rel err {err:.3e}")
     assert err <= OUT_TOL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_last_tile_heights_in_tall_plan(dtype):
+    # Every kind of last row tile a 320-row plan runs, from explicit expert offsets: T = 3480,
+    # k = 1, E = 12, no capacity limit gives a mean of 290 rows, which the plan covers with
+    # one 320-row tile rather than two 256-row ones.  The counts put each boundary in a last
+    # tile: 0, 1 and 128 rows (the 128-row tile), 129, 200 and 256 rows (the gate/up GEMM's
+    # 256-row tile; the down GEMM keeps the 320-row one), 257 and 320 rows (a partly filled
+    # and a full 320-row tile), 321 (a 1-row tail), 449 and 576 (129- and 256-row tails behind
+    # one full tile), and 740 (a 100-row tail behind two full tiles: the double-width tile).
+    # d = 384 leaves a half n-tile in the down GEMM.  Outputs against the oracle.
+    T, d, E, k, F = 3480, 384, 12, 1, 512
+    counts = np.array([128, 129, 256, 257, 320, 321, 449, 576, 0, 1, 200, 740])
+    assert counts.sum() <= T * k
+    mean = T * k // E
+    r = mean + mean // 20
+    assert -(-r // 320) < -(-r // 256)  # the plan takes the 320-row tile
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    s = moe.shape(T, d, E, k, F, 0, moe.MOE_BF16 if dtype == "bf16" else moe.MOE_F32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(offsets[-1])
+    rng = np.random.default_rng(91)
+    if dtype == "bf16":
+        cast = lambda a: mi.bf16_bits_to_f32(mi.bf16_rne_np(a.astype(np.float32)))  # noqa: E731
+    else:
+        cast = lambda a: a.astype(np.float32)  # noqa: E731
+    xp = np.zeros((moe.max_rows(s), d), np.float32)
+    xp[:N] = cast(rng.standard_normal((N, d)))
+    wg = cast(rng.standard_normal((E, F, d)) / np.sqrt(d))
+    wu = cast(rng.standard_normal((E, F, d)) / np.sqrt(d))
+    wd = cast(rng.standard_normal((E, d, F)) / np.sqrt(F))
+    ws = torch.empty(moe.workspace_size(s), dtype=torch.uint8, device="cuda")
+    y = torch.zeros((xp.shape[0], d), dtype=tdt, device="cuda")
+    log(f"last tile heights {dtype}: counts {counts.tolist()}")
+    moe.expert_ffn(s, to_device(xp, tdt), to_device(offsets, torch.int32), to_device(wg, tdt),
+                   to_device(wu, tdt), to_device(wd, tdt), ws, y)
+    torch.cuda.synchronize()
+    ref = oracle.expert_ffn(xp[:N], offsets, wg, wu, wd)
+    out = to_host(y[:N])
+    assert np.all(np.isfinite(out))
+    tol = 1e-5 if dtype == "f32" else OUT_TOL
+    for e in range(E):  # per expert, so a wrong tile path names its expert
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            err = rel_err(out[lo:hi], ref[lo:hi])
+            assert err <= tol, (e, int(counts[e]), err)
+    log(f"  rel err {rel_err(out, ref):.3e}")
