@@ -244,12 +244,17 @@ LAYER_CASES = [
     ("bf16_e256_k8_drops", SEL, 8, 4),
     ("bf16_e256_k8_decode", PAD, 0, 0),
     ("tiny_f32", PAD | SLOT | SEL, 2, 1),
+    # C = 560 padded rows per expert: the plan takes the 320-row tile and every expert's
+    # last tile holds 240 rows (the gate/up GEMM's 256-row tile, a partly filled 320-row
+    # tile in the down GEMM)
+    ("bf16_e8_tall_pad", PAD, 0, 0),
 ]
 SMALL = {
     "tiny_f32": mi.WORKLOADS["tiny_f32"],
     "bf16_e8_zipf_drops": W("bf16_e8_zipf_drops", 700, 256, 8, 2, 640, 1.25, "bf16", 1.1),
     "bf16_e256_k8_drops": W("bf16_e256_k8_drops", 512, 256, 256, 8, 256, 1.0, "bf16", 0.05),
     "bf16_e256_k8_decode": W("bf16_e256_k8_decode", 37, 512, 256, 8, 384, None, "bf16"),
+    "bf16_e8_tall_pad": W("bf16_e8_tall_pad", 1792, 256, 8, 2, 384, 1.25, "bf16", 1.1),
 }
 
 
