@@ -16,8 +16,9 @@ kernel, from which the roofline fraction is computed.  The CPU oracle, timed on 
 sample of the same workload, is reported as a baseline.  The default run also times the other
 workloads, sweeps the capacity factor of the skewed Mixtral-8x22B layer, and reports reference
 points measured on the same GPU outside the timed region: hipBLASLt on the dense equivalents
-of the two GEMMs, a device copy, and the bf16 MFMA rate and clock the chip sustains
-(--mfma-ceiling).
+of the two GEMMs, a device copy, the bf16 MFMA rate and clock the chip sustains
+(--mfma-ceiling), and the socket power and graphics clock while the layer and that MFMA loop
+run (--power).
 """
 from __future__ import annotations
 
@@ -88,6 +89,10 @@ def parse():
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                         "script into profiles/traffic_<workload>.json and exit")
+    p.add_argument("--power", action="store_true",
+                   help="only record socket power and graphics clock (driver metrics) while "
+                        "the GPU idles, loops the headline layer, the MFMA calibration loop "
+                        "and the decode layer, then exit")
     return p.parse_args()
 
 
@@ -706,6 +711,126 @@ def vendor_reference(w, N, reps=10) -> dict:
     return out
 
 
+class PowerSampler:
+    """Socket power and graphics clock of this GPU from the driver's metrics table (amdsmi
+    getters only; nothing is set), polled in a background thread.  The driver refreshes
+    the table about once a second, so each phase loops its work for several seconds and is
+    summarised over the refreshes that fall inside it."""
+
+    def __init__(self):
+        import threading
+
+        import amdsmi
+        import torch
+
+        self.smi = amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        props = torch.cuda.get_device_properties(torch.cuda.current_device())
+        want = "%04x:%02x:%02x" % (getattr(props, "pci_domain_id", 0),
+                                   getattr(props, "pci_bus_id", 0),
+                                   getattr(props, "pci_device_id", 0))
+        match = [h for h in handles
+                 if str(amdsmi.amdsmi_get_gpu_device_bdf(h)).lower().startswith(want)]
+        if not match and len(handles) != 1:
+            raise RuntimeError(f"no metrics handle for the GPU at {want}")
+        self.h = (match or handles)[0]
+        self.cap_w = amdsmi.amdsmi_get_power_cap_info(self.h)["power_cap"] / 1e6
+        self.samples, self.marks = [], []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+        self._t.start()
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+                clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int)]
+                if not clks and isinstance(m.get("current_gfxclk"), int):
+                    clks = [m["current_gfxclk"]]
+                self.samples.append((time.time(), m.get("current_socket_power"),
+                                     statistics.mean(clks) if clks else None,
+                                     m.get("temperature_hotspot")))
+            except Exception:  # noqa: BLE001  (a missed poll is retried)
+                pass
+            time.sleep(0.02)
+
+    def phase(self, name, work, seconds):
+        """Run work() (which enqueues a batch and synchronises) until `seconds` have passed."""
+        t0 = time.time()
+        while time.time() - t0 < seconds:
+            work()
+        self.marks.append((name, t0, time.time()))
+
+    def close(self) -> dict:
+        self._stop.set()
+        self._t.join()
+        return summarize_power(self.samples, self.marks, self.cap_w)
+
+
+def summarize_power(samples, marks, cap_w) -> dict:
+    """Per phase (name, t0, t1) of marks: the median socket power and graphics clock over the
+    metric-table refreshes inside it.  samples: (time, power W, clock MHz, hotspot C) polls;
+    consecutive polls that read the same power and clock are one refresh.  The first second
+    of a phase is skipped: the table read then may still describe the time before it."""
+    out = {"power_cap_w": cap_w, "source": "amdsmi gpu metrics (refreshed about once a second)"}
+    for name, t0, t1 in marks:
+        rows, prev = [], None
+        for s in samples:
+            if t0 + 1.1 <= s[0] <= t1 and (s[1], s[2]) != prev:
+                rows.append(s)
+                prev = (s[1], s[2])
+        pw = [r[1] for r in rows if isinstance(r[1], (int, float))]
+        ck = [r[2] for r in rows if isinstance(r[2], (int, float))]
+        tp = [r[3] for r in rows if isinstance(r[3], (int, float))]
+        p = statistics.median(pw) if pw else None
+        out[name] = {"seconds": round(t1 - t0, 2), "refreshes": len(rows),
+                     "socket_power_w": p,
+                     "frac_of_cap": round(p / cap_w, 3) if p is not None and cap_w else None,
+                     "gfx_clock_mhz": round(statistics.median(ck)) if ck else None,
+                     "hotspot_c_max": max(tp) if tp else None}
+    return out
+
+
+def power_clock(moe, w, s, args_l, decode=None) -> dict:
+    """Socket power and graphics clock: idle, the layer of shape s looped, the 16x16x32 MFMA
+    calibration loop on random operands, and (decode = (shape, args)) an HBM-bound layer."""
+    import torch
+
+    ps = PowerSampler()
+    ps.phase("idle", lambda: time.sleep(0.1), 2.5)
+    lay = moe.MoELayer(s)
+
+    def layer_batch(lay=lay, a=args_l):
+        for _ in range(50):
+            lay(*a)
+        torch.cuda.synchronize()
+
+    ps.phase(f"layer {w.name}", layer_batch, 5.0)
+    del lay
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus * 8, dtype=torch.float32, device="cuda")
+    cyc = torch.zeros(2 * cus, dtype=torch.int64, device="cuda")
+
+    def calib_batch():
+        for r in range(10):
+            moe.calib_mfma(cus, 300_000, 2000 + r, True, sink, cyc, shape=1)
+        torch.cuda.synchronize()
+
+    ps.phase("mfma calibration loop, 16x16x32 random", calib_batch, 4.0)
+    if decode is not None:
+        lay_d = moe.MoELayer(decode[0])
+
+        def decode_batch():
+            for _ in range(50):
+                lay_d(*decode[1])
+            torch.cuda.synchronize()
+
+        ps.phase("layer dsv3_decode", decode_batch, 4.0)
+        del lay_d
+    return ps.close()
+
+
 def mfma_ceiling(moe, iters=300_000, reps=5, operands=("random", "zero")) -> dict:
     """The bf16 MFMA rate this GPU sustains with every SIMD of every CU issuing nothing but
     independent 32x32x16 MFMAs on register operands (libmoe_calib.so), and the shader clock
@@ -783,6 +908,16 @@ def main():
         ops = {"both": ("random", "zero"), "random": ("random",), "zero": ("zero",)}
         print(json.dumps({"mfma_ceiling": mfma_ceiling(moe, operands=ops[args.mfma_ceiling])}),
               flush=True)
+        return
+    if args.power:  # the power and clock record alone
+        w = mi.WORKLOADS[DEFAULT_WORKLOAD]
+        s = moe.shape(w.T, w.d, w.E, w.k, w.F, moe.capacity(w.T, w.k, w.E, w.capacity_factor),
+                      moe.MOE_BF16)
+        wd = mi.WORKLOADS["dsv3_decode"]
+        sd = moe.shape(wd.T, wd.d, wd.E, wd.k, wd.F,
+                       moe.capacity(wd.T, wd.k, wd.E, wd.capacity_factor), moe.MOE_BF16)
+        rec = power_clock(moe, w, s, device_inputs(w), decode=(sd, device_inputs(wd)))
+        print(json.dumps({"power_clock": rec}), flush=True)
         return
     w = mi.WORKLOADS[args.workload]
     cf = w.capacity_factor if args.capacity_factor is None else (
@@ -894,6 +1029,14 @@ def main():
                     PEAK_BF16_TFLOPS:
                 roof["frac_of_mfma_ceiling"] = round(roof["achieved"] / top, 4)
                 roof["mfma_ceiling_form"] = "16x16x32"
+        # socket power and graphics clock while the headline layer and the calibration loop
+        # run (driver metrics): whether the power cap sets the clock
+        print("# power and clock record", file=sys.stderr, flush=True)
+        try:
+            result["power_clock"] = power_clock(moe, w, s, device_inputs(w))
+        except Exception as e:  # noqa: BLE001  (the record is optional, the run is not)
+            result["power_clock"] = {"error": f"{type(e).__name__}: {e}"}
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline and not (flags or G > 1):
         ntok = args.cpu_tokens or CPU_SAMPLE_TOKENS.get(w.name, 256)
         print(f"# cpu baseline: oracle on {ntok} tokens", file=sys.stderr, flush=True)

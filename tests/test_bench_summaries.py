@@ -170,3 +170,24 @@ def test_kernel_names(bench):
             == "mfma_rate_kernel (calibration, 16x16x32)")
     assert bench._short_kernel(COPY) == COPY
     assert bench._short_kernel("Cijk_Ailk_Bljk_BBS_BH_UserArgs") == "hipBLASLt GEMM (vendor reference)"
+
+
+def test_power_summary(bench):
+    """Polls that repeat one metric-table read count once; the first second of a phase and
+    polls outside it are left out; unavailable fields ('N/A') are skipped."""
+    samples = [(0.5, 240, 150.0, 45),      # before the phase
+               (10.2, 900, 1300.0, 50),    # first second of the phase: skipped
+               (11.2, 1376, 1972.5, 54), (11.25, 1376, 1972.5, 54), (11.3, 1376, 1972.5, 54),
+               (12.2, 1390, 1960.0, 56),
+               (13.2, 1380, "N/A", "N/A"),
+               (15.0, 300, 200.0, 40)]     # after the phase
+    out = bench.summarize_power(samples, [("layer", 10.0, 13.5)], 1400.0)
+    rec = out["layer"]
+    assert rec["refreshes"] == 3
+    assert rec["socket_power_w"] == 1380
+    assert rec["frac_of_cap"] == round(1380 / 1400.0, 3)
+    assert rec["gfx_clock_mhz"] == round((1972.5 + 1960.0) / 2)
+    assert rec["hotspot_c_max"] == 56
+    assert out["power_cap_w"] == 1400.0
+    empty = bench.summarize_power([], [("idle", 0.0, 2.0)], 1400.0)["idle"]
+    assert empty["refreshes"] == 0 and empty["socket_power_w"] is None
