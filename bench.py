@@ -764,8 +764,8 @@ class PowerSampler:
 
     def close(self) -> dict:
         self._stop.set()
-        self._t.join()
-        return summarize_power(self.samples, self.marks, self.cap_w)
+        self._t.join(timeout=5.0)  # a poll stuck in the driver must not hold the run
+        return summarize_power(list(self.samples), self.marks, self.cap_w)
 
 
 def summarize_power(samples, marks, cap_w) -> dict:
