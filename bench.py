@@ -765,6 +765,11 @@ class PowerSampler:
     def close(self) -> dict:
         self._stop.set()
         self._t.join(timeout=5.0)  # a poll stuck in the driver must not hold the run
+        if not self._t.is_alive():
+            try:
+                self.smi.amdsmi_shut_down()
+            except Exception:  # noqa: BLE001  (the record is complete either way)
+                pass
         return summarize_power(list(self.samples), self.marks, self.cap_w)
 
 
